@@ -1,0 +1,258 @@
+"""Benchmark of the selective scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+
+A step is one ss_fwd call over the Mamba-2.8B-shaped batch (B=8, L=2048,
+D=5120, N=16, bf16 u/delta/B/C/z/y, f32 A/D/delta_bias), inputs resident in
+HBM.  The value is forward state-updates/s (B*L*D*N per step / step time).
+The same line carries the HBM rate of the algorithmic bytes, the roofline of
+the scan kernel, the backward (ss_bwd on the B=2, L=2048, D=2048, N=16 f32
+workload), and the CPU oracle's rate on the host cores.  Prints ONE JSON line
+on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (256 CUs x 2.4 GHz x 256 flop/clk)
+# Algorithmic flops of one state update: dt*A (1), exp (1), (dt*u)*B (1),
+# a*h + x (2), h*C accumulated (2).
+FLOPS_PER_UPDATE = 7
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "mamba_selective_scan_02_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(tag: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
+    if the kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{tag}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_sources_sha:\s*(\S+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_sources_sha():
+        return None
+    return float(m_b.group(1))
+
+
+def algorithmic_bytes(w) -> int:
+    """Every input read once and every output written once."""
+    io = 4 if w.io_dtype == "f32" else 2
+    pa = 4 if w.param_dtype == "f32" else 2
+    B, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+    bld = B * L * D
+    n_in_bld = 2 + (1 if w.has_z else 0)              # u, delta, z
+    n_out_bld = 1                                      # y
+    nbytes = (n_in_bld + n_out_bld) * bld * io + 2 * B * L * N * io + D * N * pa
+    nbytes += D * pa * ((1 if w.has_D else 0) + (1 if w.has_bias else 0))
+    if w.last_state:
+        nbytes += B * D * N * pa
+    return nbytes
+
+
+def algorithmic_bytes_bwd(w) -> int:
+    io = 4 if w.io_dtype == "f32" else 2
+    pa = 4 if w.param_dtype == "f32" else 2
+    B, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+    bld = B * L * D
+    n_in = 3 + (1 if w.has_z else 0)                   # u, delta, dy, z
+    n_out = 2 + (1 if w.has_z else 0)                  # du, ddelta, dz
+    nbytes = (n_in + n_out) * bld * io + 4 * B * L * N * io + 2 * D * N * pa
+    nbytes += 2 * D * pa * ((1 if w.has_D else 0) + (1 if w.has_bias else 0))
+    return nbytes
+
+
+def time_calls(fn, steps: int, warmup: int):
+    """Average duration of fn() over `steps` back-to-back calls, from HIP events
+    recorded on the stream the kernels are launched on."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The oracle (float64 C loop, threaded over channels) on the host cores,
+    on a bounded sample of the same workload: the first channels of every
+    batch row, all time steps, sized to take about `budget_s` seconds."""
+    import numpy as np
+    import oracle
+    keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
+    cores = oracle.default_threads()
+    Bn, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+    # calibration run on a few channels, then the sized sample
+    probe = min(D, max(cores, 8))
+    cb = np.repeat(np.arange(Bn), probe)
+    cd = np.tile(np.arange(probe), Bn)
+    t0 = time.perf_counter()
+    oracle.fwd_channels(**{k: inp[k] for k in keys}, chan_b=cb, chan_d=cd, nthreads=cores)
+    dt = time.perf_counter() - t0
+    per_chan = dt / cb.size
+    nd = int(min(D, max(1, budget_s / per_chan / Bn)))
+    cb = np.repeat(np.arange(Bn), nd)
+    cd = np.tile(np.arange(nd), Bn)
+    t0 = time.perf_counter()
+    oracle.fwd_channels(**{k: inp[k] for k in keys}, chan_b=cb, chan_d=cd, nthreads=cores)
+    dt = time.perf_counter() - t0
+    updates = cb.size * L * N
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": updates / dt, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cb.size} of {Bn * D} channels (first {nd} channels of each of the "
+                      f"{Bn} batch rows), all {L} steps, N={N}: {updates:.3e} updates in "
+                      f"{dt:.1f} s on {cpu}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the "
+              "selective scan is timed at N=1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mamba_selective_scan_02_amd as ss
+    from ss_inputs import WORKLOADS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
+    w = WORKLOADS["m2p8b"]
+    log(f"generating {w.name} inputs")
+    inp = make_inputs(w)
+    dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    args_f = [dev[k] for k in keys]
+    y = torch.empty_like(dev["u"])
+    desc = ss.SsDesc(w.batch, w.seqlen, w.dim, w.dstate, 1, 2, 0, 0)
+    plan = ss.plan(desc)
+    ws = torch.empty(max(1, ss.workspace_size(desc)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ss.fwd(*args_f, y=y, workspace=ws)
+
+    log(f"timing forward: warmup {args.warmup}, steps {args.steps}")
+    ms, wall = time_calls(step, args.steps, args.warmup)
+    updates = w.updates
+    value = updates / (ms * 1e-3)
+    abytes = algorithmic_bytes(w)
+    gbs = abytes / (ms * 1e-3) / 1e9
+    tflops = FLOPS_PER_UPDATE * value / 1e12
+    log(f"forward {ms * 1e3:.1f} us/step, {value:.3e} updates/s, {gbs:.0f} GB/s")
+
+    result = {
+        "metric": "selective_scan fwd state-updates/s and HBM GB/s (% of peak), 1 MI355X",
+        "value": value,
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Mamba-2.8B-shaped selective_scan forward: B=8, L=2048, D=5120, "
+                               "N=16, bf16 u/delta/B/C/z/y, f32 A/D/delta_bias, softplus on",
+                   "batch": w.batch, "seq_len": w.seqlen, "dim": w.dim, "dstate": w.dstate,
+                   "io_dtype": w.io_dtype, "param_dtype": w.param_dtype,
+                   "n_chunks": plan.n_chunks, "kernels_per_step": plan.n_launches},
+        "hbm_gbs": gbs,
+        "hbm_frac": gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes": abytes,
+        "roofline": {"bound": "alu", "kernel": "fwd_scan (single pass)",
+                     "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / FP32_VECTOR_PEAK_TFLOPS,
+                     "flops_per_update": FLOPS_PER_UPDATE,
+                     "traffic": stored_traffic("fwd_scan_m2p8b"),
+                     "hbm_achieved_gbs": gbs, "hbm_peak_gbs": HBM_PEAK_GBS},
+        "wall_s": wall,
+    }
+    del y, ws
+
+    if not args.no_bwd:
+        wb = WORKLOADS["bwd"]
+        log("generating bwd inputs")
+        ib = make_inputs(wb)
+        db = {k: (None if v is None else v.cuda()) for k, v in ib.items()}
+        descb = ss.SsDesc(wb.batch, wb.seqlen, wb.dim, wb.dstate, 1, 0, 0, 0)
+        wsb = torch.empty(max(1, ss.workspace_size(descb, True)), dtype=torch.uint8,
+                          device="cuda")
+        argsb = [db[k] for k in keys]
+
+        def bstep():
+            ss.bwd(*argsb, dy=db["dy"], workspace=wsb)
+
+        bsteps = max(3, args.steps // 2)
+        log(f"timing backward: steps {bsteps}")
+        bms, _ = time_calls(bstep, bsteps, max(1, args.warmup))
+        bb = algorithmic_bytes_bwd(wb)
+        result["backward"] = {
+            "workload": "B=2, L=2048, D=2048, N=16, f32, D/z/delta_bias, dy",
+            "ms_per_call": bms, "state_updates_per_s": wb.updates / (bms * 1e-3),
+            "hbm_gbs": bb / (bms * 1e-3) / 1e9, "hbm_frac": bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": bb,
+            "n_kernels": ss.plan(descb, True).n_launches,
+            "traffic": stored_traffic("ss_bwd_bwd"),
+        }
+        log(f"backward {bms * 1e3:.1f} us/call")
+        del wsb, db
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

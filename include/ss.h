@@ -1,0 +1,126 @@
+/* Mamba-1 selective scan for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * Operation (baracuda-kernels page "src/attention/selective_scan.rs", module
+ * docs, section "Algorithm summary"), per batch b, channel d and state n:
+ *
+ *     x        = delta[b,t,d] + delta_bias[d]            (bias optional)
+ *     dt       = softplus(x) = log(1 + e^x)  if delta_softplus, else x
+ *     a        = exp(dt * A[d,n])
+ *     h[n]     = a * h[n] + dt * B[b,t,n] * u[b,t,d]     (h = 0 before t = 0)
+ *     o        = sum_n C[b,t,n] * h[n] + D[d] * u[b,t,d] (D optional)
+ *     y[b,t,d] = o * z * sigmoid(z), z = z[b,t,d]       (z optional)
+ *     last_state[b,d,n] = h[n] after t = L-1            (optional)
+ *
+ * Layouts (same page, "Shape contract"): every tensor is contiguous
+ * row-major; u, delta, z, y, dy, du, ddelta, dz are [B, L, D]; A and dA are
+ * [D, N]; B, C, dB, dC are [B, L, N]; D, delta_bias, dD, ddelta_bias are
+ * [D]; last_state is [B, D, N].
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller (workspace included).
+ *    The library allocates no memory, keeps no state between calls, is
+ *    reentrant, enqueues work only on the given stream (a hipStream_t; NULL
+ *    means the default stream) and never synchronises.  Calls return after
+ *    enqueueing; results are ready when the stream reaches that point.
+ *  - Validation happens before anything is enqueued; on any error nothing is
+ *    written.  Status codes follow the page's error variants
+ *    (InvalidProblem, Unsupported, WorkspaceTooSmall); SS_ERR_HIP reports a
+ *    failed kernel launch.  ss_last_error() gives a message for the calling
+ *    thread's last failed call.
+ *  - Outputs are overwritten (never accumulated into).
+ *  - Arithmetic and state accumulation are f32.  io-dtype outputs are rounded
+ *    to nearest even.  All reductions run in a fixed order without atomics,
+ *    so every output is bitwise reproducible run to run on one device.
+ */
+#ifndef SS_H
+#define SS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  Ids follow the page's workspace query (f32 = 0, f16 = 1,
+ * bf16 = 2). */
+typedef enum { SS_F32 = 0, SS_F16 = 1, SS_BF16 = 2 } ss_dtype;
+
+typedef enum {
+  SS_OK = 0,
+  SS_ERR_INVALID_PROBLEM = 1,     /* bad extents, null or misaligned pointer, presence mismatch */
+  SS_ERR_UNSUPPORTED = 2,         /* dstate > 256, dtype outside {f32, f16, bf16} */
+  SS_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < ss_workspace_size() */
+  SS_ERR_HIP = 4                  /* a launch failed (e.g. no gfx950 code for the device) */
+} ss_status;
+
+/* Problem descriptor (the page's SelectiveScanDescriptor, plus a separate
+ * parameter dtype and a schedule override). */
+typedef struct ss_desc {
+  int32_t batch;          /* B >= 0 */
+  int32_t seqlen;         /* L >= 0 */
+  int32_t dim;            /* D >= 0 (channels) */
+  int32_t dstate;         /* N, 0 <= N <= 256 */
+  int32_t delta_softplus; /* 0 or 1 */
+  int32_t io_dtype;       /* ss_dtype of u, delta, B, C, z, y, dy, du, ddelta, dB, dC, dz */
+  int32_t param_dtype;    /* ss_dtype of A, D, delta_bias, last_state, dA, dD, ddelta_bias:
+                             SS_F32 or equal to io_dtype */
+  int32_t chunk_len;      /* 0: the library picks the time-chunk length from the shape
+                             (the normal setting).  > 0: force chunks of this many steps
+                             (for testing the chunked schedule); >= L means one chunk. */
+} ss_desc;
+
+/* Workspace bytes that ss_fwd (backward = 0) or ss_bwd (backward = 1) needs
+ * for this descriptor: pure arithmetic, no device access.  Returns 0 for an
+ * invalid descriptor (ss_fwd / ss_bwd then report the error). */
+size_t ss_workspace_size(const ss_desc* desc, int32_t backward);
+
+/* Forward.  u, delta, A, B, C, y are required; Dskip, z, delta_bias and
+ * last_state may be NULL (absent).  A, B, C may be NULL only when N = 0.
+ * workspace must be 256-byte aligned and hold ss_workspace_size(desc, 0)
+ * bytes (it may be NULL when that size is 0).  Empty problems (B*L*D = 0)
+ * return SS_OK; if L = 0 and last_state is given, last_state is set to 0
+ * (the state before the first step). */
+int ss_fwd(const ss_desc* desc, const void* u, const void* delta, const void* A,
+           const void* B, const void* C, const void* Dskip, const void* z,
+           const void* delta_bias, void* y, void* last_state, void* workspace,
+           size_t workspace_bytes, void* stream);
+
+/* Backward (BPTT) of the forward above for the loss sum(dy * y): the
+ * gradient set of the page's SelectiveScanBackwardArgs.  Saved forward
+ * inputs plus dy are read; du, ddelta, dA, dB, dC are required outputs; dD,
+ * dz, ddelta_bias must be given exactly when Dskip, z, delta_bias are
+ * (otherwise SS_ERR_INVALID_PROBLEM).  ddelta is the gradient with respect to
+ * the raw delta input (through the bias and the softplus); dA is with respect
+ * to A.  workspace: ss_workspace_size(desc, 1) bytes, 256-byte aligned. */
+int ss_bwd(const ss_desc* desc, const void* u, const void* delta, const void* A,
+           const void* B, const void* C, const void* Dskip, const void* z,
+           const void* delta_bias, const void* dy, void* du, void* ddelta, void* dA,
+           void* dB, void* dC, void* dD, void* dz, void* ddelta_bias, void* workspace,
+           size_t workspace_bytes, void* stream);
+
+/* The schedule the library would use for a descriptor (informational). */
+typedef struct ss_plan {
+  int32_t chunk_len;          /* time steps per chunk */
+  int32_t n_chunks;           /* chunks along L (1 = single pass) */
+  int32_t states_per_lane;    /* state registers per lane (>= N / lanes_per_channel) */
+  int32_t lanes_per_channel;  /* lanes sharing one channel's states */
+  int32_t n_launches;         /* kernels enqueued per call */
+} ss_plan;
+
+/* Fills *out for ss_fwd (backward = 0) or ss_bwd (backward = 1).  Returns a
+ * status like the entry points (no device access). */
+int ss_plan_query(const ss_desc* desc, int32_t backward, ss_plan* out);
+
+/* Static text for a status code. */
+const char* ss_status_string(int status);
+
+/* Message describing the calling thread's most recent failed call ("" if
+ * none).  The pointer stays valid until that thread's next call. */
+const char* ss_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_H */

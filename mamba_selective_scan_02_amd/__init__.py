@@ -1,0 +1,272 @@
+"""Mamba-1 selective scan on AMD Instinct MI355X (gfx950).
+
+A thin binding over the C library ``libss.so`` (declared in ``include/ss.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only validates Python arguments, allocates outputs and workspace with torch
+on the tensors' device and passes raw pointers plus the current HIP stream.
+If the library is missing, every call raises: there is no fallback.
+
+Raw C entry points with the header's names: ``ss_workspace_size``,
+``ss_fwd``, ``ss_bwd``, ``ss_plan_query``, ``ss_status_string``,
+``ss_last_error``.  Tensor-level helpers: ``fwd``, ``bwd`` and the autograd
+function ``selective_scan``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+__all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "selective_scan", "plan", "workspace_size",
+           "ss_workspace_size", "ss_fwd", "ss_bwd", "ss_plan_query", "ss_status_string",
+           "ss_last_error", "library_path", "load_library",
+           "SS_OK", "SS_ERR_INVALID_PROBLEM", "SS_ERR_UNSUPPORTED",
+           "SS_ERR_WORKSPACE_TOO_SMALL", "SS_ERR_HIP"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libss.so")
+
+SS_F32, SS_F16, SS_BF16 = 0, 1, 2
+SS_OK, SS_ERR_INVALID_PROBLEM, SS_ERR_UNSUPPORTED, SS_ERR_WORKSPACE_TOO_SMALL, SS_ERR_HIP = range(5)
+
+_DTYPE_ID = {torch.float32: SS_F32, torch.float16: SS_F16, torch.bfloat16: SS_BF16}
+
+
+class SsDesc(ctypes.Structure):
+    """Mirror of ``ss_desc``."""
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("dstate", ctypes.c_int32),
+                ("delta_softplus", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("param_dtype", ctypes.c_int32), ("chunk_len", ctypes.c_int32)]
+
+
+class SsPlan(ctypes.Structure):
+    """Mirror of ``ss_plan``."""
+    _fields_ = [("chunk_len", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
+                ("states_per_lane", ctypes.c_int32), ("lanes_per_channel", ctypes.c_int32),
+                ("n_launches", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libss.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or library_path
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with "
+                           "`python -m mamba_selective_scan_02_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    dp = ctypes.POINTER(SsDesc)
+    lib.ss_workspace_size.argtypes = [dp, ctypes.c_int32]
+    lib.ss_workspace_size.restype = sz
+    lib.ss_fwd.argtypes = [dp] + [vp] * 11 + [sz, vp]
+    lib.ss_fwd.restype = ctypes.c_int
+    lib.ss_bwd.argtypes = [dp] + [vp] * 18 + [sz, vp]
+    lib.ss_bwd.restype = ctypes.c_int
+    lib.ss_plan_query.argtypes = [dp, ctypes.c_int32, ctypes.POINTER(SsPlan)]
+    lib.ss_plan_query.restype = ctypes.c_int
+    lib.ss_status_string.argtypes = [ctypes.c_int]
+    lib.ss_status_string.restype = ctypes.c_char_p
+    lib.ss_last_error.argtypes = []
+    lib.ss_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------- raw C entry points
+
+def _ref(desc):
+    return None if desc is None else ctypes.byref(desc)
+
+
+def ss_workspace_size(desc: SsDesc, backward: int) -> int:
+    return load_library().ss_workspace_size(_ref(desc), int(backward))
+
+
+def ss_fwd(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, y, last_state,
+           workspace, workspace_bytes: int, stream) -> int:
+    return load_library().ss_fwd(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias,
+                                 y, last_state, workspace, workspace_bytes, stream)
+
+
+def ss_bwd(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, dy, du, ddelta, dA, dB, dC,
+           dD, dz, ddelta_bias, workspace, workspace_bytes: int, stream) -> int:
+    return load_library().ss_bwd(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias,
+                                 dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, workspace,
+                                 workspace_bytes, stream)
+
+
+def ss_plan_query(desc: SsDesc, backward: int, out: SsPlan) -> int:
+    return load_library().ss_plan_query(_ref(desc), int(backward), _ref(out))
+
+
+def ss_status_string(status: int) -> str:
+    return load_library().ss_status_string(int(status)).decode()
+
+
+def ss_last_error() -> str:
+    return load_library().ss_last_error().decode()
+
+
+# ------------------------------------------------------------- tensor helpers
+
+def _raise(status: int, who: str):
+    msg = f"{who}: {ss_status_string(status)}: {ss_last_error()}"
+    if status == SS_ERR_INVALID_PROBLEM:
+        raise ValueError(msg)
+    if status == SS_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: Optional[torch.Tensor], name: str, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _desc_for(u: torch.Tensor, A: torch.Tensor, delta_softplus: bool, chunk_len: int) -> SsDesc:
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [B, L, D] and A [D, N]")
+    if u.dtype not in _DTYPE_ID or A.dtype not in _DTYPE_ID:
+        raise NotImplementedError("dtypes must be float32, float16 or bfloat16")
+    Bn, L, D = u.shape
+    N = A.shape[1]
+    return SsDesc(Bn, L, D, N, 1 if delta_softplus else 0, _DTYPE_ID[u.dtype],
+                  _DTYPE_ID[A.dtype], int(chunk_len))
+
+
+def plan(desc: SsDesc, backward: bool = False) -> SsPlan:
+    out = SsPlan()
+    st = ss_plan_query(desc, int(backward), out)
+    if st != SS_OK:
+        _raise(st, "ss_plan_query")
+    return out
+
+
+def workspace_size(desc: SsDesc, backward: bool = False) -> int:
+    return ss_workspace_size(desc, int(backward))
+
+
+def _stream_of(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = True,
+        return_last_state: bool = False, chunk_len: int = 0, y: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Selective-scan forward on the tensors' GPU.
+
+    u, delta, z: [B, L, D]; A: [D, N]; B, C: [B, L, N]; D, delta_bias: [D].
+    u / delta / B / C / z share one dtype (f32, f16 or bf16); A / D /
+    delta_bias are float32 or that dtype.  Returns (y, last_state or None).
+    """
+    desc = _desc_for(u, A, delta_softplus, chunk_len)
+    dev, io, pa = u.device, u.dtype, A.dtype
+    Bn, L, Dd, N = desc.batch, desc.seqlen, desc.dim, desc.dstate
+    for t, name, shape, dt in ((u, "u", (Bn, L, Dd), io), (delta, "delta", (Bn, L, Dd), io),
+                               (A, "A", (Dd, N), pa), (B, "B", (Bn, L, N), io),
+                               (C, "C", (Bn, L, N), io), (D, "D", (Dd,), pa),
+                               (z, "z", (Bn, L, Dd), io), (delta_bias, "delta_bias", (Dd,), pa)):
+        _check(t, name, shape, dt, dev)
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    if y is None:
+        y = torch.empty((Bn, L, Dd), dtype=io, device=dev)
+    _check(y, "y", (Bn, L, Dd), io, dev)
+    ls = torch.empty((Bn, Dd, N), dtype=pa, device=dev) if return_last_state else None
+    need = workspace_size(desc, False)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = ss_fwd(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(delta_bias), _ptr(y), _ptr(ls), _ptr(workspace), workspace.numel(),
+                _stream_of(dev))
+    if st != SS_OK:
+        _raise(st, "ss_fwd")
+    return y, ls
+
+
+def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None,
+        delta_softplus: bool = True, chunk_len: int = 0,
+        workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Selective-scan backward: gradients of sum(dy * y).
+
+    Returns a dict with du, ddelta, dA, dB, dC, dD, dz, ddelta_bias (dD / dz /
+    ddelta_bias are None when D / z / delta_bias are None).
+    """
+    desc = _desc_for(u, A, delta_softplus, chunk_len)
+    dev, io, pa = u.device, u.dtype, A.dtype
+    Bn, L, Dd, N = desc.batch, desc.seqlen, desc.dim, desc.dstate
+    for t, name, shape, dt in ((u, "u", (Bn, L, Dd), io), (delta, "delta", (Bn, L, Dd), io),
+                               (A, "A", (Dd, N), pa), (B, "B", (Bn, L, N), io),
+                               (C, "C", (Bn, L, N), io), (D, "D", (Dd,), pa),
+                               (z, "z", (Bn, L, Dd), io), (delta_bias, "delta_bias", (Dd,), pa),
+                               (dy, "dy", (Bn, L, Dd), io)):
+        _check(t, name, shape, dt, dev)
+    if dy is None:
+        raise ValueError("dy is required")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    out = {
+        "du": torch.empty((Bn, L, Dd), dtype=io, device=dev),
+        "ddelta": torch.empty((Bn, L, Dd), dtype=io, device=dev),
+        "dA": torch.empty((Dd, N), dtype=pa, device=dev),
+        "dB": torch.empty((Bn, L, N), dtype=io, device=dev),
+        "dC": torch.empty((Bn, L, N), dtype=io, device=dev),
+        "dD": torch.empty((Dd,), dtype=pa, device=dev) if D is not None else None,
+        "dz": torch.empty((Bn, L, Dd), dtype=io, device=dev) if z is not None else None,
+        "ddelta_bias": torch.empty((Dd,), dtype=pa, device=dev) if delta_bias is not None else None,
+    }
+    need = workspace_size(desc, True)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = ss_bwd(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                _ptr(delta_bias), _ptr(dy), _ptr(out["du"]), _ptr(out["ddelta"]),
+                _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(workspace), workspace.numel(),
+                _stream_of(dev))
+    if st != SS_OK:
+        _raise(st, "ss_bwd")
+    return out
+
+
+class _SelectiveScanFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, u, delta, A, B, C, D, z, delta_bias, delta_softplus):
+        y, _ = fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus)
+        ctx.delta_softplus = delta_softplus
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        u, delta, A, B, C, D, z, delta_bias = ctx.saved_tensors
+        g = bwd(u, delta, A, B, C, D, z, delta_bias, dy.contiguous(), ctx.delta_softplus)
+        return (g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"],
+                g["ddelta_bias"], None)
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                   delta_softplus: bool = True) -> torch.Tensor:
+    """Differentiable forward (autograd backward runs ``ss_bwd``)."""
+    return _SelectiveScanFn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus)

@@ -1,0 +1,227 @@
+// C entry points of libss: validation, schedule planning and launches.
+//
+// Validation follows the baracuda-kernels page "src/attention/selective_scan.rs"
+// (SelectiveScanPlan::select / can_implement and the backward plan's run):
+// negative extents are an invalid problem, dstate above 256 and dtypes outside
+// {f32, f16, bf16} are unsupported, a workspace smaller than the query is
+// WorkspaceTooSmall, the optional-input / gradient pairs of the backward must
+// be both given or both omitted, and empty problems (B * L * D = 0) return
+// success without launching.  Raw pointers carry no shapes, so shape checks
+// become descriptor checks; null and misaligned pointers are rejected here.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/ss.h"
+#include "ss_device.h"
+#include "ss_plan.h"
+
+namespace ss {
+hipError_t launch_fwd(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_t s);
+hipError_t launch_zero_param(void* p, int64_t n, int dtype, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, const Plan& p, int io_dtype, hipStream_t s);
+}  // namespace ss
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int64_t dtype_size(int32_t dt) { return dt == SS_F32 ? 4 : 2; }
+
+bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
+
+// Descriptor checks shared by forward and backward.
+int check_desc(const ss_desc* d, const char* who) {
+  if (!d) return fail(SS_ERR_INVALID_PROBLEM, "%s: descriptor is NULL", who);
+  if (d->batch < 0 || d->seqlen < 0 || d->dim < 0 || d->dstate < 0)
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: extents must be non-negative", who);
+  if (d->dstate > 256)
+    return fail(SS_ERR_UNSUPPORTED, "%s: dstate must be <= 256 (got %d)", who, d->dstate);
+  if (d->io_dtype != SS_F32 && d->io_dtype != SS_F16 && d->io_dtype != SS_BF16)
+    return fail(SS_ERR_UNSUPPORTED, "%s: io_dtype must be f32, f16 or bf16", who);
+  if (d->param_dtype != SS_F32 && d->param_dtype != d->io_dtype)
+    return fail(SS_ERR_UNSUPPORTED, "%s: param_dtype must be f32 or equal to io_dtype", who);
+  if (d->delta_softplus != 0 && d->delta_softplus != 1)
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: delta_softplus must be 0 or 1", who);
+  if (d->chunk_len < 0)
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: chunk_len must be >= 0", who);
+  return SS_OK;
+}
+
+struct PtrCheck {
+  const char* who;
+  int status = SS_OK;
+  void need(const void* p, const char* name, int64_t elem) {
+    if (status != SS_OK) return;
+    if (!p) status = fail(SS_ERR_INVALID_PROBLEM, "%s: %s is NULL", who, name);
+    else if (!aligned(p, elem))
+      status = fail(SS_ERR_INVALID_PROBLEM, "%s: %s is not aligned to its element size", who, name);
+  }
+  void opt(const void* p, const char* name, int64_t elem) {
+    if (status != SS_OK || !p) return;
+    if (!aligned(p, elem))
+      status = fail(SS_ERR_INVALID_PROBLEM, "%s: %s is not aligned to its element size", who, name);
+  }
+};
+
+int check_workspace(size_t need, void* ws, size_t ws_bytes, const char* who) {
+  if (ws_bytes < need)
+    return fail(SS_ERR_WORKSPACE_TOO_SMALL, "%s: workspace too small (need %zu bytes, got %zu)",
+                who, need, ws_bytes);
+  if (need > 0 && !ws) return fail(SS_ERR_INVALID_PROBLEM, "%s: workspace is NULL", who);
+  if (need > 0 && !aligned(ws, 256))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: workspace must be 256-byte aligned", who);
+  return SS_OK;
+}
+
+int hip_status(hipError_t e, const char* who) {
+  if (e == hipSuccess) return SS_OK;
+  return fail(SS_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ss_workspace_size(const ss_desc* d, int32_t backward) {
+  if (check_desc(d, "ss_workspace_size") != SS_OK) return 0;
+  return ss::make_plan(*d, backward != 0).ws_bytes;
+}
+
+int ss_plan_query(const ss_desc* d, int32_t backward, ss_plan* out) {
+  g_err[0] = 0;
+  int st = check_desc(d, "ss_plan_query");
+  if (st != SS_OK) return st;
+  if (!out) return fail(SS_ERR_INVALID_PROBLEM, "ss_plan_query: out is NULL");
+  const ss::Plan p = ss::make_plan(*d, backward != 0);
+  out->chunk_len = (int32_t)p.chunk_len;
+  out->n_chunks = (int32_t)p.K;
+  out->states_per_lane = p.NS;
+  out->lanes_per_channel = p.G;
+  out->n_launches = p.n_launches;
+  return SS_OK;
+}
+
+int ss_fwd(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,
+           const void* C, const void* Dskip, const void* z, const void* delta_bias, void* y,
+           void* last_state, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "ss_fwd";
+  int st = check_desc(d, who);
+  if (st != SS_OK) return st;
+  const int64_t Bn = d->batch, L = d->seqlen, D = d->dim, N = d->dstate;
+  const int64_t io = dtype_size(d->io_dtype), pa = dtype_size(d->param_dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PtrCheck pc{who};
+  pc.opt(last_state, "last_state", pa);
+  if (pc.status != SS_OK) return pc.status;
+  if (Bn * L * D == 0) {
+    // Nothing to scan.  An empty sequence leaves the initial (zero) state.
+    if (L == 0 && last_state && Bn * D * N > 0)
+      return hip_status(ss::launch_zero_param(last_state, Bn * D * N, d->param_dtype, s), who);
+    return SS_OK;
+  }
+  pc.need(u, "u", io);
+  pc.need(delta, "delta", io);
+  pc.need(y, "y", io);
+  if (N > 0) {
+    pc.need(A, "A", pa);
+    pc.need(B, "B", io);
+    pc.need(C, "C", io);
+  }
+  pc.opt(Dskip, "D", pa);
+  pc.opt(z, "z", io);
+  pc.opt(delta_bias, "delta_bias", pa);
+  if (pc.status != SS_OK) return pc.status;
+  const ss::Plan p = ss::make_plan(*d, false);
+  st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
+  if (st != SS_OK) return st;
+
+  ss::FwdArgs a{};
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C;
+  a.Dskip = Dskip; a.z = z; a.bias = delta_bias; a.y = y; a.last_state = last_state;
+  char* ws = static_cast<char*>(workspace);
+  a.chunk_dsum = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_dsum) : nullptr;
+  a.chunk_state = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_state) : nullptr;
+  a.Bn = Bn; a.L = L; a.D = D; a.N = N;
+  a.chunk_len = p.chunk_len; a.K = p.K;
+  a.softplus = d->delta_softplus;
+  a.param_dtype = d->param_dtype;
+  return hip_status(ss::launch_fwd(a, d->io_dtype, p.NS, p.G, s), who);
+}
+
+int ss_bwd(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,
+           const void* C, const void* Dskip, const void* z, const void* delta_bias,
+           const void* dy, void* du, void* ddelta, void* dA, void* dB, void* dC, void* dD,
+           void* dz, void* ddelta_bias, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const char* who = "ss_bwd";
+  int st = check_desc(d, who);
+  if (st != SS_OK) return st;
+  if ((Dskip == nullptr) != (dD == nullptr))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: D and dD must be both given or both omitted", who);
+  if ((z == nullptr) != (dz == nullptr))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: z and dz must be both given or both omitted", who);
+  if ((delta_bias == nullptr) != (ddelta_bias == nullptr))
+    return fail(SS_ERR_INVALID_PROBLEM,
+                "%s: delta_bias and ddelta_bias must be both given or both omitted", who);
+  const int64_t Bn = d->batch, L = d->seqlen, D = d->dim, N = d->dstate;
+  const int64_t io = dtype_size(d->io_dtype), pa = dtype_size(d->param_dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ss::Plan p = ss::make_plan(*d, true);
+  PtrCheck pc{who};
+  if (Bn * L * D > 0) {
+    pc.need(u, "u", io); pc.need(delta, "delta", io); pc.need(dy, "dy", io);
+    pc.need(du, "du", io); pc.need(ddelta, "ddelta", io);
+    if (N > 0) {
+      pc.need(A, "A", pa); pc.need(B, "B", io); pc.need(C, "C", io);
+    }
+    pc.opt(z, "z", io); pc.opt(dz, "dz", io);
+  }
+  if (D * N > 0) pc.need(dA, "dA", pa);
+  if (Bn * L * N > 0) { pc.need(dB, "dB", io); pc.need(dC, "dC", io); }
+  pc.opt(Dskip, "D", pa); pc.opt(dD, "dD", pa);
+  pc.opt(delta_bias, "delta_bias", pa); pc.opt(ddelta_bias, "ddelta_bias", pa);
+  if (pc.status != SS_OK) return pc.status;
+  st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
+  if (st != SS_OK) return st;
+  if (Bn * L * D == 0 && D * N == 0 && Bn * L * N == 0 && D == 0) return SS_OK;
+
+  ss::BwdArgs a{};
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C;
+  a.Dskip = Dskip; a.z = z; a.bias = delta_bias; a.dy = dy;
+  a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC;
+  a.dD = dD; a.dz = dz; a.dbias = ddelta_bias;
+  a.ws = static_cast<char*>(workspace);
+  a.Bn = Bn; a.L = L; a.D = D; a.N = N;
+  a.chunk_len = p.chunk_len; a.K = p.K;
+  a.softplus = d->delta_softplus;
+  a.param_dtype = d->param_dtype;
+  a.io_dtype = d->io_dtype;
+  return hip_status(ss::launch_bwd(a, p, d->io_dtype, s), who);
+}
+
+const char* ss_status_string(int status) {
+  switch (status) {
+    case SS_OK: return "success";
+    case SS_ERR_INVALID_PROBLEM: return "invalid problem";
+    case SS_ERR_UNSUPPORTED: return "unsupported";
+    case SS_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SS_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+const char* ss_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,439 @@
+// Backward (BPTT) selective scan kernels for gfx950.
+//
+// The gradient set is the one of SelectiveScanBackwardArgs on the
+// baracuda-kernels page "src/attention/selective_scan.rs" (du, dB, dC,
+// ddelta, dA, dD, dz, ddelta_bias).  The equations are the chain rule through
+// the forward recurrence of that page's "Algorithm summary"; per channel, with
+// g_t = dL/d(pre-gate output) = dy * silu(z) (or dy):
+//   dh_t    = g_t C_t + a_{t+1} dh_{t+1}                (dh after L-1 is 0)
+//   dC_t   += g_t h_t,   dB_t += dh_t dt_t u_t          (summed over d)
+//   q_t     = dh_t a_t h_{t-1}                         (= dL/da_t * a_t)
+//   ddt_t   = sum_n (q_t A_n + dh_t B_t u_t),  dA_n += q_t dt_t
+//   du_t    = dt_t sum_n dh_t B_t + g_t D
+//   ddelta_t = ddt_t * sigmoid(x_t) (softplus) or ddt_t,  ddelta_bias += ddelta_t
+//   dz_t    = dy_t o_t s (1 + z_t (1 - s)),  s = sigmoid(z_t),  dD += g_t u_t
+// The per-channel reverse sweep follows stage B3 "SSM BPTT + reductions" of the
+// mamba-rs page "mamba_ssm/gpu/backward.rs"; the reductions there are
+// per-channel partials followed by fixed-order reduction kernels, which is also
+// the scheme here (no atomics anywhere, so every output is bitwise
+// reproducible).
+//
+// Schedule.  Time is cut into chunks of at most 16 steps (one register tile).
+//  1. bwd_summary: per chunk, from zero: S (forward end state), Sb (the
+//     adjoint the chunk hands to the step before it, sum_s (prod_{r<=s} a_r)
+//     g_s C_s, accumulated forward with a running decay product) and sum dt.
+//  2. bwd_carry: per (b, n, d) the forward chain h_in(k+1) = P_k h_in(k) + S_k
+//     and the reverse chain c_{k-1} = P_k c_k + Sb_k, P_k = exp(A sum_k dt).
+//  3. bwd_main: per chunk, one state n at a time: recompute the chunk's states
+//     from h_in into registers, sweep back from c, accumulate the per-t sums
+//     (ddt, du, o) in registers; dB and dC partials are summed over the 256
+//     channels of the workgroup through LDS in a fixed order.
+//  4. bwd_finalize_bc / bwd_finalize_d: fixed-order sums of the partials.
+#include "ss_device.h"
+#include "ss_plan.h"
+
+namespace ss {
+
+constexpr int T = kBwdTile;            // 16 steps per chunk (max)
+constexpr int kRedStride = 257;        // LDS row stride of the dB/dC reduction buffer
+
+// Per-chunk inputs shared by all channels of a workgroup: B and C for the
+// chunk's steps, as f32 in LDS, [n][t] with t fastest; steps beyond the chunk
+// are zero (their dt is zero too, so they are identity steps).
+template <typename Tio>
+__device__ __forceinline__ void load_bc_tile(float* sB, float* sC, const Tio* B, const Tio* C,
+                                             int64_t b, int64_t t0, int nt, int64_t L,
+                                             int64_t N) {
+  const int64_t total = N * T;
+  for (int64_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int64_t tt = idx / N, n = idx % N;   // n fastest: coalesced global reads
+    float bv = 0.0f, cv = 0.0f;
+    if (tt < nt) {
+      const int64_t g = (b * L + t0 + tt) * N + n;
+      bv = ld(B, g);
+      cv = ld(C, g);
+    }
+    sB[n * T + tt] = bv;
+    sC[n * T + tt] = cv;
+  }
+}
+
+// ---------------------------------------------------------------- summary
+
+template <typename Tio>
+__global__ __launch_bounds__(kChannelsPerBlock) void bwd_summary(const BwdArgs a) {
+  extern __shared__ float smem[];
+  float* sB = smem;
+  float* sC = smem + a.N * T;
+  const int64_t nbd = a.nwgd;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t k = blk % a.K;
+  const int64_t b = blk / a.K;
+  const int64_t L = a.L, D = a.D, N = a.N;
+  const int64_t d_raw = db * kChannelsPerBlock + threadIdx.x;
+  const bool active = d_raw < D;
+  const int64_t d = active ? d_raw : D - 1;
+  const int64_t t0 = k * a.chunk_len;
+  const int nt = (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
+
+  load_bc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C), b, t0, nt, L, N);
+
+  const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
+  const bool has_z = a.z != nullptr, sp = a.softplus != 0;
+  const Tio* up = static_cast<const Tio*>(a.u) + b * L * D + d;
+  const Tio* dp = static_cast<const Tio*>(a.delta) + b * L * D + d;
+  const Tio* zp = has_z ? static_cast<const Tio*>(a.z) + b * L * D + d : up;
+  const Tio* yp = static_cast<const Tio*>(a.dy) + b * L * D + d;
+  float dl[T], xu[T], gg[T];
+  float dsum = 0.0f;
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    const bool ok = tt < nt;
+    const int64_t t = t0 + (ok ? tt : nt - 1);
+    const float uu = ld(up, t * D), x = ld(dp, t * D) + bv;
+    const float dlv = sp ? softplus(x) : x;
+    float g = ld(yp, t * D);
+    if (has_z) { const float zz = ld(zp, t * D); g *= zz * sigmoid(zz); }
+    dl[tt] = ok ? dlv : 0.0f;
+    xu[tt] = ok ? dlv * uu : 0.0f;
+    gg[tt] = ok ? g : 0.0f;
+    dsum += dl[tt];
+  }
+  __syncthreads();
+
+  for (int64_t n = 0; n < N; ++n) {
+    const float A2 = ld_param(a.A, d * N + n, a.param_dtype) * kLog2e;
+    const float* bn = sB + n * T;
+    const float* cn = sC + n * T;
+    float h = 0.0f, E = 1.0f, Sb = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+      const float av = fast_exp2(dl[tt] * A2);
+      h = __builtin_fmaf(av, h, xu[tt] * bn[tt]);
+      E *= av;
+      Sb = __builtin_fmaf(E, gg[tt] * cn[tt], Sb);
+    }
+    if (active) {
+      const int64_t o = ((b * a.K + k) * N + n) * D + d;
+      a.fstate[o] = h;
+      a.bstate[o] = Sb;
+    }
+  }
+  if (active) a.dsum[(b * a.K + k) * D + d] = dsum;
+}
+
+// ------------------------------------------------------------------ carry
+
+// Thread per (b, n, d), d fastest.  Forward chain over k = 0 .. K-2 (fstate
+// slot k becomes the state entering chunk k+1) and reverse chain over
+// k = K-1 .. 1 (bstate slot k becomes the adjoint at the end of chunk k-1),
+// interleaved so both chains' loads are in flight together.
+__global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) {
+  const int64_t nbd = a.nwgd;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t n = blk % a.N;
+  const int64_t b = blk / a.N;
+  const int64_t d = db * kChannelsPerBlock + threadIdx.x;
+  if (d >= a.D) return;
+  const int64_t D = a.D, N = a.N, K = a.K;
+  const float A2 = ld_param(a.A, d * N + n, a.param_dtype) * kLog2e;
+  float* fs = a.fstate + (b * K * N + n) * D + d;   // + k * N * D
+  float* bs = a.bstate + (b * K * N + n) * D + d;
+  const float* ds = a.dsum + b * K * D + d;         // + k * D
+  float hc = 0.0f, cc = 0.0f;
+  constexpr int KB = 8;
+  for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
+    float sf[KB], df[KB], sb[KB], dbk[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int64_t jj = (j0 + j < K - 1) ? j0 + j : K - 2;
+      sf[j] = fs[jj * N * D];
+      df[j] = ds[jj * D];
+      sb[j] = bs[(K - 1 - jj) * N * D];
+      dbk[j] = ds[(K - 1 - jj) * D];
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (j0 + j < K - 1) {
+        hc = __builtin_fmaf(fast_exp2(A2 * df[j]), hc, sf[j]);
+        fs[(j0 + j) * N * D] = hc;
+        cc = __builtin_fmaf(fast_exp2(A2 * dbk[j]), cc, sb[j]);
+        bs[(K - 1 - (j0 + j)) * N * D] = cc;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------- main
+
+template <typename Tio>
+__global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
+  extern __shared__ float smem[];
+  float* sB = smem;
+  float* sC = smem + a.N * T;
+  float* red = smem + 2 * a.N * T;  // [32][kRedStride]
+  const int tid = threadIdx.x;
+  const int64_t nbd = a.nwgd;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t kg = blk % a.KG;
+  const int64_t b = blk / a.KG;
+  const int64_t L = a.L, D = a.D, N = a.N, K = a.K;
+  const int64_t d_raw = db * kChannelsPerBlock + tid;
+  const bool active = d_raw < D;
+  const int64_t d = active ? d_raw : D - 1;
+  const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
+  const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
+  const bool has_z = a.z != nullptr, has_D = a.Dskip != nullptr, sp = a.softplus != 0;
+  const Tio* up = static_cast<const Tio*>(a.u) + b * L * D + d;
+  const Tio* dp = static_cast<const Tio*>(a.delta) + b * L * D + d;
+  const Tio* zp = has_z ? static_cast<const Tio*>(a.z) + b * L * D + d : up;
+  const Tio* yp = static_cast<const Tio*>(a.dy) + b * L * D + d;
+  Tio* dup = static_cast<Tio*>(a.du) + b * L * D + d;
+  Tio* ddp = static_cast<Tio*>(a.ddelta) + b * L * D + d;
+  Tio* dzp = has_z ? static_cast<Tio*>(a.dz) + b * L * D + d : dup;
+
+  // reduction lane roles: value v (0..15 dB, 16..31 dC), channel slice p
+  const int rv = tid >> 3, rp = tid & 7;
+  float dD_acc = 0.0f, db_acc = 0.0f;
+  const int64_t k_lo = kg * kBwdChunksPerGroup;
+  const int64_t k_hi = (k_lo + kBwdChunksPerGroup < K) ? k_lo + kBwdChunksPerGroup : K;
+
+  for (int64_t k = k_hi - 1; k >= k_lo; --k) {
+    const int64_t t0 = k * a.chunk_len;
+    const int nt = (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
+    __syncthreads();  // previous chunk's tile readers are done
+    load_bc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C), b, t0, nt,
+                 L, N);
+
+    float uu[T], dl[T], xu[T], gg[T], gz[T], sx[T], oo[T], ddl[T], dua[T];
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+      const bool ok = tt < nt;
+      const int64_t t = t0 + (ok ? tt : nt - 1);
+      const float u_ = ld(up, t * D), x = ld(dp, t * D) + bv, dy = ld(yp, t * D);
+      float dlv, sxv;
+      if (sp) { dlv = softplus(x); sxv = sigmoid(x); } else { dlv = x; sxv = 1.0f; }
+      float g = dy, gzv = 0.0f;
+      if (has_z) {
+        const float zz = ld(zp, t * D), s = sigmoid(zz);
+        g = dy * zz * s;
+        gzv = dy * s * __builtin_fmaf(zz, 1.0f - s, 1.0f);
+      }
+      uu[tt] = ok ? u_ : 0.0f;
+      dl[tt] = ok ? dlv : 0.0f;
+      xu[tt] = ok ? dlv * u_ : 0.0f;
+      gg[tt] = ok ? g : 0.0f;
+      gz[tt] = gzv;
+      sx[tt] = sxv;
+      oo[tt] = 0.0f;
+      ddl[tt] = 0.0f;
+      dua[tt] = 0.0f;
+    }
+    __syncthreads();  // tile visible
+
+    for (int64_t n = 0; n < N; ++n) {
+      const float An = ld_param(a.A, d * N + n, a.param_dtype);
+      const float A2 = An * kLog2e;
+      const float h0 = (k > 0) ? a.fstate[((b * K + (k - 1)) * N + n) * D + d] : 0.0f;
+      float dh = (k < K - 1) ? a.bstate[((b * K + (k + 1)) * N + n) * D + d] : 0.0f;
+      const float* bn = sB + n * T;
+      const float* cn = sC + n * T;
+      float hs[T], ah[T];
+      float hp = h0;
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) {
+        const float av = fast_exp2(dl[tt] * A2);
+        hp = __builtin_fmaf(av, hp, xu[tt] * bn[tt]);
+        hs[tt] = hp;
+        ah[tt] = av;
+        oo[tt] = __builtin_fmaf(cn[tt], hp, oo[tt]);
+      }
+      float vB[T], vC[T];
+      float dA_acc = 0.0f;
+#pragma unroll
+      for (int tt = T - 1; tt >= 0; --tt) {
+        dh = __builtin_fmaf(gg[tt], cn[tt], dh);         // dL/dh_t
+        vC[tt] = gg[tt] * hs[tt];
+        vB[tt] = dh * xu[tt];
+        dua[tt] = __builtin_fmaf(dh, bn[tt], dua[tt]);
+        const float m = dh * ah[tt];
+        const float q = m * (tt > 0 ? hs[tt - 1] : h0);
+        ddl[tt] = __builtin_fmaf(q, An, ddl[tt]);
+        dA_acc = __builtin_fmaf(q, dl[tt], dA_acc);
+        dh = m;
+      }
+      if (active) {
+        float* pa = a.part_dA + ((b * a.KG + kg) * N + n) * D + d;
+        *pa = (k == k_hi - 1) ? dA_acc : *pa + dA_acc;
+      }
+      // dB / dC for this n: sum over the workgroup's channels in LDS.
+      // Inactive (tail) lanes contribute zero.
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) {
+        red[tt * kRedStride + tid] = active ? vB[tt] : 0.0f;
+        red[(T + tt) * kRedStride + tid] = active ? vC[tt] : 0.0f;
+      }
+      __syncthreads();
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s += red[rv * kRedStride + rp * 32 + ((i + 8 * rp) & 31)];
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      s += __shfl_xor(s, 4, 64);
+      if (rp == 0) {
+        const int tt = rv & (T - 1), which = rv >> 4;
+        if (tt < nt)
+          a.part_bc[((b * L + t0 + tt) * a.nwgd + db) * 2 * N + which * N + n] = s;
+      }
+      __syncthreads();  // red free for the next n
+    }
+
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+      if (tt < nt && active) {
+        const int64_t t = t0 + tt;
+        const float du = __builtin_fmaf(dl[tt], dua[tt], has_D ? gg[tt] * Dv : 0.0f);
+        const float dde = __builtin_fmaf(uu[tt], dua[tt], ddl[tt]);
+        const float dx = dde * sx[tt];
+        dup[t * D] = from_f32<Tio>(du);
+        ddp[t * D] = from_f32<Tio>(dx);
+        if (has_z) dzp[t * D] = from_f32<Tio>(gz[tt] * __builtin_fmaf(Dv, uu[tt], oo[tt]));
+        db_acc += dx;
+        dD_acc = __builtin_fmaf(gg[tt], uu[tt], dD_acc);
+      }
+    }
+  }
+  if (active) {
+    a.part_dD[(b * a.KG + kg) * D + d] = dD_acc;
+    a.part_db[(b * a.KG + kg) * D + d] = db_acc;
+  }
+}
+
+// --------------------------------------------------------------- finalize
+
+// dB[b,t,n], dC[b,t,n] = sums over the channel blocks, in block order.
+template <typename Tio>
+__global__ void bwd_finalize_bc(const BwdArgs a) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // (b*L + t)*N + n
+  const int64_t N = a.N;
+  if (i >= a.Bn * a.L * N) return;
+  const int64_t bt = i / N, n = i % N;
+  const float* p = a.part_bc + bt * a.nwgd * 2 * N + n;
+  float sb = 0.0f, sc = 0.0f;
+  for (int64_t w = 0; w < a.nwgd; ++w) {
+    sb += p[w * 2 * N];
+    sc += p[w * 2 * N + N];
+  }
+  static_cast<Tio*>(a.dB)[i] = from_f32<Tio>(sb);
+  static_cast<Tio*>(a.dC)[i] = from_f32<Tio>(sc);
+}
+
+// dA[d,n] = sum over (b, chunk group) in that order; dD, ddelta_bias likewise.
+// Thread per (n', d), d fastest, n' < max(N, 1); n' = 0 also does dD / dbias.
+__global__ void bwd_finalize_d(const BwdArgs a) {
+  const int64_t N = a.N, D = a.D;
+  const int64_t nn = N > 0 ? N : 1;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= nn * D) return;
+  const int64_t n = i / D, d = i % D;
+  if (N > 0) {
+    float s = 0.0f;
+    for (int64_t bk = 0; bk < a.Bn * a.KG; ++bk) s += a.part_dA[(bk * N + n) * D + d];
+    st_param(a.dA, d * N + n, a.param_dtype, s);
+  }
+  if (n == 0) {
+    if (a.dD) {
+      float s = 0.0f;
+      for (int64_t bk = 0; bk < a.Bn * a.KG; ++bk) s += a.part_dD[bk * D + d];
+      st_param(a.dD, d, a.param_dtype, s);
+    }
+    if (a.dbias) {
+      float s = 0.0f;
+      for (int64_t bk = 0; bk < a.Bn * a.KG; ++bk) s += a.part_db[bk * D + d];
+      st_param(a.dbias, d, a.param_dtype, s);
+    }
+  }
+}
+
+__global__ void fill_zero_words(uint16_t* p, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+static hipError_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
+  if (!p || bytes <= 0) return hipSuccess;
+  const int64_t n = bytes / 2;  // every element type here is 2 or 4 bytes
+  fill_zero_words<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+      static_cast<uint16_t*>(p), n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ launch
+
+template <typename Tio>
+static hipError_t launch_bwd_t(BwdArgs a, const Plan& p, hipStream_t s) {
+  const int64_t Bn = a.Bn, L = a.L, D = a.D, N = a.N;
+  const int64_t io = a.io_dtype == 0 ? 4 : 2, pa = a.param_dtype == 0 ? 4 : 2;
+  if (Bn * L * D == 0) {
+    // No (b, t, d) terms: every reduced gradient is an empty sum.
+    hipError_t e = zero_bytes(a.dA, D * N * pa, s);
+    if (e == hipSuccess) e = zero_bytes(a.dD, D * pa, s);
+    if (e == hipSuccess) e = zero_bytes(a.dbias, D * pa, s);
+    if (e == hipSuccess) e = zero_bytes(a.dB, Bn * L * N * io, s);
+    if (e == hipSuccess) e = zero_bytes(a.dC, Bn * L * N * io, s);
+    return e;
+  }
+  a.dsum = reinterpret_cast<float*>(a.ws + p.off_dsum);
+  a.fstate = reinterpret_cast<float*>(a.ws + p.off_state);
+  a.bstate = reinterpret_cast<float*>(a.ws + p.off_bstate);
+  a.part_bc = reinterpret_cast<float*>(a.ws + p.off_part_bc);
+  a.part_dA = reinterpret_cast<float*>(a.ws + p.off_part_dA);
+  a.part_dD = reinterpret_cast<float*>(a.ws + p.off_part_dD);
+  a.part_db = reinterpret_cast<float*>(a.ws + p.off_part_db);
+  a.KG = p.KG;
+  a.nwgd = p.nwgd;
+  hipError_t e;
+  const size_t tile_bytes = sizeof(float) * 2 * (size_t)N * T;
+  if (a.K > 1) {
+    bwd_summary<Tio><<<dim3((unsigned)(Bn * a.K * a.nwgd)), dim3(kChannelsPerBlock), tile_bytes,
+                       s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (N > 0) {
+      bwd_carry<<<dim3((unsigned)(Bn * N * a.nwgd)), dim3(kChannelsPerBlock), 0, s>>>(a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  const size_t main_bytes = tile_bytes + sizeof(float) * 32 * kRedStride;
+  if (main_bytes > 64 * 1024) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_main<Tio>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)main_bytes);
+    if (e != hipSuccess) return e;
+  }
+  bwd_main<Tio><<<dim3((unsigned)(Bn * a.KG * a.nwgd)), dim3(kChannelsPerBlock), main_bytes, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (Bn * L * N > 0) {
+    const int64_t n = Bn * L * N;
+    bwd_finalize_bc<Tio><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t nd = (N > 0 ? N : 1) * D;
+  bwd_finalize_d<<<dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, const Plan& p, int io_dtype, hipStream_t s) {
+  switch (io_dtype) {
+    case 0: return launch_bwd_t<float>(a, p, s);
+    case 1: return launch_bwd_t<f16_t>(a, p, s);
+    case 2: return launch_bwd_t<bf16_t>(a, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ss

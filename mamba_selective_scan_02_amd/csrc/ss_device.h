@@ -1,0 +1,170 @@
+// Device-side helpers for the selective-scan kernels (gfx950 only).
+//
+// Element access (f32 / f16 / bf16 storage, f32 arithmetic), the softplus and
+// gate maps of the recurrence, and the launch-parameter blocks shared by the
+// forward and backward kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Storage types.  bf16 and f16 are kept as raw 16-bit words and converted
+// explicitly so that every load is a plain integer load.
+struct bf16_t { uint16_t bits; };
+struct f16_t { uint16_t bits; };
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(v.bits) << 16);
+}
+__device__ __forceinline__ float to_f32(f16_t v) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, v.bits));
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
+  // Round to nearest even (hardware conversion on gfx950).
+  return bf16_t{__builtin_bit_cast(uint16_t, static_cast<__bf16>(v))};
+}
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float v) {
+  return f16_t{__builtin_bit_cast(uint16_t, static_cast<_Float16>(v))};
+}
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* __restrict__ p, int64_t i) { return to_f32(p[i]); }
+
+// Two consecutive 16-bit elements from one 32-bit word (element 2i in the low
+// half).  For wave-uniform addresses this keeps the load on the scalar path
+// (there are no 16-bit scalar loads); for bf16 the split is two bit ops.
+__device__ __forceinline__ void split_pair(uint32_t w, const bf16_t*, float* lo, float* hi) {
+  *lo = __builtin_bit_cast(float, w << 16);
+  *hi = __builtin_bit_cast(float, w & 0xffff0000u);
+}
+__device__ __forceinline__ void split_pair(uint32_t w, const f16_t*, float* lo, float* hi) {
+  *lo = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+  *hi = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// Load NS consecutive elements row[0 .. NS-1] as f32.  PAIRS: 16-bit type,
+// row 4-byte aligned, NS even.
+template <typename T, int NS, bool PAIRS>
+__device__ __forceinline__ void ld_row(const T* row, float* out) {
+  if constexpr (PAIRS && sizeof(T) == 2) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(row);
+#pragma unroll
+    for (int i = 0; i < NS / 2; ++i) split_pair(w[i], row, &out[2 * i], &out[2 * i + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) out[i] = to_f32(row[i]);
+  }
+}
+
+// Parameters (A, D, delta_bias, last_state, dA, dD, ddelta_bias) are either f32
+// or the io type; the choice is a kernel argument, read once per lane.
+__device__ __forceinline__ float ld_param(const void* p, int64_t i, int dtype) {
+  if (dtype == 0) return static_cast<const float*>(p)[i];
+  if (dtype == 2) return to_f32(static_cast<const bf16_t*>(p)[i]);
+  return to_f32(static_cast<const f16_t*>(p)[i]);
+}
+__device__ __forceinline__ void st_param(void* p, int64_t i, int dtype, float v) {
+  if (dtype == 0) static_cast<float*>(p)[i] = v;
+  else if (dtype == 2) static_cast<bf16_t*>(p)[i] = from_f32<bf16_t>(v);
+  else static_cast<f16_t*>(p)[i] = from_f32<f16_t>(v);
+}
+
+// exp2 / log2 / reciprocal on the transcendental unit (v_exp_f32, v_log_f32,
+// v_rcp_f32: about 1 ulp on gfx950).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// log(1 + w) for w >= 0, accurate in relative terms also for tiny w:
+// with s = 1 + w rounded, log(s) * w / (s - 1) corrects the rounding of s
+// (the classic compensated form; exact to a few ulp when log is).
+__device__ __forceinline__ float log1p_pos(float w) {
+  const float s = 1.0f + w;
+  const float den = s - 1.0f;
+  const float l = fast_log2(s) * kLn2;
+  return den == 0.0f ? w : l * (w * fast_rcp(den));
+}
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^{-|x|}).
+__device__ __forceinline__ float softplus(float x) {
+  const float e = fast_exp2(-__builtin_fabsf(x) * kLog2e);
+  return __builtin_fmaxf(x, 0.0f) + log1p_pos(e);
+}
+
+// sigmoid(x) = 1 / (1 + e^{-x}); exp overflow gives rcp(inf) = 0.
+__device__ __forceinline__ float sigmoid(float x) {
+  return fast_rcp(1.0f + fast_exp2(-x * kLog2e));
+}
+
+// Forward launch parameters.
+struct FwdArgs {
+  const void* u;
+  const void* delta;
+  const void* A;
+  const void* B;
+  const void* C;
+  const void* Dskip;       // nullable
+  const void* z;           // nullable
+  const void* bias;        // nullable
+  void* y;
+  void* last_state;        // nullable
+  float* chunk_dsum;       // [Bn, K, D]   sum of delta_eff over each chunk
+  float* chunk_state;      // [Bn, K, N, D] chunk-end state from zero / carried-in state
+  int64_t Bn, L, D, N;
+  int64_t chunk_len, K;    // chunk length and number of chunks
+  int softplus;
+  int param_dtype;
+};
+
+// Backward launch parameters.  Workspace sub-buffers (f32):
+//   dsum    [Bn, K, D]       sum of dt over each chunk
+//   fstate  [Bn, K, N, D]    chunk-end state from zero, then (after the carry)
+//                            slot k = state entering chunk k+1
+//   bstate  [Bn, K, N, D]    chunk reverse summary, then slot k = adjoint
+//                            handed to the end of chunk k-1
+//   part_bc [Bn, L, nwgd, 2, N]  per channel-block partial sums of dB, dC
+//   part_dA [Bn, KG, N, D], part_dD / part_db [Bn, KG, D]  per chunk-group
+//                            partial sums of dA, dD, ddelta_bias
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const void* A;
+  const void* B;
+  const void* C;
+  const void* Dskip;       // nullable
+  const void* z;           // nullable
+  const void* bias;        // nullable
+  const void* dy;
+  void* du;
+  void* ddelta;
+  void* dA;
+  void* dB;
+  void* dC;
+  void* dD;                // nullable (iff Dskip)
+  void* dz;                // nullable (iff z)
+  void* dbias;             // nullable (iff bias)
+  char* ws;
+  float* dsum;
+  float* fstate;
+  float* bstate;
+  float* part_bc;
+  float* part_dA;
+  float* part_dD;
+  float* part_db;
+  int64_t Bn, L, D, N;
+  int64_t chunk_len, K, KG, nwgd;
+  int softplus;
+  int param_dtype;
+  int io_dtype;
+};
+
+}  // namespace ss

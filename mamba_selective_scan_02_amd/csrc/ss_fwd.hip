@@ -1,0 +1,282 @@
+// Forward selective scan kernels for gfx950.
+//
+// Recurrence: baracuda-kernels page "src/attention/selective_scan.rs", module
+// docs, "Algorithm summary".  Per channel (b, d) and state n:
+//   dt = softplus(delta + bias) (or delta + bias), a = exp(dt * A[d,n]),
+//   h = a * h + dt * B[b,t,n] * u[b,t,d], y = (sum_n C[b,t,n] h + D u) * silu(z).
+//
+// Mapping.  One lane owns one channel d of one batch row b (or, for N > 64,
+// G = 2 or 4 consecutive lanes share a channel, each holding 64 states).  A
+// workgroup is 256 lanes = 256 / G consecutive channels, so loads and stores of
+// u / delta / z / y are coalesced along D.  The lane keeps its states h[n] and
+// its row of A (pre-scaled by log2 e) in VGPRs.  B[b,t,:] and C[b,t,:] are
+// the same for every lane of the workgroup: with G = 1 their addresses are
+// wave-uniform, so they are fetched with scalar loads into SGPRs and used
+// directly as VALU operands.
+//
+// Time is walked sequentially inside a chunk.  When B * D alone cannot fill the
+// GPU, L is cut into K chunks and the scan runs in two levels:
+//   1. fwd_scan<SUMMARY>: every chunk but the last runs from h = 0 and writes
+//      its end state S_k[n] and sum_k = sum of dt over the chunk;
+//   2. fwd_carry: per (b, d, n), h_in(k+1) = exp(A * sum_k) * h_in(k) + S_k,
+//      the composition (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) of the chunk
+//      summaries, folded over k (the product of a chunk's decays is
+//      exp(A * sum of its dt) in closed form);
+//   3. fwd_scan<FULL>: every chunk runs again from its carried-in state and
+//      writes y (and last_state for the final chunk).
+// With K = 1 only step 3 runs, from h = 0.
+#include "ss_device.h"
+
+namespace ss {
+
+enum { MODE_FULL = 0, MODE_SUMMARY = 1 };
+constexpr int kBlock = 256;
+
+// The streamed tensors are separate __restrict__ arguments: that tells the
+// compiler the y stores never alias B / C, which lets it keep the uniform
+// B / C loads on the scalar path inside the loop.
+template <typename T, int NS, int G, bool EXACT, int MODE>
+__global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
+                                                   const T* __restrict__ delta_in,
+                                                   const T* __restrict__ B_in,
+                                                   const T* __restrict__ C_in,
+                                                   const T* __restrict__ z_in,
+                                                   T* __restrict__ y_out, const FwdArgs a) {
+  constexpr int CPB = kBlock / G;  // channels per workgroup
+  const int tid = threadIdx.x;
+  const int g = (G == 1) ? 0 : (tid % G);
+  const int cl = (G == 1) ? tid : (tid / G);
+  const int64_t nbd = (a.D + CPB - 1) / CPB;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  // the summary pass covers chunks 0 .. K-2 only (the last chunk's end state
+  // is never needed), the full pass all K chunks
+  const int64_t Kg = (MODE == MODE_SUMMARY) ? a.K - 1 : a.K;
+  const int64_t k = blk % Kg;
+  const int64_t b = blk / Kg;
+  const int64_t d_raw = db * CPB + cl;
+  const bool active = d_raw < a.D;
+  const int64_t d = active ? d_raw : a.D - 1;  // tail lanes compute on a valid channel, store nothing
+  const int64_t t0 = k * a.chunk_len;
+  const int64_t t1 = (t0 + a.chunk_len < a.L) ? t0 + a.chunk_len : a.L;
+  const int64_t L = a.L, D = a.D, N = a.N;
+  const int n0 = g * NS;
+
+  float A2[NS], h[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int n = n0 + i;
+    const bool ok = EXACT || n < N;
+    A2[i] = ok ? ld_param(a.A, d * N + n, a.param_dtype) * kLog2e : 0.0f;
+    h[i] = 0.0f;
+    if (MODE == MODE_FULL && k > 0 && ok)
+      h[i] = a.chunk_state[((b * a.K + (k - 1)) * N + n) * D + d];
+  }
+  const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
+  const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
+  const bool has_z = z_in != nullptr, has_D = a.Dskip != nullptr, sp = a.softplus != 0;
+
+  const T* up = u_in + b * L * D + d;
+  const T* dp = delta_in + b * L * D + d;
+  const T* zp = has_z ? z_in + b * L * D + d : up;
+  T* yp = y_out + b * L * D + d;
+  const T* Bp = B_in + b * L * N + n0;
+  const T* Cp = C_in + b * L * N + n0;
+
+  float dsum = 0.0f;
+
+  auto step = [&](int64_t t, float uu, float dr, float zz) {
+    const float x = dr + bv;
+    const float dl = sp ? softplus(x) : x;
+    const float xu = dl * uu;
+    float o = 0.0f;
+    float Bt[NS], Ct[NS];
+    if constexpr (EXACT) {
+      // whole rows; 16-bit rows are read as 32-bit words (host checked alignment)
+      ld_row<T, NS, true>(Bp + t * N, Bt);
+      if (MODE == MODE_FULL) ld_row<T, NS, true>(Cp + t * N, Ct);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const bool ok = n0 + i < N;
+        Bt[i] = ok ? ld(Bp, t * N + i) : 0.0f;
+        Ct[i] = (MODE == MODE_FULL && ok) ? ld(Cp, t * N + i) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const float dA = fast_exp2(dl * A2[i]);
+      h[i] = __builtin_fmaf(dA, h[i], xu * Bt[i]);
+      if (MODE == MODE_FULL) o = __builtin_fmaf(Ct[i], h[i], o);
+    }
+    if (MODE == MODE_SUMMARY) dsum += dl;
+    if (MODE == MODE_FULL) {
+#pragma unroll
+      for (int m = 1; m < G; m <<= 1) o += __shfl_xor(o, m, 64);
+      if (has_D) o = __builtin_fmaf(Dv, uu, o);
+      if (has_z) o *= zz * sigmoid(zz);
+      if (active && g == 0) yp[t * D] = from_f32<T>(o);
+    }
+  };
+
+  // Software pipeline: the per-lane inputs of the next U steps are loaded
+  // while the current U steps compute.  Indices are clamped into the chunk,
+  // so every load is in bounds; clamped values are never used.
+  constexpr int U = 4;
+  float cu[U], cd[U], cz[U];
+  auto load_group = [&](int64_t tb, float* lu, float* ldl, float* lz) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t tt = (tb + j < t1) ? tb + j : t1 - 1;
+      lu[j] = ld(up, tt * D);
+      ldl[j] = ld(dp, tt * D);
+      lz[j] = (MODE == MODE_FULL && has_z) ? ld(zp, tt * D) : 0.0f;
+    }
+  };
+  load_group(t0, cu, cd, cz);
+  int64_t t = t0;
+  for (; t + U <= t1; t += U) {
+    float nu[U], nd[U], nz[U];
+    load_group(t + U, nu, nd, nz);
+#pragma unroll
+    for (int j = 0; j < U; ++j) step(t + j, cu[j], cd[j], cz[j]);
+#pragma unroll
+    for (int j = 0; j < U; ++j) { cu[j] = nu[j]; cd[j] = nd[j]; cz[j] = nz[j]; }
+  }
+#pragma unroll
+  for (int j = 0; j < U - 1; ++j)
+    if (t + j < t1) step(t + j, cu[j], cd[j], cz[j]);
+
+  if (!active) return;
+  if (MODE == MODE_SUMMARY) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (EXACT || n0 + i < N) a.chunk_state[((b * a.K + k) * N + n0 + i) * D + d] = h[i];
+    if (g == 0) a.chunk_dsum[(b * a.K + k) * D + d] = dsum;
+  } else if (a.last_state != nullptr && k == a.K - 1) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (EXACT || n0 + i < N) st_param(a.last_state, (b * D + d) * N + n0 + i, a.param_dtype, h[i]);
+  }
+}
+
+// Carry across chunks.  Thread per (b, n, d), d fastest.  Slot k of
+// chunk_state holds S_k on entry and h_in(k+1) = state entering chunk k+1 on
+// exit (k = 0 .. K-2; the last chunk's summary is never produced or used).
+// The loads of a batch of KB chunks are issued before the dependent chain.
+__global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
+  const int64_t nbd = (a.D + kBlock - 1) / kBlock;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t n = blk % a.N;
+  const int64_t b = blk / a.N;
+  const int64_t d = db * kBlock + threadIdx.x;
+  if (d >= a.D) return;
+  const int64_t D = a.D, N = a.N, K = a.K;
+  const float A2 = ld_param(a.A, d * N + n, a.param_dtype) * kLog2e;
+  float* __restrict__ st = a.chunk_state + (b * K * N + n) * D + d;  // + k * N * D
+  const float* __restrict__ ds = a.chunk_dsum + b * K * D + d;       // + k * D
+  float hc = 0.0f;
+  constexpr int KB = 16;
+  for (int64_t k0 = 0; k0 < K - 1; k0 += KB) {
+    float sv[KB], dv[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int64_t kk = (k0 + j < K - 1) ? k0 + j : K - 2;
+      sv[j] = st[kk * N * D];
+      dv[j] = ds[kk * D];
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (k0 + j < K - 1) {
+        hc = __builtin_fmaf(fast_exp2(A2 * dv[j]), hc, sv[j]);
+        st[(k0 + j) * N * D] = hc;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+template <typename T, int NS, int G, bool EXACT>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
+  const T* U = static_cast<const T*>(a.u);
+  const T* DL = static_cast<const T*>(a.delta);
+  const T* Bm = static_cast<const T*>(a.B);
+  const T* Cm = static_cast<const T*>(a.C);
+  const T* Z = static_cast<const T*>(a.z);
+  T* Y = static_cast<T*>(a.y);
+  const int64_t cpb = kBlock / G;
+  const int64_t nbd = (a.D + cpb - 1) / cpb;
+  if (a.K > 1) {
+    const int64_t grid_sum = a.Bn * (a.K - 1) * nbd;  // chunks 0 .. K-2
+    fwd_scan<T, NS, G, EXACT, MODE_SUMMARY><<<dim3((unsigned)grid_sum), dim3(kBlock), 0, s>>>(
+        U, DL, Bm, Cm, Z, Y, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.N > 0) {
+      const int64_t nbd2 = (a.D + kBlock - 1) / kBlock;
+      fwd_carry<<<dim3((unsigned)(a.Bn * a.N * nbd2)), dim3(kBlock), 0, s>>>(a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  const int64_t grid = a.Bn * a.K * nbd;
+  fwd_scan<T, NS, G, EXACT, MODE_FULL><<<dim3((unsigned)grid), dim3(kBlock), 0, s>>>(
+      U, DL, Bm, Cm, Z, Y, a);
+  return hipGetLastError();
+}
+
+// EXACT (N fills the bucket) reads whole B / C rows; for 16-bit types that
+// needs 4-byte aligned rows, i.e. 4-byte aligned B and C (N is even here).
+template <typename T, int NS, int G>
+static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t s) {
+  const bool rows_ok = sizeof(T) == 4 || ((reinterpret_cast<uintptr_t>(a.B) % 4 == 0) &&
+                                          (reinterpret_cast<uintptr_t>(a.C) % 4 == 0));
+  return (a.N == (int64_t)NS * G && rows_ok) ? launch_fwd_t<T, NS, G, true>(a, s)
+                                             : launch_fwd_t<T, NS, G, false>(a, s);
+}
+
+template <typename T>
+static hipError_t launch_fwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s) {
+  if (gl == 1) {
+    switch (ns) {
+      case 4: return launch_fwd_e<T, 4, 1>(a, s);
+      case 8: return launch_fwd_e<T, 8, 1>(a, s);
+      case 16: return launch_fwd_e<T, 16, 1>(a, s);
+      case 32: return launch_fwd_e<T, 32, 1>(a, s);
+      case 64: return launch_fwd_e<T, 64, 1>(a, s);
+    }
+  } else if (ns == 64 && gl == 2) {
+    return launch_fwd_e<T, 64, 2>(a, s);
+  } else if (ns == 64 && gl == 4) {
+    return launch_fwd_e<T, 64, 4>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_t s) {
+  switch (io_dtype) {
+    case 0: return launch_fwd_ty<float>(a, ns, gl, s);
+    case 1: return launch_fwd_ty<f16_t>(a, ns, gl, s);
+    case 2: return launch_fwd_ty<bf16_t>(a, ns, gl, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Fill a float / param-typed buffer with zeros (used for last_state when
+// L = 0).  A kernel rather than a memset so the call can be graph-captured.
+__global__ void fill_zero_param(void* p, int64_t n, int dtype) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) st_param(p, i, dtype, 0.0f);
+}
+
+hipError_t launch_zero_param(void* p, int64_t n, int dtype, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_zero_param<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p, n, dtype);
+  return hipGetLastError();
+}
+
+}  // namespace ss

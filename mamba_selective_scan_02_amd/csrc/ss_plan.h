@@ -1,0 +1,118 @@
+// Schedule and workspace layout of one call (host side, pure arithmetic).
+//
+// The schedule is a function of the descriptor only (never of the device),
+// so results do not depend on how many compute units a device exposes.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ss.h"
+
+namespace ss {
+
+// Backward register tile: time steps one lane holds per chunk.
+constexpr int kBwdTile = 16;
+// Chunks of one channel block handled by one backward workgroup (their dA /
+// dD / ddelta_bias partials are summed in registers / in place).
+constexpr int kBwdChunksPerGroup = 4;
+// Channels per workgroup.
+constexpr int kChannelsPerBlock = 256;
+
+struct Plan {
+  int NS = 4, G = 1;          // forward: states per lane, lanes per channel
+  int64_t chunk_len = 0, K = 1;
+  int n_launches = 0;
+  // workspace (bytes, 256-aligned offsets)
+  size_t off_dsum = 0, off_state = 0, off_bstate = 0, off_part_bc = 0, off_part_dA = 0,
+         off_part_dD = 0, off_part_db = 0;
+  size_t ws_bytes = 0;
+  int64_t KG = 0, nwgd = 0;   // backward: chunk groups, channel blocks
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline void pick_bucket(int64_t N, int* NS, int* G) {
+  if (N <= 4) { *NS = 4; *G = 1; }
+  else if (N <= 8) { *NS = 8; *G = 1; }
+  else if (N <= 16) { *NS = 16; *G = 1; }
+  else if (N <= 32) { *NS = 32; *G = 1; }
+  else if (N <= 64) { *NS = 64; *G = 1; }
+  else if (N <= 128) { *NS = 64; *G = 2; }
+  else { *NS = 64; *G = 4; }
+}
+
+inline Plan make_plan(const ss_desc& d, bool backward) {
+  Plan p;
+  const int64_t Bn = d.batch, L = d.seqlen, D = d.dim, N = d.dstate;
+  pick_bucket(N, &p.NS, &p.G);
+  if (Bn * L * D == 0) {
+    p.chunk_len = L;
+    p.K = 1;
+    p.n_launches = 0;
+    return p;
+  }
+  if (!backward) {
+    int64_t lc;
+    if (d.chunk_len > 0) {
+      lc = d.chunk_len < L ? d.chunk_len : L;
+    } else {
+      // Waves that one chunk index provides.  At half the SIMDs or more a
+      // single pass (no second sweep) is cheaper; below that the time axis
+      // is cut so the grid reaches about two waves per SIMD, with chunks of
+      // at least 64 steps.
+      const int64_t cpw = 64 / p.G;
+      const int64_t waves = Bn * ((D + cpw - 1) / cpw);
+      const int64_t target = 2048;
+      int64_t K = 1;
+      if (waves < 512) {
+        K = (target + waves - 1) / waves;
+        const int64_t kmax = (L + 63) / 64;
+        if (K > kmax) K = kmax;
+        if (K < 1) K = 1;
+      }
+      lc = (L + K - 1) / K;
+      lc = (lc + 3) & ~int64_t(3);
+    }
+    p.chunk_len = lc;
+    p.K = (L + lc - 1) / lc;
+    size_t off = 0;
+    if (p.K > 1) {
+      p.off_dsum = off;
+      off = align256(off + sizeof(float) * (size_t)(Bn * p.K * D));
+      p.off_state = off;
+      off = align256(off + sizeof(float) * (size_t)(Bn * p.K * N * D));
+    }
+    p.ws_bytes = off;
+    p.n_launches = p.K > 1 ? (N > 0 ? 3 : 2) : 1;
+    return p;
+  }
+  // backward
+  int64_t lc = kBwdTile;
+  if (d.chunk_len > 0 && d.chunk_len < lc) lc = d.chunk_len;
+  if (lc > L) lc = L;
+  p.chunk_len = lc;
+  p.K = (L + lc - 1) / lc;
+  p.KG = (p.K + kBwdChunksPerGroup - 1) / kBwdChunksPerGroup;
+  p.nwgd = (D + kChannelsPerBlock - 1) / kChannelsPerBlock;
+  size_t off = 0;
+  p.off_dsum = off;
+  off = align256(off + sizeof(float) * (size_t)(Bn * p.K * D));
+  p.off_state = off;
+  off = align256(off + sizeof(float) * (size_t)(Bn * p.K * N * D));
+  p.off_bstate = off;
+  off = align256(off + sizeof(float) * (size_t)(Bn * p.K * N * D));
+  p.off_part_bc = off;
+  off = align256(off + sizeof(float) * (size_t)(Bn * L * p.nwgd * 2 * N));
+  p.off_part_dA = off;
+  off = align256(off + sizeof(float) * (size_t)(Bn * p.KG * N * D));
+  p.off_part_dD = off;
+  off = align256(off + sizeof(float) * (size_t)(Bn * p.KG * D));
+  p.off_part_db = off;
+  off = align256(off + sizeof(float) * (size_t)(Bn * p.KG * D));
+  p.ws_bytes = off;
+  p.n_launches = p.K > 1 ? 5 : 3;
+  return p;
+}
+
+}  // namespace ss

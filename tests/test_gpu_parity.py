@@ -1,0 +1,276 @@
+"""GPU parity: the HIP library against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (mamba_selective_scan_02_amd wraps it with
+ctypes).  Outputs are compared element by element with the float64 oracle on
+the same seeded inputs; the bound is the one the target states (1e-5 f32,
+2e-2 f16/bf16) on max |x - r| / max(|r|, rms(r)).  The five workloads run
+in the schedule the bench times (chunk_len = 0); the large ones are checked
+on sampled channels (all time steps of those channels) where the oracle would
+take too long in full.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import mamba_selective_scan_02_amd as ss
+import oracle
+from ss_inputs import WORKLOADS, make_inputs, random_inputs
+from tests.parity_util import GRADS, KEYS, TOL, rel_err, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ss.load_library()
+    yield
+
+
+def _run_fwd(inp, sp=True, chunk_len=0, last_state=True):
+    d = to_dev(inp)
+    y, ls = ss.fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"],
+                   delta_softplus=sp, return_last_state=last_state, chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    return y, ls
+
+
+def _check_fwd(inp, sp=True, chunk_len=0, tol=None, label=""):
+    say("fwd", label, tuple(inp["u"].shape), inp["A"].shape[1], inp["u"].dtype, "chunk", chunk_len)
+    y, ls = _run_fwd(inp, sp, chunk_len)
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, delta_softplus=sp, return_last_state=True)
+    tol = tol or TOL[inp["u"].dtype]
+    e_y, e_s = rel_err(to_np(y), yr), rel_err(to_np(ls), lsr)
+    assert e_y <= tol, f"{label} y err {e_y:.3e} > {tol}"
+    assert e_s <= max(tol, TOL[inp["A"].dtype]), f"{label} last_state err {e_s:.3e}"
+    return e_y
+
+
+# ------------------------------------------------------------------ forward
+
+SHAPES = [  # (B, L, D, N)
+    (1, 1, 1, 1), (1, 2, 31, 4), (3, 63, 64, 16), (2, 64, 65, 16), (1, 65, 300, 16),
+    (2, 1000, 33, 16), (1, 300, 257, 8), (2, 129, 70, 17), (1, 77, 40, 32), (1, 50, 20, 64),
+    (1, 40, 20, 65), (1, 33, 10, 128), (1, 21, 9, 200), (1, 19, 7, 256), (2, 17, 5, 3),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_shapes_f32(shape):
+    Bn, L, D, N = shape
+    _check_fwd(random_inputs(Bn, L, D, N, seed=hash(shape) % 10000), label=str(shape))
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 16, 64, 100])
+def test_fwd_forced_chunks(chunk):
+    inp = random_inputs(2, 700, 96, 16, seed=77)
+    _check_fwd(inp, chunk_len=chunk, label=f"chunk{chunk}")
+
+
+@pytest.mark.parametrize("combo", range(16))
+def test_fwd_optional_combinations(combo):
+    has_D, has_z, has_bias, sp = [bool(combo >> i & 1) for i in range(4)]
+    inp = random_inputs(2, 150, 70, 16, seed=200 + combo, has_D=has_D, has_z=has_z,
+                        has_bias=has_bias)
+    if not sp:  # keep delta_eff positive without softplus
+        inp["delta"] = inp["delta"].abs() * 0.3
+    for chunk in (0, 32):
+        _check_fwd(inp, sp=sp, chunk_len=chunk, label=f"combo{combo}/chunk{chunk}")
+
+
+@pytest.mark.parametrize("io,pa", [("bf16", "f32"), ("f16", "f32"), ("bf16", "bf16"),
+                                   ("f16", "f16")])
+@pytest.mark.parametrize("N", [16, 5, 64])
+def test_fwd_half_dtypes(io, pa, N):
+    inp = random_inputs(2, 200, 130, N, seed=300 + N, io_dtype=io, param_dtype=pa)
+    for chunk in (0, 48):
+        _check_fwd(inp, chunk_len=chunk, label=f"{io}/{pa}/N{N}/chunk{chunk}")
+
+
+def test_fwd_misaligned_16bit_rows():
+    """bf16 B / C at an odd element offset take the element-wise load path."""
+    inp = random_inputs(1, 40, 64, 16, seed=401, io_dtype="bf16")
+    d = to_dev(inp)
+    Bbig = torch.empty(d["B"].numel() + 1, dtype=torch.bfloat16, device=DEV)
+    Bbig[1:] = d["B"].reshape(-1)
+    Bv = Bbig[1:].view_as(d["B"])
+    assert Bv.data_ptr() % 4 == 2
+    y, _ = ss.fwd(d["u"], d["delta"], d["A"], Bv, d["C"], d["D"], d["z"], d["delta_bias"])
+    yr, _ = oracle.fwd(**{k: inp[k] for k in KEYS})
+    assert rel_err(to_np(y), yr) <= 2e-2
+
+
+def test_fwd_degenerate():
+    # N = 0: y = D u silu(z)
+    inp = random_inputs(2, 30, 40, 1, seed=501)
+    inp["A"], inp["B"], inp["C"] = inp["A"][:, :0], inp["B"][:, :, :0], inp["C"][:, :, :0]
+    _check_fwd(inp, label="N0")
+    # L = 0 with last_state: zeros
+    inp = random_inputs(2, 1, 40, 16, seed=502)
+    for k in ("u", "delta", "z", "B", "C"):
+        inp[k] = inp[k][:, :0].contiguous()
+    y, ls = _run_fwd(inp)
+    assert y.shape == (2, 0, 40) and torch.all(ls == 0)
+    # B = 0, D = 0: nothing to do
+    for shp in ((0, 10, 8, 4), (2, 10, 0, 4)):
+        inp = random_inputs(*shp, seed=503)
+        y, ls = _run_fwd(inp)
+        assert y.numel() == 0
+
+
+def test_fwd_workloads_tiny_and_m130m():
+    for name in ("tiny", "m130m"):
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        say("workload", name)
+        _check_fwd(inp, label=name)
+
+
+def _sampled_channels(Bn, D, count, seed):
+    rng = np.random.default_rng(seed)
+    bs = list(rng.integers(0, Bn, size=count))
+    ds = list(rng.integers(0, D, size=count))
+    # workgroup and wave edges
+    for d in (0, 63, 64, 255, 256, D - 1):
+        if d < D:
+            bs.append(Bn - 1)
+            ds.append(d)
+    return np.array(bs), np.array(ds)
+
+
+@pytest.mark.parametrize("name", ["m2p8b", "long"])
+def test_fwd_workloads_sampled(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    say("workload", name, "sampled")
+    y, ls = _run_fwd(inp)
+    cb, cd = _sampled_channels(w.batch, w.dim, 24 if name == "long" else 64, w.seed)
+    yr, lsr = oracle.fwd_channels(**{k: inp[k] for k in KEYS}, chan_b=cb, chan_d=cd)
+    yg = y[torch.as_tensor(cb), :, torch.as_tensor(cd)]          # [nchan, L]
+    lg = ls[torch.as_tensor(cb), torch.as_tensor(cd)]             # [nchan, N]
+    tol = TOL[inp["u"].dtype]
+    assert rel_err(to_np(yg), yr) <= tol
+    assert rel_err(to_np(lg), lsr) <= max(tol, 1e-5)
+
+
+def test_fwd_deterministic():
+    w = WORKLOADS["m2p8b"]
+    inp = to_dev(make_inputs(w))
+    args = [inp[k] for k in KEYS]
+    y1, _ = ss.fwd(*args)
+    y2, _ = ss.fwd(*args)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y3, _ = ss.fwd(*args)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    inp = to_dev(make_inputs(WORKLOADS["m130m"]))
+    args = [inp[k] for k in KEYS]
+    a, la = ss.fwd(*args, return_last_state=True)
+    b, lb = ss.fwd(*args, return_last_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_native_library_is_loaded():
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert os.path.realpath(ss.library_path) in maps
+
+
+# ----------------------------------------------------------------- backward
+
+def _check_bwd(inp, sp=True, chunk_len=0, label=""):
+    say("bwd", label, tuple(inp["u"].shape), inp["A"].shape[1], inp["u"].dtype)
+    d = to_dev(inp)
+    g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"], delta_softplus=sp, chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    r = oracle.bwd(**{k: inp[k] for k in KEYS}, dy=inp["dy"], delta_softplus=sp)
+    tol = TOL[inp["u"].dtype]
+    errs = {}
+    for k in GRADS:
+        if r[k] is None:
+            assert g[k] is None
+            continue
+        errs[k] = rel_err(to_np(g[k]), r[k])
+    bad = {k: v for k, v in errs.items() if v > tol}
+    assert not bad, f"{label}: {bad} (tol {tol})"
+    return errs
+
+
+BWD_SHAPES = [(1, 1, 1, 1), (1, 5, 3, 4), (2, 16, 64, 16), (2, 17, 65, 16), (1, 100, 300, 16),
+              (3, 63, 31, 8), (1, 47, 20, 17), (1, 33, 10, 64), (1, 20, 9, 130), (1, 18, 5, 256),
+              (2, 300, 257, 16)]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_shapes_f32(shape):
+    Bn, L, D, N = shape
+    _check_bwd(random_inputs(Bn, L, D, N, seed=600 + sum(shape), backward=True),
+               label=str(shape))
+
+
+@pytest.mark.parametrize("combo", range(16))
+def test_bwd_optional_combinations(combo):
+    has_D, has_z, has_bias, sp = [bool(combo >> i & 1) for i in range(4)]
+    inp = random_inputs(2, 70, 40, 16, seed=700 + combo, has_D=has_D, has_z=has_z,
+                        has_bias=has_bias, backward=True)
+    if not sp:
+        inp["delta"] = inp["delta"].abs() * 0.3
+    for chunk in (0, 5):
+        _check_bwd(inp, sp=sp, chunk_len=chunk, label=f"combo{combo}/chunk{chunk}")
+
+
+@pytest.mark.parametrize("io,pa", [("bf16", "f32"), ("f16", "f32"), ("bf16", "bf16")])
+def test_bwd_half_dtypes(io, pa):
+    inp = random_inputs(2, 90, 70, 16, seed=800, io_dtype=io, param_dtype=pa, backward=True)
+    _check_bwd(inp, label=f"{io}/{pa}")
+
+
+def test_bwd_degenerate():
+    inp = random_inputs(2, 30, 20, 1, seed=901, backward=True)
+    inp["A"], inp["B"], inp["C"] = inp["A"][:, :0], inp["B"][:, :, :0], inp["C"][:, :, :0]
+    _check_bwd(inp, label="N0")
+    # L = 0: every reduced gradient is an empty sum
+    inp = random_inputs(2, 1, 20, 4, seed=902, backward=True)
+    for k in ("u", "delta", "z", "B", "C", "dy"):
+        inp[k] = inp[k][:, :0].contiguous()
+    d = to_dev(inp)
+    g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"])
+    torch.cuda.synchronize()
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert torch.all(g[k] == 0), k
+
+
+def test_bwd_workload():
+    w = WORKLOADS["bwd"]
+    inp = make_inputs(w)
+    errs = _check_bwd(inp, label="bwd workload")
+    say("bwd workload errors", errs)
+
+
+def test_bwd_deterministic():
+    inp = to_dev(make_inputs(WORKLOADS["bwd"]))
+    args = [inp[k] for k in KEYS]
+    g1 = ss.bwd(*args, dy=inp["dy"])
+    g2 = ss.bwd(*args, dy=inp["dy"])
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_autograd_function():
+    inp = random_inputs(2, 40, 24, 16, seed=950, backward=True)
+    d = to_dev(inp)
+    leaves = {k: (None if d[k] is None else d[k].clone().requires_grad_(True)) for k in KEYS}
+    y = ss.selective_scan(*[leaves[k] for k in KEYS])
+    y.backward(d["dy"])
+    g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"])
+    for k, gk in zip(KEYS, GRADS):
+        assert torch.equal(leaves[k].grad, g[gk]), k
