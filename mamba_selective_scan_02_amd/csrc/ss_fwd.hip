@@ -25,6 +25,8 @@
 //   3. fwd_scan<FULL>: every chunk runs again from its carried-in state and
 //      writes y (and last_state for the final chunk).
 // With K = 1 only step 3 runs, from h = 0.
+#include <type_traits>
+
 #include "ss_device.h"
 
 namespace ss {
@@ -35,7 +37,13 @@ constexpr int kBlock = 256;
 // The streamed tensors are separate __restrict__ arguments: that tells the
 // compiler the y stores never alias B / C, which lets it keep the uniform
 // B / C loads on the scalar path inside the loop.
-template <typename T, int NS, int G, bool EXACT, int MODE>
+//
+// The time loop has no data-dependent or flag-dependent branches: z presence
+// is a template parameter, the other options are selects, and the y store is
+// unconditional (tail lanes compute the clamped channel D-1 and store the same
+// value to the same address).  Branches inside the loop would force the
+// compiler to drain outstanding loads at every join and undo the prefetch.
+template <typename T, int NS, int G, bool EXACT, int MODE, bool HAS_Z>
 __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
                                                    const T* __restrict__ delta_in,
                                                    const T* __restrict__ B_in,
@@ -57,7 +65,7 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
   const int64_t b = blk / Kg;
   const int64_t d_raw = db * CPB + cl;
   const bool active = d_raw < a.D;
-  const int64_t d = active ? d_raw : a.D - 1;  // tail lanes compute on a valid channel, store nothing
+  const int64_t d = active ? d_raw : a.D - 1;  // tail lanes compute on a valid channel
   const int64_t t0 = k * a.chunk_len;
   const int64_t t1 = (t0 + a.chunk_len < a.L) ? t0 + a.chunk_len : a.L;
   const int64_t L = a.L, D = a.D, N = a.N;
@@ -75,35 +83,67 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
   }
   const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
-  const bool has_z = z_in != nullptr, has_D = a.Dskip != nullptr, sp = a.softplus != 0;
+  const bool sp = a.softplus != 0;
 
   const T* up = u_in + b * L * D + d;
   const T* dp = delta_in + b * L * D + d;
-  const T* zp = has_z ? z_in + b * L * D + d : up;
+  const T* zp = HAS_Z ? z_in + b * L * D + d : up;
   T* yp = y_out + b * L * D + d;
   const T* Bp = B_in + b * L * N + n0;
   const T* Cp = C_in + b * L * N + n0;
 
-  float dsum = 0.0f;
-
-  auto step = [&](int64_t t, float uu, float dr, float zz) {
-    const float x = dr + bv;
-    const float dl = sp ? softplus(x) : x;
-    const float xu = dl * uu;
-    float o = 0.0f;
-    float Bt[NS], Ct[NS];
-    if constexpr (EXACT) {
-      // whole rows; 16-bit rows are read as 32-bit words (host checked alignment)
-      ld_row<T, NS, true>(Bp + t * N, Bt);
-      if (MODE == MODE_FULL) ld_row<T, NS, true>(Cp + t * N, Ct);
+  // B / C rows, software-pipelined one step ahead (wave-uniform: SGPRs).
+  // EXACT rows are prefetched as raw 32-bit words and converted at their use
+  // one step later: a conversion right after the load would make the wave wait
+  // for the load immediately (scalar-load waits cannot be partial).
+  constexpr bool PAIRS = EXACT && sizeof(T) == 2;
+  constexpr int RW = PAIRS ? NS / 2 : NS;  // row words
+  using RowT = typename std::conditional<PAIRS, uint32_t, float>::type;
+  auto fetch_rows = [&](int64_t t, RowT* Br, RowT* Cr) {
+    if constexpr (PAIRS) {
+      const uint32_t* bw = reinterpret_cast<const uint32_t*>(Bp + t * N);
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(Cp + t * N);
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        Br[i] = bw[i];
+        if (MODE == MODE_FULL) Cr[i] = cw[i];
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        const bool ok = n0 + i < N;
-        Bt[i] = ok ? ld(Bp, t * N + i) : 0.0f;
-        Ct[i] = (MODE == MODE_FULL && ok) ? ld(Cp, t * N + i) : 0.0f;
+        const bool ok = EXACT || n0 + i < N;
+        Br[i] = ok ? ld(Bp, t * N + i) : 0.0f;
+        Cr[i] = (MODE == MODE_FULL && ok) ? ld(Cp, t * N + i) : 0.0f;
       }
     }
+  };
+  auto unpack_row = [&](const RowT* r, float* out) {
+    if constexpr (PAIRS) {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) split_pair(r[i], Bp, &out[2 * i], &out[2 * i + 1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) out[i] = r[i];
+    }
+  };
+  RowT Bc[RW], Cc[RW];
+  fetch_rows(t0, Bc, Cc);
+
+  float dsum = 0.0f;
+  auto step = [&](int64_t t, float uu, float dr, float zz) {
+    RowT Bn[RW], Cn[RW];
+    fetch_rows((t + 1 < t1) ? t + 1 : t, Bn, Cn);
+    float Bt[NS], Ct[NS];
+    unpack_row(Bc, Bt);
+    if (MODE == MODE_FULL) unpack_row(Cc, Ct);
+    const float x = dr + bv;
+    float spx = softplus(x);
+    // keep the select branch-free: the empty asm makes spx a computed value
+    // the compiler cannot sink into a branch on the (uniform) flag
+    __asm__ volatile("" : "+v"(spx));
+    const float dl = sp ? spx : x;
+    const float xu = dl * uu;
+    float o = 0.0f;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const float dA = fast_exp2(dl * A2[i]);
@@ -114,13 +154,15 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
     if (MODE == MODE_FULL) {
 #pragma unroll
       for (int m = 1; m < G; m <<= 1) o += __shfl_xor(o, m, 64);
-      if (has_D) o = __builtin_fmaf(Dv, uu, o);
-      if (has_z) o *= zz * sigmoid(zz);
-      if (active && g == 0) yp[t * D] = from_f32<T>(o);
+      o = __builtin_fmaf(Dv, uu, o);
+      if (HAS_Z) o *= zz * sigmoid(zz);
+      yp[t * D] = from_f32<T>(o);   // every lane of a channel holds the same o
     }
+#pragma unroll
+    for (int i = 0; i < RW; ++i) { Bc[i] = Bn[i]; Cc[i] = Cn[i]; }
   };
 
-  // Software pipeline: the per-lane inputs of the next U steps are loaded
+  // Software pipeline for the per-lane inputs: the next U steps are loaded
   // while the current U steps compute.  Indices are clamped into the chunk,
   // so every load is in bounds; clamped values are never used.
   constexpr int U = 4;
@@ -131,7 +173,7 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
       const int64_t tt = (tb + j < t1) ? tb + j : t1 - 1;
       lu[j] = ld(up, tt * D);
       ldl[j] = ld(dp, tt * D);
-      lz[j] = (MODE == MODE_FULL && has_z) ? ld(zp, tt * D) : 0.0f;
+      lz[j] = (MODE == MODE_FULL && HAS_Z) ? ld(zp, tt * D) : 0.0f;
     }
   };
   load_group(t0, cu, cd, cz);
@@ -144,7 +186,6 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
 #pragma unroll
     for (int j = 0; j < U; ++j) { cu[j] = nu[j]; cd[j] = nd[j]; cz[j] = nz[j]; }
   }
-#pragma unroll
   for (int j = 0; j < U - 1; ++j)
     if (t + j < t1) step(t + j, cu[j], cd[j], cz[j]);
 
@@ -200,7 +241,7 @@ __global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
 
 // ------------------------------------------------------------------ launch
 
-template <typename T, int NS, int G, bool EXACT>
+template <typename T, int NS, int G, bool EXACT, bool HAS_Z>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const T* U = static_cast<const T*>(a.u);
   const T* DL = static_cast<const T*>(a.delta);
@@ -212,7 +253,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const int64_t nbd = (a.D + cpb - 1) / cpb;
   if (a.K > 1) {
     const int64_t grid_sum = a.Bn * (a.K - 1) * nbd;  // chunks 0 .. K-2
-    fwd_scan<T, NS, G, EXACT, MODE_SUMMARY><<<dim3((unsigned)grid_sum), dim3(kBlock), 0, s>>>(
+    fwd_scan<T, NS, G, EXACT, MODE_SUMMARY, false><<<dim3((unsigned)grid_sum), dim3(kBlock), 0, s>>>(
         U, DL, Bm, Cm, Z, Y, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -224,7 +265,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
     }
   }
   const int64_t grid = a.Bn * a.K * nbd;
-  fwd_scan<T, NS, G, EXACT, MODE_FULL><<<dim3((unsigned)grid), dim3(kBlock), 0, s>>>(
+  fwd_scan<T, NS, G, EXACT, MODE_FULL, HAS_Z><<<dim3((unsigned)grid), dim3(kBlock), 0, s>>>(
       U, DL, Bm, Cm, Z, Y, a);
   return hipGetLastError();
 }
@@ -235,8 +276,10 @@ template <typename T, int NS, int G>
 static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t s) {
   const bool rows_ok = sizeof(T) == 4 || ((reinterpret_cast<uintptr_t>(a.B) % 4 == 0) &&
                                           (reinterpret_cast<uintptr_t>(a.C) % 4 == 0));
-  return (a.N == (int64_t)NS * G && rows_ok) ? launch_fwd_t<T, NS, G, true>(a, s)
-                                             : launch_fwd_t<T, NS, G, false>(a, s);
+  const bool exact = a.N == (int64_t)NS * G && rows_ok;
+  if (a.z != nullptr)
+    return exact ? launch_fwd_t<T, NS, G, true, true>(a, s) : launch_fwd_t<T, NS, G, false, true>(a, s);
+  return exact ? launch_fwd_t<T, NS, G, true, false>(a, s) : launch_fwd_t<T, NS, G, false, false>(a, s);
 }
 
 template <typename T>

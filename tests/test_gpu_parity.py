@@ -79,6 +79,8 @@ def test_fwd_optional_combinations(combo):
                         has_bias=has_bias)
     if not sp:  # keep delta_eff positive without softplus
         inp["delta"] = inp["delta"].abs() * 0.3
+        if inp["delta_bias"] is not None:
+            inp["delta_bias"] = inp["delta_bias"].abs() * 0.01
     for chunk in (0, 32):
         _check_fwd(inp, sp=sp, chunk_len=chunk, label=f"combo{combo}/chunk{chunk}")
 
@@ -223,6 +225,8 @@ def test_bwd_optional_combinations(combo):
                         has_bias=has_bias, backward=True)
     if not sp:
         inp["delta"] = inp["delta"].abs() * 0.3
+        if inp["delta_bias"] is not None:
+            inp["delta_bias"] = inp["delta_bias"].abs() * 0.01
     for chunk in (0, 5):
         _check_bwd(inp, sp=sp, chunk_len=chunk, label=f"combo{combo}/chunk{chunk}")
 
