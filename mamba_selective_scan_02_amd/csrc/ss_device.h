@@ -105,6 +105,44 @@ __device__ __forceinline__ float sigmoid(float x) {
   return fast_rcp(1.0f + fast_exp2(-x * kLog2e));
 }
 
+// Buffer resources (raw, stride 0) over a byte range: loads beyond the range
+// return 0 and stores beyond it are dropped, which replaces clamping and
+// predication for tails.  Offsets are 32-bit (the range is < 2^31 bytes).
+constexpr int kBufferFlags = 0x00020000;  // gfx9 family raw buffer, 32-bit dwords
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferFlags);
+}
+template <typename T> __device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, int voff, int soff);
+template <> __device__ __forceinline__ float buf_ld<float>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+template <> __device__ __forceinline__ float buf_ld<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return to_f32(bf16_t{__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)});
+}
+template <> __device__ __forceinline__ float buf_ld<f16_t>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return to_f32(f16_t{__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)});
+}
+template <typename T> __device__ __forceinline__ void buf_st(float v, __amdgpu_buffer_rsrc_t r, int voff, int soff);
+template <> __device__ __forceinline__ void buf_st<float>(float v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ void buf_st<bf16_t>(float v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(v).bits, r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ void buf_st<f16_t>(float v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(from_f32<f16_t>(v).bits, r, voff, soff, 0);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
+// Within every aligned group of 16 workgroup ids this remap puts logical
+// neighbours 2j and 2j+1 on the same XCD (ids r and r + 8), so two channel
+// blocks that share 128-byte lines fetch them through one L2.
+__device__ __forceinline__ int64_t xcd_pair_remap(int64_t x, int64_t total) {
+  const int64_t q = x >> 4, r = x & 15;
+  return (q * 16 + 16 <= total) ? q * 16 + 2 * (r & 7) + (r >> 3) : x;
+}
+
 // Forward launch parameters.
 struct FwdArgs {
   const void* u;

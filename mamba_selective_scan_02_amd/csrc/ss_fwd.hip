@@ -241,6 +241,15 @@ __global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
 
 // ------------------------------------------------------------------ launch
 
+hipError_t launch_fwd_carry(const FwdArgs& a, hipStream_t s) {
+  if (a.N <= 0 || a.K <= 1) return hipSuccess;
+  const int64_t nbd2 = (a.D + kBlock - 1) / kBlock;
+  fwd_carry<<<dim3((unsigned)(a.Bn * a.N * nbd2)), dim3(kBlock), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_tile(const FwdArgs& a, int io_dtype, int ns, hipStream_t s);
+
 template <typename T, int NS, int G, bool EXACT, bool HAS_Z>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const T* U = static_cast<const T*>(a.u);
@@ -257,12 +266,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
         U, DL, Bm, Cm, Z, Y, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.N > 0) {
-      const int64_t nbd2 = (a.D + kBlock - 1) / kBlock;
-      fwd_carry<<<dim3((unsigned)(a.Bn * a.N * nbd2)), dim3(kBlock), 0, s>>>(a);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+    if ((e = launch_fwd_carry(a, s)) != hipSuccess) return e;
   }
   const int64_t grid = a.Bn * a.K * nbd;
   fwd_scan<T, NS, G, EXACT, MODE_FULL, HAS_Z><<<dim3((unsigned)grid), dim3(kBlock), 0, s>>>(
@@ -282,16 +286,12 @@ static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t s) {
   return exact ? launch_fwd_t<T, NS, G, true, false>(a, s) : launch_fwd_t<T, NS, G, false, false>(a, s);
 }
 
+// One lane per channel (G = 1) or G = 2, 4 lanes per channel, 64 states per
+// lane: the path for N > 32 (N <= 32 uses the 8-lane tile kernel).
 template <typename T>
 static hipError_t launch_fwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s) {
-  if (gl == 1) {
-    switch (ns) {
-      case 4: return launch_fwd_e<T, 4, 1>(a, s);
-      case 8: return launch_fwd_e<T, 8, 1>(a, s);
-      case 16: return launch_fwd_e<T, 16, 1>(a, s);
-      case 32: return launch_fwd_e<T, 32, 1>(a, s);
-      case 64: return launch_fwd_e<T, 64, 1>(a, s);
-    }
+  if (ns == 64 && gl == 1) {
+    return launch_fwd_e<T, 64, 1>(a, s);
   } else if (ns == 64 && gl == 2) {
     return launch_fwd_e<T, 64, 2>(a, s);
   } else if (ns == 64 && gl == 4) {
@@ -301,6 +301,7 @@ static hipError_t launch_fwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s)
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_t s) {
+  if (gl == 8) return launch_fwd_tile(a, io_dtype, ns, s);
   switch (io_dtype) {
     case 0: return launch_fwd_ty<float>(a, ns, gl, s);
     case 1: return launch_fwd_ty<f16_t>(a, ns, gl, s);

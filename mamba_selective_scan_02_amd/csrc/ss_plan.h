@@ -18,6 +18,9 @@ constexpr int kBwdTile = 16;
 constexpr int kBwdChunksPerGroup = 4;
 // Channels per workgroup.
 constexpr int kChannelsPerBlock = 256;
+// Tile kernel: steps of one prep tile (the own-step loads run up to two tiles
+// past the chunk; those offsets must also stay below 2^31).
+constexpr int64_t GL_MAX_TILE = 24;
 
 struct Plan {
   int NS = 4, G = 1;          // forward: states per lane, lanes per channel
@@ -32,11 +35,13 @@ struct Plan {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Forward mapping by state count: N <= 32 uses 8 lanes per channel with NS
+// states each (the tile kernel); larger N one lane per channel with 64 states
+// (G = 2 or 4 lanes above 64 states).
 inline void pick_bucket(int64_t N, int* NS, int* G) {
-  if (N <= 4) { *NS = 4; *G = 1; }
-  else if (N <= 8) { *NS = 8; *G = 1; }
-  else if (N <= 16) { *NS = 16; *G = 1; }
-  else if (N <= 32) { *NS = 32; *G = 1; }
+  if (N <= 8) { *NS = 1; *G = 8; }
+  else if (N <= 16) { *NS = 2; *G = 8; }
+  else if (N <= 32) { *NS = 4; *G = 8; }
   else if (N <= 64) { *NS = 64; *G = 1; }
   else if (N <= 128) { *NS = 64; *G = 2; }
   else { *NS = 64; *G = 4; }
@@ -57,15 +62,16 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
     if (d.chunk_len > 0) {
       lc = d.chunk_len < L ? d.chunk_len : L;
     } else {
-      // Waves that one chunk index provides.  At half the SIMDs or more a
-      // single pass (no second sweep) is cheaper; below that the time axis
-      // is cut so the grid reaches about two waves per SIMD, with chunks of
-      // at least 64 steps.
+      // Waves that one chunk index provides.  A SIMD needs several resident
+      // waves to approach its VALU rate (a lone wave issues at about a third
+      // of it), so below ~3 waves per SIMD (1024 SIMDs) the time axis is cut
+      // into chunks until the grid reaches about 4 waves per SIMD, with chunks
+      // of at least 64 steps; the chunk summaries cost one extra sweep.
       const int64_t cpw = 64 / p.G;
       const int64_t waves = Bn * ((D + cpw - 1) / cpw);
-      const int64_t target = 2048;
+      const int64_t target = 4096;
       int64_t K = 1;
-      if (waves < 512) {
+      if (waves < 3072) {
         K = (target + waves - 1) / waves;
         const int64_t kmax = (L + 63) / 64;
         if (K > kmax) K = kmax;
@@ -74,6 +80,9 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
       lc = (L + K - 1) / K;
       lc = (lc + 3) & ~int64_t(3);
     }
+    // a chunk's rows of one [B, L, D] tensor must fit a 32-bit buffer range
+    const int64_t lc_cap = (int64_t)0x7fffffff / ((D > 0 ? D : 1) * 4) - GL_MAX_TILE;
+    if (lc > lc_cap) lc = lc_cap > 8 ? lc_cap & ~int64_t(7) : 8;
     p.chunk_len = lc;
     p.K = (L + lc - 1) / lc;
     size_t off = 0;

@@ -146,7 +146,7 @@ def test_empty_problem_is_a_noop():
 def test_plan_is_a_function_of_shape():
     # large B * D: single pass
     p = ss.plan(_desc(B=8, L=2048, D=5120, N=16, io=ss.SS_BF16))
-    assert (p.n_chunks, p.n_launches, p.states_per_lane, p.lanes_per_channel) == (1, 1, 16, 1)
+    assert (p.n_chunks, p.n_launches, p.states_per_lane, p.lanes_per_channel) == (1, 1, 2, 8)
     assert ss.ss_workspace_size(_desc(B=8, L=2048, D=5120, N=16, io=ss.SS_BF16), 0) == 0
     # small B * D, long L: chunked two-level scan
     p = ss.plan(_desc(B=1, L=262144, D=512, N=16))
@@ -156,8 +156,9 @@ def test_plan_is_a_function_of_shape():
     p = ss.plan(_desc(B=1, L=100, D=32, N=16, chunk=7))
     assert (p.chunk_len, p.n_chunks) == (7, 15)
     # N buckets
-    for n, (ns, g) in {1: (4, 1), 5: (8, 1), 16: (16, 1), 17: (32, 1), 64: (64, 1),
-                       65: (64, 2), 200: (64, 4), 256: (64, 4)}.items():
+    for n, (ns, g) in {0: (1, 8), 1: (1, 8), 5: (1, 8), 9: (2, 8), 16: (2, 8), 17: (4, 8),
+                       32: (4, 8), 33: (64, 1), 64: (64, 1), 65: (64, 2), 200: (64, 4),
+                       256: (64, 4)}.items():
         p = ss.plan(_desc(N=n))
         assert (p.states_per_lane, p.lanes_per_channel) == (ns, g), n
     # backward: chunks of at most 16 steps
