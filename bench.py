@@ -36,26 +36,47 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha() -> str:
+# Sources each measured kernel is built from (its counters go stale when any changes).
+KERNEL_SOURCES = {
+    "fwd_tile_m2p8b": ["ss_fwd_tile.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp"],
+    "ss_bwd_bwd": ["ss_bwd.hip", "ss_fwd.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp"],
+}
+
+
+def kernel_sources_sha(tag: str) -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in KERNEL_SOURCES[tag]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(tag: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
-    if the kernel sources changed since the counters were taken."""
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary
+    (profiles/<tag>_pmc.txt), or None if the kernel's sources changed since
+    the counters were taken."""
     path = os.path.join(PROFILES, f"{tag}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_sha = re.search(r"kernel_sources_sha:\s*(\S+)", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_b or m_sha.group(1) != kernel_sources_sha():
+    if not m_sha or not m_b or m_sha.group(1) != kernel_sources_sha(tag):
         return None
     return float(m_b.group(1))
+
+
+def calibration_copy(nbytes: int = 512 << 20, reps: int = 3):
+    """A plain device copy of known size: what FETCH_SIZE / WRITE_SIZE read for
+    it calibrates the counters (rocprofv3 --pmc runs of this script)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def algorithmic_bytes(w) -> int:
@@ -114,13 +135,17 @@ def cpu_baseline(w, inp, budget_s: float):
     keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
     cores = oracle.default_threads()
     Bn, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
-    # calibration run on a few channels, then the sized sample
-    probe = min(D, max(cores, 8))
-    cb = np.repeat(np.arange(Bn), probe)
-    cd = np.tile(np.arange(probe), Bn)
-    t0 = time.perf_counter()
-    oracle.fwd_channels(**{k: inp[k] for k in keys}, chan_b=cb, chan_d=cd, nthreads=cores)
-    dt = time.perf_counter() - t0
+    # calibration: grow a probe until it runs for a second, then size the sample
+    nd = min(D, max(1, cores // Bn))
+    while True:
+        cb = np.repeat(np.arange(Bn), nd)
+        cd = np.tile(np.arange(nd), Bn)
+        t0 = time.perf_counter()
+        oracle.fwd_channels(**{k: inp[k] for k in keys}, chan_b=cb, chan_d=cd, nthreads=cores)
+        dt = time.perf_counter() - t0
+        if dt >= 1.0 or nd >= D:
+            break
+        nd = min(D, nd * 4)
     per_chan = dt / cb.size
     nd = int(min(D, max(1, budget_s / per_chan / Bn)))
     cb = np.repeat(np.arange(Bn), nd)
@@ -153,6 +178,8 @@ def main():
                     help="approximate CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run a plain 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the "
@@ -164,6 +191,8 @@ def main():
     from ss_inputs import WORKLOADS, make_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calib_copy:
+        calibration_copy()
     keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
     w = WORKLOADS["m2p8b"]
     log(f"generating {w.name} inputs")
@@ -208,7 +237,7 @@ def main():
         "hbm_gbs": gbs,
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "algorithmic_bytes": abytes,
-        "roofline": {"bound": "alu", "kernel": "fwd_scan (single pass)",
+        "roofline": {"bound": "alu", "kernel": "fwd_tile (single pass, 8 lanes per channel)",
                      "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / FP32_VECTOR_PEAK_TFLOPS,
                      "flops_per_update": FLOPS_PER_UPDATE,

@@ -60,5 +60,20 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_microbench(verbose: bool = False) -> str:
+    """Hardware-rate microbenchmark (microbench/rates.hip -> microbench/rates)."""
+    src = os.path.join(PKG, "microbench", "rates.hip")
+    out = os.path.join(PKG, "microbench", "rates")
+    cmd = [HIPCC, "-O3", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-Wno-unused-result", src, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("microbench build failed:\n" + r.stdout + r.stderr)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose="-q" not in sys.argv)
+    build_microbench(verbose="-q" not in sys.argv)
