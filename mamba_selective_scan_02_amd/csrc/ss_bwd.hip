@@ -317,7 +317,8 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
 
 // --------------------------------------------------------------- finalize
 
-// dB[b,t,n], dC[b,t,n] = sums over the channel blocks, in block order.
+// dB[b,t,n], dC[b,t,n] = sums over the channel blocks, in block order (loads
+// are issued in batches of 8, the adds stay in index order).
 template <typename Tio>
 __global__ void bwd_finalize_bc(const BwdArgs a) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // (b*L + t)*N + n
@@ -326,12 +327,40 @@ __global__ void bwd_finalize_bc(const BwdArgs a) {
   const int64_t bt = i / N, n = i % N;
   const float* p = a.part_bc + bt * a.nwgd * 2 * N + n;
   float sb = 0.0f, sc = 0.0f;
-  for (int64_t w = 0; w < a.nwgd; ++w) {
+  constexpr int U = 8;
+  int64_t w = 0;
+  for (; w + U <= a.nwgd; w += U) {
+    float vb[U], vc[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      vb[j] = p[(w + j) * 2 * N];
+      vc[j] = p[(w + j) * 2 * N + N];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) { sb += vb[j]; sc += vc[j]; }
+  }
+  for (; w < a.nwgd; ++w) {
     sb += p[w * 2 * N];
     sc += p[w * 2 * N + N];
   }
   static_cast<Tio*>(a.dB)[i] = from_f32<Tio>(sb);
   static_cast<Tio*>(a.dC)[i] = from_f32<Tio>(sc);
+}
+
+// Fixed-order sum of `count` partials p[0], p[stride], ... (loads batched).
+__device__ __forceinline__ float ordered_sum(const float* p, int64_t count, int64_t stride) {
+  float s = 0.0f;
+  constexpr int U = 8;
+  int64_t j = 0;
+  for (; j + U <= count; j += U) {
+    float v[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) v[q] = p[(j + q) * stride];
+#pragma unroll
+    for (int q = 0; q < U; ++q) s += v[q];
+  }
+  for (; j < count; ++j) s += p[j * stride];
+  return s;
 }
 
 // dA[d,n] = sum over (b, chunk group) in that order; dD, ddelta_bias likewise.
@@ -342,22 +371,11 @@ __global__ void bwd_finalize_d(const BwdArgs a) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= nn * D) return;
   const int64_t n = i / D, d = i % D;
-  if (N > 0) {
-    float s = 0.0f;
-    for (int64_t bk = 0; bk < a.Bn * a.KG; ++bk) s += a.part_dA[(bk * N + n) * D + d];
-    st_param(a.dA, d * N + n, a.param_dtype, s);
-  }
+  const int64_t cnt = a.Bn * a.KG;
+  if (N > 0) st_param(a.dA, d * N + n, a.param_dtype, ordered_sum(a.part_dA + n * D + d, cnt, N * D));
   if (n == 0) {
-    if (a.dD) {
-      float s = 0.0f;
-      for (int64_t bk = 0; bk < a.Bn * a.KG; ++bk) s += a.part_dD[bk * D + d];
-      st_param(a.dD, d, a.param_dtype, s);
-    }
-    if (a.dbias) {
-      float s = 0.0f;
-      for (int64_t bk = 0; bk < a.Bn * a.KG; ++bk) s += a.part_db[bk * D + d];
-      st_param(a.dbias, d, a.param_dtype, s);
-    }
+    if (a.dD) st_param(a.dD, d, a.param_dtype, ordered_sum(a.part_dD + d, cnt, D));
+    if (a.dbias) st_param(a.dbias, d, a.param_dtype, ordered_sum(a.part_db + d, cnt, D));
   }
 }
 
@@ -376,8 +394,57 @@ static hipError_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
 
 // ------------------------------------------------------------------ launch
 
+hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t s) {
+  if (a.K <= 1 || a.N <= 0) return hipSuccess;
+  const int64_t nbd = (a.D + kChannelsPerBlock - 1) / kChannelsPerBlock;
+  BwdArgs c = a;
+  c.nwgd = nbd;  // the carry's own channel blocking (256 per workgroup)
+  bwd_carry<<<dim3((unsigned)(a.Bn * a.N * nbd)), dim3(kChannelsPerBlock), 0, s>>>(c);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_finalize(const BwdArgs& a, hipStream_t s) {
+  hipError_t e;
+  if (a.Bn * a.L * a.N > 0) {
+    const int64_t n = a.Bn * a.L * a.N;
+    switch (a.io_dtype) {
+      case 0: bwd_finalize_bc<float><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a); break;
+      case 1: bwd_finalize_bc<f16_t><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a); break;
+      default: bwd_finalize_bc<bf16_t><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a); break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t nd = (a.N > 0 ? a.N : 1) * a.D;
+  bwd_finalize_d<<<dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <typename Tio>
-static hipError_t launch_bwd_t(BwdArgs a, const Plan& p, hipStream_t s) {
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  const int64_t Bn = a.Bn, N = a.N;
+  hipError_t e;
+  const size_t tile_bytes = sizeof(float) * 2 * (size_t)N * T;
+  if (a.K > 1) {
+    bwd_summary<Tio><<<dim3((unsigned)(Bn * a.K * a.nwgd)), dim3(kChannelsPerBlock), tile_bytes,
+                       s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_bwd_carry(a, s)) != hipSuccess) return e;
+  }
+  const size_t main_bytes = tile_bytes + sizeof(float) * 32 * kRedStride;
+  if (main_bytes > 64 * 1024) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_main<Tio>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)main_bytes);
+    if (e != hipSuccess) return e;
+  }
+  bwd_main<Tio><<<dim3((unsigned)(Bn * a.KG * a.nwgd)), dim3(kChannelsPerBlock), main_bytes, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_bwd_finalize(a, s);
+}
+
+hipError_t launch_bwd_tile(const BwdArgs& a, int ns, hipStream_t s);  // ss_bwd_tile.hip
+
+hipError_t launch_bwd(const BwdArgs& a_in, const Plan& p, int io_dtype, hipStream_t s) {
+  BwdArgs a = a_in;
   const int64_t Bn = a.Bn, L = a.L, D = a.D, N = a.N;
   const int64_t io = a.io_dtype == 0 ? 4 : 2, pa = a.param_dtype == 0 ? 4 : 2;
   if (Bn * L * D == 0) {
@@ -398,40 +465,11 @@ static hipError_t launch_bwd_t(BwdArgs a, const Plan& p, hipStream_t s) {
   a.part_db = reinterpret_cast<float*>(a.ws + p.off_part_db);
   a.KG = p.KG;
   a.nwgd = p.nwgd;
-  hipError_t e;
-  const size_t tile_bytes = sizeof(float) * 2 * (size_t)N * T;
-  if (a.K > 1) {
-    bwd_summary<Tio><<<dim3((unsigned)(Bn * a.K * a.nwgd)), dim3(kChannelsPerBlock), tile_bytes,
-                       s>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (N > 0) {
-      bwd_carry<<<dim3((unsigned)(Bn * N * a.nwgd)), dim3(kChannelsPerBlock), 0, s>>>(a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-  }
-  const size_t main_bytes = tile_bytes + sizeof(float) * 32 * kRedStride;
-  if (main_bytes > 64 * 1024) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_main<Tio>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)main_bytes);
-    if (e != hipSuccess) return e;
-  }
-  bwd_main<Tio><<<dim3((unsigned)(Bn * a.KG * a.nwgd)), dim3(kChannelsPerBlock), main_bytes, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (Bn * L * N > 0) {
-    const int64_t n = Bn * L * N;
-    bwd_finalize_bc<Tio><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  const int64_t nd = (N > 0 ? N : 1) * D;
-  bwd_finalize_d<<<dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd(const BwdArgs& a, const Plan& p, int io_dtype, hipStream_t s) {
+  if (p.bwd_tile) return launch_bwd_tile(a, p.NS, s);
   switch (io_dtype) {
-    case 0: return launch_bwd_t<float>(a, p, s);
-    case 1: return launch_bwd_t<f16_t>(a, p, s);
-    case 2: return launch_bwd_t<bf16_t>(a, p, s);
+    case 0: return launch_bwd_t<float>(a, s);
+    case 1: return launch_bwd_t<f16_t>(a, s);
+    case 2: return launch_bwd_t<bf16_t>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,531 @@
+// Backward selective scan for N <= 16 with a channel's states split over 8
+// lanes (gfx950).
+//
+// Same gradients and equations as ss_bwd.hip (chain rule through the
+// recurrence of the baracuda-kernels page "src/attention/selective_scan.rs",
+// "Algorithm summary"; gradient set of its SelectiveScanBackwardArgs;
+// per-channel reverse sweep and fixed-order partial reductions as in stage B3
+// of the mamba-rs page "mamba_ssm/gpu/backward.rs").  Mapping as in the
+// forward tile kernel: 8 lanes own a channel, lane g holds states
+// n = g*NS .. g*NS+NS-1 (NS = 1 or 2); a wave is 8 channels, a 256-lane
+// workgroup 32; per 8-step tile, lane g prepares the per-step scalars of step
+// t0 + 8j + g and hands them to the channel's lanes through LDS; sums over a
+// channel's states are DPP reduce-scatters over its 8 lanes.
+//
+// Time is cut into chunks of at most 64 steps (8 tiles):
+//   bwd_tile_sum   per chunk, from zero: forward end state S, reverse summary
+//                  Sb = sum_s (prod_{r<=s} a_r) g_s C_s (built per 8-step tile
+//                  and combined with the tiles' decays), and sum of dt;
+//   bwd_carry      (ss_bwd.hip) the forward and reverse chains over chunks;
+//   bwd_tile_main  per chunk: pass 1 runs forward from the carried-in state
+//                  and keeps the state at every tile start (LDS); pass 2 walks
+//                  the tiles backwards, recomputes each tile's states and
+//                  decays in registers and runs the adjoint from the carried
+//                  end-of-chunk adjoint, reset at each tile start from a
+//                  tile-level chain (accuracy: see pass 2).  dB / dC are summed over the
+//                  workgroup's 32 channels through LDS in a fixed order and
+//                  written as per-channel-block partials; dA / dD / dbias are
+//                  written as per-chunk partials.
+//   bwd_finalize_* (ss_bwd.hip) fixed-order sums of the partials.
+#include "ss_device.h"
+#include "ss_plan.h"
+
+namespace ss {
+
+namespace {
+
+constexpr int kBT = 256;              // threads per workgroup
+constexpr int BGL = 8;                // lanes per channel
+constexpr int BCPW = kBT / BGL;       // channels per workgroup (32)
+constexpr int BTC = 64;               // max steps per chunk
+constexpr int BNT = BTC / BGL;        // tiles per chunk (8)
+constexpr int BTS = 68;               // staged B/C row stride (floats)
+constexpr int BXS = 9;                // exchange row stride (float4) per channel
+
+template <int CTRL>
+__device__ __forceinline__ float bdpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xf, 0xf, true));
+}
+
+// Sum over each group of 8 consecutive lanes; every lane gets the sum.
+__device__ __forceinline__ float bsum8(float v) {
+  v += bdpp<0xB1>(v);
+  v += bdpp<0x4E>(v);
+  v += bdpp<0x141>(v);
+  return v;
+}
+
+// Lane g of each 8-lane group ends with the group's sum of o[g] (butterfly
+// over partners g^7, g^2, g^1; see the forward tile kernel).
+__device__ __forceinline__ float brs8(const float (&o)[8], int g) {
+  const bool lo4 = (g & 4) == 0, lo2 = (g & 2) == 0, lo1 = (g & 1) == 0;
+  float ra[4], rb[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float send = lo4 ? o[4 + k] : o[k];
+    const float keep = lo4 ? o[k] : o[4 + k];
+    ra[k] = keep + bdpp<0x141>(send);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float send = lo2 ? ra[2 + k] : ra[k];
+    const float keep = lo2 ? ra[k] : ra[2 + k];
+    rb[k] = keep + bdpp<0x4E>(send);
+  }
+  const float send = lo1 ? rb[1] : rb[0];
+  const float keep = lo1 ? rb[0] : rb[1];
+  return keep + bdpp<0xB1>(send);
+}
+
+}  // namespace
+
+// Decoded position of a workgroup / lane (shared by the two kernels).
+struct BTilePos {
+  int g, cl;
+  int64_t db, k, b, d, t0, t1;
+  bool active;
+};
+
+__device__ __forceinline__ BTilePos btile_pos(const BwdArgs& a) {
+  BTilePos p;
+  const int tid = threadIdx.x;
+  p.g = tid % BGL;
+  p.cl = tid / BGL;
+  int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
+  p.db = blk % a.nwgd;
+  blk /= a.nwgd;
+  p.k = blk % a.K;
+  p.b = blk / a.K;
+  const int64_t d_raw = p.db * BCPW + p.cl;
+  p.active = d_raw < a.D;
+  p.d = p.active ? d_raw : a.D - 1;
+  p.t0 = p.k * a.chunk_len;
+  p.t1 = (p.t0 + a.chunk_len < a.L) ? p.t0 + a.chunk_len : a.L;
+  return p;
+}
+
+// Stage the chunk's B and C rows as f32, [n][t], rows padded; states n >= N
+// and steps past the chunk are zero.
+template <typename T, int NP>
+__device__ __forceinline__ void bstage(float (*sB)[BTS], float (*sC)[BTS], const T* B, const T* C,
+                                       int64_t b, int64_t t0, int64_t nsteps, int64_t L,
+                                       int64_t N) {
+  constexpr int ES = sizeof(T);
+  const auto rB = make_rsrc(B + (b * L + t0) * N, nsteps * N * ES);
+  const auto rC = make_rsrc(C + (b * L + t0) * N, nsteps * N * ES);
+  for (int e = threadIdx.x; e < BTC * NP; e += kBT) {
+    const int tt = e / NP, n = e % NP;
+    const bool ok = n < N;
+    const int off = (tt * (int)N + (ok ? n : 0)) * ES;
+    const float vb = buf_ld<T>(rB, off, 0), vc = buf_ld<T>(rC, off, 0);
+    sB[n][tt] = ok ? vb : 0.0f;
+    sC[n][tt] = ok ? vc : 0.0f;
+  }
+}
+
+// ----------------------------------------------------------------- summary
+
+template <typename T, int NS, bool HAS_Z>
+__global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
+                                                    const T* __restrict__ delta_in,
+                                                    const T* __restrict__ B_in,
+                                                    const T* __restrict__ C_in,
+                                                    const T* __restrict__ z_in,
+                                                    const T* __restrict__ dy_in, const BwdArgs a) {
+  constexpr int NP = NS * BGL;
+  constexpr int ES = sizeof(T);
+  __shared__ __attribute__((aligned(16))) float sB[NP][BTS];
+  __shared__ __attribute__((aligned(16))) float sC[NP][BTS];
+  __shared__ __attribute__((aligned(16))) float4 xch[BCPW][BXS];
+  const BTilePos P = btile_pos(a);
+  const int g = P.g, cl = P.cl, n0 = g * NS;
+  const int64_t L = a.L, D = a.D, N = a.N, b = P.b, d = P.d;
+  const int64_t nsteps = P.t1 - P.t0;
+
+  bstage<T, NP>(sB, sC, B_in, C_in, b, P.t0, nsteps, L, N);
+
+  // Sb is built two-level: per tile from its own start (E, sbl) and then
+  // Sb += (decay of the chunk's earlier tiles) * sbl, the decay of a tile
+  // being exp2(A2 * sum of its dt); a product of per-step decays over 64 steps
+  // would drift by one rounding per step.
+  float A2[NS], h[NS], Sb[NS], PP[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int n = n0 + i;
+    A2[i] = n < N ? ld_param(a.A, d * N + n, a.param_dtype) * kLog2e : 0.0f;
+    h[i] = 0.0f;
+    Sb[i] = 0.0f;
+    PP[i] = 1.0f;
+  }
+  const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
+  const bool sp = a.softplus != 0;
+  const int64_t row0 = (b * L + P.t0) * D;
+  const auto rs_u = make_rsrc(u_in + row0, nsteps * D * ES);
+  const auto rs_d = make_rsrc(delta_in + row0, nsteps * D * ES);
+  const auto rs_z = make_rsrc(HAS_Z ? z_in + row0 : u_in + row0, nsteps * D * ES);
+  const auto rs_y = make_rsrc(dy_in + row0, nsteps * D * ES);
+  const int voff = (int)((g * D + d) * ES);
+  const int sstep = (int)(BGL * D * ES);
+  __syncthreads();
+
+  float dsum = 0.0f;
+  const int ntile = (int)((nsteps + BGL - 1) / BGL);
+  for (int j = 0; j < ntile; ++j) {
+    const int so = j * sstep;
+    const float uu = buf_ld<T>(rs_u, voff, so), dr = buf_ld<T>(rs_d, voff, so);
+    const float dyv = buf_ld<T>(rs_y, voff, so);
+    const float zz = HAS_Z ? buf_ld<T>(rs_z, voff, so) : 0.0f;
+    const bool valid = (int64_t)j * BGL + g < nsteps;
+    const float x = dr + bv;
+    float spx = softplus(x);
+    __asm__ volatile("" : "+v"(spx));
+    float dl = sp ? spx : x;
+    float gg = HAS_Z ? dyv * zz * sigmoid(zz) : dyv;
+    dl = valid ? dl : 0.0f;
+    const float xu = valid ? dl * uu : 0.0f;
+    gg = valid ? gg : 0.0f;
+    dsum += dl;
+    xch[cl][g] = make_float4(dl, xu, gg, 0.0f);
+    const float dst = bsum8(dl);       // the tile's sum of dt (same on the 8 lanes)
+    float4 ex[BGL];
+#pragma unroll
+    for (int s = 0; s < BGL; ++s) ex[s] = xch[cl][s];
+    float E[NS], sbl[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      E[i] = 1.0f;
+      sbl[i] = 0.0f;
+    }
+#pragma unroll
+    for (int sh = 0; sh < BGL; sh += 4) {
+      float4 bq[NS], cq[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        bq[i] = *reinterpret_cast<const float4*>(&sB[n0 + i][j * BGL + sh]);
+        cq[i] = *reinterpret_cast<const float4*>(&sC[n0 + i][j * BGL + sh]);
+      }
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss) {
+        const float4 e = ex[sh + ss];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const float bvs = ss == 0 ? bq[i].x : ss == 1 ? bq[i].y : ss == 2 ? bq[i].z : bq[i].w;
+          const float cvs = ss == 0 ? cq[i].x : ss == 1 ? cq[i].y : ss == 2 ? cq[i].z : cq[i].w;
+          const float av = fast_exp2(e.x * A2[i]);
+          h[i] = __builtin_fmaf(av, h[i], e.y * bvs);
+          E[i] *= av;
+          sbl[i] = __builtin_fmaf(E[i], e.z * cvs, sbl[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      Sb[i] = __builtin_fmaf(PP[i], sbl[i], Sb[i]);
+      PP[i] *= fast_exp2(A2[i] * dst);
+    }
+  }
+  dsum = bsum8(dsum);
+  if (!P.active) return;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int n = n0 + i;
+    if (n < N) {
+      const int64_t o = ((b * a.K + P.k) * N + n) * D + d;
+      a.fstate[o] = h[i];
+      a.bstate[o] = Sb[i];
+    }
+  }
+  if (g == 0) a.dsum[(b * a.K + P.k) * D + d] = dsum;
+}
+
+// -------------------------------------------------------------------- main
+
+template <typename T, int NS, bool HAS_Z>
+__global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
+                                                     const T* __restrict__ delta_in,
+                                                     const T* __restrict__ B_in,
+                                                     const T* __restrict__ C_in,
+                                                     const T* __restrict__ z_in,
+                                                     const T* __restrict__ dy_in,
+                                                     T* __restrict__ du_out,
+                                                     T* __restrict__ ddelta_out,
+                                                     T* __restrict__ dz_out, const BwdArgs a) {
+  constexpr int NP = NS * BGL;
+  constexpr int ES = sizeof(T);
+  constexpr int RP = BGL * NP + 4;      // reduction row (one channel: 8 steps x NP) + pad
+  __shared__ __attribute__((aligned(16))) float sB[NP][BTS];
+  __shared__ __attribute__((aligned(16))) float sC[NP][BTS];
+  __shared__ __attribute__((aligned(16))) float4 xch[BCPW][BXS];
+  __shared__ __attribute__((aligned(16))) float hts[BNT][NS][kBT];  // tile-start states
+  __shared__ __attribute__((aligned(16))) float red[2][BCPW][RP];   // dB / dC of one tile
+  const BTilePos P = btile_pos(a);
+  const int tid = threadIdx.x;
+  const int g = P.g, cl = P.cl, n0 = g * NS;
+  const int64_t L = a.L, D = a.D, N = a.N, K = a.K, b = P.b, d = P.d, k = P.k;
+  const int64_t nsteps = P.t1 - P.t0;
+
+  bstage<T, NP>(sB, sC, B_in, C_in, b, P.t0, nsteps, L, N);
+
+  float A2[NS], An[NS], h[NS], dh[NS], dA_acc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int n = n0 + i;
+    An[i] = n < N ? ld_param(a.A, d * N + n, a.param_dtype) : 0.0f;
+    A2[i] = An[i] * kLog2e;
+    h[i] = (k > 0 && n < N) ? a.fstate[((b * K + (k - 1)) * N + n) * D + d] : 0.0f;
+    dh[i] = (k < K - 1 && n < N) ? a.bstate[((b * K + (k + 1)) * N + n) * D + d] : 0.0f;
+    dA_acc[i] = 0.0f;
+  }
+  const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
+  const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
+  const bool sp = a.softplus != 0;
+  const int64_t row0 = (b * L + P.t0) * D;
+  const int64_t rbytes = nsteps * D * ES;
+  const auto rs_u = make_rsrc(u_in + row0, rbytes);
+  const auto rs_d = make_rsrc(delta_in + row0, rbytes);
+  const auto rs_z = make_rsrc(HAS_Z ? z_in + row0 : u_in + row0, rbytes);
+  const auto rs_y = make_rsrc(dy_in + row0, rbytes);
+  const auto ws_du = make_rsrc(du_out + row0, rbytes);
+  const auto ws_dd = make_rsrc(ddelta_out + row0, rbytes);
+  const auto ws_dz = make_rsrc(HAS_Z ? dz_out + row0 : du_out + row0, HAS_Z ? rbytes : 0);
+  const int voff = (int)((g * D + d) * ES);
+  const int sstep = (int)(BGL * D * ES);
+  const int ntile = (int)((nsteps + BGL - 1) / BGL);
+  __syncthreads();
+
+  // per-step scalars of the lane's own step in tile j
+  struct Own { float uu, dl, xu, gg, sx, gz; bool valid; };
+  auto own = [&](int j, bool full) {
+    Own o;
+    const int so = j * sstep;
+    o.uu = buf_ld<T>(rs_u, voff, so);
+    const float dr = buf_ld<T>(rs_d, voff, so);
+    o.valid = (int64_t)j * BGL + g < nsteps;
+    const float x = dr + bv;
+    float spx = softplus(x);
+    __asm__ volatile("" : "+v"(spx));
+    const float dl = sp ? spx : x;
+    o.dl = o.valid ? dl : 0.0f;
+    o.xu = o.valid ? dl * o.uu : 0.0f;
+    o.gg = 0.0f;
+    o.sx = 1.0f;
+    o.gz = 0.0f;
+    if (full) {
+      const float dyv = buf_ld<T>(rs_y, voff, so);
+      float gv = dyv;
+      if (HAS_Z) {
+        const float zz = buf_ld<T>(rs_z, voff, so);
+        const float s = sigmoid(zz);
+        gv = dyv * zz * s;
+        o.gz = dyv * s * __builtin_fmaf(zz, 1.0f - s, 1.0f);
+      }
+      o.gg = o.valid ? gv : 0.0f;
+      float sxv = sigmoid(x);
+      __asm__ volatile("" : "+v"(sxv));
+      o.sx = sp ? sxv : 1.0f;
+    }
+    return o;
+  };
+
+  // ---- pass 1: forward from the carried-in state, keep tile-start states
+  for (int j = 0; j < ntile; ++j) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) hts[j][i][tid] = h[i];
+    const Own o = own(j, false);
+    xch[cl][g] = make_float4(o.dl, o.xu, 0.0f, 0.0f);
+    float4 ex[BGL];
+#pragma unroll
+    for (int s = 0; s < BGL; ++s) ex[s] = xch[cl][s];
+#pragma unroll
+    for (int sh = 0; sh < BGL; sh += 4) {
+      float4 bq[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        bq[i] = *reinterpret_cast<const float4*>(&sB[n0 + i][j * BGL + sh]);
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss) {
+        const float4 e = ex[sh + ss];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const float bvs = ss == 0 ? bq[i].x : ss == 1 ? bq[i].y : ss == 2 ? bq[i].z : bq[i].w;
+          h[i] = __builtin_fmaf(fast_exp2(e.x * A2[i]), h[i], e.y * bvs);
+        }
+      }
+    }
+  }
+
+  // ---- pass 2: tiles backwards.  Within a tile the adjoint dh runs step by
+  // step; at each tile start it is replaced by the tile-level chain
+  // cj <- exp2(A2 * tile sum of dt) * cj + (tile's reverse summary from zero),
+  // so that rounding accumulates over at most 8 steps plus one step per tile.
+  float cj[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) cj[i] = dh[i];
+  float dD_acc = 0.0f, db_acc = 0.0f;
+  for (int j = ntile - 1; j >= 0; --j) {
+    const Own o = own(j, true);
+    const float dst = bsum8(o.dl);
+    xch[cl][g] = make_float4(o.dl, o.xu, o.gg, 0.0f);
+    float4 ex[BGL];
+#pragma unroll
+    for (int s = 0; s < BGL; ++s) ex[s] = xch[cl][s];
+
+    // recompute the tile's states and decays from the tile-start state
+    float hh[BGL][NS], aa[BGL][NS], h0[NS], po[BGL];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) h0[i] = hts[j][i][tid];
+    float bt[BGL][NS], ct[BGL][NS];
+#pragma unroll
+    for (int sh = 0; sh < BGL; sh += 4) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const float4 bq = *reinterpret_cast<const float4*>(&sB[n0 + i][j * BGL + sh]);
+        const float4 cq = *reinterpret_cast<const float4*>(&sC[n0 + i][j * BGL + sh]);
+        bt[sh][i] = bq.x; bt[sh + 1][i] = bq.y; bt[sh + 2][i] = bq.z; bt[sh + 3][i] = bq.w;
+        ct[sh][i] = cq.x; ct[sh + 1][i] = cq.y; ct[sh + 2][i] = cq.z; ct[sh + 3][i] = cq.w;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < BGL; ++s) {
+      float ov = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const float prev = s > 0 ? hh[s - 1][i] : h0[i];
+        aa[s][i] = fast_exp2(ex[s].x * A2[i]);
+        hh[s][i] = __builtin_fmaf(aa[s][i], prev, ex[s].y * bt[s][i]);
+        ov = __builtin_fmaf(ct[s][i], hh[s][i], ov);
+      }
+      po[s] = ov;
+    }
+    // adjoint sweep (dl0: the tile's adjoint from zero at its end)
+    float pdua[BGL], pddl[BGL], dl0[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) dl0[i] = 0.0f;
+#pragma unroll
+    for (int s = BGL - 1; s >= 0; --s) {
+      float vdua = 0.0f, vddl = 0.0f;
+      float vb[NS], vc[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        dh[i] = __builtin_fmaf(ex[s].z, ct[s][i], dh[i]);          // dL/dh_t
+        dl0[i] = __builtin_fmaf(ex[s].z, ct[s][i], dl0[i]);
+        vc[i] = ex[s].z * hh[s][i];
+        vb[i] = dh[i] * ex[s].y;
+        vdua = __builtin_fmaf(dh[i], bt[s][i], vdua);
+        const float m = dh[i] * aa[s][i];
+        const float q = m * (s > 0 ? hh[s - 1][i] : h0[i]);
+        vddl = __builtin_fmaf(q, An[i], vddl);
+        dA_acc[i] = __builtin_fmaf(q, ex[s].x, dA_acc[i]);
+        dh[i] = m;
+        dl0[i] *= aa[s][i];
+      }
+      pdua[s] = vdua;
+      pddl[s] = vddl;
+      // dB / dC of (step s, these states) for the workgroup reduction
+      // (tail lanes duplicate channel D-1 and must add nothing)
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        vb[i] = P.active ? vb[i] : 0.0f;
+        vc[i] = P.active ? vc[i] : 0.0f;
+      }
+      if (NS == 2) {
+        *reinterpret_cast<float2*>(&red[0][cl][s * NP + n0]) = make_float2(vb[0], vb[NS - 1]);
+        *reinterpret_cast<float2*>(&red[1][cl][s * NP + n0]) = make_float2(vc[0], vc[NS - 1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          red[0][cl][s * NP + n0 + i] = vb[i];
+          red[1][cl][s * NP + n0 + i] = vc[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      cj[i] = __builtin_fmaf(fast_exp2(A2[i] * dst), cj[i], dl0[i]);
+      dh[i] = cj[i];
+    }
+    // per-step sums over the channel's states: lane g gets its own step's
+    const float o_own = brs8(po, g);
+    const float dua_own = brs8(pdua, g);
+    const float ddl_own = brs8(pddl, g);
+    const float du = __builtin_fmaf(o.dl, dua_own, o.gg * Dv);
+    const float dx = o.valid ? __builtin_fmaf(o.uu, dua_own, ddl_own) * o.sx : 0.0f;
+    const int so = j * sstep;
+    buf_st<T>(du, ws_du, voff, so);          // steps past the chunk are dropped
+    buf_st<T>(dx, ws_dd, voff, so);
+    if (HAS_Z) buf_st<T>(o.gz * __builtin_fmaf(Dv, o.uu, o_own), ws_dz, voff, so);
+    dD_acc = __builtin_fmaf(o.gg, o.uu, dD_acc);
+    db_acc += dx;
+
+    // dB / dC of this tile: sum over the workgroup's 32 channels (fixed order)
+    __syncthreads();
+    for (int v = tid; v < 2 * BGL * NP; v += kBT) {
+      const int w = v / (BGL * NP), sn = v % (BGL * NP);
+      const int s = sn / NP, n = sn % NP;
+      float acc = 0.0f;
+#pragma unroll 8
+      for (int c = 0; c < BCPW; ++c) acc += red[w][c][sn];
+      const int64_t t = (int64_t)j * BGL + s;
+      if (n < N && t < nsteps)
+        a.part_bc[((b * L + P.t0 + t) * a.nwgd + P.db) * 2 * N + w * N + n] = acc;
+    }
+    __syncthreads();
+  }
+  // tail channels (d >= D) duplicate channel D-1: they must not add to the sums
+  if (!P.active) { dD_acc = 0.0f; db_acc = 0.0f; }
+  dD_acc = bsum8(dD_acc);
+  db_acc = bsum8(db_acc);
+  if (!P.active) return;
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (n0 + i < N) a.part_dA[((b * a.KG + k) * N + n0 + i) * D + d] = dA_acc[i];
+  if (g == 0) {
+    a.part_dD[(b * a.KG + k) * D + d] = dD_acc;
+    a.part_db[(b * a.KG + k) * D + d] = db_acc;
+  }
+}
+
+hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t s);   // ss_bwd.hip
+hipError_t launch_bwd_finalize(const BwdArgs& a, hipStream_t s);  // ss_bwd.hip
+
+template <typename T, int NS, bool HAS_Z>
+static hipError_t launch_btile_t(const BwdArgs& a, hipStream_t s) {
+  const T* U = static_cast<const T*>(a.u);
+  const T* DL = static_cast<const T*>(a.delta);
+  const T* Bm = static_cast<const T*>(a.B);
+  const T* Cm = static_cast<const T*>(a.C);
+  const T* Z = static_cast<const T*>(a.z);
+  const T* DY = static_cast<const T*>(a.dy);
+  const unsigned grid = (unsigned)(a.Bn * a.K * a.nwgd);
+  hipError_t e;
+  if (a.K > 1) {
+    bwd_tile_sum<T, NS, HAS_Z><<<dim3(grid), dim3(kBT), 0, s>>>(U, DL, Bm, Cm, Z, DY, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_bwd_carry(a, s)) != hipSuccess) return e;
+  }
+  bwd_tile_main<T, NS, HAS_Z><<<dim3(grid), dim3(kBT), 0, s>>>(
+      U, DL, Bm, Cm, Z, DY, static_cast<T*>(a.du), static_cast<T*>(a.ddelta),
+      static_cast<T*>(a.dz), a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_bwd_finalize(a, s);
+}
+
+template <typename T>
+static hipError_t launch_btile_ty(const BwdArgs& a, int ns, hipStream_t s) {
+  const bool z = a.z != nullptr;
+  if (ns == 1) return z ? launch_btile_t<T, 1, true>(a, s) : launch_btile_t<T, 1, false>(a, s);
+  if (ns == 2) return z ? launch_btile_t<T, 2, true>(a, s) : launch_btile_t<T, 2, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_tile(const BwdArgs& a, int ns, hipStream_t s) {
+  switch (a.io_dtype) {
+    case 0: return launch_btile_ty<float>(a, ns, s);
+    case 1: return launch_btile_ty<f16_t>(a, ns, s);
+    case 2: return launch_btile_ty<bf16_t>(a, ns, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ss

@@ -11,8 +11,10 @@
 
 namespace ss {
 
-// Backward register tile: time steps one lane holds per chunk.
+// Backward register tile: time steps one lane holds per chunk (general path).
 constexpr int kBwdTile = 16;
+// Backward chunk length of the tile path (N <= 16): 8 tiles of 8 steps.
+constexpr int kBwdTileChunk = 64;
 // Chunks of one channel block handled by one backward workgroup (their dA /
 // dD / ddelta_bias partials are summed in registers / in place).
 constexpr int kBwdChunksPerGroup = 4;
@@ -31,6 +33,7 @@ struct Plan {
          off_part_dD = 0, off_part_db = 0;
   size_t ws_bytes = 0;
   int64_t KG = 0, nwgd = 0;   // backward: chunk groups, channel blocks
+  bool bwd_tile = false;      // backward: 8-lanes-per-channel tile kernels (N <= 16)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -96,14 +99,29 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
     p.n_launches = p.K > 1 ? (N > 0 ? 3 : 2) : 1;
     return p;
   }
-  // backward
-  int64_t lc = kBwdTile;
+  // backward.  N <= 16: tile kernels, chunks of up to 64 steps, 32 channels
+  // per workgroup, per-chunk partials.  Otherwise the general kernels: chunks
+  // of up to 16 steps (one register tile), 256 channels per workgroup,
+  // partials per group of 4 chunks.
+  p.bwd_tile = N <= 16;
+  int64_t lc = p.bwd_tile ? kBwdTileChunk : kBwdTile;
   if (d.chunk_len > 0 && d.chunk_len < lc) lc = d.chunk_len;
   if (lc > L) lc = L;
+  const int64_t lc_cap = (int64_t)0x7fffffff / ((D > 0 ? D : 1) * 4) - GL_MAX_TILE;
+  if (lc > lc_cap) lc = lc_cap > 1 ? lc_cap : 1;
   p.chunk_len = lc;
   p.K = (L + lc - 1) / lc;
-  p.KG = (p.K + kBwdChunksPerGroup - 1) / kBwdChunksPerGroup;
-  p.nwgd = (D + kChannelsPerBlock - 1) / kChannelsPerBlock;
+  if (p.bwd_tile) {
+    p.NS = N <= 8 ? 1 : 2;
+    p.G = 8;
+    p.KG = p.K;
+    p.nwgd = (D + 31) / 32;
+  } else {
+    p.NS = 1;
+    p.G = 1;
+    p.KG = (p.K + kBwdChunksPerGroup - 1) / kBwdChunksPerGroup;
+    p.nwgd = (D + kChannelsPerBlock - 1) / kChannelsPerBlock;
+  }
   size_t off = 0;
   p.off_dsum = off;
   off = align256(off + sizeof(float) * (size_t)(Bn * p.K * D));
