@@ -84,14 +84,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// log(1 + w) for w >= 0, accurate in relative terms also for tiny w:
-// with s = 1 + w rounded, log(s) * w / (s - 1) corrects the rounding of s
-// (the classic compensated form; exact to a few ulp when log is).
+// log(1 + w) for 0 <= w <= 1, accurate in relative terms also for tiny w.
+// With s = 1 + w rounded, c = w - (s - 1) is the rounding error of s, computed
+// exactly (s - 1 and the difference are exact by Sterbenz's lemma), and
+// log(1 + w) = log(s) + log(1 + c / s) ~= log(s) + c.  Replacing c / s by c
+// errs by |c| * w <= 2^-24 * w, i.e. below 1.5 ulp of the result; no division.
 __device__ __forceinline__ float log1p_pos(float w) {
   const float s = 1.0f + w;
-  const float den = s - 1.0f;
-  const float l = fast_log2(s) * kLn2;
-  return den == 0.0f ? w : l * (w * fast_rcp(den));
+  const float c = w - (s - 1.0f);
+  return __builtin_fmaf(fast_log2(s), kLn2, c);
 }
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^{-|x|}).

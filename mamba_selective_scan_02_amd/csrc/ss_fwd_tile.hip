@@ -81,8 +81,14 @@ __device__ __forceinline__ float sum8(float v) {
 
 enum { TMODE_FULL = 0, TMODE_SUMMARY = 1 };
 
+// Resident waves per SIMD the register budget is held to: a 2.8B-shaped grid
+// (5120 waves of 8 channels) is exactly 5 waves on each of the 1024 SIMDs, and
+// 5 waves fit 96 VGPRs.  NS = 4 needs more registers and gets 3.
+template <int NS>
+constexpr int tile_waves_per_simd() { return NS <= 2 ? 5 : 3; }
+
 template <typename T, int NS, int MODE, bool HAS_Z>
-__global__ __launch_bounds__(kBlockT) void fwd_tile(const T* __restrict__ u_in,
+__global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(const T* __restrict__ u_in,
                                                     const T* __restrict__ delta_in,
                                                     const T* __restrict__ B_in,
                                                     const T* __restrict__ C_in,
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(kBlockT) void fwd_tile(const T* __restrict__ u_in,
   struct Prep { float dl, xu, uu, gate; };
   auto prep = [&](int p, float uu, float dr, float zz) {
     Prep r;
-    const bool valid = (int64_t)p * GL + g < nsteps;
+    const bool valid = p * GL + g < (int)nsteps;
     const float x = dr + bv;
     float spx = softplus(x);
     __asm__ volatile("" : "+v"(spx));
@@ -210,71 +216,74 @@ __global__ __launch_bounds__(kBlockT) void fwd_tile(const T* __restrict__ u_in,
   load_own(2, pu1, pd1, pz1);
   xch[0][cl][g] = make_float2(cur.dl, cur.xu);
 
-  const int nprep = (int)((nsteps + GL - 1) / GL);
-  for (int p = 0; p < nprep; ++p) {
-    const int tile = p / (TB / GL);
-    const int pt = p % (TB / GL);
-    const int buf = tile & 1;
-    const int64_t tb = t0 + (int64_t)tile * TB;
-    const bool has_next_tile = tb + TB < t1;
-    if (pt == 0 && has_next_tile) stage_load(tb + TB);
-
-    float2 ex[GL];
+  // The time loop runs whole 64-step stages (8 tiles, unrolled, so that every
+  // LDS offset is an immediate and the prefetch registers rotate by
+  // renaming).  Tiles past the chunk's end are identity steps (dt = 0) whose
+  // stores fall outside the buffer range and are dropped.
+  const int nstage = (int)((nsteps + TB - 1) / TB);
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    const bool has_next = st + 1 < nstage;
+    if (has_next) stage_load(t0 + (int64_t)(st + 1) * TB);
+    // (the summary pass, with no readout to order the exps, would hoist them
+    //  across the unrolled tiles and spill; it keeps a rolled loop)
+    constexpr int kUnroll = MODE == TMODE_FULL ? TB / GL : 1;
+#pragma unroll kUnroll
+    for (int pt = 0; pt < TB / GL; ++pt) {
+      const int p = st * (TB / GL) + pt;
+      float2 ex[GL];
 #pragma unroll
-    for (int j = 0; j < GL; j += 2) {
-      const float4 v = *reinterpret_cast<const float4*>(&xch[p & 1][cl][j]);
-      ex[j] = make_float2(v.x, v.y);
-      ex[j + 1] = make_float2(v.z, v.w);
-    }
-    // next tile's per-step inputs (independent of this tile's recurrence)
-    const Prep nxt = prep(p + 1, pu0, pd0, pz0);
-    pu0 = pu1; pd0 = pd1; pz0 = pz1;
-    load_own(p + 3, pu1, pd1, pz1);
-    xch[(p + 1) & 1][cl][g] = make_float2(nxt.dl, nxt.xu);
-    if (MODE == TMODE_SUMMARY) dsum += cur.dl;
-
-    float ot[GL];                                  // this lane's partial readout per step
-    const int ls0 = pt * GL;
-#pragma unroll
-    for (int jh = 0; jh < GL; jh += 4) {
-      float4 bq[NS], cq[NS];
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        bq[i] = *reinterpret_cast<const float4*>(&sBC[buf][0][n0 + i][ls0 + jh]);
-        if (MODE == TMODE_FULL)
-          cq[i] = *reinterpret_cast<const float4*>(&sBC[buf][1][n0 + i][ls0 + jh]);
+      for (int j = 0; j < GL; j += 2) {
+        const float4 v = *reinterpret_cast<const float4*>(&xch[pt & 1][cl][j]);
+        ex[j] = make_float2(v.x, v.y);
+        ex[j + 1] = make_float2(v.z, v.w);
       }
+      // next tile's per-step inputs (independent of this tile's recurrence)
+      const Prep nxt = prep(p + 1, pu0, pd0, pz0);
+      pu0 = pu1; pd0 = pd1; pz0 = pz1;
+      load_own(p + 3, pu1, pd1, pz1);
+      xch[(pt + 1) & 1][cl][g] = make_float2(nxt.dl, nxt.xu);
+      if (MODE == TMODE_SUMMARY) dsum += cur.dl;
+
+      float ot[GL];                                // this lane's partial readout per step
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = jh + jj;
-        const float dlj = ex[j].x, xuj = ex[j].y;
-        float o = 0.0f;
+      for (int jh = 0; jh < GL; jh += 4) {
+        float4 bq[NS], cq[NS];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-          const float bvj = jj == 0 ? bq[i].x : jj == 1 ? bq[i].y : jj == 2 ? bq[i].z : bq[i].w;
-          const float dA = fast_exp2(dlj * A2[i]);
-          h[i] = __builtin_fmaf(dA, h[i], xuj * bvj);
-          if (MODE == TMODE_FULL) {
-            const float cvj = jj == 0 ? cq[i].x : jj == 1 ? cq[i].y : jj == 2 ? cq[i].z : cq[i].w;
-            o = __builtin_fmaf(cvj, h[i], o);
-          }
+          bq[i] = *reinterpret_cast<const float4*>(&sBC[buf][0][n0 + i][pt * GL + jh]);
+          if (MODE == TMODE_FULL)
+            cq[i] = *reinterpret_cast<const float4*>(&sBC[buf][1][n0 + i][pt * GL + jh]);
         }
-        ot[j] = o;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = jh + jj;
+          const float dlj = ex[j].x, xuj = ex[j].y;
+          float o = 0.0f;
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            const float bvj = jj == 0 ? bq[i].x : jj == 1 ? bq[i].y : jj == 2 ? bq[i].z : bq[i].w;
+            const float dA = fast_exp2(dlj * A2[i]);
+            h[i] = __builtin_fmaf(dA, h[i], xuj * bvj);
+            if (MODE == TMODE_FULL) {
+              const float cvj = jj == 0 ? cq[i].x : jj == 1 ? cq[i].y : jj == 2 ? cq[i].z : cq[i].w;
+              o = __builtin_fmaf(cvj, h[i], o);
+            }
+          }
+          ot[j] = o;
+        }
       }
+      if (MODE == TMODE_FULL) {
+        const float o_own = reduce_scatter8(ot, g);   // full readout of step t0 + p*8 + g
+        const float yv = __builtin_fmaf(Dv, cur.uu, o_own) * cur.gate;
+        // tail lanes (d >= D) store channel D-1's value to channel D-1's
+        // address; steps past the chunk fall outside the buffer and are dropped
+        buf_st<T>(yv, rs_y, voff_own, p * soff_step);
+      }
+      cur = nxt;
     }
-    if (MODE == TMODE_FULL) {
-      const float o_own = reduce_scatter8(ot, g);   // full readout of step t0 + p*8 + g
-      const float yv = __builtin_fmaf(Dv, cur.uu, o_own) * cur.gate;
-      // tail lanes (d >= D) store channel D-1's value to channel D-1's
-      // address; steps past the chunk fall outside the buffer and are dropped
-      buf_st<T>(yv, rs_y, voff_own, p * soff_step);
-    }
-    cur = nxt;
-
-    if (pt == TB / GL - 1 || p == nprep - 1) {
-      if (has_next_tile) stage_store(buf ^ 1);
-      __syncthreads();
-    }
+    if (has_next) stage_store(buf ^ 1);
+    __syncthreads();
   }
 
   if (MODE == TMODE_SUMMARY) dsum = sum8(dsum);
@@ -291,7 +300,270 @@ __global__ __launch_bounds__(kBlockT) void fwd_tile(const T* __restrict__ u_in,
   }
 }
 
+// ------------------------------------------------------------------ wide
+//
+// The same computation for rows whose byte length is a multiple of 16 (and
+// 16-byte aligned tensors): u / delta / z and y go through LDS, so that every
+// global access of these streams is 16 bytes per lane.  A workgroup's rows are
+// only 32 channels (64 or 128 bytes) wide, and one 16-bit element per lane per
+// 8 steps, as fwd_tile loads them, reaches about half the bandwidth of 16-byte
+// pieces on such strips.
+//
+// Per stage of TB steps (one 16-byte piece per thread and tensor):
+//   start: issue the next stage's loads (u, delta, z, B, C) into registers;
+//   tiles: lane g of a channel reads its own step's u / delta / z from LDS,
+//          prepares it, and the 8 lanes run the tile as in fwd_tile; y goes
+//          to an LDS row buffer;
+//   end:   barrier; the registers go to LDS and y leaves in 16-byte pieces;
+//          barrier.
+template <typename T>
+struct WideCfg {
+  static constexpr int ES = sizeof(T);
+  static constexpr int TB = 128 / ES;                  // steps per stage: 64 (16-bit), 32 (f32)
+  static constexpr int ROWB = CPW * ES;                // bytes of one row of the block: 64 / 128
+  static constexpr int LPR = ROWB / 16;                // 16-byte pieces per row: 4 / 8
+  static constexpr int RS = ROWB + (ES == 2 ? 16 : 32);  // padded LDS row stride (bytes)
+  static constexpr int TSW = TB + 4;                   // staged B/C row stride (floats)
+  static_assert(TB * LPR == kBlockT, "one piece per thread and tensor");
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ float lds_elem(const uint8_t* p) {
+  if constexpr (sizeof(T) == 4) return *reinterpret_cast<const float*>(p);
+  else return to_f32(T{*reinterpret_cast<const uint16_t*>(p)});
+}
+template <typename T>
+__device__ __forceinline__ void lds_put(uint8_t* p, float v) {
+  if constexpr (sizeof(T) == 4) *reinterpret_cast<float*>(p) = v;
+  else *reinterpret_cast<uint16_t*>(p) = from_f32<T>(v).bits;
+}
+
+template <typename T, int NS, int MODE, bool HAS_Z>
+__global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
+    const T* __restrict__ u_in, const T* __restrict__ delta_in, const T* __restrict__ B_in,
+    const T* __restrict__ C_in, const T* __restrict__ z_in, T* __restrict__ y_out,
+    const FwdArgs a) {
+  using W = WideCfg<T>;
+  constexpr int ES = W::ES, TB = W::TB, RS = W::RS, TSW = W::TSW;
+  constexpr int NP = NS * GL;                          // == N on this path
+  constexpr bool FULL = MODE == TMODE_FULL;
+  constexpr int NT = (FULL && HAS_Z) ? 3 : 2;          // streamed inputs: u, delta[, z]
+  constexpr int NTILE = TB / GL;
+  // B / C of a stage in 16-byte pieces: PPR per row, PB per tensor, NPC per thread
+  constexpr int EPP = 16 / ES;
+  constexpr int PPR = NP * ES / 16;
+  constexpr int PB = TB * PPR;
+  constexpr int NBC = FULL ? 2 : 1;
+  constexpr int NPC = (NBC * PB + kBlockT - 1) / kBlockT;
+  static_assert(PB % 64 == 0, "a wave's pieces come from one tensor");
+  __shared__ __attribute__((aligned(16))) uint8_t sIn[NT][TB * RS];
+  __shared__ __attribute__((aligned(16))) uint8_t sY[FULL ? TB * RS : 16];
+  __shared__ __attribute__((aligned(16))) float sBC[FULL ? 2 : 1][NP][TSW];
+  __shared__ __attribute__((aligned(16))) float2 xch[CPW][XS];
+
+  const int tid = threadIdx.x;
+  const int g = tid % GL;
+  const int cl = tid / GL;
+  const int64_t nbd = (a.D + CPW - 1) / CPW;
+  int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t Kg = FULL ? a.K : a.K - 1;
+  const int64_t k = blk % Kg;
+  const int64_t b = blk / Kg;
+  const int64_t d0 = db * CPW;
+  const int64_t d_raw = d0 + cl;
+  const bool active = d_raw < a.D;
+  const int64_t d = active ? d_raw : a.D - 1;
+  const int64_t L = a.L, D = a.D, N = a.N;
+  const int64_t t0 = k * a.chunk_len;
+  const int64_t t1 = (t0 + a.chunk_len < L) ? t0 + a.chunk_len : L;
+  const int n0 = g * NS;
+
+  float A2[NS], h[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int n = n0 + i;
+    A2[i] = n < N ? ld_param(a.A, d * N + n, a.param_dtype) * kLog2e : 0.0f;
+    h[i] = 0.0f;
+    if (FULL && k > 0 && n < N) h[i] = a.chunk_state[((b * a.K + (k - 1)) * N + n) * D + d];
+  }
+  const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
+  const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
+  const bool sp = a.softplus != 0;
+
+  const int64_t nsteps = t1 - t0;
+  const int64_t row0 = (b * L + t0) * D;
+  const int64_t rbytes = nsteps * D * ES;
+  __amdgpu_buffer_rsrc_t rs_in[NT];
+  rs_in[0] = make_rsrc(u_in + row0, rbytes);
+  rs_in[1] = make_rsrc(delta_in + row0, rbytes);
+  if constexpr (NT == 3) rs_in[2] = make_rsrc(z_in + row0, rbytes);
+  const auto rs_y = make_rsrc(y_out + row0, FULL ? rbytes : 0);
+  const auto rs_B = make_rsrc(B_in + (b * L + t0) * N, nsteps * N * ES);
+  const auto rs_C = make_rsrc(C_in + (b * L + t0) * N, nsteps * N * ES);
+
+  // this thread's 16-byte piece of every stage: row pr, piece pq of the block's row
+  const int pr = tid / W::LPR, pq = tid % W::LPR;
+  const int voff_piece = (int)(((int64_t)pr * D + d0) * ES) + pq * 16;
+  const int soff_stage = (int)((int64_t)TB * D * ES);
+  const int lds_piece = pr * RS + pq * 16;
+  const int lds_own_col = cl * ES;                    // column of this lane's channel
+
+  u32x4 rin[NT], rbc[NPC];
+  auto issue_loads = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+      rin[q] = __builtin_amdgcn_raw_buffer_load_b128(rs_in[q], voff_piece, st * soff_stage, 0);
+#pragma unroll
+    for (int r = 0; r < NPC; ++r) {
+      const int pi = tid + r * kBlockT;
+      const int q = pi % PB;                          // rows past the chunk read 0
+      const int off = (st * TB * NP + q * EPP) * ES;
+      // PB is a multiple of 64, so B or C is a per-wave choice
+      const bool isB = __builtin_amdgcn_readfirstlane(pi / PB) == 0;
+      rbc[r] = __builtin_amdgcn_raw_buffer_load_b128(isB ? rs_B : rs_C, off, 0, 0);
+    }
+  };
+  auto commit_loads = [&]() {
+#pragma unroll
+    for (int q = 0; q < NT; ++q) *reinterpret_cast<u32x4*>(&sIn[q][lds_piece]) = rin[q];
+#pragma unroll
+    for (int r = 0; r < NPC; ++r) {
+      const int pi = tid + r * kBlockT;
+      if (pi < NBC * PB) {
+        const int w = pi / PB, q = pi % PB;
+        const int tt = q / PPR, n = (q % PPR) * EPP;
+        const uint32_t v[4] = {rbc[r].x, rbc[r].y, rbc[r].z, rbc[r].w};
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) {
+          float f;
+          if constexpr (ES == 4) f = __builtin_bit_cast(float, v[e]);
+          else f = to_f32(T{(uint16_t)(e & 1 ? v[e / 2] >> 16 : v[e / 2] & 0xffffu)});
+          sBC[w][n + e][tt] = f;
+        }
+      }
+    }
+  };
+  // y of the stage just finished leaves in 16-byte pieces; the last channel
+  // block of a row, where the block runs past D, stores element by element.
+  const bool full_row = d0 + CPW <= D;
+  auto drain_y = [&](int st) {
+    if (full_row) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&sY[lds_piece]);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs_y, voff_piece, st * soff_stage, 0);
+    } else {
+      const int rowb = (int)(D * ES), colb = (int)(d0 * ES);
+      for (int e = tid; e < TB * CPW; e += kBlockT) {
+        const int r = e / CPW, c = e % CPW;
+        if (d0 + c < D) {
+          const float v = lds_elem<T>(&sY[r * RS + c * ES]);
+          buf_st<T>(v, rs_y, r * rowb + colb + c * ES, st * soff_stage);
+        }
+      }
+    }
+  };
+
+  issue_loads(0);
+  commit_loads();
+  __syncthreads();
+
+  float dsum = 0.0f;
+  const int nstage = (int)((nsteps + TB - 1) / TB);
+  for (int st = 0; st < nstage; ++st) {
+    const bool has_next = st + 1 < nstage;
+    if (has_next) issue_loads(st + 1);
+    constexpr int kUnroll = FULL ? NTILE : 1;
+#pragma unroll kUnroll
+    for (int pt = 0; pt < NTILE; ++pt) {
+      const int row = pt * GL + g;                    // this lane's own step in the stage
+      const uint8_t* own = &sIn[0][row * RS + lds_own_col];
+      const float uu = lds_elem<T>(own);
+      const float dr = lds_elem<T>(own + TB * RS);
+      const float x = dr + bv;
+      float spx = softplus(x);
+      __asm__ volatile("" : "+v"(spx));
+      const bool valid = st * TB + row < (int)nsteps;
+      const float dl0 = sp ? spx : x;
+      const float dl = valid ? dl0 : 0.0f;
+      const float xu = valid ? dl0 * uu : 0.0f;
+      if (!FULL) dsum += dl;
+      xch[cl][g] = make_float2(dl, xu);
+      float2 ex[GL];
+#pragma unroll
+      for (int j = 0; j < GL; j += 2) {
+        const float4 v = *reinterpret_cast<const float4*>(&xch[cl][j]);
+        ex[j] = make_float2(v.x, v.y);
+        ex[j + 1] = make_float2(v.z, v.w);
+      }
+      float ot[GL];
+#pragma unroll
+      for (int jh = 0; jh < GL; jh += 4) {
+        float4 bq[NS], cq[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          bq[i] = *reinterpret_cast<const float4*>(&sBC[0][n0 + i][pt * GL + jh]);
+          if (FULL) cq[i] = *reinterpret_cast<const float4*>(&sBC[FULL ? 1 : 0][n0 + i][pt * GL + jh]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = jh + jj;
+          const float dlj = ex[j].x, xuj = ex[j].y;
+          float o = 0.0f;
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            const float bvj = jj == 0 ? bq[i].x : jj == 1 ? bq[i].y : jj == 2 ? bq[i].z : bq[i].w;
+            const float dA = fast_exp2(dlj * A2[i]);
+            h[i] = __builtin_fmaf(dA, h[i], xuj * bvj);
+            if (FULL) {
+              const float cvj = jj == 0 ? cq[i].x : jj == 1 ? cq[i].y : jj == 2 ? cq[i].z : cq[i].w;
+              o = __builtin_fmaf(cvj, h[i], o);
+            }
+          }
+          ot[j] = o;
+        }
+      }
+      if constexpr (FULL) {
+        float gate = 1.0f;
+        if constexpr (HAS_Z) {
+          const float zz = lds_elem<T>(own + 2 * TB * RS);
+          gate = zz * sigmoid(zz);
+        }
+        const float o_own = reduce_scatter8(ot, g);   // full readout of this lane's step
+        lds_put<T>(&sY[row * RS + lds_own_col], __builtin_fmaf(Dv, uu, o_own) * gate);
+      }
+    }
+    __syncthreads();
+    if (has_next) commit_loads();
+    if (FULL) drain_y(st);                          // steps past the chunk are dropped
+    __syncthreads();
+  }
+
+  if (!FULL) dsum = sum8(dsum);
+  if (!active) return;
+  if (!FULL) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (n0 + i < N) a.chunk_state[((b * a.K + k) * N + n0 + i) * D + d] = h[i];
+    if (g == 0) a.chunk_dsum[(b * a.K + k) * D + d] = dsum;
+  } else if (a.last_state != nullptr && k == a.K - 1) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (n0 + i < N) st_param(a.last_state, (b * D + d) * N + n0 + i, a.param_dtype, h[i]);
+  }
+}
+
 hipError_t launch_fwd_carry(const FwdArgs& a, hipStream_t s);  // ss_fwd.hip
+
+// fwd_wide takes rows of a multiple of 16 bytes, N = 8 * NS (B / C rows of 16,
+// 32 or 64 bytes) and 16-byte aligned streams.
+static bool wide_ok(const FwdArgs& a, int es, int ns) {
+  auto al = [](const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  return (a.D * es) % 16 == 0 && a.N == 8 * ns && al(a.u) && al(a.delta) && al(a.z) &&
+         al(a.y) && al(a.B) && al(a.C);
+}
 
 template <typename T, int NS, bool HAS_Z>
 static hipError_t launch_tile_t(const FwdArgs& a, hipStream_t s) {
@@ -302,17 +574,22 @@ static hipError_t launch_tile_t(const FwdArgs& a, hipStream_t s) {
   const T* Z = static_cast<const T*>(a.z);
   T* Y = static_cast<T*>(a.y);
   const int64_t nbd = (a.D + CPW - 1) / CPW;
+  const bool wide = wide_ok(a, (int)sizeof(T), NS);
   hipError_t e;
   if (a.K > 1) {
-    const int64_t gs = a.Bn * (a.K - 1) * nbd;
-    fwd_tile<T, NS, TMODE_SUMMARY, false><<<dim3((unsigned)gs), dim3(kBlockT), 0, s>>>(
-        U, DL, Bm, Cm, Z, Y, a);
+    const dim3 gs((unsigned)(a.Bn * (a.K - 1) * nbd));
+    if (wide)
+      fwd_wide<T, NS, TMODE_SUMMARY, false><<<gs, dim3(kBlockT), 0, s>>>(U, DL, Bm, Cm, Z, Y, a);
+    else
+      fwd_tile<T, NS, TMODE_SUMMARY, false><<<gs, dim3(kBlockT), 0, s>>>(U, DL, Bm, Cm, Z, Y, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_fwd_carry(a, s)) != hipSuccess) return e;
   }
-  const int64_t gf = a.Bn * a.K * nbd;
-  fwd_tile<T, NS, TMODE_FULL, HAS_Z><<<dim3((unsigned)gf), dim3(kBlockT), 0, s>>>(
-      U, DL, Bm, Cm, Z, Y, a);
+  const dim3 gf((unsigned)(a.Bn * a.K * nbd));
+  if (wide)
+    fwd_wide<T, NS, TMODE_FULL, HAS_Z><<<gf, dim3(kBlockT), 0, s>>>(U, DL, Bm, Cm, Z, Y, a);
+  else
+    fwd_tile<T, NS, TMODE_FULL, HAS_Z><<<gf, dim3(kBlockT), 0, s>>>(U, DL, Bm, Cm, Z, Y, a);
   return hipGetLastError();
 }
 

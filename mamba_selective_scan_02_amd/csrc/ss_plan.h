@@ -20,9 +20,10 @@ constexpr int kBwdTileChunk = 64;
 constexpr int kBwdChunksPerGroup = 4;
 // Channels per workgroup.
 constexpr int kChannelsPerBlock = 256;
-// Tile kernel: steps of one prep tile (the own-step loads run up to two tiles
-// past the chunk; those offsets must also stay below 2^31).
-constexpr int64_t GL_MAX_TILE = 24;
+// Tile kernels: steps that the own-step loads may run past a chunk (the last
+// 64-step stage is run whole and loads are prefetched three 8-step tiles
+// ahead); those byte offsets must also stay below 2^31.
+constexpr int64_t GL_MAX_TILE = 128;
 
 struct Plan {
   int NS = 4, G = 1;          // forward: states per lane, lanes per channel

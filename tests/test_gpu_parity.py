@@ -94,6 +94,33 @@ def test_fwd_half_dtypes(io, pa, N):
         _check_fwd(inp, chunk_len=chunk, label=f"{io}/{pa}/N{N}/chunk{chunk}")
 
 
+def _offset_copy(x, elems=1):
+    """x's values in a view that starts `elems` elements past an aligned address."""
+    big = torch.empty(x.numel() + elems, dtype=x.dtype, device=x.device)
+    big[elems:] = x.reshape(-1)
+    return big[elems:].view_as(x)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("N", [8, 16, 32])
+def test_fwd_wide_path(io, N):
+    """Rows of a multiple of 16 bytes with N = 8, 16, 32 take the LDS-staged
+    kernel (D = 72: two full channel blocks and a partial one; L = 150: partial
+    stages).  It must match the oracle, and match bit for bit the element-wise
+    kernel that misaligned inputs take, since both do the same arithmetic."""
+    inp = random_inputs(2, 150, 72, N, seed=450 + N, io_dtype=io)
+    d = to_dev(inp)
+    args = [d[k] for k in KEYS]
+    for chunk in (0, 24, 100):
+        _check_fwd(inp, chunk_len=chunk, label=f"wide {io}/N{N}/chunk{chunk}")
+        y1, l1 = ss.fwd(*args, return_last_state=True, chunk_len=chunk)
+        mis = list(args)
+        mis[0] = _offset_copy(args[0])
+        y2, l2 = ss.fwd(*mis, return_last_state=True, chunk_len=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(l1, l2), f"{io}/N{N}/chunk{chunk}"
+
+
 def test_fwd_misaligned_16bit_rows():
     """bf16 B / C at an odd element offset take the element-wise load path."""
     inp = random_inputs(1, 40, 64, 16, seed=401, io_dtype="bf16")
