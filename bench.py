@@ -38,7 +38,7 @@ def log(*a):
 
 # Sources each measured kernel is built from (its counters go stale when any changes).
 KERNEL_SOURCES = {
-    "fwd_tile_m2p8b": ["ss_fwd_tile.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp"],
+    "fwd_wide_m2p8b": ["ss_fwd_tile.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp"],
     "ss_bwd_bwd": ["ss_bwd.hip", "ss_bwd_tile.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp"],
 }
 
@@ -237,11 +237,11 @@ def main():
         "hbm_gbs": gbs,
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "algorithmic_bytes": abytes,
-        "roofline": {"bound": "alu", "kernel": "fwd_tile (single pass, 8 lanes per channel)",
+        "roofline": {"bound": "alu", "kernel": "fwd_wide (single pass, 8 lanes per channel, LDS-staged streams)",
                      "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / FP32_VECTOR_PEAK_TFLOPS,
                      "flops_per_update": FLOPS_PER_UPDATE,
-                     "traffic": stored_traffic("fwd_tile_m2p8b"),
+                     "traffic": stored_traffic("fwd_wide_m2p8b"),
                      "hbm_achieved_gbs": gbs, "hbm_peak_gbs": HBM_PEAK_GBS},
         "wall_s": wall,
     }
