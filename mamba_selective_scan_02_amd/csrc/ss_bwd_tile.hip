@@ -171,11 +171,19 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
 
   float dsum = 0.0f;
   const int ntile = (int)((nsteps + BGL - 1) / BGL);
-  for (int j = 0; j < ntile; ++j) {
+  // the lane's own-step inputs, loaded one tile ahead
+  auto raw = [&](int j, float& uu, float& dr, float& dyv, float& zz) {
     const int so = j * sstep;
-    const float uu = buf_ld<T>(rs_u, voff, so), dr = buf_ld<T>(rs_d, voff, so);
-    const float dyv = buf_ld<T>(rs_y, voff, so);
-    const float zz = HAS_Z ? buf_ld<T>(rs_z, voff, so) : 0.0f;
+    uu = buf_ld<T>(rs_u, voff, so);
+    dr = buf_ld<T>(rs_d, voff, so);
+    dyv = buf_ld<T>(rs_y, voff, so);
+    zz = HAS_Z ? buf_ld<T>(rs_z, voff, so) : 0.0f;
+  };
+  float nu, nd, ny, nz;
+  raw(0, nu, nd, ny, nz);
+  for (int j = 0; j < ntile; ++j) {
+    const float uu = nu, dr = nd, dyv = ny, zz = nz;
+    raw(j + 1, nu, nd, ny, nz);                       // past the chunk: reads 0
     const bool valid = (int64_t)j * BGL + g < nsteps;
     const float x = dr + bv;
     float spx = softplus(x);
@@ -294,13 +302,23 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
   const int ntile = (int)((nsteps + BGL - 1) / BGL);
   __syncthreads();
 
+  // raw inputs of the lane's own step in tile j (loaded one tile ahead)
+  struct Raw { float uu, dr, dyv, zz; };
+  auto raw = [&](int j, bool full) {
+    Raw r;
+    const int so = j * sstep;
+    r.uu = buf_ld<T>(rs_u, voff, so);
+    r.dr = buf_ld<T>(rs_d, voff, so);
+    r.dyv = full ? buf_ld<T>(rs_y, voff, so) : 0.0f;
+    r.zz = (full && HAS_Z) ? buf_ld<T>(rs_z, voff, so) : 0.0f;
+    return r;
+  };
   // per-step scalars of the lane's own step in tile j
   struct Own { float uu, dl, xu, gg, sx, gz; bool valid; };
-  auto own = [&](int j, bool full) {
+  auto own = [&](int j, bool full, const Raw& rw) {
     Own o;
-    const int so = j * sstep;
-    o.uu = buf_ld<T>(rs_u, voff, so);
-    const float dr = buf_ld<T>(rs_d, voff, so);
+    o.uu = rw.uu;
+    const float dr = rw.dr;
     o.valid = (int64_t)j * BGL + g < nsteps;
     const float x = dr + bv;
     float spx = softplus(x);
@@ -312,10 +330,10 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
     o.sx = 1.0f;
     o.gz = 0.0f;
     if (full) {
-      const float dyv = buf_ld<T>(rs_y, voff, so);
+      const float dyv = rw.dyv;
       float gv = dyv;
       if (HAS_Z) {
-        const float zz = buf_ld<T>(rs_z, voff, so);
+        const float zz = rw.zz;
         const float s = sigmoid(zz);
         gv = dyv * zz * s;
         o.gz = dyv * s * __builtin_fmaf(zz, 1.0f - s, 1.0f);
@@ -329,10 +347,13 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
   };
 
   // ---- pass 1: forward from the carried-in state, keep tile-start states
+  Raw nxt = raw(0, false);
   for (int j = 0; j < ntile; ++j) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) hts[j][i][tid] = h[i];
-    const Own o = own(j, false);
+    const Raw cur = nxt;
+    nxt = raw(j + 1, false);                          // past the chunk: reads 0
+    const Own o = own(j, false, cur);
     xch[cl][g] = make_float4(o.dl, o.xu, 0.0f, 0.0f);
     float4 ex[BGL];
 #pragma unroll
@@ -363,8 +384,11 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
 #pragma unroll
   for (int i = 0; i < NS; ++i) cj[i] = dh[i];
   float dD_acc = 0.0f, db_acc = 0.0f;
+  Raw prv = raw(ntile - 1, true);
   for (int j = ntile - 1; j >= 0; --j) {
-    const Own o = own(j, true);
+    const Raw cur = prv;
+    prv = raw(j > 0 ? j - 1 : 0, true);
+    const Own o = own(j, true, cur);
     const float dst = bsum8(o.dl);
     xch[cl][g] = make_float4(o.dl, o.xu, o.gg, 0.0f);
     float4 ex[BGL];
