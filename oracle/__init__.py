@@ -22,9 +22,14 @@ reductions" of the mamba-rs page "mamba_ssm/gpu/backward.rs"):
     x  = delta[b,t,d] + delta_bias[d]               (bias optional)
     dt = softplus(x) if delta_softplus else x
     a  = exp(dt * A[d,n])
-    h  = a * h + dt * B[b,t,n] * u[b,t,d]           (h = 0 before t = 0)
+    h  = a * h + dt * B[b,t,n] * u[b,t,d]           (h = h0 or 0 before t = 0)
     o  = sum_n C[b,t,n] * h[n] + D[d] * u[b,t,d]    (D optional)
     y  = o * z * sigmoid(z)                          (z optional)
+
+The optional initial state h0 [B, D, N] is the per-layer SSM state that the
+forward pipeline of the mamba-rs page "mamba_ssm/gpu/backward.rs" carries from
+one call to the next; its gradient dh0 = dL/dh_{-1} is what the reverse sweep
+carries past t = 0.
 
 Inputs are decoded to float64 from whatever dtype they are stored in, so the
 oracle reads exactly the values the GPU reads.
@@ -60,15 +65,15 @@ def _load():
         vp = ctypes.c_void_p
         for name in ("ss_oracle_fwd_f64", "ss_oracle_fwd_f32"):
             f = getattr(lib, name)
-            f.argtypes = [ctypes.POINTER(_Problem)] + [vp] * 10 + [ctypes.c_int]
+            f.argtypes = [ctypes.POINTER(_Problem)] + [vp] * 11 + [ctypes.c_int]
             f.restype = ctypes.c_int
         f = lib.ss_oracle_fwd_channels_f64
-        f.argtypes = [ctypes.POINTER(_Problem)] + [vp] * 10 + [ctypes.c_int64, vp, vp,
+        f.argtypes = [ctypes.POINTER(_Problem)] + [vp] * 11 + [ctypes.c_int64, vp, vp,
                                                                 ctypes.c_int]
         f.restype = ctypes.c_int
         for name in ("ss_oracle_bwd_f64", "ss_oracle_bwd_f32"):
             f = getattr(lib, name)
-            f.argtypes = [ctypes.POINTER(_Problem)] + [vp] * 17 + [ctypes.c_int]
+            f.argtypes = [ctypes.POINTER(_Problem)] + [vp] * 19 + [ctypes.c_int]
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -101,9 +106,10 @@ def _shape(u, A, delta_softplus) -> _Problem:
     return _Problem(Bn, L, D, N, 1 if delta_softplus else 0)
 
 
-def _check_shapes(u, delta, A, B, C, D, z, bias, dy=None):
+def _check_shapes(u, delta, A, B, C, D, z, bias, dy=None, h0=None):
     Bn, L, Dd = u.shape
     N = A.shape[1]
+    assert h0 is None or h0.shape == (Bn, Dd, N)
     assert delta.shape == (Bn, L, Dd) and A.shape == (Dd, N)
     assert B.shape == (Bn, L, N) and C.shape == (Bn, L, N)
     assert D is None or D.shape == (Dd,)
@@ -113,14 +119,15 @@ def _check_shapes(u, delta, A, B, C, D, z, bias, dy=None):
 
 
 def _fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-         return_last_state=False, nthreads=None, dt=np.float64):
+         return_last_state=False, nthreads=None, dt=np.float64, h0=None):
     args = [_arr(t, dt) for t in (u, delta, A, B, C, D, z, delta_bias)]
-    _check_shapes(*args)
+    h0a = _arr(h0, dt)
+    _check_shapes(*args, h0=h0a)
     p = _shape(args[0], args[2], delta_softplus)
     y = np.empty(args[0].shape, dtype=dt)
     ls = np.empty((p.batch, p.dim, p.dstate), dtype=dt) if return_last_state else None
     fn = _load().ss_oracle_fwd_f64 if dt == np.float64 else _load().ss_oracle_fwd_f32
-    st = fn(ctypes.byref(p), *[_ptr(a) for a in args], _ptr(y), _ptr(ls),
+    st = fn(ctypes.byref(p), *[_ptr(a) for a in args], _ptr(h0a), _ptr(y), _ptr(ls),
             nthreads or default_threads())
     if st != 0:
         raise RuntimeError("oracle forward failed")
@@ -128,28 +135,31 @@ def _fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True
 
 
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-        return_last_state=False, nthreads=None):
-    """Forward in float64.  Returns (y [B,L,D], last_state [B,D,N] or None)."""
+        return_last_state=False, nthreads=None, h0=None):
+    """Forward in float64.  Returns (y [B,L,D], last_state [B,D,N] or None).
+    h0 [B,D,N]: state before t = 0 (zero when None)."""
     return _fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_state,
-                nthreads, np.float64)
+                nthreads, np.float64, h0)
 
 
 def fwd_f32(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-            return_last_state=False, nthreads=None):
+            return_last_state=False, nthreads=None, h0=None):
     """The same sequential loop in float32 (diagnostic rounding floor)."""
     return _fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_state,
-                nthreads, np.float32)
+                nthreads, np.float32, h0)
 
 
 def fwd_channels(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                 chan_b: Sequence[int] = (), chan_d: Sequence[int] = (), nthreads=None):
+                 chan_b: Sequence[int] = (), chan_d: Sequence[int] = (), nthreads=None,
+                 h0=None):
     """Forward of selected channels only.
 
     Returns (y [nchan, L], last_state [nchan, N]) for channels
     (chan_b[c], chan_d[c]).
     """
     args = [_arr(t, np.float64) for t in (u, delta, A, B, C, D, z, delta_bias)]
-    _check_shapes(*args)
+    h0a = _arr(h0, np.float64)
+    _check_shapes(*args, h0=h0a)
     p = _shape(args[0], args[2], delta_softplus)
     cb = np.ascontiguousarray(chan_b, dtype=np.int64)
     cd = np.ascontiguousarray(chan_d, dtype=np.int64)
@@ -157,16 +167,19 @@ def fwd_channels(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     y = np.empty((cb.size, p.seqlen), dtype=np.float64)
     ls = np.empty((cb.size, p.dstate), dtype=np.float64)
     st = _load().ss_oracle_fwd_channels_f64(ctypes.byref(p), *[_ptr(a) for a in args],
-                                            _ptr(cb), _ptr(cd), cb.size, _ptr(y), _ptr(ls),
+                                            _ptr(h0a), _ptr(cb), _ptr(cd), cb.size, _ptr(y),
+                                            _ptr(ls),
                                             nthreads or default_threads())
     if st != 0:
         raise RuntimeError("oracle channel forward failed")
     return y, ls
 
 
-def _bwd(u, delta, A, B, C, D, z, delta_bias, dy, delta_softplus, nthreads, dt):
-    args = [_arr(t, dt) for t in (u, delta, A, B, C, D, z, delta_bias, dy)]
-    _check_shapes(*args)
+def _bwd(u, delta, A, B, C, D, z, delta_bias, dy, delta_softplus, nthreads, dt, h0=None):
+    args = [_arr(t, dt) for t in (u, delta, A, B, C, D, z, delta_bias)]
+    h0a = _arr(h0, dt)
+    dya = _arr(dy, dt)
+    _check_shapes(*args, dy=dya, h0=h0a)
     p = _shape(args[0], args[2], delta_softplus)
     Bn, L, Dd, N = p.batch, p.seqlen, p.dim, p.dstate
     out = {
@@ -176,11 +189,12 @@ def _bwd(u, delta, A, B, C, D, z, delta_bias, dy, delta_softplus, nthreads, dt):
         "dD": np.empty((Dd,), dt) if args[5] is not None else None,
         "dz": np.empty((Bn, L, Dd), dt) if args[6] is not None else None,
         "ddelta_bias": np.empty((Dd,), dt) if args[7] is not None else None,
+        "dh0": np.empty((Bn, Dd, N), dt) if h0a is not None else None,
     }
     fn = _load().ss_oracle_bwd_f64 if dt == np.float64 else _load().ss_oracle_bwd_f32
-    st = fn(ctypes.byref(p), *[_ptr(a) for a in args],
+    st = fn(ctypes.byref(p), *[_ptr(a) for a in args], _ptr(h0a), _ptr(dya),
             *[_ptr(out[k]) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz",
-                                     "ddelta_bias")],
+                                     "ddelta_bias", "dh0")],
             nthreads or default_threads())
     if st != 0:
         raise RuntimeError("oracle backward failed")
@@ -188,18 +202,20 @@ def _bwd(u, delta, A, B, C, D, z, delta_bias, dy, delta_softplus, nthreads, dt):
 
 
 def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None, delta_softplus=True,
-        nthreads=None) -> Dict[str, Optional[np.ndarray]]:
+        nthreads=None, h0=None) -> Dict[str, Optional[np.ndarray]]:
     """Backward in float64: gradients of sum(dy * y) with respect to every input.
 
-    Returns a dict with du, ddelta, dA, dB, dC, dD, dz, ddelta_bias (the last
-    three are None when D / z / delta_bias are absent).
+    Returns a dict with du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0 (the
+    last four are None when D / z / delta_bias / h0 are absent).
     """
-    return _bwd(u, delta, A, B, C, D, z, delta_bias, dy, delta_softplus, nthreads, np.float64)
+    return _bwd(u, delta, A, B, C, D, z, delta_bias, dy, delta_softplus, nthreads, np.float64,
+                h0)
 
 
 def bwd_f32(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None, delta_softplus=True,
-            nthreads=None) -> Dict[str, Optional[np.ndarray]]:
-    return _bwd(u, delta, A, B, C, D, z, delta_bias, dy, delta_softplus, nthreads, np.float32)
+            nthreads=None, h0=None) -> Dict[str, Optional[np.ndarray]]:
+    return _bwd(u, delta, A, B, C, D, z, delta_bias, dy, delta_softplus, nthreads, np.float32,
+                h0)
 
 
 # --------------------------------------------------------------------------
@@ -222,12 +238,12 @@ def _np_prep(u, delta, A, B, C, D, z, delta_bias, delta_softplus):
     return u, A, B, C, D, z, x, dt
 
 
-def np_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True):
+def np_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None):
     """numpy forward (float64). Returns (y, last_state)."""
     u, A, B, C, D, z, x, dt = _np_prep(u, delta, A, B, C, D, z, delta_bias, delta_softplus)
     Bn, L, Dd = u.shape
     N = A.shape[1]
-    h = np.zeros((Bn, Dd, N))
+    h = np.zeros((Bn, Dd, N)) if h0 is None else _arr(h0, np.float64).copy()
     y = np.zeros((Bn, L, Dd))
     for t in range(L):
         a = np.exp(dt[:, t, :, None] * A[None, :, :])                  # [B, D, N]
@@ -241,13 +257,16 @@ def np_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=Tr
     return y, h
 
 
-def np_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None, delta_softplus=True):
+def np_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None, delta_softplus=True,
+           h0=None):
     """numpy backward (float64), the adjoint of ``np_fwd``."""
     u, A, B, C, D, z, x, dt = _np_prep(u, delta, A, B, C, D, z, delta_bias, delta_softplus)
     dy = _arr(dy, np.float64)
     Bn, L, Dd = u.shape
     N = A.shape[1]
     hs = np.zeros((L + 1, Bn, Dd, N))
+    if h0 is not None:
+        hs[0] = _arr(h0, np.float64)
     As = np.zeros((L, Bn, Dd, N))
     os_ = np.zeros((L, Bn, Dd))
     for t in range(L):
@@ -284,4 +303,5 @@ def np_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None, delta_so
         carry = dh * As[t]
     dx = ddt * _np_sigmoid(x) if delta_softplus else ddt
     return {"du": du, "ddelta": dx, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz,
-            "ddelta_bias": dx.sum(axis=(0, 1)) if delta_bias is not None else None}
+            "ddelta_bias": dx.sum(axis=(0, 1)) if delta_bias is not None else None,
+            "dh0": carry if h0 is not None else None}

@@ -11,7 +11,7 @@
  *
  *     delta_eff = softplus(delta[t,d] + delta_bias[d])   (softplus optional)
  *     a         = exp(delta_eff * A[d,n])
- *     h[n]      = a * h[n] + delta_eff * B[t,n] * u[t,d]   (h = 0 before t = 0)
+ *     h[n]      = a * h[n] + delta_eff * B[t,n] * u[t,d]   (h = h0 or 0 before t = 0)
  *     y[t,d]    = sum_n C[t,n] h[n]  (+ D[d] u[t,d])  (* silu(z[t,d]))
  *     last_state[b,d,:] = h after the last step
  *
@@ -61,7 +61,7 @@ static int valid(const ss_oracle_problem* p) {
 #define DEFINE_FWD(REALT, SUF)                                                             \
   typedef struct {                                                                         \
     const ss_oracle_problem* p;                                                            \
-    const REALT *u, *delta, *A, *Bm, *Cm, *Dskip, *z, *bias;                               \
+    const REALT *u, *delta, *A, *Bm, *Cm, *Dskip, *z, *bias, *h0;                          \
     REALT *y, *last_state;                                                                 \
     const int64_t *chan_b, *chan_d; /* subset mode when non-NULL */                        \
     int64_t c0, c1;                 /* channel range: (b*D + d) or subset index */         \
@@ -74,12 +74,15 @@ static int valid(const ss_oracle_problem* p) {
     if (!h) { j->status = 1; return NULL; }                                                \
     for (int64_t c = j->c0; c < j->c1; ++c) {                                              \
       if (j->chan_b) {                                                                     \
+        const REALT* h0r = j->h0 ? j->h0 + (j->chan_b[c] * p->dim + j->chan_d[c]) * p->dstate \
+                                 : NULL;                                                   \
         fwd_channel_##SUF(p, j->u, j->delta, j->A, j->Bm, j->Cm, j->Dskip, j->z, j->bias,   \
-                          j->chan_b[c], j->chan_d[c], j->y + c * p->seqlen, 1,             \
+                          h0r, j->chan_b[c], j->chan_d[c], j->y + c * p->seqlen, 1,        \
                           j->last_state ? j->last_state + c * p->dstate : NULL, h);        \
       } else {                                                                             \
         int64_t b = c / p->dim, d = c % p->dim;                                            \
         fwd_channel_##SUF(p, j->u, j->delta, j->A, j->Bm, j->Cm, j->Dskip, j->z, j->bias,   \
+                          j->h0 ? j->h0 + c * p->dstate : NULL,                            \
                           b, d, j->y + b * p->seqlen * p->dim + d, p->dim,                 \
                           j->last_state ? j->last_state + (b * p->dim + d) * p->dstate     \
                                         : NULL,                                            \
@@ -91,9 +94,10 @@ static int valid(const ss_oracle_problem* p) {
   }                                                                                        \
   static int run_fwd_##SUF(const ss_oracle_problem* p, const REALT* u, const REALT* delta, \
                            const REALT* A, const REALT* Bm, const REALT* Cm,               \
-                           const REALT* Dskip, const REALT* z, const REALT* bias, REALT* y, \
-                           REALT* last_state, const int64_t* chan_b, const int64_t* chan_d, \
-                           int64_t nchan, int nthreads) {                                  \
+                           const REALT* Dskip, const REALT* z, const REALT* bias,          \
+                           const REALT* h0, REALT* y, REALT* last_state,                   \
+                           const int64_t* chan_b, const int64_t* chan_d, int64_t nchan,    \
+                           int nthreads) {                                                 \
     if (!valid(p)) return 1;                                                               \
     if (nchan == 0) return 0;                                                              \
     if (!u || !delta || !A || !Bm || !Cm || !y) return 1;                                  \
@@ -103,7 +107,7 @@ static int valid(const ss_oracle_problem* p) {
     int started[256];                                                                      \
     for (int i = 0; i < nthreads; ++i) {                                                   \
       fwd_job_##SUF jb = {p,     u,     delta,      A,      Bm,     Cm,                    \
-                          Dskip, z,     bias,       y,      last_state,                    \
+                          Dskip, z,     bias,       h0,     y,      last_state,            \
                           chan_b, chan_d, nchan * i / nthreads, nchan * (i + 1) / nthreads, \
                           0};                                                              \
       jobs[i] = jb;                                                                        \
@@ -123,38 +127,39 @@ static int valid(const ss_oracle_problem* p) {
 DEFINE_FWD(double, f64)
 DEFINE_FWD(float, f32)
 
-/* Full forward: y [B, L, D]; last_state [B, D, N] or NULL. */
+/* Full forward: y [B, L, D]; h0 [B, D, N] or NULL (zero initial state);
+ * last_state [B, D, N] or NULL. */
 int ss_oracle_fwd_f64(const ss_oracle_problem* p, const double* u, const double* delta,
                       const double* A, const double* Bm, const double* Cm, const double* Dskip,
-                      const double* z, const double* bias, double* y, double* last_state,
-                      int nthreads) {
+                      const double* z, const double* bias, const double* h0, double* y,
+                      double* last_state, int nthreads) {
   if (!valid(p)) return 1;
-  return run_fwd_f64(p, u, delta, A, Bm, Cm, Dskip, z, bias, y, last_state, NULL, NULL,
+  return run_fwd_f64(p, u, delta, A, Bm, Cm, Dskip, z, bias, h0, y, last_state, NULL, NULL,
                      p->batch * p->dim, nthreads);
 }
 
 int ss_oracle_fwd_f32(const ss_oracle_problem* p, const float* u, const float* delta,
                       const float* A, const float* Bm, const float* Cm, const float* Dskip,
-                      const float* z, const float* bias, float* y, float* last_state,
-                      int nthreads) {
+                      const float* z, const float* bias, const float* h0, float* y,
+                      float* last_state, int nthreads) {
   if (!valid(p)) return 1;
-  return run_fwd_f32(p, u, delta, A, Bm, Cm, Dskip, z, bias, y, last_state, NULL, NULL,
+  return run_fwd_f32(p, u, delta, A, Bm, Cm, Dskip, z, bias, h0, y, last_state, NULL, NULL,
                      p->batch * p->dim, nthreads);
 }
 
 /* Forward of a list of channels (chan_b[c], chan_d[c]), c < nchan.
- * y_out: [nchan, L]; ls_out: [nchan, N] or NULL. */
+ * h0: [B, D, N] or NULL; y_out: [nchan, L]; ls_out: [nchan, N] or NULL. */
 int ss_oracle_fwd_channels_f64(const ss_oracle_problem* p, const double* u, const double* delta,
                                const double* A, const double* Bm, const double* Cm,
                                const double* Dskip, const double* z, const double* bias,
-                               const int64_t* chan_b, const int64_t* chan_d, int64_t nchan,
-                               double* y_out, double* ls_out, int nthreads) {
+                               const double* h0, const int64_t* chan_b, const int64_t* chan_d,
+                               int64_t nchan, double* y_out, double* ls_out, int nthreads) {
   if (!valid(p) || nchan < 0 || (nchan > 0 && (!chan_b || !chan_d))) return 1;
   for (int64_t c = 0; c < nchan; ++c)
     if (chan_b[c] < 0 || chan_b[c] >= p->batch || chan_d[c] < 0 || chan_d[c] >= p->dim)
       return 1;
-  return run_fwd_f64(p, u, delta, A, Bm, Cm, Dskip, z, bias, y_out, ls_out, chan_b, chan_d,
-                     nchan, nthreads);
+  return run_fwd_f64(p, u, delta, A, Bm, Cm, Dskip, z, bias, h0, y_out, ls_out, chan_b,
+                     chan_d, nchan, nthreads);
 }
 
 /* --------------------------------------------------------------- backward */
@@ -162,8 +167,8 @@ int ss_oracle_fwd_channels_f64(const ss_oracle_problem* p, const double* u, cons
 #define DEFINE_BWD(REALT, SUF)                                                             \
   typedef struct {                                                                         \
     const ss_oracle_problem* p;                                                            \
-    const REALT *u, *delta, *A, *Bm, *Cm, *Dskip, *z, *bias, *dy;                          \
-    REALT *du, *ddelta, *dA, *dB_part, *dC_part, *dD, *dz, *dbias;                         \
+    const REALT *u, *delta, *A, *Bm, *Cm, *Dskip, *z, *bias, *h0, *dy;                     \
+    REALT *du, *ddelta, *dA, *dB_part, *dC_part, *dD, *dz, *dbias, *dh0;                   \
     int64_t d0, d1;                                                                        \
     int status;                                                                            \
   } bwd_job_##SUF;                                                                         \
@@ -181,8 +186,9 @@ int ss_oracle_fwd_channels_f64(const ss_oracle_problem* p, const double* u, cons
       j->status = 1;                                                                       \
     } else {                                                                               \
       bwd_range_##SUF(p, j->u, j->delta, j->A, j->Bm, j->Cm, j->Dskip, j->z, j->bias,       \
-                      j->dy, j->du, j->ddelta, j->dA, j->dB_part, j->dC_part, j->dD,       \
-                      j->dz, j->dbias, j->d0, j->d1, hist, ahist, dls, xs, os, dh);        \
+                      j->h0, j->dy, j->du, j->ddelta, j->dA, j->dB_part, j->dC_part,       \
+                      j->dD, j->dz, j->dbias, j->dh0, j->d0, j->d1, hist, ahist, dls, xs,  \
+                      os, dh);                                                             \
     }                                                                                      \
     free(hist); free(ahist); free(dls); free(xs); free(os); free(dh);                      \
     return NULL;                                                                           \
@@ -190,13 +196,17 @@ int ss_oracle_fwd_channels_f64(const ss_oracle_problem* p, const double* u, cons
   int ss_oracle_bwd_##SUF(const ss_oracle_problem* p, const REALT* u, const REALT* delta,  \
                           const REALT* A, const REALT* Bm, const REALT* Cm,                \
                           const REALT* Dskip, const REALT* z, const REALT* bias,           \
-                          const REALT* dy, REALT* du, REALT* ddelta, REALT* dA, REALT* dB, \
-                          REALT* dC, REALT* dD, REALT* dz, REALT* dbias, int nthreads) {   \
+                          const REALT* h0, const REALT* dy, REALT* du, REALT* ddelta,      \
+                          REALT* dA, REALT* dB, REALT* dC, REALT* dD, REALT* dz,           \
+                          REALT* dbias, REALT* dh0, int nthreads) {                        \
     if (!valid(p)) return 1;                                                               \
     const int64_t B = p->batch, L = p->seqlen, D = p->dim, N = p->dstate;                  \
     if (!u || !delta || !A || !Bm || !Cm || !dy || !du || !ddelta || !dA || !dB || !dC)    \
       return 1;                                                                            \
-    if ((!Dskip) != (!dD) || (!z) != (!dz) || (!bias) != (!dbias)) return 1;              \
+    if ((!Dskip) != (!dD) || (!z) != (!dz) || (!bias) != (!dbias) || (!h0) != (!dh0))     \
+      return 1;                                                                            \
+    if (dh0) /* with L = 0 the loss does not depend on h0 */                              \
+      memset(dh0, 0, sizeof(REALT) * (size_t)(B * D * N));                                 \
     const size_t bln = (size_t)(B * L * N);                                                \
     memset(dB, 0, sizeof(REALT) * bln);                                                    \
     memset(dC, 0, sizeof(REALT) * bln);                                                    \
@@ -212,9 +222,9 @@ int ss_oracle_fwd_channels_f64(const ss_oracle_problem* p, const double* u, cons
     int started[256];                                                                      \
     for (int i = 0; i < nthreads; ++i) {                                                   \
       bwd_job_##SUF jb = {p,  u,      delta, A,  Bm,                                       \
-                          Cm, Dskip,  z,     bias, dy,                                     \
+                          Cm, Dskip,  z,     bias, h0, dy,                                 \
                           du, ddelta, dA,    parts + (size_t)(2 * i) * bln,                \
-                          parts + (size_t)(2 * i + 1) * bln, dD, dz, dbias,                \
+                          parts + (size_t)(2 * i + 1) * bln, dD, dz, dbias, dh0,           \
                           D * i / nthreads, D * (i + 1) / nthreads, 0};                    \
       jobs[i] = jb;                                                                        \
     }                                                                                      \
@@ -236,8 +246,9 @@ int ss_oracle_fwd_channels_f64(const ss_oracle_problem* p, const double* u, cons
     return st;                                                                             \
   }
 
-/* Full backward.  Saved forward inputs plus dy [B, L, D]; outputs du, ddelta,
- * dz [B, L, D]; dB, dC [B, L, N]; dA [D, N]; dD, dbias [D].  dD / dz / dbias
- * must be given exactly when Dskip / z / bias are.  Outputs are overwritten. */
+/* Full backward.  Saved forward inputs (h0 [B, D, N] or NULL) plus dy
+ * [B, L, D]; outputs du, ddelta, dz [B, L, D]; dB, dC [B, L, N]; dA [D, N];
+ * dD, dbias [D]; dh0 [B, D, N].  dD / dz / dbias / dh0 must be given exactly
+ * when Dskip / z / bias / h0 are.  Outputs are overwritten. */
 DEFINE_BWD(double, f64)
 DEFINE_BWD(float, f32)

@@ -27,13 +27,16 @@ static REAL FN(sigmoid)(REAL x) { return (REAL)1 / ((REAL)1 + (REAL)exp(-(double
 
 /* Forward of one channel (b, d).  Writes y[b, t, d] for every t to
  * y_out[t * y_stride]; if ls_out is not NULL, writes the state after the last
- * step to ls_out[0 .. N-1].  h: [N] scratch. */
+ * step to ls_out[0 .. N-1].  h0_row: this channel's state before t = 0
+ * ([N]), or NULL for zero (the carried per-layer state of the mamba-rs page
+ * "mamba_ssm/gpu/backward.rs", whose forward pipeline runs the SSM from
+ * carried states).  h: [N] scratch. */
 static void FN(fwd_channel)(const ss_oracle_problem* p, const REAL* u, const REAL* delta,
                             const REAL* A, const REAL* Bm, const REAL* Cm, const REAL* Dskip,
-                            const REAL* z, const REAL* bias, int64_t b, int64_t d,
-                            REAL* y_out, int64_t y_stride, REAL* ls_out, REAL* h) {
+                            const REAL* z, const REAL* bias, const REAL* h0_row, int64_t b,
+                            int64_t d, REAL* y_out, int64_t y_stride, REAL* ls_out, REAL* h) {
   const int64_t L = p->seqlen, D = p->dim, N = p->dstate;
-  for (int64_t n = 0; n < N; ++n) h[n] = 0;           /* state before t = 0 */
+  for (int64_t n = 0; n < N; ++n) h[n] = h0_row ? h0_row[n] : 0;  /* state before t = 0 */
   for (int64_t t = 0; t < L; ++t) {
     const int64_t i = (b * L + t) * D + d;             /* [B, L, D] */
     const REAL* Bt = Bm + (b * L + t) * N;             /* [B, L, N] */
@@ -55,16 +58,18 @@ static void FN(fwd_channel)(const ss_oracle_problem* p, const REAL* u, const REA
 }
 
 /* Backward for the channels d in [d0, d1), every b.
- * Per-channel outputs (du, ddelta, dz, dA, dD, dbias) are written directly:
- * each (d, *) belongs to exactly one range.  dB and dC are sums over d, so
- * this range accumulates into its own dB_part / dC_part ([B, L, N], zeroed by
- * the caller); the caller adds the ranges' parts in range order.
+ * Per-channel outputs (du, ddelta, dz, dA, dD, dbias, dh0) are written
+ * directly: each (d, *) belongs to exactly one range.  dB and dC are sums over
+ * d, so this range accumulates into its own dB_part / dC_part ([B, L, N],
+ * zeroed by the caller); the caller adds the ranges' parts in range order.
+ * h0 / dh0: [B, D, N] state before t = 0 and its gradient, both NULL or both
+ * given (dh0 = dL/dh_{-1}, what the reverse sweep carries past t = 0).
  * hist: [L + 1, N] scratch (h_{-1} .. h_{L-1}); ahist: [L, N]; dl/xs/os: [L]. */
 static void FN(bwd_range)(const ss_oracle_problem* p, const REAL* u, const REAL* delta,
                           const REAL* A, const REAL* Bm, const REAL* Cm, const REAL* Dskip,
-                          const REAL* z, const REAL* bias, const REAL* dy,
+                          const REAL* z, const REAL* bias, const REAL* h0, const REAL* dy,
                           REAL* du, REAL* ddelta, REAL* dA, REAL* dB_part, REAL* dC_part,
-                          REAL* dD, REAL* dz, REAL* dbias, int64_t d0, int64_t d1,
+                          REAL* dD, REAL* dz, REAL* dbias, REAL* dh0, int64_t d0, int64_t d1,
                           REAL* hist, REAL* ahist, REAL* dls, REAL* xs, REAL* os, REAL* dh) {
   const int64_t B = p->batch, L = p->seqlen, D = p->dim, N = p->dstate;
   for (int64_t d = d0; d < d1; ++d) {
@@ -75,7 +80,8 @@ static void FN(bwd_range)(const ss_oracle_problem* p, const REAL* u, const REAL*
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t d = d0; d < d1; ++d) {
       /* forward, keeping every state, decay, delta and pre-gate output */
-      for (int64_t n = 0; n < N; ++n) hist[n] = 0;     /* row 0 = h_{-1} */
+      for (int64_t n = 0; n < N; ++n)                  /* row 0 = h_{-1} */
+        hist[n] = h0 ? h0[(b * D + d) * N + n] : 0;
       for (int64_t t = 0; t < L; ++t) {
         const int64_t i = (b * L + t) * D + d;
         const REAL* Bt = Bm + (b * L + t) * N;
@@ -127,6 +133,8 @@ static void FN(bwd_range)(const ss_oracle_problem* p, const REAL* u, const REAL*
         if (dbias) dbias[d] += dx;
         du[i] = dui;
       }
+      if (dh0)                                         /* dh = a_0 dL/dh_0 = dL/dh_{-1} */
+        for (int64_t n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = dh[n];
     }
   }
 }

@@ -44,6 +44,11 @@ MUTANTS = [
     ("du skip term dropped", "REAL dui = Dskip ? g * Dskip[d] : (REAL)0;", "REAL dui = 0;", None),
     ("dC uses previous state", "dC_part[(b * L + t) * N + n] += g * hcur;",
      "dC_part[(b * L + t) * N + n] += g * hprev;", None),
+    ("h0 ignored in forward", "h[n] = h0_row ? h0_row[n] : 0;", "h[n] = 0;", None),
+    ("h0 ignored in backward recompute", "hist[n] = h0 ? h0[(b * D + d) * N + n] : 0;",
+     "hist[n] = 0;", None),
+    ("dh0 without the first decay", "dh0[(b * D + d) * N + n] = dh[n];",
+     "dh0[(b * D + d) * N + n] = dh[n] / ahist[n];", None),
 ]
 
 

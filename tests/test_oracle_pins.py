@@ -5,7 +5,10 @@ examples, closed forms of the recurrence (A = 0, constant inputs, L = 1),
 an O(L^2) unrolled formula evaluated by brute force, softplus / gate identities,
 linearity, and, for the backward, central finite differences and a
 dot-product (adjoint) test.  The recurrence is the "Algorithm summary" of the
-baracuda-kernels page src/attention/selective_scan.rs.
+baracuda-kernels page src/attention/selective_scan.rs.  The initial state h0
+(the carried per-layer state of the mamba-rs page mamba_ssm/gpu/backward.rs)
+is pinned by a hand-worked decode step, the split-sequence identity, a closed
+form with no input drive, and finite differences.
 """
 import json
 import math
@@ -355,6 +358,122 @@ def test_backward_c_matches_numpy():
                 assert gn[k] is None
             else:
                 np.testing.assert_allclose(v, gn[k], rtol=1e-11, atol=1e-12, err_msg=k)
+
+
+# ------------------------------------------------------------ initial state
+
+def _h0(args, seed):
+    Bn, L, D = args["u"].shape
+    N = args["A"].shape[1]
+    return np.random.default_rng(seed).normal(size=(Bn, D, N))
+
+
+def test_h0_golden_decode_step():
+    with open(os.path.join(GOLDEN, "h0_examples.json")) as f:
+        doc = json.load(f)
+    for ex in doc["examples"]:
+        args = {k: (None if ex[k] is None else np.array(ex[k], dtype=np.float64)) for k in KEYS}
+        h0 = np.array(ex["h0"])
+        dy = np.array(ex["dy"])
+        for impl in ("c", "np"):
+            if impl == "c":
+                y, ls = oracle.fwd(**args, delta_softplus=ex["delta_softplus"],
+                                   return_last_state=True, h0=h0)
+                g = oracle.bwd(**args, dy=dy, delta_softplus=ex["delta_softplus"], h0=h0)
+            else:
+                y, ls = oracle.np_fwd(**args, delta_softplus=ex["delta_softplus"], h0=h0)
+                g = oracle.np_bwd(**args, dy=dy, delta_softplus=ex["delta_softplus"], h0=h0)
+            np.testing.assert_allclose(y, np.array(ex["y"]), rtol=1e-13, atol=1e-13)
+            np.testing.assert_allclose(ls, np.array(ex["last_state"]), rtol=1e-13, atol=1e-13)
+            for k, v in ex["grads"].items():
+                np.testing.assert_allclose(g[k], np.array(v), rtol=1e-13, atol=1e-13,
+                                           err_msg=f"{ex['name']} {k} ({impl})")
+
+
+@pytest.mark.parametrize("split", [1, 6, 13])
+def test_h0_split_sequence(split):
+    """Running t < s, then t >= s from the state reached at s, is the same
+    recurrence as one run (outputs and final state)."""
+    a = _rand(301, Bn=2, L=19, D=4, N=5)
+    h0 = _h0(a, 302)
+    y, ls = oracle.fwd(**a, return_last_state=True, h0=h0)
+    first = {k: (v[:, :split] if v is not None and v.ndim == 3 else v) for k, v in a.items()}
+    second = {k: (v[:, split:] if v is not None and v.ndim == 3 else v) for k, v in a.items()}
+    y1, ls1 = oracle.fwd(**first, return_last_state=True, h0=h0)
+    y2, ls2 = oracle.fwd(**second, return_last_state=True, h0=ls1)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), y, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ls2, ls, rtol=1e-12, atol=1e-13)
+
+
+def test_h0_closed_form_without_input():
+    """With B = 0 the state only decays: h_t = exp(A * sum_{s<=t} dt_s) h0."""
+    a = _rand(311, Bn=2, L=9, D=3, N=4, has_D=False, has_z=False)
+    a["B"] = np.zeros_like(a["B"])
+    h0 = _h0(a, 312)
+    y, ls = oracle.fwd(**a, return_last_state=True, h0=h0)
+    x = a["delta"] + a["delta_bias"][None, None, :]
+    dt = np.vectorize(_softplus)(x)
+    cum = np.cumsum(dt, axis=1)                                     # [B, L, D]
+    hs = np.exp(cum[..., None] * a["A"][None, None]) * h0[:, None]  # [B, L, D, N]
+    yr = np.einsum("bldn,bln->bld", hs, a["C"])
+    np.testing.assert_allclose(y, yr, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ls, hs[:, -1], rtol=1e-12, atol=1e-14)
+
+
+def test_h0_finite_differences_and_numpy():
+    a = _rand(321, Bn=2, L=5, D=3, N=4)
+    h0 = _h0(a, 322)
+    dy = np.random.default_rng(323).normal(size=a["u"].shape)
+    g = oracle.bwd(**a, dy=dy, h0=h0)
+    fd = np.zeros_like(h0)
+    it = np.nditer(h0, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        eps = 1e-6 * max(1.0, abs(h0[idx]))
+        hp, hm = h0.copy(), h0.copy()
+        hp[idx] += eps
+        hm[idx] -= eps
+        lp = float(np.sum(oracle.fwd(**a, h0=hp)[0] * dy))
+        lm = float(np.sum(oracle.fwd(**a, h0=hm)[0] * dy))
+        fd[idx] = (lp - lm) / (2 * eps)
+    np.testing.assert_allclose(g["dh0"], fd, rtol=2e-6, atol=2e-7)
+    # the other gradients see h0 through the recurrence: finite differences in A
+    fda = np.zeros_like(a["A"])
+    it = np.nditer(a["A"], flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        eps = 1e-6 * max(1.0, abs(a["A"][idx]))
+        ap, am = {**a, "A": a["A"].copy()}, {**a, "A": a["A"].copy()}
+        ap["A"][idx] += eps
+        am["A"][idx] -= eps
+        lp = float(np.sum(oracle.fwd(**ap, h0=h0)[0] * dy))
+        lm = float(np.sum(oracle.fwd(**am, h0=h0)[0] * dy))
+        fda[idx] = (lp - lm) / (2 * eps)
+    np.testing.assert_allclose(g["dA"], fda, rtol=2e-6, atol=2e-7)
+    gn = oracle.np_bwd(**a, dy=dy, h0=h0)
+    for k, v in g.items():
+        if v is None:
+            assert gn[k] is None
+        else:
+            np.testing.assert_allclose(v, gn[k], rtol=1e-11, atol=1e-12, err_msg=k)
+    yn, lsn = oracle.np_fwd(**a, h0=h0)
+    yc, lsc = oracle.fwd(**a, h0=h0, return_last_state=True)
+    np.testing.assert_allclose(yc, yn, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lsc, lsn, rtol=1e-12, atol=1e-13)
+
+
+def test_h0_zero_is_no_h0():
+    a = _rand(331)
+    z0 = np.zeros((2, 5, 3))
+    y0, l0 = oracle.fwd(**a, return_last_state=True)
+    y1, l1 = oracle.fwd(**a, return_last_state=True, h0=z0)
+    assert np.array_equal(y0, y1) and np.array_equal(l0, l1)
+    dy = np.random.default_rng(332).normal(size=a["u"].shape)
+    g0 = oracle.bwd(**a, dy=dy)
+    g1 = oracle.bwd(**a, dy=dy, h0=z0)
+    for k in g0:
+        if g0[k] is not None:
+            assert np.array_equal(g0[k], g1[k]), k
 
 
 def test_f32_floor_is_close():
