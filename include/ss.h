@@ -6,7 +6,7 @@
  *     x        = delta[b,t,d] + delta_bias[d]            (bias optional)
  *     dt       = softplus(x) = log(1 + e^x)  if delta_softplus, else x
  *     a        = exp(dt * A[d,n])
- *     h[n]     = a * h[n] + dt * B[b,t,n] * u[b,t,d]     (h = 0 before t = 0)
+ *     h[n]     = a * h[n] + dt * B[b,t,n] * u[b,t,d]     (h = h0[b,d,n], or 0, before t = 0)
  *     o        = sum_n C[b,t,n] * h[n] + D[d] * u[b,t,d] (D optional)
  *     y[b,t,d] = o * z * sigmoid(z), z = z[b,t,d]       (z optional)
  *     last_state[b,d,n] = h[n] after t = L-1            (optional)
@@ -14,7 +14,7 @@
  * Layouts (same page, "Shape contract"): every tensor is contiguous
  * row-major; u, delta, z, y, dy, du, ddelta, dz are [B, L, D]; A and dA are
  * [D, N]; B, C, dB, dC are [B, L, N]; D, delta_bias, dD, ddelta_bias are
- * [D]; last_state is [B, D, N].
+ * [D]; last_state, h0 and dh0 are [B, D, N].
  *
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers owned by the caller (workspace included).
@@ -98,6 +98,31 @@ int ss_bwd(const ss_desc* desc, const void* u, const void* delta, const void* A,
            const void* delta_bias, const void* dy, void* du, void* ddelta, void* dA,
            void* dB, void* dC, void* dD, void* dz, void* ddelta_bias, void* workspace,
            size_t workspace_bytes, void* stream);
+
+/* Forward from a given initial state h0 [B, D, N] (param dtype; NULL means
+ * zero, i.e. ss_fwd).  This is the state carried from one call to the next:
+ * the mamba-rs page "mamba_ssm/gpu/backward.rs" runs its SSM forward from
+ * per-layer states carried between calls (module docs, forward pipeline;
+ * ssm_states [B*n_layers*d_inner*d_state] of its target-forward scratch).
+ * With seqlen = 1 it is one decode step.  last_state may be the same buffer
+ * as h0 (an in-place state update); the call then runs as a single chunk and
+ * returns SS_ERR_UNSUPPORTED if one chunk's rows would exceed 2^31 bytes.
+ * h0 and last_state must otherwise not overlap.  If L = 0, last_state = h0.
+ * Everything else as ss_fwd. */
+int ss_fwd_h0(const ss_desc* desc, const void* u, const void* delta, const void* A,
+              const void* B, const void* C, const void* Dskip, const void* z,
+              const void* delta_bias, const void* h0, void* y, void* last_state,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of ss_fwd_h0: as ss_bwd, plus dh0 [B, D, N] (param dtype), the
+ * gradient with respect to h0, which must be given exactly when h0 is
+ * (otherwise SS_ERR_INVALID_PROBLEM) and must not overlap h0.  If L = 0,
+ * dh0 = 0.  Same workspace as ss_bwd. */
+int ss_bwd_h0(const ss_desc* desc, const void* u, const void* delta, const void* A,
+              const void* B, const void* C, const void* Dskip, const void* z,
+              const void* delta_bias, const void* h0, const void* dy, void* du, void* ddelta,
+              void* dA, void* dB, void* dC, void* dD, void* dz, void* ddelta_bias, void* dh0,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /* The schedule the library would use for a descriptor (informational). */
 typedef struct ss_plan {

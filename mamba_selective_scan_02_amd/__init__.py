@@ -7,9 +7,10 @@ on the tensors' device and passes raw pointers plus the current HIP stream.
 If the library is missing, every call raises: there is no fallback.
 
 Raw C entry points with the header's names: ``ss_workspace_size``,
-``ss_fwd``, ``ss_bwd``, ``ss_plan_query``, ``ss_status_string``,
-``ss_last_error``.  Tensor-level helpers: ``fwd``, ``bwd`` and the autograd
-function ``selective_scan``.
+``ss_fwd``, ``ss_bwd``, ``ss_fwd_h0``, ``ss_bwd_h0``, ``ss_plan_query``,
+``ss_status_string``, ``ss_last_error``.  Tensor-level helpers: ``fwd``,
+``bwd`` (both with an optional initial state ``h0``), ``decode_step`` and the
+autograd function ``selective_scan``.
 """
 from __future__ import annotations
 
@@ -19,8 +20,9 @@ from typing import Dict, Optional, Tuple
 
 import torch
 
-__all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "selective_scan", "plan", "workspace_size",
-           "ss_workspace_size", "ss_fwd", "ss_bwd", "ss_plan_query", "ss_status_string",
+__all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "decode_step", "selective_scan", "plan",
+           "workspace_size", "ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0", "ss_bwd_h0",
+           "ss_plan_query", "ss_status_string",
            "ss_last_error", "library_path", "load_library",
            "SS_OK", "SS_ERR_INVALID_PROBLEM", "SS_ERR_UNSUPPORTED",
            "SS_ERR_WORKSPACE_TOO_SMALL", "SS_ERR_HIP"]
@@ -70,6 +72,10 @@ def load_library(path: Optional[str] = None):
     lib.ss_fwd.restype = ctypes.c_int
     lib.ss_bwd.argtypes = [dp] + [vp] * 18 + [sz, vp]
     lib.ss_bwd.restype = ctypes.c_int
+    lib.ss_fwd_h0.argtypes = [dp] + [vp] * 12 + [sz, vp]
+    lib.ss_fwd_h0.restype = ctypes.c_int
+    lib.ss_bwd_h0.argtypes = [dp] + [vp] * 20 + [sz, vp]
+    lib.ss_bwd_h0.restype = ctypes.c_int
     lib.ss_plan_query.argtypes = [dp, ctypes.c_int32, ctypes.POINTER(SsPlan)]
     lib.ss_plan_query.restype = ctypes.c_int
     lib.ss_status_string.argtypes = [ctypes.c_int]
@@ -101,6 +107,19 @@ def ss_bwd(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, dy, du, ddelta
     return load_library().ss_bwd(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias,
                                  dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, workspace,
                                  workspace_bytes, stream)
+
+
+def ss_fwd_h0(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, h0, y, last_state,
+              workspace, workspace_bytes: int, stream) -> int:
+    return load_library().ss_fwd_h0(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias, h0,
+                                    y, last_state, workspace, workspace_bytes, stream)
+
+
+def ss_bwd_h0(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, h0, dy, du, ddelta, dA,
+              dB, dC, dD, dz, ddelta_bias, dh0, workspace, workspace_bytes: int, stream) -> int:
+    return load_library().ss_bwd_h0(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias, h0,
+                                    dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                                    workspace, workspace_bytes, stream)
 
 
 def ss_plan_query(desc: SsDesc, backward: int, out: SsPlan) -> int:
@@ -174,12 +193,17 @@ def _stream_of(device: torch.device):
 
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = True,
         return_last_state: bool = False, chunk_len: int = 0, y: Optional[torch.Tensor] = None,
-        workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        workspace: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None,
+        last_state: Optional[torch.Tensor] = None
+        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective-scan forward on the tensors' GPU.
 
-    u, delta, z: [B, L, D]; A: [D, N]; B, C: [B, L, N]; D, delta_bias: [D].
+    u, delta, z: [B, L, D]; A: [D, N]; B, C: [B, L, N]; D, delta_bias: [D];
+    h0 (state before the first step, zero if None): [B, D, N].
     u / delta / B / C / z share one dtype (f32, f16 or bf16); A / D /
-    delta_bias are float32 or that dtype.  Returns (y, last_state or None).
+    delta_bias / h0 / last_state are float32 or that dtype.  last_state, if
+    given, receives the final state (it may be h0 itself: an in-place state
+    update).  Returns (y, last_state or None).
     """
     desc = _desc_for(u, A, delta_softplus, chunk_len)
     dev, io, pa = u.device, u.dtype, A.dtype
@@ -191,28 +215,47 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool
         _check(t, name, shape, dt, dev)
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU")
+    _check(h0, "h0", (Bn, Dd, N), pa, dev)
+    _check(last_state, "last_state", (Bn, Dd, N), pa, dev)
     if y is None:
         y = torch.empty((Bn, L, Dd), dtype=io, device=dev)
     _check(y, "y", (Bn, L, Dd), io, dev)
-    ls = torch.empty((Bn, Dd, N), dtype=pa, device=dev) if return_last_state else None
+    ls = last_state
+    if ls is None and return_last_state:
+        ls = torch.empty((Bn, Dd, N), dtype=pa, device=dev)
     need = workspace_size(desc, False)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = ss_fwd(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                _ptr(delta_bias), _ptr(y), _ptr(ls), _ptr(workspace), workspace.numel(),
-                _stream_of(dev))
+    st = ss_fwd_h0(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                   _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls), _ptr(workspace),
+                   workspace.numel(), _stream_of(dev))
     if st != SS_OK:
-        _raise(st, "ss_fwd")
+        _raise(st, "ss_fwd_h0" if h0 is not None else "ss_fwd")
     return y, ls
+
+
+def decode_step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                delta_softplus: bool = True) -> torch.Tensor:
+    """One recurrence step on a carried state, updated in place.
+
+    state: [B, D, N] (param dtype); u, delta, z: [B, D]; B, C: [B, N].
+    Returns y: [B, D].
+    """
+    y, _ = fwd(u.unsqueeze(1), delta.unsqueeze(1), A, B.unsqueeze(1), C.unsqueeze(1), D,
+               None if z is None else z.unsqueeze(1), delta_bias, delta_softplus,
+               h0=state, last_state=state)
+    return y.squeeze(1)
 
 
 def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None,
         delta_softplus: bool = True, chunk_len: int = 0,
-        workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
+        workspace: Optional[torch.Tensor] = None,
+        h0: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
     """Selective-scan backward: gradients of sum(dy * y).
 
-    Returns a dict with du, ddelta, dA, dB, dC, dD, dz, ddelta_bias (dD / dz /
-    ddelta_bias are None when D / z / delta_bias are None).
+    Returns a dict with du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0
+    (dD / dz / ddelta_bias / dh0 are None when D / z / delta_bias / h0 are
+    None).
     """
     desc = _desc_for(u, A, delta_softplus, chunk_len)
     dev, io, pa = u.device, u.dtype, A.dtype
@@ -221,7 +264,7 @@ def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None,
                                (A, "A", (Dd, N), pa), (B, "B", (Bn, L, N), io),
                                (C, "C", (Bn, L, N), io), (D, "D", (Dd,), pa),
                                (z, "z", (Bn, L, Dd), io), (delta_bias, "delta_bias", (Dd,), pa),
-                               (dy, "dy", (Bn, L, Dd), io)):
+                               (dy, "dy", (Bn, L, Dd), io), (h0, "h0", (Bn, Dd, N), pa)):
         _check(t, name, shape, dt, dev)
     if dy is None:
         raise ValueError("dy is required")
@@ -236,37 +279,39 @@ def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None,
         "dD": torch.empty((Dd,), dtype=pa, device=dev) if D is not None else None,
         "dz": torch.empty((Bn, L, Dd), dtype=io, device=dev) if z is not None else None,
         "ddelta_bias": torch.empty((Dd,), dtype=pa, device=dev) if delta_bias is not None else None,
+        "dh0": torch.empty((Bn, Dd, N), dtype=pa, device=dev) if h0 is not None else None,
     }
     need = workspace_size(desc, True)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = ss_bwd(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                _ptr(delta_bias), _ptr(dy), _ptr(out["du"]), _ptr(out["ddelta"]),
-                _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
-                _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(workspace), workspace.numel(),
-                _stream_of(dev))
+    st = ss_bwd_h0(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                   _ptr(delta_bias), _ptr(h0), _ptr(dy), _ptr(out["du"]), _ptr(out["ddelta"]),
+                   _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                   _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
+                   _ptr(workspace), workspace.numel(), _stream_of(dev))
     if st != SS_OK:
-        _raise(st, "ss_bwd")
+        _raise(st, "ss_bwd_h0" if h0 is not None else "ss_bwd")
     return out
 
 
 class _SelectiveScanFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, u, delta, A, B, C, D, z, delta_bias, delta_softplus):
-        y, _ = fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus)
+    def forward(ctx, u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0):
+        y, _ = fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0=h0)
         ctx.delta_softplus = delta_softplus
-        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias)
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0)
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        u, delta, A, B, C, D, z, delta_bias = ctx.saved_tensors
-        g = bwd(u, delta, A, B, C, D, z, delta_bias, dy.contiguous(), ctx.delta_softplus)
+        u, delta, A, B, C, D, z, delta_bias, h0 = ctx.saved_tensors
+        g = bwd(u, delta, A, B, C, D, z, delta_bias, dy.contiguous(), ctx.delta_softplus,
+                h0=h0)
         return (g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"],
-                g["ddelta_bias"], None)
+                g["ddelta_bias"], None, g["dh0"])
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                   delta_softplus: bool = True) -> torch.Tensor:
-    """Differentiable forward (autograd backward runs ``ss_bwd``)."""
-    return _SelectiveScanFn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus)
+                   delta_softplus: bool = True, h0=None) -> torch.Tensor:
+    """Differentiable forward (autograd backward runs ``ss_bwd_h0``)."""
+    return _SelectiveScanFn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0)

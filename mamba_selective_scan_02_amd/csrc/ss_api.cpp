@@ -21,6 +21,7 @@
 namespace ss {
 hipError_t launch_fwd(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_t s);
 hipError_t launch_zero_param(void* p, int64_t n, int dtype, hipStream_t s);
+hipError_t launch_copy_param(void* dst, const void* src, int64_t n, int dtype, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, const Plan& p, int io_dtype, hipStream_t s);
 }  // namespace ss
 
@@ -84,6 +85,12 @@ int check_workspace(size_t need, void* ws, size_t ws_bytes, const char* who) {
   return SS_OK;
 }
 
+// [p, p + bytes) and [q, q + bytes) share at least one byte
+bool overlap(const void* p, const void* q, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return bytes > 0 && a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes;
+}
+
 int hip_status(hipError_t e, const char* who) {
   if (e == hipSuccess) return SS_OK;
   return fail(SS_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -115,8 +122,16 @@ int ss_plan_query(const ss_desc* d, int32_t backward, ss_plan* out) {
 int ss_fwd(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,
            const void* C, const void* Dskip, const void* z, const void* delta_bias, void* y,
            void* last_state, void* workspace, size_t workspace_bytes, void* stream) {
+  return ss_fwd_h0(d, u, delta, A, B, C, Dskip, z, delta_bias, nullptr, y, last_state,
+                   workspace, workspace_bytes, stream);
+}
+
+int ss_fwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,
+              const void* C, const void* Dskip, const void* z, const void* delta_bias,
+              const void* h0, void* y, void* last_state, void* workspace,
+              size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  const char* who = "ss_fwd";
+  const char* who = h0 ? "ss_fwd_h0" : "ss_fwd";
   int st = check_desc(d, who);
   if (st != SS_OK) return st;
   const int64_t Bn = d->batch, L = d->seqlen, D = d->dim, N = d->dstate;
@@ -124,11 +139,19 @@ int ss_fwd(const ss_desc* d, const void* u, const void* delta, const void* A, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   PtrCheck pc{who};
   pc.opt(last_state, "last_state", pa);
+  if (Bn * D * N > 0) pc.opt(h0, "h0", pa);
   if (pc.status != SS_OK) return pc.status;
+  const int64_t state_bytes = Bn * D * N * pa;
+  const bool in_place = h0 && last_state == h0 && state_bytes > 0;
+  if (h0 && last_state && !in_place && overlap(h0, last_state, state_bytes))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: h0 and last_state must be the same buffer or "
+                "not overlap", who);
   if (Bn * L * D == 0) {
-    // Nothing to scan.  An empty sequence leaves the initial (zero) state.
-    if (L == 0 && last_state && Bn * D * N > 0)
-      return hip_status(ss::launch_zero_param(last_state, Bn * D * N, d->param_dtype, s), who);
+    // Nothing to scan.  An empty sequence leaves the initial state (h0 or 0).
+    if (L == 0 && last_state && state_bytes > 0)
+      return hip_status(h0 ? ss::launch_copy_param(last_state, h0, Bn * D * N, d->param_dtype, s)
+                           : ss::launch_zero_param(last_state, Bn * D * N, d->param_dtype, s),
+                        who);
     return SS_OK;
   }
   pc.need(u, "u", io);
@@ -143,13 +166,21 @@ int ss_fwd(const ss_desc* d, const void* u, const void* delta, const void* A, co
   pc.opt(z, "z", io);
   pc.opt(delta_bias, "delta_bias", pa);
   if (pc.status != SS_OK) return pc.status;
-  const ss::Plan p = ss::make_plan(*d, false);
+  // In place (last_state == h0): one chunk, so that the only reader of h0 is
+  // the lane that later writes the same elements of last_state.
+  ss_desc dd = *d;
+  if (in_place) dd.chunk_len = d->seqlen;
+  const ss::Plan p = ss::make_plan(dd, false);
+  if (in_place && p.K > 1)
+    return fail(SS_ERR_UNSUPPORTED, "%s: an in-place state update (last_state == h0) needs a "
+                "single chunk, and this shape's rows exceed one chunk's 32-bit range", who);
   st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
   if (st != SS_OK) return st;
 
   ss::FwdArgs a{};
   a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C;
   a.Dskip = Dskip; a.z = z; a.bias = delta_bias; a.y = y; a.last_state = last_state;
+  a.h0 = N > 0 ? h0 : nullptr;
   char* ws = static_cast<char*>(workspace);
   a.chunk_dsum = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_dsum) : nullptr;
   a.chunk_state = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_state) : nullptr;
@@ -164,10 +195,21 @@ int ss_bwd(const ss_desc* d, const void* u, const void* delta, const void* A, co
            const void* C, const void* Dskip, const void* z, const void* delta_bias,
            const void* dy, void* du, void* ddelta, void* dA, void* dB, void* dC, void* dD,
            void* dz, void* ddelta_bias, void* workspace, size_t workspace_bytes, void* stream) {
+  return ss_bwd_h0(d, u, delta, A, B, C, Dskip, z, delta_bias, nullptr, dy, du, ddelta, dA, dB,
+                   dC, dD, dz, ddelta_bias, nullptr, workspace, workspace_bytes, stream);
+}
+
+int ss_bwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,
+              const void* C, const void* Dskip, const void* z, const void* delta_bias,
+              const void* h0, const void* dy, void* du, void* ddelta, void* dA, void* dB,
+              void* dC, void* dD, void* dz, void* ddelta_bias, void* dh0, void* workspace,
+              size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  const char* who = "ss_bwd";
+  const char* who = h0 ? "ss_bwd_h0" : "ss_bwd";
   int st = check_desc(d, who);
   if (st != SS_OK) return st;
+  if ((h0 == nullptr) != (dh0 == nullptr))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: h0 and dh0 must be both given or both omitted", who);
   if ((Dskip == nullptr) != (dD == nullptr))
     return fail(SS_ERR_INVALID_PROBLEM, "%s: D and dD must be both given or both omitted", who);
   if ((z == nullptr) != (dz == nullptr))
@@ -192,16 +234,22 @@ int ss_bwd(const ss_desc* d, const void* u, const void* delta, const void* A, co
   if (Bn * L * N > 0) { pc.need(dB, "dB", io); pc.need(dC, "dC", io); }
   pc.opt(Dskip, "D", pa); pc.opt(dD, "dD", pa);
   pc.opt(delta_bias, "delta_bias", pa); pc.opt(ddelta_bias, "ddelta_bias", pa);
+  if (Bn * D * N > 0) { pc.opt(h0, "h0", pa); pc.opt(dh0, "dh0", pa); }
   if (pc.status != SS_OK) return pc.status;
+  if (h0 && overlap(h0, dh0, Bn * D * N * pa))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: dh0 must not overlap h0", who);
   st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
   if (st != SS_OK) return st;
   if (Bn * L * D == 0 && D * N == 0 && Bn * L * N == 0 && D == 0) return SS_OK;
+  const bool has_state = h0 && Bn * D * N > 0;
 
   ss::BwdArgs a{};
   a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C;
   a.Dskip = Dskip; a.z = z; a.bias = delta_bias; a.dy = dy;
   a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC;
   a.dD = dD; a.dz = dz; a.dbias = ddelta_bias;
+  a.h0 = has_state ? h0 : nullptr;
+  a.dh0 = has_state ? dh0 : nullptr;
   a.ws = static_cast<char*>(workspace);
   a.Bn = Bn; a.L = L; a.D = D; a.N = N;
   a.chunk_len = p.chunk_len; a.K = p.K;

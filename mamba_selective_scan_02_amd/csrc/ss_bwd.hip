@@ -144,7 +144,8 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) 
   float* fs = a.fstate + (b * K * N + n) * D + d;   // + k * N * D
   float* bs = a.bstate + (b * K * N + n) * D + d;
   const float* ds = a.dsum + b * K * D + d;         // + k * D
-  float hc = 0.0f, cc = 0.0f;
+  float hc = a.h0 ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0f;  // h_in(0)
+  float cc = 0.0f;
   constexpr int KB = 8;
   for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
     float sf[KB], df[KB], sb[KB], dbk[KB];
@@ -240,12 +241,14 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
     for (int64_t n = 0; n < N; ++n) {
       const float An = ld_param(a.A, d * N + n, a.param_dtype);
       const float A2 = An * kLog2e;
-      const float h0 = (k > 0) ? a.fstate[((b * K + (k - 1)) * N + n) * D + d] : 0.0f;
+      const float hin = (k > 0)  ? a.fstate[((b * K + (k - 1)) * N + n) * D + d]
+                        : a.h0   ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype)
+                                 : 0.0f;
       float dh = (k < K - 1) ? a.bstate[((b * K + (k + 1)) * N + n) * D + d] : 0.0f;
       const float* bn = sB + n * T;
       const float* cn = sC + n * T;
       float hs[T], ah[T];
-      float hp = h0;
+      float hp = hin;
 #pragma unroll
       for (int tt = 0; tt < T; ++tt) {
         const float av = fast_exp2(dl[tt] * A2);
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
         vB[tt] = dh * xu[tt];
         dua[tt] = __builtin_fmaf(dh, bn[tt], dua[tt]);
         const float m = dh * ah[tt];
-        const float q = m * (tt > 0 ? hs[tt - 1] : h0);
+        const float q = m * (tt > 0 ? hs[tt - 1] : hin);
         ddl[tt] = __builtin_fmaf(q, An, ddl[tt]);
         dA_acc = __builtin_fmaf(q, dl[tt], dA_acc);
         dh = m;
@@ -271,6 +274,8 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
       if (active) {
         float* pa = a.part_dA + ((b * a.KG + kg) * N + n) * D + d;
         *pa = (k == k_hi - 1) ? dA_acc : *pa + dA_acc;
+        // after step 0 of chunk 0, dh is dL/dh_{-1}
+        if (k == 0 && a.dh0) st_param(a.dh0, (b * D + d) * N + n, a.param_dtype, dh);
       }
       // dB / dC for this n: sum over the workgroup's channels in LDS.
       // Inactive (tail) lanes contribute zero.
@@ -454,6 +459,7 @@ hipError_t launch_bwd(const BwdArgs& a_in, const Plan& p, int io_dtype, hipStrea
     if (e == hipSuccess) e = zero_bytes(a.dbias, D * pa, s);
     if (e == hipSuccess) e = zero_bytes(a.dB, Bn * L * N * io, s);
     if (e == hipSuccess) e = zero_bytes(a.dC, Bn * L * N * io, s);
+    if (e == hipSuccess) e = zero_bytes(a.dh0, Bn * D * N * pa, s);  // L = 0: y ignores h0
     return e;
   }
   a.dsum = reinterpret_cast<float*>(a.ws + p.off_dsum);

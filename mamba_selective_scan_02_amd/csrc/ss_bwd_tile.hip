@@ -281,7 +281,9 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
     const int n = n0 + i;
     An[i] = n < N ? ld_param(a.A, d * N + n, a.param_dtype) : 0.0f;
     A2[i] = An[i] * kLog2e;
-    h[i] = (k > 0 && n < N) ? a.fstate[((b * K + (k - 1)) * N + n) * D + d] : 0.0f;
+    h[i] = (k > 0 && n < N) ? a.fstate[((b * K + (k - 1)) * N + n) * D + d]
+           : (a.h0 && n < N) ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype)
+                             : 0.0f;
     dh[i] = (k < K - 1 && n < N) ? a.bstate[((b * K + (k + 1)) * N + n) * D + d] : 0.0f;
     dA_acc[i] = 0.0f;
   }
@@ -502,8 +504,12 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
   db_acc = bsum8(db_acc);
   if (!P.active) return;
 #pragma unroll
-  for (int i = 0; i < NS; ++i)
+  for (int i = 0; i < NS; ++i) {
     if (n0 + i < N) a.part_dA[((b * a.KG + k) * N + n0 + i) * D + d] = dA_acc[i];
+    // after tile 0 of chunk 0, dh is the adjoint carried past t = 0: dL/dh_{-1}
+    if (k == 0 && a.dh0 && n0 + i < N)
+      st_param(a.dh0, (b * D + d) * N + n0 + i, a.param_dtype, dh[i]);
+  }
   if (g == 0) {
     a.part_dD[(b * a.KG + k) * D + d] = dD_acc;
     a.part_db[(b * a.KG + k) * D + d] = db_acc;

@@ -156,6 +156,7 @@ struct FwdArgs {
   const void* bias;        // nullable
   void* y;
   void* last_state;        // nullable
+  const void* h0;          // nullable: [Bn, D, N] state before t = 0 (param dtype)
   float* chunk_dsum;       // [Bn, K, D]   sum of delta_eff over each chunk
   float* chunk_state;      // [Bn, K, N, D] chunk-end state from zero / carried-in state
   int64_t Bn, L, D, N;
@@ -182,6 +183,7 @@ struct BwdArgs {
   const void* Dskip;       // nullable
   const void* z;           // nullable
   const void* bias;        // nullable
+  const void* h0;          // nullable: [Bn, D, N] state before t = 0 (param dtype)
   const void* dy;
   void* du;
   void* ddelta;
@@ -191,6 +193,7 @@ struct BwdArgs {
   void* dD;                // nullable (iff Dskip)
   void* dz;                // nullable (iff z)
   void* dbias;             // nullable (iff bias)
+  void* dh0;               // nullable (iff h0): [Bn, D, N] gradient of h0
   char* ws;
   float* dsum;
   float* fstate;

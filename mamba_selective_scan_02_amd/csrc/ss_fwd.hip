@@ -80,6 +80,8 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
     h[i] = 0.0f;
     if (MODE == MODE_FULL && k > 0 && ok)
       h[i] = a.chunk_state[((b * a.K + (k - 1)) * N + n) * D + d];
+    else if (MODE == MODE_FULL && k == 0 && ok && a.h0)
+      h[i] = ld_param(a.h0, (b * D + d) * N + n, a.param_dtype);
   }
   const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
   const float A2 = ld_param(a.A, d * N + n, a.param_dtype) * kLog2e;
   float* __restrict__ st = a.chunk_state + (b * K * N + n) * D + d;  // + k * N * D
   const float* __restrict__ ds = a.chunk_dsum + b * K * D + d;       // + k * D
-  float hc = 0.0f;
+  float hc = a.h0 ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0f;  // h_in(0)
   constexpr int KB = 16;
   for (int64_t k0 = 0; k0 < K - 1; k0 += KB) {
     float sv[KB], dv[KB];
@@ -320,6 +322,18 @@ __global__ void fill_zero_param(void* p, int64_t n, int dtype) {
 hipError_t launch_zero_param(void* p, int64_t n, int dtype, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   fill_zero_param<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p, n, dtype);
+  return hipGetLastError();
+}
+
+// Copy a param-typed buffer (last_state = h0 when L = 0).
+__global__ void copy_param(void* dst, const void* src, int64_t n, int dtype) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) st_param(dst, i, dtype, ld_param(src, i, dtype));
+}
+
+hipError_t launch_copy_param(void* dst, const void* src, int64_t n, int dtype, hipStream_t s) {
+  if (n <= 0 || dst == src) return hipSuccess;
+  copy_param<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(dst, src, n, dtype);
   return hipGetLastError();
 }
 

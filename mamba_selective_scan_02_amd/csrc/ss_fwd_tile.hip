@@ -125,6 +125,8 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
     h[i] = 0.0f;
     if (MODE == TMODE_FULL && k > 0 && n < N)
       h[i] = a.chunk_state[((b * a.K + (k - 1)) * N + n) * D + d];
+    else if (MODE == TMODE_FULL && k == 0 && n < N && a.h0)
+      h[i] = ld_param(a.h0, (b * D + d) * N + n, a.param_dtype);
   }
   const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
@@ -389,6 +391,8 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
     A2[i] = n < N ? ld_param(a.A, d * N + n, a.param_dtype) * kLog2e : 0.0f;
     h[i] = 0.0f;
     if (FULL && k > 0 && n < N) h[i] = a.chunk_state[((b * a.K + (k - 1)) * N + n) * D + d];
+    else if (FULL && k == 0 && n < N && a.h0)
+      h[i] = ld_param(a.h0, (b * D + d) * N + n, a.param_dtype);
   }
   const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;

@@ -26,14 +26,14 @@ P = ctypes.c_void_p(0x7F0000000000)
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ss_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ss_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = ss.load_library()
     names = _declared_functions()
-    assert set(names) == {"ss_workspace_size", "ss_fwd", "ss_bwd", "ss_plan_query",
-                          "ss_status_string", "ss_last_error"}
+    assert set(names) == {"ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0", "ss_bwd_h0",
+                          "ss_plan_query", "ss_status_string", "ss_last_error"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -60,6 +60,37 @@ def _bwd(desc, **over):
                                                "delta_bias", "dy", "du", "ddelta", "dA", "dB",
                                                "dC", "dD", "dz", "ddelta_bias", "workspace")],
                      args["workspace_bytes"], None)
+
+
+def _fwd_h0(desc, h0, last_state):
+    return ss.ss_fwd_h0(desc, P, P, P, P, P, None, None, None, h0, P, last_state, None, 0, None)
+
+
+def _bwd_h0(desc, h0, dh0):
+    return ss.ss_bwd_h0(desc, P, P, P, P, P, None, None, None, h0, P, P, P, P, P, P, None, None,
+                        None, dh0, P, 1 << 40, None)
+
+
+def test_h0_rules():
+    d = _desc()                                   # B=2, D=96, N=16: a state is 12 KiB in f32
+    q = ctypes.c_void_p(0x7F0000100000)
+    # h0 and dh0 come together
+    assert _bwd_h0(d, P, None) == ss.SS_ERR_INVALID_PROBLEM
+    assert "h0 and dh0" in ss.ss_last_error()
+    assert _bwd_h0(d, None, P) == ss.SS_ERR_INVALID_PROBLEM
+    # alignment to the parameter element size
+    odd = ctypes.c_void_p(0x7F0000000002)
+    assert _fwd_h0(d, odd, None) == ss.SS_ERR_INVALID_PROBLEM
+    assert "h0" in ss.ss_last_error()
+    # last_state may be h0 itself, never a partial overlap
+    assert _fwd_h0(d, P, ctypes.c_void_p(0x7F0000000000 + 256)) == ss.SS_ERR_INVALID_PROBLEM
+    assert "overlap" in ss.ss_last_error()
+    assert _bwd_h0(d, P, ctypes.c_void_p(0x7F0000000000 + 4)) == ss.SS_ERR_INVALID_PROBLEM
+    assert "overlap" in ss.ss_last_error()
+    # disjoint buffers pass validation up to the workspace check
+    ws = ss.ss_workspace_size(d, 0)
+    if ws > 0:
+        assert _fwd_h0(d, P, q) == ss.SS_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_status_strings():

@@ -305,3 +305,122 @@ def test_autograd_function():
     g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"])
     for k, gk in zip(KEYS, GRADS):
         assert torch.equal(leaves[k].grad, g[gk]), k
+
+
+# ------------------------------------------------------------- initial state
+
+def _state(inp, seed, scale=1.0):
+    """A seeded initial state [B, D, N] in the parameter dtype."""
+    Bn, L, D = inp["u"].shape
+    N = inp["A"].shape[1]
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(Bn, D, N, generator=g, dtype=torch.float64) * scale).to(inp["A"].dtype)
+
+
+H0_SHAPES = [((2, 150, 72, 16), "f32"), ((2, 100, 65, 16), "f32"), ((1, 60, 20, 64), "f32"),
+             ((1, 40, 9, 130), "f32"), ((2, 90, 72, 8), "bf16"), ((2, 70, 40, 32), "f16"),
+             ((1, 1, 33, 16), "f32")]
+
+
+@pytest.mark.parametrize("shape,io", H0_SHAPES, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_fwd_h0(shape, io):
+    inp = random_inputs(*shape, seed=1200 + sum(shape), io_dtype=io)
+    h0 = _state(inp, 1300 + shape[2])
+    d = to_dev(inp)
+    for chunk in (0, 24):
+        say("fwd h0", shape, io, "chunk", chunk)
+        y, ls = ss.fwd(*[d[k] for k in KEYS], return_last_state=True, chunk_len=chunk,
+                       h0=h0.to(DEV))
+        torch.cuda.synchronize()
+        yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+        tol = TOL[inp["u"].dtype]
+        assert rel_err(to_np(y), yr) <= tol, f"y chunk {chunk}"
+        assert rel_err(to_np(ls), lsr) <= max(tol, TOL[inp["A"].dtype]), f"state chunk {chunk}"
+
+
+def test_fwd_h0_split_sequence_and_empty():
+    inp = random_inputs(2, 300, 96, 16, seed=1401)
+    h0 = _state(inp, 1402).to(DEV)
+    d = to_dev(inp)
+    args = [d[k] for k in KEYS]
+    y, ls = ss.fwd(*args, return_last_state=True, h0=h0)
+    cut = lambda t, a, b: t[:, a:b].contiguous() if t is not None and t.dim() == 3 else t
+    first = [cut(t, 0, 113) for t in args]
+    second = [cut(t, 113, 300) for t in args]
+    y1, l1 = ss.fwd(*first, return_last_state=True, h0=h0)
+    y2, l2 = ss.fwd(*second, return_last_state=True, h0=l1)
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0.cpu())
+    assert rel_err(to_np(torch.cat([y1, y2], 1)), yr) <= 1e-5
+    assert rel_err(to_np(l2), lsr) <= 1e-5
+    assert rel_err(to_np(y), yr) <= 1e-5
+    # L = 0: the final state is h0; in place it stays h0
+    e = [cut(t, 0, 0) for t in args]
+    _, le = ss.fwd(*e, return_last_state=True, h0=h0)
+    st = h0.clone()
+    ss.fwd(*e, h0=st, last_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(le, h0) and torch.equal(st, h0)
+
+
+@pytest.mark.parametrize("io,D", [("f32", 64), ("bf16", 72), ("f32", 33)])
+def test_decode_step_in_place(io, D):
+    """L steps of decode_step on one state equal one call over the sequence."""
+    inp = random_inputs(3, 24, D, 16, seed=1500 + D, io_dtype=io)
+    h0 = _state(inp, 1501)
+    d = to_dev(inp)
+    state = h0.to(DEV).clone()
+    ys = []
+    for t in range(24):
+        sl = lambda k: None if d[k] is None else d[k][:, t].contiguous()
+        ys.append(ss.decode_step(state, sl("u"), sl("delta"), d["A"], sl("B"), sl("C"), d["D"],
+                                 sl("z"), d["delta_bias"]))
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+    tol = TOL[inp["u"].dtype]
+    assert rel_err(to_np(torch.stack(ys, 1)), yr) <= tol
+    assert rel_err(to_np(state), lsr) <= max(tol, 1e-5)
+
+
+BWD_H0_SHAPES = [((2, 150, 72, 16), "f32"), ((2, 300, 257, 16), "f32"), ((1, 47, 20, 17), "f32"),
+                 ((1, 33, 10, 64), "f32"), ((2, 90, 70, 16), "bf16"), ((1, 1, 9, 16), "f32")]
+
+
+@pytest.mark.parametrize("shape,io", BWD_H0_SHAPES, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_bwd_h0(shape, io):
+    inp = random_inputs(*shape, seed=1600 + sum(shape), io_dtype=io, backward=True)
+    h0 = _state(inp, 1700 + shape[2])
+    d = to_dev(inp)
+    r = oracle.bwd(**{k: inp[k] for k in KEYS}, dy=inp["dy"], h0=h0)
+    tol = TOL[inp["u"].dtype]
+    for chunk in (0, 24):
+        say("bwd h0", shape, io, "chunk", chunk)
+        g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"], chunk_len=chunk, h0=h0.to(DEV))
+        torch.cuda.synchronize()
+        for k in GRADS + ("dh0",):
+            if r[k] is None:
+                assert g[k] is None
+                continue
+            e = rel_err(to_np(g[k]), r[k])
+            assert e <= tol, f"{k} chunk {chunk}: {e:.3e}"
+
+
+def test_bwd_h0_empty_and_autograd():
+    inp = random_inputs(2, 1, 20, 4, seed=1801, backward=True)
+    h0 = _state(inp, 1802).to(DEV)
+    for k in ("u", "delta", "z", "B", "C", "dy"):
+        inp[k] = inp[k][:, :0].contiguous()
+    d = to_dev(inp)
+    g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"], h0=h0)
+    torch.cuda.synchronize()
+    assert torch.all(g["dh0"] == 0)
+    inp = random_inputs(2, 40, 24, 16, seed=1803, backward=True)
+    d = to_dev(inp)
+    h0 = _state(inp, 1804).to(DEV).requires_grad_(True)
+    leaves = {k: (None if d[k] is None else d[k].clone().requires_grad_(True)) for k in KEYS}
+    y = ss.selective_scan(*[leaves[k] for k in KEYS], h0=h0)
+    (y * d["dy"]).sum().backward()
+    g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"], h0=h0.detach())
+    torch.cuda.synchronize()
+    assert torch.equal(h0.grad, g["dh0"])
+    assert torch.equal(leaves["A"].grad, g["dA"])
