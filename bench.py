@@ -178,6 +178,7 @@ def main():
                     help="approximate CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a plain 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
@@ -274,6 +275,37 @@ def main():
         }
         log(f"backward {bms * 1e3:.1f} us/call")
         del wsb, db
+
+    if not args.no_decode:
+        # One recurrence step on a carried state, updated in place (ss_fwd_h0
+        # with L = 1 and last_state == h0), for the 2.8B-shaped layer: the
+        # first step of the forward inputs, a seeded N(0, 1) f32 state.
+        B8, D8, N8 = w.batch, w.dim, w.dstate
+        step_args = [None if t is None else (t[:, :1].contiguous() if t.dim() == 3 else t)
+                     for t in args_f]
+        gen = torch.Generator().manual_seed(2024)
+        state = torch.randn(B8, D8, N8, generator=gen).cuda()
+        ys = torch.empty((B8, 1, D8), dtype=dev["u"].dtype, device="cuda")
+
+        def dstep():
+            ss.fwd(*step_args, y=ys, h0=state, last_state=state)
+
+        dsteps = 200
+        log(f"timing decode step: {dsteps} steps")
+        dms, _ = time_calls(dstep, dsteps, 20)
+        io2 = 2 if w.io_dtype != "f32" else 4
+        dbytes = (2 * B8 * D8 * N8 * 4 + 4 * B8 * D8 * io2 + 2 * B8 * N8 * io2 + D8 * N8 * 4
+                  + 2 * D8 * 4)
+        result["decode"] = {
+            "workload": "one step of the 2.8B-shaped layer on a carried state: B=8, D=5120, "
+                        "N=16, bf16 u/delta/z/y/B/C, f32 A/D/delta_bias/state, in place",
+            "us_per_step": dms * 1e3, "tokens_per_s": B8 / (dms * 1e-3),
+            "state_updates_per_s": B8 * D8 * N8 / (dms * 1e-3),
+            "algorithmic_bytes": dbytes, "hbm_gbs": dbytes / (dms * 1e-3) / 1e9,
+            "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        }
+        log(f"decode {dms * 1e3:.2f} us/step")
+        del state
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

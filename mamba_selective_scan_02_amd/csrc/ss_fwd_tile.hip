@@ -218,10 +218,11 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
   load_own(2, pu1, pd1, pz1);
   xch[0][cl][g] = make_float2(cur.dl, cur.xu);
 
-  // The time loop runs whole 64-step stages (8 tiles, unrolled, so that every
-  // LDS offset is an immediate and the prefetch registers rotate by
-  // renaming).  Tiles past the chunk's end are identity steps (dt = 0) whose
-  // stores fall outside the buffer range and are dropped.
+  // The time loop runs 64-step stages (8 tiles, unrolled, so that every LDS
+  // offset is an immediate and the prefetch registers rotate by renaming).
+  // The last stage stops after the chunk's last tile; inside that tile, steps
+  // past the chunk are identity steps (dt = 0) whose stores fall outside the
+  // buffer range and are dropped.
   const int nstage = (int)((nsteps + TB - 1) / TB);
   for (int st = 0; st < nstage; ++st) {
     const int buf = st & 1;
@@ -232,6 +233,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
     constexpr int kUnroll = MODE == TMODE_FULL ? TB / GL : 1;
 #pragma unroll kUnroll
     for (int pt = 0; pt < TB / GL; ++pt) {
+      if (pt * GL >= (int)nsteps - st * TB) break;   // tiles past the chunk (uniform)
       const int p = st * (TB / GL) + pt;
       float2 ex[GL];
 #pragma unroll
@@ -482,6 +484,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
     constexpr int kUnroll = FULL ? NTILE : 1;
 #pragma unroll kUnroll
     for (int pt = 0; pt < NTILE; ++pt) {
+      if (pt * GL >= (int)nsteps - st * TB) break;   // tiles past the chunk (uniform)
       const int row = pt * GL + g;                    // this lane's own step in the stage
       const uint8_t* own = &sIn[0][row * RS + lds_own_col];
       const float uu = lds_elem<T>(own);

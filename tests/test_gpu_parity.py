@@ -424,3 +424,19 @@ def test_bwd_h0_empty_and_autograd():
     torch.cuda.synchronize()
     assert torch.equal(h0.grad, g["dh0"])
     assert torch.equal(leaves["A"].grad, g["dA"])
+
+
+def test_decode_step_2p8b_layer():
+    """One in-place step at the 2.8B-shaped layer size (every channel)."""
+    w = WORKLOADS["m2p8b"]
+    full = make_inputs(w)
+    inp = {k: (None if v is None else (v[:, :1].contiguous() if v.dim() == 3 else v))
+           for k, v in full.items()}
+    h0 = _state(inp, 1901)
+    d = to_dev(inp)
+    state = h0.to(DEV).clone()
+    y, _ = ss.fwd(*[d[k] for k in KEYS], h0=state, last_state=state)
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+    assert rel_err(to_np(y), yr) <= TOL[inp["u"].dtype]
+    assert rel_err(to_np(state), lsr) <= 1e-5
