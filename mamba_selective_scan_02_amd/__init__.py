@@ -224,11 +224,12 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool
     if ls is None and return_last_state:
         ls = torch.empty((Bn, Dd, N), dtype=pa, device=dev)
     need = workspace_size(desc, False)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     st = ss_fwd_h0(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                    _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls), _ptr(workspace),
-                   workspace.numel(), _stream_of(dev))
+                   ws_bytes, _stream_of(dev))
     if st != SS_OK:
         _raise(st, "ss_fwd_h0" if h0 is not None else "ss_fwd")
     return y, ls

@@ -302,7 +302,143 @@ static hipError_t launch_fwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s)
   return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------- short sequences
+//
+// L <= 16 (decode steps), N <= 32: 4 lanes per channel, lane g holds states
+// g*NS .. g*NS+NS-1; every lane prepares its channel's step itself (cheap at
+// this length), the readout is a 2-step DPP sum over the channel's lanes.  A
+// 256-lane workgroup covers 64 channels of one batch row; no LDS, no chunks.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xf, 0xf, true));
+}
+
+// NS consecutive f32 values at p + off as 16-byte loads / stores (VEC: the
+// caller checked 16-byte alignment and N == 4 * NS), else element by element
+// in the parameter dtype with states n >= N read as 0 / not written.
+template <int NS, bool VEC>
+__device__ __forceinline__ void row_ld(const void* p, int64_t off, int n0, int64_t N, int dtype,
+                                       float* out) {
+  if constexpr (VEC && NS % 4 == 0) {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + off);
+#pragma unroll
+    for (int j = 0; j < NS / 4; ++j) {
+      const float4 v = q[j];
+      out[4 * j] = v.x; out[4 * j + 1] = v.y; out[4 * j + 2] = v.z; out[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) out[k] = n0 + k < N ? ld_param(p, off + k, dtype) : 0.0f;
+  }
+}
+template <int NS, bool VEC>
+__device__ __forceinline__ void row_st(void* p, int64_t off, int n0, int64_t N, int dtype,
+                                       const float* v) {
+  if constexpr (VEC && NS % 4 == 0) {
+    float4* q = reinterpret_cast<float4*>(static_cast<float*>(p) + off);
+#pragma unroll
+    for (int j = 0; j < NS / 4; ++j) q[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+      if (n0 + k < N) st_param(p, off + k, dtype, v[k]);
+  }
+}
+
+template <typename T, int NS, bool HAS_Z, bool VEC>
+__global__ __launch_bounds__(kBlock) void fwd_short(const T* __restrict__ u_in,
+                                                    const T* __restrict__ delta_in,
+                                                    const T* __restrict__ B_in,
+                                                    const T* __restrict__ C_in,
+                                                    const T* __restrict__ z_in,
+                                                    T* __restrict__ y_out, const FwdArgs a) {
+  constexpr int G = 4, CPB = kBlock / G;
+  const int g = threadIdx.x % G;
+  const int64_t nbd = (a.D + CPB - 1) / CPB;
+  const int64_t db = blockIdx.x % nbd, b = blockIdx.x / nbd;
+  const int64_t d_raw = db * CPB + threadIdx.x / G;
+  const bool active = d_raw < a.D;
+  const int64_t d = active ? d_raw : a.D - 1;
+  const int64_t L = a.L, D = a.D, N = a.N;
+  const int n0 = g * NS;
+  float A2[NS], h[NS];
+  row_ld<NS, VEC>(a.A, d * N + n0, n0, N, a.param_dtype, A2);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    A2[i] *= kLog2e;
+    h[i] = 0.0f;
+  }
+  if (a.h0) row_ld<NS, VEC>(a.h0, (b * D + d) * N + n0, n0, N, a.param_dtype, h);
+  const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
+  const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
+  for (int64_t t = 0; t < L; ++t) {
+    const int64_t i = (b * L + t) * D + d;
+    const float uu = ld(u_in, i);
+    const float x = ld(delta_in, i) + bv;
+    const float dl = a.softplus ? softplus(x) : x;
+    const float xu = dl * uu;
+    const T* Bt = B_in + (b * L + t) * N;
+    const T* Ct = C_in + (b * L + t) * N;
+    float o = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int n = n0 + k;
+      const bool ok = n < N;
+      const float bb = ok ? ld(Bt, n) : 0.0f, cc = ok ? ld(Ct, n) : 0.0f;
+      h[k] = __builtin_fmaf(fast_exp2(dl * A2[k]), h[k], xu * bb);
+      o = __builtin_fmaf(cc, h[k], o);
+    }
+    o += dpp_f<0xB1>(o);   // quad_perm [1,0,3,2]
+    o += dpp_f<0x4E>(o);   // quad_perm [2,3,0,1]: every lane of the quad has the sum
+    float yv = __builtin_fmaf(Dv, uu, o);
+    if (HAS_Z) {
+      const float zz = ld(z_in, i);
+      yv *= zz * sigmoid(zz);
+    }
+    if (active && g == 0) y_out[i] = from_f32<T>(yv);
+  }
+  if (active && a.last_state) row_st<NS, VEC>(a.last_state, (b * D + d) * N + n0, n0, N,
+                                               a.param_dtype, h);
+}
+
+template <typename T, bool HAS_Z, bool VEC>
+static hipError_t launch_short_z(const FwdArgs& a, int ns, hipStream_t s) {
+  const T* U = static_cast<const T*>(a.u);
+  const T* DL = static_cast<const T*>(a.delta);
+  const T* Bm = static_cast<const T*>(a.B);
+  const T* Cm = static_cast<const T*>(a.C);
+  const T* Z = static_cast<const T*>(a.z);
+  T* Y = static_cast<T*>(a.y);
+  const dim3 grid((unsigned)(a.Bn * ((a.D + kBlock / 4 - 1) / (kBlock / 4))));
+  switch (ns) {
+    case 1: fwd_short<T, 1, HAS_Z, VEC><<<grid, dim3(kBlock), 0, s>>>(U, DL, Bm, Cm, Z, Y, a); break;
+    case 2: fwd_short<T, 2, HAS_Z, VEC><<<grid, dim3(kBlock), 0, s>>>(U, DL, Bm, Cm, Z, Y, a); break;
+    case 4: fwd_short<T, 4, HAS_Z, VEC><<<grid, dim3(kBlock), 0, s>>>(U, DL, Bm, Cm, Z, Y, a); break;
+    case 8: fwd_short<T, 8, HAS_Z, VEC><<<grid, dim3(kBlock), 0, s>>>(U, DL, Bm, Cm, Z, Y, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_short(const FwdArgs& a, int ns, hipStream_t s) {
+  auto al = [](const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = a.param_dtype == 0 && (ns == 4 || ns == 8) && a.N == 4 * ns && al(a.A) &&
+                   al(a.h0) && al(a.last_state);
+  if (vec) return a.z ? launch_short_z<T, true, true>(a, ns, s) : launch_short_z<T, false, true>(a, ns, s);
+  return a.z ? launch_short_z<T, true, false>(a, ns, s) : launch_short_z<T, false, false>(a, ns, s);
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_t s) {
+  if (gl == 4 && ns <= 8) {                     // short sequences (single chunk)
+    switch (io_dtype) {
+      case 0: return launch_short<float>(a, ns, s);
+      case 1: return launch_short<f16_t>(a, ns, s);
+      case 2: return launch_short<bf16_t>(a, ns, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (gl == 8) return launch_fwd_tile(a, io_dtype, ns, s);
   switch (io_dtype) {
     case 0: return launch_fwd_ty<float>(a, ns, gl, s);

@@ -51,10 +51,21 @@ inline void pick_bucket(int64_t N, int* NS, int* G) {
   else { *NS = 64; *G = 4; }
 }
 
+// Forward sequences of at most this many steps (decode steps) with N <= 32
+// run the short-sequence kernel: 4 lanes per channel, NS = N/4 (rounded up
+// to 1, 2, 4 or 8) states each, no staging (the tile kernel's 64-step stages
+// would be mostly empty).
+constexpr int64_t kShortSeq = 16;
+
 inline Plan make_plan(const ss_desc& d, bool backward) {
   Plan p;
   const int64_t Bn = d.batch, L = d.seqlen, D = d.dim, N = d.dstate;
   pick_bucket(N, &p.NS, &p.G);
+  const bool short_seq = !backward && L <= kShortSeq && N <= 32;
+  if (short_seq) {
+    p.NS = N <= 4 ? 1 : N <= 8 ? 2 : N <= 16 ? 4 : 8;
+    p.G = 4;
+  }
   if (Bn * L * D == 0) {
     p.chunk_len = L;
     p.K = 1;
@@ -87,6 +98,7 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
     // a chunk's rows of one [B, L, D] tensor must fit a 32-bit buffer range
     const int64_t lc_cap = (int64_t)0x7fffffff / ((D > 0 ? D : 1) * 4) - GL_MAX_TILE;
     if (lc > lc_cap) lc = lc_cap > 8 ? lc_cap & ~int64_t(7) : 8;
+    if (short_seq) lc = L;   // one kernel over the whole sequence (64-bit addressing)
     p.chunk_len = lc;
     p.K = (L + lc - 1) / lc;
     size_t off = 0;

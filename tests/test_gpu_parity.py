@@ -440,3 +440,20 @@ def test_decode_step_2p8b_layer():
     yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
     assert rel_err(to_np(y), yr) <= TOL[inp["u"].dtype]
     assert rel_err(to_np(state), lsr) <= 1e-5
+
+
+@pytest.mark.parametrize("L", [1, 2, 7, 16])
+@pytest.mark.parametrize("N,io", [(4, "f32"), (16, "f32"), (16, "bf16"), (32, "f16"), (9, "bf16")])
+def test_fwd_short_sequences(L, N, io):
+    """Sequences of at most 16 steps run one lane per channel (decode steps)."""
+    inp = random_inputs(3, L, 300, N, seed=2000 + 37 * L + N, io_dtype=io)
+    for with_h0 in (False, True):
+        h0 = _state(inp, 2100 + L) if with_h0 else None
+        d = to_dev(inp)
+        y, ls = ss.fwd(*[d[k] for k in KEYS], return_last_state=True,
+                       h0=None if h0 is None else h0.to(DEV))
+        torch.cuda.synchronize()
+        yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+        tol = TOL[inp["u"].dtype]
+        assert rel_err(to_np(y), yr) <= tol
+        assert rel_err(to_np(ls), lsr) <= max(tol, TOL[inp["A"].dtype])
