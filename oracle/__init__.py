@@ -31,6 +31,10 @@ forward pipeline of the mamba-rs page "mamba_ssm/gpu/backward.rs" carries from
 one call to the next; its gradient dh0 = dL/dh_{-1} is what the reverse sweep
 carries past t = 0.
 
+Packed variable-length sequences (``fwd_varlen`` / ``bwd_varlen``; the scan
+page leaves cu_seqlens out of its scope, "Trailblazer scope") are read the
+usual way: each sequence is an independent scan of its rows.
+
 Inputs are decoded to float64 from whatever dtype they are stored in, so the
 oracle reads exactly the values the GPU reads.
 """
@@ -216,6 +220,72 @@ def bwd_f32(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None, delta_s
             nthreads=None, h0=None) -> Dict[str, Optional[np.ndarray]]:
     return _bwd(u, delta, A, B, C, D, z, delta_bias, dy, delta_softplus, nthreads, np.float32,
                 h0)
+
+
+# --------------------------------------------------------------------------
+# Packed variable-length sequences: each sequence is its own scan.
+# --------------------------------------------------------------------------
+
+def _segments(cu_seqlens):
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    assert cu.ndim == 1 and cu[0] == 0 and np.all(np.diff(cu) >= 0)
+    return [(int(cu[i]), int(cu[i + 1])) for i in range(cu.size - 1)]
+
+
+def _seg(x, a, b):
+    """Rows a..b of a packed [T, C] tensor as a [1, b - a, C] batch."""
+    return None if x is None else _arr(x, np.float64)[a:b][None]
+
+
+def fwd_varlen(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+               cu_seqlens=(0,), h0=None, nthreads=None):
+    """Forward over packed sequences: u, delta, z [T, D]; B, C [T, N];
+    sequence s is rows cu_seqlens[s] .. cu_seqlens[s+1] - 1, scanned from
+    h0[s] (or 0).  Returns (y [T, D], last_state [S, D, N])."""
+    segs = _segments(cu_seqlens)
+    Dd, N = _arr(A, np.float64).shape
+    y = np.zeros(_arr(u, np.float64).shape)
+    ls = np.zeros((len(segs), Dd, N))
+    h0a = _arr(h0, np.float64)
+    for s, (a, b) in enumerate(segs):
+        ys, lss = fwd(_seg(u, a, b), _seg(delta, a, b), A, _seg(B, a, b), _seg(C, a, b), D,
+                      _seg(z, a, b), delta_bias, delta_softplus, return_last_state=True,
+                      nthreads=nthreads, h0=None if h0a is None else h0a[s:s + 1])
+        y[a:b] = ys[0]
+        ls[s] = lss[0]
+    return y, ls
+
+
+def bwd_varlen(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None,
+               delta_softplus=True, cu_seqlens=(0,), h0=None, nthreads=None):
+    """Backward of ``fwd_varlen`` for the loss sum(dy * y): per-row gradients
+    in the packed layout, parameter gradients summed over the sequences in
+    sequence order, dh0 [S, D, N] when h0 is given."""
+    segs = _segments(cu_seqlens)
+    Dd, N = _arr(A, np.float64).shape
+    T = _arr(u, np.float64).shape[0]
+    h0a = _arr(h0, np.float64)
+    out = {"du": np.zeros((T, Dd)), "ddelta": np.zeros((T, Dd)), "dA": np.zeros((Dd, N)),
+           "dB": np.zeros((T, N)), "dC": np.zeros((T, N)),
+           "dD": np.zeros(Dd) if D is not None else None,
+           "dz": np.zeros((T, Dd)) if z is not None else None,
+           "ddelta_bias": np.zeros(Dd) if delta_bias is not None else None,
+           "dh0": np.zeros((len(segs), Dd, N)) if h0a is not None else None}
+    for s, (a, b) in enumerate(segs):
+        if b == a:
+            continue
+        g = bwd(_seg(u, a, b), _seg(delta, a, b), A, _seg(B, a, b), _seg(C, a, b), D,
+                _seg(z, a, b), delta_bias, _seg(dy, a, b), delta_softplus, nthreads=nthreads,
+                h0=None if h0a is None else h0a[s:s + 1])
+        for k in ("du", "ddelta", "dB", "dC", "dz"):
+            if out[k] is not None:
+                out[k][a:b] = g[k][0]
+        for k in ("dA", "dD", "ddelta_bias"):
+            if out[k] is not None:
+                out[k] += g[k]
+        if h0a is not None:
+            out["dh0"][s] = g["dh0"][0]
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -476,6 +476,45 @@ def test_h0_zero_is_no_h0():
             assert np.array_equal(g0[k], g1[k]), k
 
 
+# ------------------------------------------------------- packed sequences
+
+def test_varlen_equal_lengths_match_the_dense_batch():
+    a = _rand(341, Bn=3, L=11, D=4, N=5)
+    h0 = _h0(a, 342)
+    dy = np.random.default_rng(343).normal(size=a["u"].shape)
+    pack = lambda x: None if x is None else (x.reshape(-1, x.shape[-1]) if x.ndim == 3 else x)
+    p = {k: pack(v) for k, v in a.items()}
+    cu = [0, 11, 22, 33]
+    y, ls = oracle.fwd(**a, return_last_state=True, h0=h0)
+    yv, lsv = oracle.fwd_varlen(**p, cu_seqlens=cu, h0=h0)
+    np.testing.assert_allclose(yv, y.reshape(33, 4), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lsv, ls, rtol=1e-14, atol=1e-15)
+    g = oracle.bwd(**a, dy=dy, h0=h0)
+    gv = oracle.bwd_varlen(**p, dy=dy.reshape(33, 4), cu_seqlens=cu, h0=h0)
+    for k in ("du", "ddelta", "dB", "dC", "dz"):
+        np.testing.assert_allclose(gv[k], g[k].reshape(33, -1), rtol=1e-13, atol=1e-14, err_msg=k)
+    for k in ("dA", "dD", "ddelta_bias", "dh0"):
+        np.testing.assert_allclose(gv[k], g[k], rtol=1e-12, atol=1e-13, err_msg=k)
+
+
+def test_varlen_sequences_are_independent():
+    """Changing one sequence's rows leaves every other sequence's outputs alone,
+    and an empty sequence returns its initial state."""
+    rng = np.random.default_rng(351)
+    a = _rand(352, Bn=1, L=20, D=3, N=4)
+    p = {k: (None if v is None else (v[0] if v.ndim == 3 else v)) for k, v in a.items()}
+    cu = [0, 6, 6, 13, 20]
+    h0 = rng.normal(size=(4, 3, 4))
+    y, ls = oracle.fwd_varlen(**p, cu_seqlens=cu, h0=h0)
+    q = {**p, "u": p["u"].copy()}
+    q["u"][6:13] += 1.0
+    y2, ls2 = oracle.fwd_varlen(**q, cu_seqlens=cu, h0=h0)
+    assert np.array_equal(y[:6], y2[:6]) and np.array_equal(y[13:], y2[13:])
+    assert not np.allclose(y[6:13], y2[6:13])
+    assert np.array_equal(ls[[0, 1, 3]], ls2[[0, 1, 3]])
+    np.testing.assert_array_equal(ls[1], h0[1])
+
+
 def test_f32_floor_is_close():
     """The float build of the same loop stays near the double one (diagnostic)."""
     a = _rand(99, Bn=2, L=256, D=8, N=16)
