@@ -124,6 +124,25 @@ int ss_bwd_h0(const ss_desc* desc, const void* u, const void* delta, const void*
               void* dA, void* dB, void* dC, void* dD, void* dz, void* ddelta_bias, void* dh0,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward over packed variable-length sequences.  The scan page leaves
+ * variable-length sequences (cu_seqlens) out of its scope (module docs,
+ * "Trailblazer scope"); this is the usual packed layout.  desc->batch is the
+ * number of sequences S and desc->seqlen an upper bound on every sequence's
+ * length; cu_seqlens is a DEVICE array of S + 1 int32 row offsets
+ * (cu_seqlens[0] = 0, non-decreasing, cu_seqlens[S] = total_len).  Sequence s
+ * occupies rows cu_seqlens[s] .. cu_seqlens[s+1] - 1 of u, delta, z, y
+ * ([total_len, D]) and of B, C ([total_len, N]); each sequence is scanned
+ * independently from h0[s] (or 0), and last_state[s] is its final state
+ * ([S, D, N]).  The offsets are read on the device and not validated there
+ * beyond clamping into [0, total_len] and lengths to desc->seqlen: rows no
+ * sequence covers are not written.  Workspace: ss_workspace_size(desc, 0)
+ * with the same desc.  Everything else as ss_fwd_h0. */
+int ss_fwd_varlen(const ss_desc* desc, const int32_t* cu_seqlens, int64_t total_len,
+                  const void* u, const void* delta, const void* A, const void* B, const void* C,
+                  const void* Dskip, const void* z, const void* delta_bias, const void* h0,
+                  void* y, void* last_state, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 /* The schedule the library would use for a descriptor (informational). */
 typedef struct ss_plan {
   int32_t chunk_len;          /* time steps per chunk */

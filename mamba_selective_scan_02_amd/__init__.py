@@ -7,9 +7,10 @@ on the tensors' device and passes raw pointers plus the current HIP stream.
 If the library is missing, every call raises: there is no fallback.
 
 Raw C entry points with the header's names: ``ss_workspace_size``,
-``ss_fwd``, ``ss_bwd``, ``ss_fwd_h0``, ``ss_bwd_h0``, ``ss_plan_query``,
-``ss_status_string``, ``ss_last_error``.  Tensor-level helpers: ``fwd``,
-``bwd`` (both with an optional initial state ``h0``), ``decode_step`` and the
+``ss_fwd``, ``ss_bwd``, ``ss_fwd_h0``, ``ss_bwd_h0``, ``ss_fwd_varlen``,
+``ss_plan_query``, ``ss_status_string``, ``ss_last_error``.  Tensor-level
+helpers: ``fwd``, ``bwd`` (both with an optional initial state ``h0``),
+``fwd_varlen`` (packed variable-length sequences), ``decode_step`` and the
 autograd function ``selective_scan``.
 """
 from __future__ import annotations
@@ -20,8 +21,9 @@ from typing import Dict, Optional, Tuple
 
 import torch
 
-__all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "decode_step", "selective_scan", "plan",
-           "workspace_size", "ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0", "ss_bwd_h0",
+__all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "fwd_varlen", "decode_step", "selective_scan",
+           "plan", "workspace_size", "ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0",
+           "ss_bwd_h0", "ss_fwd_varlen",
            "ss_plan_query", "ss_status_string",
            "ss_last_error", "library_path", "load_library",
            "SS_OK", "SS_ERR_INVALID_PROBLEM", "SS_ERR_UNSUPPORTED",
@@ -76,6 +78,8 @@ def load_library(path: Optional[str] = None):
     lib.ss_fwd_h0.restype = ctypes.c_int
     lib.ss_bwd_h0.argtypes = [dp] + [vp] * 20 + [sz, vp]
     lib.ss_bwd_h0.restype = ctypes.c_int
+    lib.ss_fwd_varlen.argtypes = [dp, vp, ctypes.c_int64] + [vp] * 12 + [sz, vp]
+    lib.ss_fwd_varlen.restype = ctypes.c_int
     lib.ss_plan_query.argtypes = [dp, ctypes.c_int32, ctypes.POINTER(SsPlan)]
     lib.ss_plan_query.restype = ctypes.c_int
     lib.ss_status_string.argtypes = [ctypes.c_int]
@@ -120,6 +124,13 @@ def ss_bwd_h0(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, h0, dy, du,
     return load_library().ss_bwd_h0(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias, h0,
                                     dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
                                     workspace, workspace_bytes, stream)
+
+
+def ss_fwd_varlen(desc: SsDesc, cu_seqlens, total_len: int, u, delta, A, B, C, Dskip, z,
+                  delta_bias, h0, y, last_state, workspace, workspace_bytes: int, stream) -> int:
+    return load_library().ss_fwd_varlen(_ref(desc), cu_seqlens, int(total_len), u, delta, A, B,
+                                        C, Dskip, z, delta_bias, h0, y, last_state, workspace,
+                                        workspace_bytes, stream)
 
 
 def ss_plan_query(desc: SsDesc, backward: int, out: SsPlan) -> int:
@@ -232,6 +243,61 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool
                    ws_bytes, _stream_of(dev))
     if st != SS_OK:
         _raise(st, "ss_fwd_h0" if h0 is not None else "ss_fwd")
+    return y, ls
+
+
+def _varlen_desc(u, A, cu_seqlens, max_seqlen, delta_softplus, chunk_len) -> SsDesc:
+    if u.dim() != 2 or A.dim() != 2:
+        raise ValueError("packed u must be [T, D] and A [D, N]")
+    if u.dtype not in _DTYPE_ID or A.dtype not in _DTYPE_ID:
+        raise NotImplementedError("dtypes must be float32, float16 or bfloat16")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of S + 1 offsets")
+    if cu_seqlens.device != u.device or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous on the tensors' device")
+    return SsDesc(cu_seqlens.numel() - 1, int(max_seqlen), u.shape[1], A.shape[1],
+                  1 if delta_softplus else 0, _DTYPE_ID[u.dtype], _DTYPE_ID[A.dtype],
+                  int(chunk_len))
+
+
+def fwd_varlen(u, delta, A, B, C, cu_seqlens, max_seqlen: int, D=None, z=None,
+               delta_bias=None, delta_softplus: bool = True, h0=None,
+               return_last_state: bool = False, chunk_len: int = 0,
+               y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               last_state: Optional[torch.Tensor] = None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward over packed variable-length sequences.
+
+    u, delta, z: [T, D]; B, C: [T, N]; cu_seqlens: int32 [S + 1] row offsets
+    on the device; max_seqlen >= every sequence's length; h0 / last_state:
+    [S, D, N].  Returns (y [T, D], last_state or None).
+    """
+    desc = _varlen_desc(u, A, cu_seqlens, max_seqlen, delta_softplus, chunk_len)
+    dev, io, pa = u.device, u.dtype, A.dtype
+    S, Dd, N = desc.batch, desc.dim, desc.dstate
+    T = u.shape[0]
+    for t, name, shape, dt in ((u, "u", (T, Dd), io), (delta, "delta", (T, Dd), io),
+                               (A, "A", (Dd, N), pa), (B, "B", (T, N), io),
+                               (C, "C", (T, N), io), (D, "D", (Dd,), pa),
+                               (z, "z", (T, Dd), io), (delta_bias, "delta_bias", (Dd,), pa),
+                               (h0, "h0", (S, Dd, N), pa),
+                               (last_state, "last_state", (S, Dd, N), pa)):
+        _check(t, name, shape, dt, dev)
+    if y is None:
+        y = torch.empty((T, Dd), dtype=io, device=dev)
+    _check(y, "y", (T, Dd), io, dev)
+    ls = last_state
+    if ls is None and return_last_state:
+        ls = torch.empty((S, Dd, N), dtype=pa, device=dev)
+    need = workspace_size(desc, False)
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = ss_fwd_varlen(desc, _ptr(cu_seqlens), T, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                       _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls),
+                       _ptr(workspace), ws_bytes, _stream_of(dev))
+    if st != SS_OK:
+        _raise(st, "ss_fwd_varlen")
     return y, ls
 
 

@@ -126,15 +126,25 @@ int ss_fwd(const ss_desc* d, const void* u, const void* delta, const void* A, co
                    workspace, workspace_bytes, stream);
 }
 
-int ss_fwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,
-              const void* C, const void* Dskip, const void* z, const void* delta_bias,
-              const void* h0, void* y, void* last_state, void* workspace,
-              size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Forward of a dense problem (cu = NULL: B sequences of L steps) or of a packed
+// variable-length one (cu = cu_seqlens on the device, B sequences of at most
+// L steps in `total` rows).
+int fwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total,
+             const void* u, const void* delta, const void* A, const void* B, const void* C,
+             const void* Dskip, const void* z, const void* delta_bias, const void* h0, void* y,
+             void* last_state, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  const char* who = h0 ? "ss_fwd_h0" : "ss_fwd";
   int st = check_desc(d, who);
   if (st != SS_OK) return st;
   const int64_t Bn = d->batch, L = d->seqlen, D = d->dim, N = d->dstate;
+  if (cu && total < 0) return fail(SS_ERR_INVALID_PROBLEM, "%s: total_len must be >= 0", who);
+  if (cu && !aligned(cu, 4))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: cu_seqlens is not 4-byte aligned", who);
+  const int64_t rows = cu ? total : Bn * L;          // rows of the [rows, D] tensors
   const int64_t io = dtype_size(d->io_dtype), pa = dtype_size(d->param_dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   PtrCheck pc{who};
@@ -146,9 +156,9 @@ int ss_fwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A,
   if (h0 && last_state && !in_place && overlap(h0, last_state, state_bytes))
     return fail(SS_ERR_INVALID_PROBLEM, "%s: h0 and last_state must be the same buffer or "
                 "not overlap", who);
-  if (Bn * L * D == 0) {
+  if (rows * D == 0 || Bn == 0) {
     // Nothing to scan.  An empty sequence leaves the initial state (h0 or 0).
-    if (L == 0 && last_state && state_bytes > 0)
+    if (rows == 0 && last_state && state_bytes > 0)
       return hip_status(h0 ? ss::launch_copy_param(last_state, h0, Bn * D * N, d->param_dtype, s)
                            : ss::launch_zero_param(last_state, Bn * D * N, d->param_dtype, s),
                         who);
@@ -186,9 +196,35 @@ int ss_fwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A,
   a.chunk_state = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_state) : nullptr;
   a.Bn = Bn; a.L = L; a.D = D; a.N = N;
   a.chunk_len = p.chunk_len; a.K = p.K;
+  a.cu = cu; a.Lt = rows;
   a.softplus = d->delta_softplus;
   a.param_dtype = d->param_dtype;
   return hip_status(ss::launch_fwd(a, d->io_dtype, p.NS, p.G, s), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss_fwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,
+              const void* C, const void* Dskip, const void* z, const void* delta_bias,
+              const void* h0, void* y, void* last_state, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return fwd_impl(h0 ? "ss_fwd_h0" : "ss_fwd", d, nullptr, 0, u, delta, A, B, C, Dskip, z,
+                  delta_bias, h0, y, last_state, workspace, workspace_bytes, stream);
+}
+
+int ss_fwd_varlen(const ss_desc* d, const int32_t* cu_seqlens, int64_t total_len,
+                  const void* u, const void* delta, const void* A, const void* B, const void* C,
+                  const void* Dskip, const void* z, const void* delta_bias, const void* h0,
+                  void* y, void* last_state, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!cu_seqlens) {
+    g_err[0] = 0;
+    return fail(SS_ERR_INVALID_PROBLEM, "ss_fwd_varlen: cu_seqlens is NULL");
+  }
+  return fwd_impl("ss_fwd_varlen", d, cu_seqlens, total_len, u, delta, A, B, C, Dskip, z,
+                  delta_bias, h0, y, last_state, workspace, workspace_bytes, stream);
 }
 
 int ss_bwd(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,

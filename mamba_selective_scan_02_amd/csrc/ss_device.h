@@ -144,6 +144,25 @@ __device__ __forceinline__ int64_t xcd_pair_remap(int64_t x, int64_t total) {
   return (q * 16 + 16 <= total) ? q * 16 + 2 * (r & 7) + (r >> 3) : x;
 }
 
+// Rows of sequence b in the [rows, D] / [rows, N] tensors: dense problems
+// hold B sequences of L steps (rows b*L ..); packed variable-length problems
+// (cu = cu_seqlens, device, [B+1]) hold sequence b at rows cu[b] .. cu[b+1].
+// The bounds are clamped to [0, Lt] (Lt = total rows) and the length to L,
+// so that no entry of cu can send an access outside the tensors.
+struct SeqRows { int64_t start, len; };
+__device__ __forceinline__ SeqRows seq_rows(const int32_t* cu, int64_t b, int64_t L, int64_t Lt) {
+  if (!cu) return {b * L, L};
+  int64_t s = cu[b], e = cu[b + 1];
+  s = s < 0 ? 0 : (s > Lt ? Lt : s);
+  e = e < s ? s : (e > Lt ? Lt : e);
+  return {s, (e - s < L) ? e - s : L};
+}
+
+// Chunk of sequence length len that holds its last step (0 when len = 0).
+__device__ __forceinline__ int64_t last_chunk(int64_t len, int64_t chunk_len) {
+  return len > 0 ? (len - 1) / chunk_len : 0;
+}
+
 // Forward launch parameters.
 struct FwdArgs {
   const void* u;
@@ -161,6 +180,8 @@ struct FwdArgs {
   float* chunk_state;      // [Bn, K, N, D] chunk-end state from zero / carried-in state
   int64_t Bn, L, D, N;
   int64_t chunk_len, K;    // chunk length and number of chunks
+  const int32_t* cu;       // nullable: cu_seqlens [Bn+1] of a packed problem
+  int64_t Lt;              // rows of the [rows, D] tensors (Bn*L when dense)
   int softplus;
   int param_dtype;
 };
@@ -204,6 +225,8 @@ struct BwdArgs {
   float* part_db;
   int64_t Bn, L, D, N;
   int64_t chunk_len, K, KG, nwgd;
+  const int32_t* cu;       // nullable: cu_seqlens [Bn+1] of a packed problem
+  int64_t Lt;              // rows of the [rows, D] tensors (Bn*L when dense)
   int softplus;
   int param_dtype;
   int io_dtype;

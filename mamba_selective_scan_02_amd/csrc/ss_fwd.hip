@@ -66,9 +66,11 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
   const int64_t d_raw = db * CPB + cl;
   const bool active = d_raw < a.D;
   const int64_t d = active ? d_raw : a.D - 1;  // tail lanes compute on a valid channel
+  const int64_t D = a.D, N = a.N;
+  const SeqRows sr = seq_rows(a.cu, b, a.L, a.Lt);
   const int64_t t0 = k * a.chunk_len;
-  const int64_t t1 = (t0 + a.chunk_len < a.L) ? t0 + a.chunk_len : a.L;
-  const int64_t L = a.L, D = a.D, N = a.N;
+  int64_t t1 = (t0 + a.chunk_len < sr.len) ? t0 + a.chunk_len : sr.len;
+  if (t1 < t0) t1 = t0;                         // a chunk past a short sequence's end
   const int n0 = g * NS;
 
   float A2[NS], h[NS];
@@ -87,12 +89,12 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
   const bool sp = a.softplus != 0;
 
-  const T* up = u_in + b * L * D + d;
-  const T* dp = delta_in + b * L * D + d;
-  const T* zp = HAS_Z ? z_in + b * L * D + d : up;
-  T* yp = y_out + b * L * D + d;
-  const T* Bp = B_in + b * L * N + n0;
-  const T* Cp = C_in + b * L * N + n0;
+  const T* up = u_in + sr.start * D + d;
+  const T* dp = delta_in + sr.start * D + d;
+  const T* zp = HAS_Z ? z_in + sr.start * D + d : up;
+  T* yp = y_out + sr.start * D + d;
+  const T* Bp = B_in + sr.start * N + n0;
+  const T* Cp = C_in + sr.start * N + n0;
 
   // B / C rows, software-pipelined one step ahead (wave-uniform: SGPRs).
   // EXACT rows are prefetched as raw 32-bit words and converted at their use
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
     }
   };
   RowT Bc[RW], Cc[RW];
-  fetch_rows(t0, Bc, Cc);
+  if (t1 > t0) fetch_rows(t0, Bc, Cc);
 
   float dsum = 0.0f;
   auto step = [&](int64_t t, float uu, float dr, float zz) {
@@ -178,18 +180,20 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
       lz[j] = (MODE == MODE_FULL && HAS_Z) ? ld(zp, tt * D) : 0.0f;
     }
   };
-  load_group(t0, cu, cd, cz);
-  int64_t t = t0;
-  for (; t + U <= t1; t += U) {
-    float nu[U], nd[U], nz[U];
-    load_group(t + U, nu, nd, nz);
+  if (t1 > t0) {                                // (clamped indices need a step)
+    load_group(t0, cu, cd, cz);
+    int64_t t = t0;
+    for (; t + U <= t1; t += U) {
+      float nu[U], nd[U], nz[U];
+      load_group(t + U, nu, nd, nz);
 #pragma unroll
-    for (int j = 0; j < U; ++j) step(t + j, cu[j], cd[j], cz[j]);
+      for (int j = 0; j < U; ++j) step(t + j, cu[j], cd[j], cz[j]);
 #pragma unroll
-    for (int j = 0; j < U; ++j) { cu[j] = nu[j]; cd[j] = nd[j]; cz[j] = nz[j]; }
+      for (int j = 0; j < U; ++j) { cu[j] = nu[j]; cd[j] = nd[j]; cz[j] = nz[j]; }
+    }
+    for (int j = 0; j < U - 1; ++j)
+      if (t + j < t1) step(t + j, cu[j], cd[j], cz[j]);
   }
-  for (int j = 0; j < U - 1; ++j)
-    if (t + j < t1) step(t + j, cu[j], cd[j], cz[j]);
 
   if (!active) return;
   if (MODE == MODE_SUMMARY) {
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
     for (int i = 0; i < NS; ++i)
       if (EXACT || n0 + i < N) a.chunk_state[((b * a.K + k) * N + n0 + i) * D + d] = h[i];
     if (g == 0) a.chunk_dsum[(b * a.K + k) * D + d] = dsum;
-  } else if (a.last_state != nullptr && k == a.K - 1) {
+  } else if (a.last_state != nullptr && k == last_chunk(sr.len, a.chunk_len)) {
 #pragma unroll
     for (int i = 0; i < NS; ++i)
       if (EXACT || n0 + i < N) st_param(a.last_state, (b * D + d) * N + n0 + i, a.param_dtype, h[i]);
@@ -360,7 +364,9 @@ __global__ __launch_bounds__(kBlock) void fwd_short(const T* __restrict__ u_in,
   const int64_t d_raw = db * CPB + threadIdx.x / G;
   const bool active = d_raw < a.D;
   const int64_t d = active ? d_raw : a.D - 1;
-  const int64_t L = a.L, D = a.D, N = a.N;
+  const int64_t D = a.D, N = a.N;
+  const SeqRows sr = seq_rows(a.cu, b, a.L, a.Lt);
+  const int64_t L = sr.len;
   const int n0 = g * NS;
   float A2[NS], h[NS];
   row_ld<NS, VEC>(a.A, d * N + n0, n0, N, a.param_dtype, A2);
@@ -373,13 +379,13 @@ __global__ __launch_bounds__(kBlock) void fwd_short(const T* __restrict__ u_in,
   const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
   for (int64_t t = 0; t < L; ++t) {
-    const int64_t i = (b * L + t) * D + d;
+    const int64_t i = (sr.start + t) * D + d;
     const float uu = ld(u_in, i);
     const float x = ld(delta_in, i) + bv;
     const float dl = a.softplus ? softplus(x) : x;
     const float xu = dl * uu;
-    const T* Bt = B_in + (b * L + t) * N;
-    const T* Ct = C_in + (b * L + t) * N;
+    const T* Bt = B_in + (sr.start + t) * N;
+    const T* Ct = C_in + (sr.start + t) * N;
     float o = 0.0f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {

@@ -112,9 +112,11 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
   const int64_t d_raw = db * CPW + cl;
   const bool active = d_raw < a.D;
   const int64_t d = active ? d_raw : a.D - 1;   // tail lanes duplicate channel D-1
-  const int64_t L = a.L, D = a.D, N = a.N;
+  const int64_t D = a.D, N = a.N;
+  const SeqRows sr = seq_rows(a.cu, b, a.L, a.Lt);
   const int64_t t0 = k * a.chunk_len;
-  const int64_t t1 = (t0 + a.chunk_len < L) ? t0 + a.chunk_len : L;
+  int64_t t1 = (t0 + a.chunk_len < sr.len) ? t0 + a.chunk_len : sr.len;
+  if (t1 < t0) t1 = t0;                         // a chunk past a short sequence's end
   const int n0 = g * NS;
 
   float A2[NS], h[NS];
@@ -137,15 +139,15 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
   // voff_own + soff(p), steps past the chunk read 0 / are not stored.
   constexpr int ES = sizeof(T);
   const int64_t nsteps = t1 - t0;
-  const int64_t row0 = (b * L + t0) * D;
+  const int64_t row0 = (sr.start + t0) * D;
   const auto rs_u = make_rsrc(u_in + row0, nsteps * D * ES);
   const auto rs_d = make_rsrc(delta_in + row0, nsteps * D * ES);
   const auto rs_z = make_rsrc(HAS_Z ? z_in + row0 : u_in + row0, nsteps * D * ES);
   const auto rs_y = make_rsrc(y_out + row0, nsteps * D * ES);
   const int voff_own = (int)((g * D + d) * ES);
   const int soff_step = (int)(GL * D * ES);            // one 8-step tile
-  const auto rs_B = make_rsrc(B_in + (b * L + t0) * N, nsteps * N * ES);
-  const auto rs_C = make_rsrc(C_in + (b * L + t0) * N, nsteps * N * ES);
+  const auto rs_B = make_rsrc(B_in + (sr.start + t0) * N, nsteps * N * ES);
+  const auto rs_C = make_rsrc(C_in + (sr.start + t0) * N, nsteps * N * ES);
 
   // ---- B / C staging (whole workgroup) ----
   float rb[RB], rc[RB];
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
     for (int i = 0; i < NS; ++i)
       if (n0 + i < N) a.chunk_state[((b * a.K + k) * N + n0 + i) * D + d] = h[i];
     if (g == 0) a.chunk_dsum[(b * a.K + k) * D + d] = dsum;
-  } else if (a.last_state != nullptr && k == a.K - 1) {
+  } else if (a.last_state != nullptr && k == last_chunk(sr.len, a.chunk_len)) {
 #pragma unroll
     for (int i = 0; i < NS; ++i)
       if (n0 + i < N) st_param(a.last_state, (b * D + d) * N + n0 + i, a.param_dtype, h[i]);
@@ -381,9 +383,11 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   const int64_t d_raw = d0 + cl;
   const bool active = d_raw < a.D;
   const int64_t d = active ? d_raw : a.D - 1;
-  const int64_t L = a.L, D = a.D, N = a.N;
+  const int64_t D = a.D, N = a.N;
+  const SeqRows sr = seq_rows(a.cu, b, a.L, a.Lt);
   const int64_t t0 = k * a.chunk_len;
-  const int64_t t1 = (t0 + a.chunk_len < L) ? t0 + a.chunk_len : L;
+  int64_t t1 = (t0 + a.chunk_len < sr.len) ? t0 + a.chunk_len : sr.len;
+  if (t1 < t0) t1 = t0;                         // a chunk past a short sequence's end
   const int n0 = g * NS;
 
   float A2[NS], h[NS];
@@ -401,15 +405,15 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   const bool sp = a.softplus != 0;
 
   const int64_t nsteps = t1 - t0;
-  const int64_t row0 = (b * L + t0) * D;
+  const int64_t row0 = (sr.start + t0) * D;
   const int64_t rbytes = nsteps * D * ES;
   __amdgpu_buffer_rsrc_t rs_in[NT];
   rs_in[0] = make_rsrc(u_in + row0, rbytes);
   rs_in[1] = make_rsrc(delta_in + row0, rbytes);
   if constexpr (NT == 3) rs_in[2] = make_rsrc(z_in + row0, rbytes);
   const auto rs_y = make_rsrc(y_out + row0, FULL ? rbytes : 0);
-  const auto rs_B = make_rsrc(B_in + (b * L + t0) * N, nsteps * N * ES);
-  const auto rs_C = make_rsrc(C_in + (b * L + t0) * N, nsteps * N * ES);
+  const auto rs_B = make_rsrc(B_in + (sr.start + t0) * N, nsteps * N * ES);
+  const auto rs_C = make_rsrc(C_in + (sr.start + t0) * N, nsteps * N * ES);
 
   // this thread's 16-byte piece of every stage: row pr, piece pq of the block's row
   const int pr = tid / W::LPR, pq = tid % W::LPR;
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
     for (int i = 0; i < NS; ++i)
       if (n0 + i < N) a.chunk_state[((b * a.K + k) * N + n0 + i) * D + d] = h[i];
     if (g == 0) a.chunk_dsum[(b * a.K + k) * D + d] = dsum;
-  } else if (a.last_state != nullptr && k == a.K - 1) {
+  } else if (a.last_state != nullptr && k == last_chunk(sr.len, a.chunk_len)) {
 #pragma unroll
     for (int i = 0; i < NS; ++i)
       if (n0 + i < N) st_param(a.last_state, (b * D + d) * N + n0 + i, a.param_dtype, h[i]);

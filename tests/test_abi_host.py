@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     lib = ss.load_library()
     names = _declared_functions()
     assert set(names) == {"ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0", "ss_bwd_h0",
-                          "ss_plan_query", "ss_status_string", "ss_last_error"}
+                          "ss_fwd_varlen", "ss_plan_query", "ss_status_string",
+                          "ss_last_error"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -91,6 +92,18 @@ def test_h0_rules():
     ws = ss.ss_workspace_size(d, 0)
     if ws > 0:
         assert _fwd_h0(d, P, q) == ss.SS_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_varlen_rules():
+    d = _desc()
+    call = lambda cu, total: ss.ss_fwd_varlen(d, cu, total, P, P, P, P, P, None, None, None,
+                                              None, P, None, None, 0, None)
+    assert call(None, 10) == ss.SS_ERR_INVALID_PROBLEM
+    assert "cu_seqlens" in ss.ss_last_error()
+    assert call(ctypes.c_void_p(0x7F0000000002), 10) == ss.SS_ERR_INVALID_PROBLEM
+    assert "aligned" in ss.ss_last_error()
+    assert call(P, -1) == ss.SS_ERR_INVALID_PROBLEM
+    assert "total_len" in ss.ss_last_error()
 
 
 def test_status_strings():

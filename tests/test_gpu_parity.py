@@ -457,3 +457,43 @@ def test_fwd_short_sequences(L, N, io):
         tol = TOL[inp["u"].dtype]
         assert rel_err(to_np(y), yr) <= tol
         assert rel_err(to_np(ls), lsr) <= max(tol, TOL[inp["A"].dtype])
+
+
+# ------------------------------------------------------- packed sequences
+
+def _packed(S, lens, D, N, seed, io="f32", backward=False):
+    """Packed inputs for sequences of the given lengths (rows of one long
+    seeded batch), their int32 offsets and the longest length."""
+    T = int(sum(lens))
+    inp = random_inputs(1, max(T, 1), D, N, seed=seed, io_dtype=io, backward=backward)
+    p = {k: (None if v is None else (v[0, :T].contiguous() if v.dim() == 3 else v))
+         for k, v in inp.items()}
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return p, cu, int(max(lens)) if len(lens) else 0
+
+
+VARLEN_CASES = [([37, 0, 130, 5, 64], 72, 16, "f32"), ([300, 1, 77], 96, 16, "bf16"),
+                ([9, 16, 3, 12], 40, 16, "f32"), ([50, 200], 20, 64, "f32"),
+                ([129, 64, 1000], 65, 8, "f16"), ([2048] * 2 + [100], 128, 16, "bf16")]
+
+
+@pytest.mark.parametrize("lens,D,N,io", VARLEN_CASES, ids=lambda v: str(v))
+def test_fwd_varlen(lens, D, N, io):
+    p, cu, Lmax = _packed(len(lens), lens, D, N, seed=2200 + sum(lens) % 97, io=io)
+    S = len(lens)
+    g = torch.Generator().manual_seed(2300 + S)
+    h0 = torch.randn(S, D, N, generator=g, dtype=torch.float64).to(p["A"].dtype)
+    d = to_dev(p)
+    cu_d = torch.as_tensor(cu, device=DEV)
+    for chunk in (0, 24):
+        for with_h0 in (False, True):
+            say("fwd varlen", lens, D, N, io, "chunk", chunk, "h0", with_h0)
+            y, ls = ss.fwd_varlen(d["u"], d["delta"], d["A"], d["B"], d["C"], cu_d, Lmax,
+                                  d["D"], d["z"], d["delta_bias"], chunk_len=chunk,
+                                  h0=h0.to(DEV) if with_h0 else None, return_last_state=True)
+            torch.cuda.synchronize()
+            yr, lsr = oracle.fwd_varlen(**{k: p[k] for k in KEYS}, cu_seqlens=cu,
+                                        h0=h0 if with_h0 else None)
+            tol = TOL[p["u"].dtype]
+            assert rel_err(to_np(y), yr) <= tol
+            assert rel_err(to_np(ls), lsr) <= max(tol, TOL[p["A"].dtype])
