@@ -135,13 +135,25 @@ int ss_bwd_h0(const ss_desc* desc, const void* u, const void* delta, const void*
  * independently from h0[s] (or 0), and last_state[s] is its final state
  * ([S, D, N]).  The offsets are read on the device and not validated there
  * beyond clamping into [0, total_len] and lengths to desc->seqlen: rows no
- * sequence covers are not written.  Workspace: ss_workspace_size(desc, 0)
- * with the same desc.  Everything else as ss_fwd_h0. */
+ * sequence covers are not written (their backward gradients are unspecified).
+ * total_len > batch * seqlen is SS_ERR_INVALID_PROBLEM.  Workspace:
+ * ss_workspace_size(desc, 0) with the same desc.  Everything else as
+ * ss_fwd_h0. */
 int ss_fwd_varlen(const ss_desc* desc, const int32_t* cu_seqlens, int64_t total_len,
                   const void* u, const void* delta, const void* A, const void* B, const void* C,
                   const void* Dskip, const void* z, const void* delta_bias, const void* h0,
                   void* y, void* last_state, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* Backward of ss_fwd_varlen: as ss_bwd_h0 with the packed layout (du,
+ * ddelta, dz, dy [total_len, D]; dB, dC [total_len, N]; h0 / dh0 [S, D, N]).
+ * Workspace: ss_workspace_size(desc, 1) with the same desc. */
+int ss_bwd_varlen(const ss_desc* desc, const int32_t* cu_seqlens, int64_t total_len,
+                  const void* u, const void* delta, const void* A, const void* B, const void* C,
+                  const void* Dskip, const void* z, const void* delta_bias, const void* h0,
+                  const void* dy, void* du, void* ddelta, void* dA, void* dB, void* dC,
+                  void* dD, void* dz, void* ddelta_bias, void* dh0, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /* The schedule the library would use for a descriptor (informational). */
 typedef struct ss_plan {

@@ -8,10 +8,11 @@ If the library is missing, every call raises: there is no fallback.
 
 Raw C entry points with the header's names: ``ss_workspace_size``,
 ``ss_fwd``, ``ss_bwd``, ``ss_fwd_h0``, ``ss_bwd_h0``, ``ss_fwd_varlen``,
-``ss_plan_query``, ``ss_status_string``, ``ss_last_error``.  Tensor-level
-helpers: ``fwd``, ``bwd`` (both with an optional initial state ``h0``),
-``fwd_varlen`` (packed variable-length sequences), ``decode_step`` and the
-autograd function ``selective_scan``.
+``ss_bwd_varlen``, ``ss_plan_query``, ``ss_status_string``,
+``ss_last_error``.  Tensor-level helpers: ``fwd``, ``bwd`` (both with an
+optional initial state ``h0``), ``fwd_varlen`` / ``bwd_varlen`` (packed
+variable-length sequences), ``decode_step`` and the autograd function
+``selective_scan``.
 """
 from __future__ import annotations
 
@@ -21,9 +22,9 @@ from typing import Dict, Optional, Tuple
 
 import torch
 
-__all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "fwd_varlen", "decode_step", "selective_scan",
-           "plan", "workspace_size", "ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0",
-           "ss_bwd_h0", "ss_fwd_varlen",
+__all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "fwd_varlen", "bwd_varlen", "decode_step",
+           "selective_scan", "plan", "workspace_size", "ss_workspace_size", "ss_fwd", "ss_bwd",
+           "ss_fwd_h0", "ss_bwd_h0", "ss_fwd_varlen", "ss_bwd_varlen",
            "ss_plan_query", "ss_status_string",
            "ss_last_error", "library_path", "load_library",
            "SS_OK", "SS_ERR_INVALID_PROBLEM", "SS_ERR_UNSUPPORTED",
@@ -80,6 +81,8 @@ def load_library(path: Optional[str] = None):
     lib.ss_bwd_h0.restype = ctypes.c_int
     lib.ss_fwd_varlen.argtypes = [dp, vp, ctypes.c_int64] + [vp] * 12 + [sz, vp]
     lib.ss_fwd_varlen.restype = ctypes.c_int
+    lib.ss_bwd_varlen.argtypes = [dp, vp, ctypes.c_int64] + [vp] * 20 + [sz, vp]
+    lib.ss_bwd_varlen.restype = ctypes.c_int
     lib.ss_plan_query.argtypes = [dp, ctypes.c_int32, ctypes.POINTER(SsPlan)]
     lib.ss_plan_query.restype = ctypes.c_int
     lib.ss_status_string.argtypes = [ctypes.c_int]
@@ -130,6 +133,15 @@ def ss_fwd_varlen(desc: SsDesc, cu_seqlens, total_len: int, u, delta, A, B, C, D
                   delta_bias, h0, y, last_state, workspace, workspace_bytes: int, stream) -> int:
     return load_library().ss_fwd_varlen(_ref(desc), cu_seqlens, int(total_len), u, delta, A, B,
                                         C, Dskip, z, delta_bias, h0, y, last_state, workspace,
+                                        workspace_bytes, stream)
+
+
+def ss_bwd_varlen(desc: SsDesc, cu_seqlens, total_len: int, u, delta, A, B, C, Dskip, z,
+                  delta_bias, h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                  workspace, workspace_bytes: int, stream) -> int:
+    return load_library().ss_bwd_varlen(_ref(desc), cu_seqlens, int(total_len), u, delta, A,
+                                        B, C, Dskip, z, delta_bias, h0, dy, du, ddelta, dA, dB,
+                                        dC, dD, dz, ddelta_bias, dh0, workspace,
                                         workspace_bytes, stream)
 
 
@@ -358,6 +370,55 @@ def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None,
                    _ptr(workspace), workspace.numel(), _stream_of(dev))
     if st != SS_OK:
         _raise(st, "ss_bwd_h0" if h0 is not None else "ss_bwd")
+    return out
+
+
+def bwd_varlen(u, delta, A, B, C, cu_seqlens, max_seqlen: int, D=None, z=None,
+               delta_bias=None, dy=None, delta_softplus: bool = True, h0=None,
+               chunk_len: int = 0, workspace: Optional[torch.Tensor] = None
+               ) -> Dict[str, Optional[torch.Tensor]]:
+    """Backward of ``fwd_varlen``: gradients of sum(dy * y) over the packed rows.
+
+    Shapes as ``fwd_varlen`` (dy: [T, D]); returns the dict of ``bwd`` with
+    du / ddelta / dz [T, D], dB / dC [T, N] and dh0 [S, D, N].  Rows that no
+    sequence covers get unspecified gradients.
+    """
+    desc = _varlen_desc(u, A, cu_seqlens, max_seqlen, delta_softplus, chunk_len)
+    dev, io, pa = u.device, u.dtype, A.dtype
+    S, Dd, N = desc.batch, desc.dim, desc.dstate
+    T = u.shape[0]
+    for t, name, shape, dt in ((u, "u", (T, Dd), io), (delta, "delta", (T, Dd), io),
+                               (A, "A", (Dd, N), pa), (B, "B", (T, N), io),
+                               (C, "C", (T, N), io), (D, "D", (Dd,), pa),
+                               (z, "z", (T, Dd), io), (delta_bias, "delta_bias", (Dd,), pa),
+                               (dy, "dy", (T, Dd), io), (h0, "h0", (S, Dd, N), pa)):
+        _check(t, name, shape, dt, dev)
+    if dy is None:
+        raise ValueError("dy is required")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    out = {
+        "du": torch.empty((T, Dd), dtype=io, device=dev),
+        "ddelta": torch.empty((T, Dd), dtype=io, device=dev),
+        "dA": torch.empty((Dd, N), dtype=pa, device=dev),
+        "dB": torch.empty((T, N), dtype=io, device=dev),
+        "dC": torch.empty((T, N), dtype=io, device=dev),
+        "dD": torch.empty((Dd,), dtype=pa, device=dev) if D is not None else None,
+        "dz": torch.empty((T, Dd), dtype=io, device=dev) if z is not None else None,
+        "ddelta_bias": torch.empty((Dd,), dtype=pa, device=dev) if delta_bias is not None else None,
+        "dh0": torch.empty((S, Dd, N), dtype=pa, device=dev) if h0 is not None else None,
+    }
+    need = workspace_size(desc, True)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = ss_bwd_varlen(desc, _ptr(cu_seqlens), T, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                       _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dy),
+                       _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                       _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+                       _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), _ptr(workspace),
+                       workspace.numel(), _stream_of(dev))
+    if st != SS_OK:
+        _raise(st, "ss_bwd_varlen")
     return out
 
 

@@ -144,6 +144,8 @@ int fwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total
   if (cu && total < 0) return fail(SS_ERR_INVALID_PROBLEM, "%s: total_len must be >= 0", who);
   if (cu && !aligned(cu, 4))
     return fail(SS_ERR_INVALID_PROBLEM, "%s: cu_seqlens is not 4-byte aligned", who);
+  if (cu && total > (int64_t)d->batch * d->seqlen)
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: total_len exceeds batch * seqlen", who);
   const int64_t rows = cu ? total : Bn * L;          // rows of the [rows, D] tensors
   const int64_t io = dtype_size(d->io_dtype), pa = dtype_size(d->param_dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -235,15 +237,27 @@ int ss_bwd(const ss_desc* d, const void* u, const void* delta, const void* A, co
                    dC, dD, dz, ddelta_bias, nullptr, workspace, workspace_bytes, stream);
 }
 
-int ss_bwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,
-              const void* C, const void* Dskip, const void* z, const void* delta_bias,
-              const void* h0, const void* dy, void* du, void* ddelta, void* dA, void* dB,
-              void* dC, void* dD, void* dz, void* ddelta_bias, void* dh0, void* workspace,
-              size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Backward of a dense (cu = NULL) or packed variable-length problem.
+int bwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total,
+             const void* u, const void* delta, const void* A, const void* B, const void* C,
+             const void* Dskip, const void* z, const void* delta_bias, const void* h0,
+             const void* dy, void* du, void* ddelta, void* dA, void* dB, void* dC, void* dD,
+             void* dz, void* ddelta_bias, void* dh0, void* workspace, size_t workspace_bytes,
+             void* stream) {
   g_err[0] = 0;
-  const char* who = h0 ? "ss_bwd_h0" : "ss_bwd";
   int st = check_desc(d, who);
   if (st != SS_OK) return st;
+  if (cu && total < 0) return fail(SS_ERR_INVALID_PROBLEM, "%s: total_len must be >= 0", who);
+  if (cu && !aligned(cu, 4))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: cu_seqlens is not 4-byte aligned", who);
+  // The dB / dC partials are sized for batch * seqlen rows; sequences of at
+  // most seqlen steps cannot hold more.
+  if (cu && total > (int64_t)d->batch * d->seqlen)
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: total_len exceeds batch * seqlen", who);
   if ((h0 == nullptr) != (dh0 == nullptr))
     return fail(SS_ERR_INVALID_PROBLEM, "%s: h0 and dh0 must be both given or both omitted", who);
   if ((Dskip == nullptr) != (dD == nullptr))
@@ -254,11 +268,12 @@ int ss_bwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A,
     return fail(SS_ERR_INVALID_PROBLEM,
                 "%s: delta_bias and ddelta_bias must be both given or both omitted", who);
   const int64_t Bn = d->batch, L = d->seqlen, D = d->dim, N = d->dstate;
+  const int64_t rows = cu ? total : Bn * L;          // rows of the [rows, D] tensors
   const int64_t io = dtype_size(d->io_dtype), pa = dtype_size(d->param_dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ss::Plan p = ss::make_plan(*d, true);
   PtrCheck pc{who};
-  if (Bn * L * D > 0) {
+  if (rows * D > 0) {
     pc.need(u, "u", io); pc.need(delta, "delta", io); pc.need(dy, "dy", io);
     pc.need(du, "du", io); pc.need(ddelta, "ddelta", io);
     if (N > 0) {
@@ -267,7 +282,7 @@ int ss_bwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A,
     pc.opt(z, "z", io); pc.opt(dz, "dz", io);
   }
   if (D * N > 0) pc.need(dA, "dA", pa);
-  if (Bn * L * N > 0) { pc.need(dB, "dB", io); pc.need(dC, "dC", io); }
+  if (rows * N > 0) { pc.need(dB, "dB", io); pc.need(dC, "dC", io); }
   pc.opt(Dskip, "D", pa); pc.opt(dD, "dD", pa);
   pc.opt(delta_bias, "delta_bias", pa); pc.opt(ddelta_bias, "ddelta_bias", pa);
   if (Bn * D * N > 0) { pc.opt(h0, "h0", pa); pc.opt(dh0, "dh0", pa); }
@@ -276,7 +291,7 @@ int ss_bwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A,
     return fail(SS_ERR_INVALID_PROBLEM, "%s: dh0 must not overlap h0", who);
   st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
   if (st != SS_OK) return st;
-  if (Bn * L * D == 0 && D * N == 0 && Bn * L * N == 0 && D == 0) return SS_OK;
+  if (rows * D == 0 && D * N == 0 && rows * N == 0 && D == 0) return SS_OK;
   const bool has_state = h0 && Bn * D * N > 0;
 
   ss::BwdArgs a{};
@@ -289,10 +304,40 @@ int ss_bwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A,
   a.ws = static_cast<char*>(workspace);
   a.Bn = Bn; a.L = L; a.D = D; a.N = N;
   a.chunk_len = p.chunk_len; a.K = p.K;
+  a.cu = cu; a.Lt = rows;
   a.softplus = d->delta_softplus;
   a.param_dtype = d->param_dtype;
   a.io_dtype = d->io_dtype;
   return hip_status(ss::launch_bwd(a, p, d->io_dtype, s), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss_bwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A, const void* B,
+              const void* C, const void* Dskip, const void* z, const void* delta_bias,
+              const void* h0, const void* dy, void* du, void* ddelta, void* dA, void* dB,
+              void* dC, void* dD, void* dz, void* ddelta_bias, void* dh0, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return bwd_impl(h0 ? "ss_bwd_h0" : "ss_bwd", d, nullptr, 0, u, delta, A, B, C, Dskip, z,
+                  delta_bias, h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                  workspace, workspace_bytes, stream);
+}
+
+int ss_bwd_varlen(const ss_desc* d, const int32_t* cu_seqlens, int64_t total_len,
+                  const void* u, const void* delta, const void* A, const void* B, const void* C,
+                  const void* Dskip, const void* z, const void* delta_bias, const void* h0,
+                  const void* dy, void* du, void* ddelta, void* dA, void* dB, void* dC,
+                  void* dD, void* dz, void* ddelta_bias, void* dh0, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) {
+    g_err[0] = 0;
+    return fail(SS_ERR_INVALID_PROBLEM, "ss_bwd_varlen: cu_seqlens is NULL");
+  }
+  return bwd_impl("ss_bwd_varlen", d, cu_seqlens, total_len, u, delta, A, B, C, Dskip, z,
+                  delta_bias, h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                  workspace, workspace_bytes, stream);
 }
 
 const char* ss_status_string(int status) {

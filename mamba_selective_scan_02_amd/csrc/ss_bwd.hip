@@ -42,14 +42,13 @@ constexpr int kRedStride = 257;        // LDS row stride of the dB/dC reduction 
 // are zero (their dt is zero too, so they are identity steps).
 template <typename Tio>
 __device__ __forceinline__ void load_bc_tile(float* sB, float* sC, const Tio* B, const Tio* C,
-                                             int64_t b, int64_t t0, int nt, int64_t L,
-                                             int64_t N) {
+                                             int64_t row0, int nt, int64_t N) {
   const int64_t total = N * T;
   for (int64_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
     const int64_t tt = idx / N, n = idx % N;   // n fastest: coalesced global reads
     float bv = 0.0f, cv = 0.0f;
     if (tt < nt) {
-      const int64_t g = (b * L + t0 + tt) * N + n;
+      const int64_t g = (row0 + tt) * N + n;
       bv = ld(B, g);
       cv = ld(C, g);
     }
@@ -71,27 +70,31 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_summary(const BwdArgs a
   blk /= nbd;
   const int64_t k = blk % a.K;
   const int64_t b = blk / a.K;
-  const int64_t L = a.L, D = a.D, N = a.N;
+  const int64_t D = a.D, N = a.N;
   const int64_t d_raw = db * kChannelsPerBlock + threadIdx.x;
   const bool active = d_raw < D;
   const int64_t d = active ? d_raw : D - 1;
+  const SeqRows sr = seq_rows(a.cu, b, a.L, a.Lt);
   const int64_t t0 = k * a.chunk_len;
-  const int nt = (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
+  int nt = (int)((t0 + a.chunk_len < sr.len ? t0 + a.chunk_len : sr.len) - t0);
+  if (nt < 0) nt = 0;                        // a chunk past a short sequence's end
 
-  load_bc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C), b, t0, nt, L, N);
+  load_bc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C),
+               sr.start + t0, nt, N);
 
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
   const bool has_z = a.z != nullptr, sp = a.softplus != 0;
-  const Tio* up = static_cast<const Tio*>(a.u) + b * L * D + d;
-  const Tio* dp = static_cast<const Tio*>(a.delta) + b * L * D + d;
-  const Tio* zp = has_z ? static_cast<const Tio*>(a.z) + b * L * D + d : up;
-  const Tio* yp = static_cast<const Tio*>(a.dy) + b * L * D + d;
+  const Tio* up = static_cast<const Tio*>(a.u) + d;           // + row * D
+  const Tio* dp = static_cast<const Tio*>(a.delta) + d;
+  const Tio* zp = has_z ? static_cast<const Tio*>(a.z) + d : up;
+  const Tio* yp = static_cast<const Tio*>(a.dy) + d;
   float dl[T], xu[T], gg[T];
   float dsum = 0.0f;
 #pragma unroll
   for (int tt = 0; tt < T; ++tt) {
     const bool ok = tt < nt;
-    const int64_t t = t0 + (ok ? tt : nt - 1);
+    // past the chunk: a step of it, or row 0 for an empty chunk (never used)
+    const int64_t t = nt > 0 ? sr.start + t0 + (ok ? tt : nt - 1) : 0;
     const float uu = ld(up, t * D), x = ld(dp, t * D) + bv;
     const float dlv = sp ? softplus(x) : x;
     float g = ld(yp, t * D);
@@ -184,20 +187,21 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
   blk /= nbd;
   const int64_t kg = blk % a.KG;
   const int64_t b = blk / a.KG;
-  const int64_t L = a.L, D = a.D, N = a.N, K = a.K;
+  const int64_t D = a.D, N = a.N, K = a.K;
+  const SeqRows sr = seq_rows(a.cu, b, a.L, a.Lt);
   const int64_t d_raw = db * kChannelsPerBlock + tid;
   const bool active = d_raw < D;
   const int64_t d = active ? d_raw : D - 1;
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
   const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
   const bool has_z = a.z != nullptr, has_D = a.Dskip != nullptr, sp = a.softplus != 0;
-  const Tio* up = static_cast<const Tio*>(a.u) + b * L * D + d;
-  const Tio* dp = static_cast<const Tio*>(a.delta) + b * L * D + d;
-  const Tio* zp = has_z ? static_cast<const Tio*>(a.z) + b * L * D + d : up;
-  const Tio* yp = static_cast<const Tio*>(a.dy) + b * L * D + d;
-  Tio* dup = static_cast<Tio*>(a.du) + b * L * D + d;
-  Tio* ddp = static_cast<Tio*>(a.ddelta) + b * L * D + d;
-  Tio* dzp = has_z ? static_cast<Tio*>(a.dz) + b * L * D + d : dup;
+  const Tio* up = static_cast<const Tio*>(a.u) + d;           // + row * D
+  const Tio* dp = static_cast<const Tio*>(a.delta) + d;
+  const Tio* zp = has_z ? static_cast<const Tio*>(a.z) + d : up;
+  const Tio* yp = static_cast<const Tio*>(a.dy) + d;
+  Tio* dup = static_cast<Tio*>(a.du) + d;
+  Tio* ddp = static_cast<Tio*>(a.ddelta) + d;
+  Tio* dzp = has_z ? static_cast<Tio*>(a.dz) + d : dup;
 
   // reduction lane roles: value v (0..15 dB, 16..31 dC), channel slice p
   const int rv = tid >> 3, rp = tid & 7;
@@ -207,16 +211,17 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
 
   for (int64_t k = k_hi - 1; k >= k_lo; --k) {
     const int64_t t0 = k * a.chunk_len;
-    const int nt = (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
+    int nt = (int)((t0 + a.chunk_len < sr.len ? t0 + a.chunk_len : sr.len) - t0);
+    if (nt < 0) nt = 0;                      // a chunk past a short sequence's end
     __syncthreads();  // previous chunk's tile readers are done
-    load_bc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C), b, t0, nt,
-                 L, N);
+    load_bc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C),
+                 sr.start + t0, nt, N);
 
     float uu[T], dl[T], xu[T], gg[T], gz[T], sx[T], oo[T], ddl[T], dua[T];
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) {
       const bool ok = tt < nt;
-      const int64_t t = t0 + (ok ? tt : nt - 1);
+      const int64_t t = nt > 0 ? sr.start + t0 + (ok ? tt : nt - 1) : 0;   // row
       const float u_ = ld(up, t * D), x = ld(dp, t * D) + bv, dy = ld(yp, t * D);
       float dlv, sxv;
       if (sp) { dlv = softplus(x); sxv = sigmoid(x); } else { dlv = x; sxv = 1.0f; }
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
       if (rp == 0) {
         const int tt = rv & (T - 1), which = rv >> 4;
         if (tt < nt)
-          a.part_bc[((b * L + t0 + tt) * a.nwgd + db) * 2 * N + which * N + n] = s;
+          a.part_bc[((sr.start + t0 + tt) * a.nwgd + db) * 2 * N + which * N + n] = s;
       }
       __syncthreads();  // red free for the next n
     }
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) {
       if (tt < nt && active) {
-        const int64_t t = t0 + tt;
+        const int64_t t = sr.start + t0 + tt;   // row
         const float du = __builtin_fmaf(dl[tt], dua[tt], has_D ? gg[tt] * Dv : 0.0f);
         const float dde = __builtin_fmaf(uu[tt], dua[tt], ddl[tt]);
         const float dx = dde * sx[tt];
@@ -326,9 +331,9 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
 // are issued in batches of 8, the adds stay in index order).
 template <typename Tio>
 __global__ void bwd_finalize_bc(const BwdArgs a) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // (b*L + t)*N + n
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // row * N + n
   const int64_t N = a.N;
-  if (i >= a.Bn * a.L * N) return;
+  if (i >= a.Lt * N) return;
   const int64_t bt = i / N, n = i % N;
   const float* p = a.part_bc + bt * a.nwgd * 2 * N + n;
   float sb = 0.0f, sc = 0.0f;
@@ -410,8 +415,8 @@ hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_finalize(const BwdArgs& a, hipStream_t s) {
   hipError_t e;
-  if (a.Bn * a.L * a.N > 0) {
-    const int64_t n = a.Bn * a.L * a.N;
+  if (a.Lt * a.N > 0) {
+    const int64_t n = a.Lt * a.N;
     switch (a.io_dtype) {
       case 0: bwd_finalize_bc<float><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a); break;
       case 1: bwd_finalize_bc<f16_t><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a); break;
@@ -450,15 +455,15 @@ hipError_t launch_bwd_tile(const BwdArgs& a, int ns, hipStream_t s);  // ss_bwd_
 
 hipError_t launch_bwd(const BwdArgs& a_in, const Plan& p, int io_dtype, hipStream_t s) {
   BwdArgs a = a_in;
-  const int64_t Bn = a.Bn, L = a.L, D = a.D, N = a.N;
+  const int64_t Bn = a.Bn, D = a.D, N = a.N, rows = a.Lt;
   const int64_t io = a.io_dtype == 0 ? 4 : 2, pa = a.param_dtype == 0 ? 4 : 2;
-  if (Bn * L * D == 0) {
+  if (Bn * rows * D == 0) {
     // No (b, t, d) terms: every reduced gradient is an empty sum.
     hipError_t e = zero_bytes(a.dA, D * N * pa, s);
     if (e == hipSuccess) e = zero_bytes(a.dD, D * pa, s);
     if (e == hipSuccess) e = zero_bytes(a.dbias, D * pa, s);
-    if (e == hipSuccess) e = zero_bytes(a.dB, Bn * L * N * io, s);
-    if (e == hipSuccess) e = zero_bytes(a.dC, Bn * L * N * io, s);
+    if (e == hipSuccess) e = zero_bytes(a.dB, rows * N * io, s);
+    if (e == hipSuccess) e = zero_bytes(a.dC, rows * N * io, s);
     if (e == hipSuccess) e = zero_bytes(a.dh0, Bn * D * N * pa, s);  // L = 0: y ignores h0
     return e;
   }

@@ -83,7 +83,7 @@ __device__ __forceinline__ float brs8(const float (&o)[8], int g) {
 // Decoded position of a workgroup / lane (shared by the two kernels).
 struct BTilePos {
   int g, cl;
-  int64_t db, k, b, d, t0, t1;
+  int64_t db, k, b, d, t0, t1, start;   // start: the sequence's first row
   bool active;
 };
 
@@ -101,7 +101,10 @@ __device__ __forceinline__ BTilePos btile_pos(const BwdArgs& a) {
   p.active = d_raw < a.D;
   p.d = p.active ? d_raw : a.D - 1;
   p.t0 = p.k * a.chunk_len;
-  p.t1 = (p.t0 + a.chunk_len < a.L) ? p.t0 + a.chunk_len : a.L;
+  const SeqRows sr = seq_rows(a.cu, p.b, a.L, a.Lt);
+  p.start = sr.start;
+  p.t1 = (p.t0 + a.chunk_len < sr.len) ? p.t0 + a.chunk_len : sr.len;
+  if (p.t1 < p.t0) p.t1 = p.t0;                 // a chunk past a short sequence's end
   return p;
 }
 
@@ -109,11 +112,11 @@ __device__ __forceinline__ BTilePos btile_pos(const BwdArgs& a) {
 // and steps past the chunk are zero.
 template <typename T, int NP>
 __device__ __forceinline__ void bstage(float (*sB)[BTS], float (*sC)[BTS], const T* B, const T* C,
-                                       int64_t b, int64_t t0, int64_t nsteps, int64_t L,
+                                       int64_t row0, int64_t nsteps,
                                        int64_t N) {
   constexpr int ES = sizeof(T);
-  const auto rB = make_rsrc(B + (b * L + t0) * N, nsteps * N * ES);
-  const auto rC = make_rsrc(C + (b * L + t0) * N, nsteps * N * ES);
+  const auto rB = make_rsrc(B + row0 * N, nsteps * N * ES);
+  const auto rC = make_rsrc(C + row0 * N, nsteps * N * ES);
   for (int e = threadIdx.x; e < BTC * NP; e += kBT) {
     const int tt = e / NP, n = e % NP;
     const bool ok = n < N;
@@ -140,10 +143,10 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
   __shared__ __attribute__((aligned(16))) float4 xch[BCPW][BXS];
   const BTilePos P = btile_pos(a);
   const int g = P.g, cl = P.cl, n0 = g * NS;
-  const int64_t L = a.L, D = a.D, N = a.N, b = P.b, d = P.d;
+  const int64_t D = a.D, N = a.N, b = P.b, d = P.d;
   const int64_t nsteps = P.t1 - P.t0;
 
-  bstage<T, NP>(sB, sC, B_in, C_in, b, P.t0, nsteps, L, N);
+  bstage<T, NP>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N);
 
   // Sb is built two-level: per tile from its own start (E, sbl) and then
   // Sb += (decay of the chunk's earlier tiles) * sbl, the decay of a tile
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
   }
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
   const bool sp = a.softplus != 0;
-  const int64_t row0 = (b * L + P.t0) * D;
+  const int64_t row0 = (P.start + P.t0) * D;
   const auto rs_u = make_rsrc(u_in + row0, nsteps * D * ES);
   const auto rs_d = make_rsrc(delta_in + row0, nsteps * D * ES);
   const auto rs_z = make_rsrc(HAS_Z ? z_in + row0 : u_in + row0, nsteps * D * ES);
@@ -270,10 +273,10 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
   const BTilePos P = btile_pos(a);
   const int tid = threadIdx.x;
   const int g = P.g, cl = P.cl, n0 = g * NS;
-  const int64_t L = a.L, D = a.D, N = a.N, K = a.K, b = P.b, d = P.d, k = P.k;
+  const int64_t D = a.D, N = a.N, K = a.K, b = P.b, d = P.d, k = P.k;
   const int64_t nsteps = P.t1 - P.t0;
 
-  bstage<T, NP>(sB, sC, B_in, C_in, b, P.t0, nsteps, L, N);
+  bstage<T, NP>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N);
 
   float A2[NS], An[NS], h[NS], dh[NS], dA_acc[NS];
 #pragma unroll
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
   const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
   const bool sp = a.softplus != 0;
-  const int64_t row0 = (b * L + P.t0) * D;
+  const int64_t row0 = (P.start + P.t0) * D;
   const int64_t rbytes = nsteps * D * ES;
   const auto rs_u = make_rsrc(u_in + row0, rbytes);
   const auto rs_d = make_rsrc(delta_in + row0, rbytes);
@@ -494,7 +497,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
       for (int c = 0; c < BCPW; ++c) acc += red[w][c][sn];
       const int64_t t = (int64_t)j * BGL + s;
       if (n < N && t < nsteps)
-        a.part_bc[((b * L + P.t0 + t) * a.nwgd + P.db) * 2 * N + w * N + n] = acc;
+        a.part_bc[((P.start + P.t0 + t) * a.nwgd + P.db) * 2 * N + w * N + n] = acc;
     }
     __syncthreads();
   }

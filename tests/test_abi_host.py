@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     lib = ss.load_library()
     names = _declared_functions()
     assert set(names) == {"ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0", "ss_bwd_h0",
-                          "ss_fwd_varlen", "ss_plan_query", "ss_status_string",
+                          "ss_fwd_varlen", "ss_bwd_varlen", "ss_plan_query",
+                          "ss_status_string",
                           "ss_last_error"}
     for n in names:
         assert hasattr(lib, n), n
@@ -104,6 +105,21 @@ def test_varlen_rules():
     assert "aligned" in ss.ss_last_error()
     assert call(P, -1) == ss.SS_ERR_INVALID_PROBLEM
     assert "total_len" in ss.ss_last_error()
+    # more rows than batch * seqlen
+    assert call(P, 2 * 64 + 1) == ss.SS_ERR_INVALID_PROBLEM
+    assert "batch * seqlen" in ss.ss_last_error()
+    bcall = lambda cu, total: ss.ss_bwd_varlen(d, cu, total, P, P, P, P, P, None, None, None,
+                                               None, P, P, P, P, P, P, None, None, None, None,
+                                               P, 1 << 40, None)
+    assert bcall(None, 10) == ss.SS_ERR_INVALID_PROBLEM
+    assert "cu_seqlens" in ss.ss_last_error()
+    assert bcall(ctypes.c_void_p(0x7F0000000002), 10) == ss.SS_ERR_INVALID_PROBLEM
+    assert bcall(P, -1) == ss.SS_ERR_INVALID_PROBLEM
+    assert bcall(P, 2 * 64 + 1) == ss.SS_ERR_INVALID_PROBLEM
+    assert "batch * seqlen" in ss.ss_last_error()
+    # h0 / dh0 still come together
+    assert ss.ss_bwd_varlen(d, P, 10, P, P, P, P, P, None, None, None, P, P, P, P, P, P, P,
+                            None, None, None, None, P, 1 << 40, None) == ss.SS_ERR_INVALID_PROBLEM
 
 
 def test_status_strings():

@@ -497,3 +497,53 @@ def test_fwd_varlen(lens, D, N, io):
             tol = TOL[p["u"].dtype]
             assert rel_err(to_np(y), yr) <= tol
             assert rel_err(to_np(ls), lsr) <= max(tol, TOL[p["A"].dtype])
+
+
+@pytest.mark.parametrize("lens,D,N,io", VARLEN_CASES, ids=lambda v: str(v))
+def test_bwd_varlen(lens, D, N, io):
+    p, cu, Lmax = _packed(len(lens), lens, D, N, seed=2400 + sum(lens) % 89, io=io,
+                          backward=True)
+    S = len(lens)
+    g = torch.Generator().manual_seed(2500 + S)
+    h0 = torch.randn(S, D, N, generator=g, dtype=torch.float64).to(p["A"].dtype)
+    d = to_dev(p)
+    cu_d = torch.as_tensor(cu, device=DEV)
+    tol = TOL[p["u"].dtype]
+    for with_h0 in (False, True):
+        r = oracle.bwd_varlen(**{k: p[k] for k in KEYS}, dy=p["dy"], cu_seqlens=cu,
+                              h0=h0 if with_h0 else None)
+        for chunk in (0, 24):
+            say("bwd varlen", lens, D, N, io, "chunk", chunk, "h0", with_h0)
+            gr = ss.bwd_varlen(d["u"], d["delta"], d["A"], d["B"], d["C"], cu_d, Lmax, d["D"],
+                               d["z"], d["delta_bias"], d["dy"], chunk_len=chunk,
+                               h0=h0.to(DEV) if with_h0 else None)
+            torch.cuda.synchronize()
+            for k in GRADS + ("dh0",):
+                if r[k] is None:
+                    assert gr[k] is None
+                    continue
+                e = rel_err(to_np(gr[k]), r[k])
+                assert e <= tol, f"{k} chunk {chunk} h0 {with_h0}: {e:.3e}"
+
+
+def test_varlen_matches_dense_batch():
+    """Equal lengths packed back to back give the dense batch's results bit
+    for bit (same kernels, same chunking)."""
+    inp = random_inputs(3, 150, 72, 16, seed=2601, backward=True)
+    d = to_dev(inp)
+    pk = {k: (None if v is None else (v.reshape(-1, v.shape[-1]) if v.dim() == 3 else v))
+          for k, v in d.items()}
+    cu = torch.arange(0, 451, 150, dtype=torch.int32, device=DEV)
+    y, ls = ss.fwd(*[d[k] for k in KEYS], return_last_state=True)
+    yv, lsv = ss.fwd_varlen(pk["u"], pk["delta"], pk["A"], pk["B"], pk["C"], cu, 150, pk["D"],
+                            pk["z"], pk["delta_bias"], return_last_state=True)
+    g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"])
+    gv = ss.bwd_varlen(pk["u"], pk["delta"], pk["A"], pk["B"], pk["C"], cu, 150, pk["D"],
+                       pk["z"], pk["delta_bias"], pk["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.reshape(-1, 72), yv) and torch.equal(ls, lsv)
+    for k in GRADS:
+        if g[k] is None:
+            continue
+        a = g[k].reshape(gv[k].shape)
+        assert torch.equal(a, gv[k]), k
