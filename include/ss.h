@@ -155,6 +155,38 @@ int ss_bwd_varlen(const ss_desc* desc, const int32_t* cu_seqlens, int64_t total_
                   void* dD, void* dz, void* ddelta_bias, void* dh0, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* Forward and backward with B and C read as row-strided column slices.  The
+ * scan page restricts itself to contiguous layouts (module docs,
+ * "Trailblazer scope"); the mamba-rs page "mamba_ssm/gpu/backward.rs" keeps
+ * B and C as column ranges of the x-projection output xdbl (row width
+ * dt_rank + 2N, B at column dt_rank, C at dt_rank + N), gathers them into
+ * contiguous buffers before its SSM backward and scatters dB / dC back into
+ * the matching columns of d_xdbl afterwards (section "B3: SSM BPTT +
+ * reductions").  Here row t of B (and of dB) starts ldb elements after row
+ * t - 1, and likewise C / dC with ldc, so B = xdbl + dt_rank, C = xdbl +
+ * dt_rank + N, ldb = ldc = dt_rank + 2N read and write those columns in
+ * place.  ldb / ldc = 0 means N (packed); otherwise each must be >= N.  Only
+ * the first N elements of each dB / dC row are written; the elements between
+ * rows are not touched, so they may hold other data (e.g. the dt columns of
+ * d_xdbl), but they must not overlap any other argument.  cu_seqlens = NULL
+ * gives the dense layout of ss_fwd_h0 / ss_bwd_h0 (total_len is then
+ * ignored), otherwise the packed layout of ss_fwd_varlen / ss_bwd_varlen.
+ * With the tile kernels (dstate <= 32), a stride whose byte extent over one
+ * chunk exceeds 2^31 is SS_ERR_UNSUPPORTED (a shorter desc->chunk_len
+ * lifts that).  Everything else, workspace included, as those entry points. */
+int ss_fwd_strided(const ss_desc* desc, const int32_t* cu_seqlens, int64_t total_len,
+                   int64_t ldb, int64_t ldc, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, void* y, void* last_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int ss_bwd_strided(const ss_desc* desc, const int32_t* cu_seqlens, int64_t total_len,
+                   int64_t ldb, int64_t ldc, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, const void* dy, void* du,
+                   void* ddelta, void* dA, void* dB, void* dC, void* dD, void* dz,
+                   void* ddelta_bias, void* dh0, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* The schedule the library would use for a descriptor (informational). */
 typedef struct ss_plan {
   int32_t chunk_len;          /* time steps per chunk */

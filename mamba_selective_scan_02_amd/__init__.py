@@ -8,11 +8,13 @@ If the library is missing, every call raises: there is no fallback.
 
 Raw C entry points with the header's names: ``ss_workspace_size``,
 ``ss_fwd``, ``ss_bwd``, ``ss_fwd_h0``, ``ss_bwd_h0``, ``ss_fwd_varlen``,
-``ss_bwd_varlen``, ``ss_plan_query``, ``ss_status_string``,
-``ss_last_error``.  Tensor-level helpers: ``fwd``, ``bwd`` (both with an
-optional initial state ``h0``), ``fwd_varlen`` / ``bwd_varlen`` (packed
-variable-length sequences), ``decode_step`` and the autograd function
-``selective_scan``.
+``ss_bwd_varlen``, ``ss_fwd_strided``, ``ss_bwd_strided``,
+``ss_plan_query``, ``ss_status_string``, ``ss_last_error``.  Tensor-level
+helpers: ``fwd``, ``bwd`` (both with an optional initial state ``h0``),
+``fwd_varlen`` / ``bwd_varlen`` (packed variable-length sequences),
+``decode_step`` and the autograd function ``selective_scan``.  B and C (and
+the dB / dC outputs) may be row-strided views, e.g. column slices of the
+x-projection output; those calls go to the strided entry points.
 """
 from __future__ import annotations
 
@@ -24,7 +26,8 @@ import torch
 
 __all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "fwd_varlen", "bwd_varlen", "decode_step",
            "selective_scan", "plan", "workspace_size", "ss_workspace_size", "ss_fwd", "ss_bwd",
-           "ss_fwd_h0", "ss_bwd_h0", "ss_fwd_varlen", "ss_bwd_varlen",
+           "ss_fwd_h0", "ss_bwd_h0", "ss_fwd_varlen", "ss_bwd_varlen", "ss_fwd_strided",
+           "ss_bwd_strided",
            "ss_plan_query", "ss_status_string",
            "ss_last_error", "library_path", "load_library",
            "SS_OK", "SS_ERR_INVALID_PROBLEM", "SS_ERR_UNSUPPORTED",
@@ -83,6 +86,11 @@ def load_library(path: Optional[str] = None):
     lib.ss_fwd_varlen.restype = ctypes.c_int
     lib.ss_bwd_varlen.argtypes = [dp, vp, ctypes.c_int64] + [vp] * 20 + [sz, vp]
     lib.ss_bwd_varlen.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.ss_fwd_strided.argtypes = [dp, vp, i64, i64, i64] + [vp] * 12 + [sz, vp]
+    lib.ss_fwd_strided.restype = ctypes.c_int
+    lib.ss_bwd_strided.argtypes = [dp, vp, i64, i64, i64] + [vp] * 20 + [sz, vp]
+    lib.ss_bwd_strided.restype = ctypes.c_int
     lib.ss_plan_query.argtypes = [dp, ctypes.c_int32, ctypes.POINTER(SsPlan)]
     lib.ss_plan_query.restype = ctypes.c_int
     lib.ss_status_string.argtypes = [ctypes.c_int]
@@ -145,6 +153,23 @@ def ss_bwd_varlen(desc: SsDesc, cu_seqlens, total_len: int, u, delta, A, B, C, D
                                         workspace_bytes, stream)
 
 
+def ss_fwd_strided(desc: SsDesc, cu_seqlens, total_len: int, ldb: int, ldc: int, u, delta, A,
+                   B, C, Dskip, z, delta_bias, h0, y, last_state, workspace,
+                   workspace_bytes: int, stream) -> int:
+    return load_library().ss_fwd_strided(_ref(desc), cu_seqlens, int(total_len), int(ldb),
+                                         int(ldc), u, delta, A, B, C, Dskip, z, delta_bias, h0,
+                                         y, last_state, workspace, workspace_bytes, stream)
+
+
+def ss_bwd_strided(desc: SsDesc, cu_seqlens, total_len: int, ldb: int, ldc: int, u, delta, A,
+                   B, C, Dskip, z, delta_bias, h0, dy, du, ddelta, dA, dB, dC, dD, dz,
+                   ddelta_bias, dh0, workspace, workspace_bytes: int, stream) -> int:
+    return load_library().ss_bwd_strided(_ref(desc), cu_seqlens, int(total_len), int(ldb),
+                                         int(ldc), u, delta, A, B, C, Dskip, z, delta_bias, h0,
+                                         dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                                         workspace, workspace_bytes, stream)
+
+
 def ss_plan_query(desc: SsDesc, backward: int, out: SsPlan) -> int:
     return load_library().ss_plan_query(_ref(desc), int(backward), _ref(out))
 
@@ -172,7 +197,7 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _check(t: Optional[torch.Tensor], name: str, shape, dtype, device):
+def _check(t: Optional[torch.Tensor], name: str, shape, dtype, device, contiguous=True):
     if t is None:
         return
     if not isinstance(t, torch.Tensor):
@@ -183,8 +208,49 @@ def _check(t: Optional[torch.Tensor], name: str, shape, dtype, device):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if t.device != device:
         raise ValueError(f"{name} must be on {device}, got {t.device}")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _row_stride(t: Optional[torch.Tensor], name: str, shape, dtype, device) -> int:
+    """Elements between consecutive rows of a [..., N] tensor (B, C, dB, dC)
+    whose rows are contiguous and evenly spaced: N when packed, more for a
+    column slice of a wider matrix.  0 for None."""
+    _check(t, name, shape, dtype, device, contiguous=False)
+    if t is None:
+        return 0
+    N = shape[-1]
+    if t.is_contiguous():
+        return N
+    if N > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    ld, inner = None, 1
+    for i in range(len(shape) - 2, -1, -1):
+        if shape[i] > 1:
+            if ld is None:
+                ld = t.stride(i)
+            elif t.stride(i) != ld * inner:
+                raise ValueError(f"{name}: rows must be evenly spaced")
+        inner *= shape[i]
+    ld = N if ld is None else ld
+    if ld < N:
+        raise ValueError(f"{name}: row stride {ld} < {N}")
+    return ld
+
+
+def _rows_like(shape, ld: int, dtype, device) -> torch.Tensor:
+    """An output of `shape` [..., N] whose rows lie ld elements apart."""
+    N = shape[-1]
+    rows = 1
+    for x in shape[:-1]:
+        rows *= x
+    base = torch.empty(max((rows - 1) * ld + N, 0) if rows > 0 else 0, dtype=dtype,
+                       device=device)
+    strides, inner = [1], ld
+    for x in reversed(shape[:-1]):
+        strides.insert(0, inner)
+        inner *= x
+    return base.as_strided(tuple(shape), tuple(strides))
 
 
 def _desc_for(u: torch.Tensor, A: torch.Tensor, delta_softplus: bool, chunk_len: int) -> SsDesc:
@@ -232,10 +298,11 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool
     dev, io, pa = u.device, u.dtype, A.dtype
     Bn, L, Dd, N = desc.batch, desc.seqlen, desc.dim, desc.dstate
     for t, name, shape, dt in ((u, "u", (Bn, L, Dd), io), (delta, "delta", (Bn, L, Dd), io),
-                               (A, "A", (Dd, N), pa), (B, "B", (Bn, L, N), io),
-                               (C, "C", (Bn, L, N), io), (D, "D", (Dd,), pa),
+                               (A, "A", (Dd, N), pa), (D, "D", (Dd,), pa),
                                (z, "z", (Bn, L, Dd), io), (delta_bias, "delta_bias", (Dd,), pa)):
         _check(t, name, shape, dt, dev)
+    ldb = _row_stride(B, "B", (Bn, L, N), io, dev)
+    ldc = _row_stride(C, "C", (Bn, L, N), io, dev)
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU")
     _check(h0, "h0", (Bn, Dd, N), pa, dev)
@@ -250,11 +317,18 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool
     if need > 0 and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    st = ss_fwd_h0(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                   _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls), _ptr(workspace),
-                   ws_bytes, _stream_of(dev))
+    if ldb == N and ldc == N:
+        who = "ss_fwd_h0" if h0 is not None else "ss_fwd"
+        st = ss_fwd_h0(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                       _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls), _ptr(workspace),
+                       ws_bytes, _stream_of(dev))
+    else:
+        who = "ss_fwd_strided"
+        st = ss_fwd_strided(desc, None, 0, ldb, ldc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                            _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(y),
+                            _ptr(ls), _ptr(workspace), ws_bytes, _stream_of(dev))
     if st != SS_OK:
-        _raise(st, "ss_fwd_h0" if h0 is not None else "ss_fwd")
+        _raise(st, who)
     return y, ls
 
 
@@ -289,12 +363,13 @@ def fwd_varlen(u, delta, A, B, C, cu_seqlens, max_seqlen: int, D=None, z=None,
     S, Dd, N = desc.batch, desc.dim, desc.dstate
     T = u.shape[0]
     for t, name, shape, dt in ((u, "u", (T, Dd), io), (delta, "delta", (T, Dd), io),
-                               (A, "A", (Dd, N), pa), (B, "B", (T, N), io),
-                               (C, "C", (T, N), io), (D, "D", (Dd,), pa),
+                               (A, "A", (Dd, N), pa), (D, "D", (Dd,), pa),
                                (z, "z", (T, Dd), io), (delta_bias, "delta_bias", (Dd,), pa),
                                (h0, "h0", (S, Dd, N), pa),
                                (last_state, "last_state", (S, Dd, N), pa)):
         _check(t, name, shape, dt, dev)
+    ldb = _row_stride(B, "B", (T, N), io, dev)
+    ldc = _row_stride(C, "C", (T, N), io, dev)
     if y is None:
         y = torch.empty((T, Dd), dtype=io, device=dev)
     _check(y, "y", (T, Dd), io, dev)
@@ -305,11 +380,18 @@ def fwd_varlen(u, delta, A, B, C, cu_seqlens, max_seqlen: int, D=None, z=None,
     if need > 0 and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    st = ss_fwd_varlen(desc, _ptr(cu_seqlens), T, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
-                       _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls),
-                       _ptr(workspace), ws_bytes, _stream_of(dev))
+    if ldb == N and ldc == N:
+        who = "ss_fwd_varlen"
+        st = ss_fwd_varlen(desc, _ptr(cu_seqlens), T, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                           _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(y),
+                           _ptr(ls), _ptr(workspace), ws_bytes, _stream_of(dev))
+    else:
+        who = "ss_fwd_strided"
+        st = ss_fwd_strided(desc, _ptr(cu_seqlens), T, ldb, ldc, _ptr(u), _ptr(delta), _ptr(A),
+                            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0),
+                            _ptr(y), _ptr(ls), _ptr(workspace), ws_bytes, _stream_of(dev))
     if st != SS_OK:
-        _raise(st, "ss_fwd_varlen")
+        _raise(st, who)
     return y, ls
 
 
@@ -326,56 +408,89 @@ def decode_step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return y.squeeze(1)
 
 
-def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None,
-        delta_softplus: bool = True, chunk_len: int = 0,
-        workspace: Optional[torch.Tensor] = None,
-        h0: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
-    """Selective-scan backward: gradients of sum(dy * y).
-
-    Returns a dict with du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0
-    (dD / dz / ddelta_bias / dh0 are None when D / z / delta_bias / h0 are
-    None).
-    """
-    desc = _desc_for(u, A, delta_softplus, chunk_len)
+def _bwd_call(desc, cu_seqlens, row_shape, state_shape, u, delta, A, B, C, D, z, delta_bias,
+              dy, h0, workspace, dB, dC, who_packed):
+    """Shared body of ``bwd`` / ``bwd_varlen``: row_shape is (B, L) or (T,)."""
     dev, io, pa = u.device, u.dtype, A.dtype
-    Bn, L, Dd, N = desc.batch, desc.seqlen, desc.dim, desc.dstate
-    for t, name, shape, dt in ((u, "u", (Bn, L, Dd), io), (delta, "delta", (Bn, L, Dd), io),
-                               (A, "A", (Dd, N), pa), (B, "B", (Bn, L, N), io),
-                               (C, "C", (Bn, L, N), io), (D, "D", (Dd,), pa),
-                               (z, "z", (Bn, L, Dd), io), (delta_bias, "delta_bias", (Dd,), pa),
-                               (dy, "dy", (Bn, L, Dd), io), (h0, "h0", (Bn, Dd, N), pa)):
+    Dd, N = desc.dim, desc.dstate
+    rd, rn = tuple(row_shape) + (Dd,), tuple(row_shape) + (N,)
+    for t, name, shape, dt in ((u, "u", rd, io), (delta, "delta", rd, io),
+                               (A, "A", (Dd, N), pa), (D, "D", (Dd,), pa),
+                               (z, "z", rd, io), (delta_bias, "delta_bias", (Dd,), pa),
+                               (dy, "dy", rd, io), (h0, "h0", state_shape, pa)):
         _check(t, name, shape, dt, dev)
+    ldb = _row_stride(B, "B", rn, io, dev)
+    ldc = _row_stride(C, "C", rn, io, dev)
     if dy is None:
         raise ValueError("dy is required")
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU")
+    # dB / dC: given outputs must share B's / C's row stride; new ones get it
+    if dB is None:
+        dB = _rows_like(rn, ldb, io, dev)
+    if dC is None:
+        dC = _rows_like(rn, ldc, io, dev)
+    if _row_stride(dB, "dB", rn, io, dev) != ldb or _row_stride(dC, "dC", rn, io, dev) != ldc:
+        raise ValueError("dB / dC must have the row strides of B / C")
     out = {
-        "du": torch.empty((Bn, L, Dd), dtype=io, device=dev),
-        "ddelta": torch.empty((Bn, L, Dd), dtype=io, device=dev),
+        "du": torch.empty(rd, dtype=io, device=dev),
+        "ddelta": torch.empty(rd, dtype=io, device=dev),
         "dA": torch.empty((Dd, N), dtype=pa, device=dev),
-        "dB": torch.empty((Bn, L, N), dtype=io, device=dev),
-        "dC": torch.empty((Bn, L, N), dtype=io, device=dev),
+        "dB": dB, "dC": dC,
         "dD": torch.empty((Dd,), dtype=pa, device=dev) if D is not None else None,
-        "dz": torch.empty((Bn, L, Dd), dtype=io, device=dev) if z is not None else None,
+        "dz": torch.empty(rd, dtype=io, device=dev) if z is not None else None,
         "ddelta_bias": torch.empty((Dd,), dtype=pa, device=dev) if delta_bias is not None else None,
-        "dh0": torch.empty((Bn, Dd, N), dtype=pa, device=dev) if h0 is not None else None,
+        "dh0": torch.empty(state_shape, dtype=pa, device=dev) if h0 is not None else None,
     }
     need = workspace_size(desc, True)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = ss_bwd_h0(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                   _ptr(delta_bias), _ptr(h0), _ptr(dy), _ptr(out["du"]), _ptr(out["ddelta"]),
-                   _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
-                   _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
-                   _ptr(workspace), workspace.numel(), _stream_of(dev))
+    ptrs = [_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), _ptr(h0), _ptr(dy), _ptr(out["du"]), _ptr(out["ddelta"]),
+            _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+            _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), _ptr(workspace),
+            workspace.numel(), _stream_of(dev)]
+    T = 1
+    for x in row_shape:
+        T *= x
+    if ldb != N or ldc != N:
+        who = "ss_bwd_strided"
+        st = ss_bwd_strided(desc, _ptr(cu_seqlens), T if cu_seqlens is not None else 0, ldb,
+                            ldc, *ptrs)
+    elif cu_seqlens is not None:
+        who = who_packed
+        st = ss_bwd_varlen(desc, _ptr(cu_seqlens), T, *ptrs)
+    else:
+        who = who_packed
+        st = ss_bwd_h0(desc, *ptrs)
     if st != SS_OK:
-        _raise(st, "ss_bwd_h0" if h0 is not None else "ss_bwd")
+        _raise(st, who)
     return out
+
+
+def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None,
+        delta_softplus: bool = True, chunk_len: int = 0,
+        workspace: Optional[torch.Tensor] = None,
+        h0: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
+        dC: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Selective-scan backward: gradients of sum(dy * y).
+
+    Returns a dict with du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0
+    (dD / dz / ddelta_bias / dh0 are None when D / z / delta_bias / h0 are
+    None).  dB / dC, if given, are written in place and must have the row
+    strides of B / C (for column slices of a wider matrix, only those
+    columns are written); new ones are allocated with those strides.
+    """
+    desc = _desc_for(u, A, delta_softplus, chunk_len)
+    return _bwd_call(desc, None, (desc.batch, desc.seqlen), (desc.batch, desc.dim, desc.dstate),
+                     u, delta, A, B, C, D, z, delta_bias, dy, h0, workspace, dB, dC,
+                     "ss_bwd_h0" if h0 is not None else "ss_bwd")
 
 
 def bwd_varlen(u, delta, A, B, C, cu_seqlens, max_seqlen: int, D=None, z=None,
                delta_bias=None, dy=None, delta_softplus: bool = True, h0=None,
-               chunk_len: int = 0, workspace: Optional[torch.Tensor] = None
+               chunk_len: int = 0, workspace: Optional[torch.Tensor] = None,
+               dB: Optional[torch.Tensor] = None, dC: Optional[torch.Tensor] = None
                ) -> Dict[str, Optional[torch.Tensor]]:
     """Backward of ``fwd_varlen``: gradients of sum(dy * y) over the packed rows.
 
@@ -384,42 +499,9 @@ def bwd_varlen(u, delta, A, B, C, cu_seqlens, max_seqlen: int, D=None, z=None,
     sequence covers get unspecified gradients.
     """
     desc = _varlen_desc(u, A, cu_seqlens, max_seqlen, delta_softplus, chunk_len)
-    dev, io, pa = u.device, u.dtype, A.dtype
-    S, Dd, N = desc.batch, desc.dim, desc.dstate
-    T = u.shape[0]
-    for t, name, shape, dt in ((u, "u", (T, Dd), io), (delta, "delta", (T, Dd), io),
-                               (A, "A", (Dd, N), pa), (B, "B", (T, N), io),
-                               (C, "C", (T, N), io), (D, "D", (Dd,), pa),
-                               (z, "z", (T, Dd), io), (delta_bias, "delta_bias", (Dd,), pa),
-                               (dy, "dy", (T, Dd), io), (h0, "h0", (S, Dd, N), pa)):
-        _check(t, name, shape, dt, dev)
-    if dy is None:
-        raise ValueError("dy is required")
-    if dev.type != "cuda":
-        raise ValueError("tensors must be on a GPU")
-    out = {
-        "du": torch.empty((T, Dd), dtype=io, device=dev),
-        "ddelta": torch.empty((T, Dd), dtype=io, device=dev),
-        "dA": torch.empty((Dd, N), dtype=pa, device=dev),
-        "dB": torch.empty((T, N), dtype=io, device=dev),
-        "dC": torch.empty((T, N), dtype=io, device=dev),
-        "dD": torch.empty((Dd,), dtype=pa, device=dev) if D is not None else None,
-        "dz": torch.empty((T, Dd), dtype=io, device=dev) if z is not None else None,
-        "ddelta_bias": torch.empty((Dd,), dtype=pa, device=dev) if delta_bias is not None else None,
-        "dh0": torch.empty((S, Dd, N), dtype=pa, device=dev) if h0 is not None else None,
-    }
-    need = workspace_size(desc, True)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = ss_bwd_varlen(desc, _ptr(cu_seqlens), T, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
-                       _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dy),
-                       _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
-                       _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
-                       _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), _ptr(workspace),
-                       workspace.numel(), _stream_of(dev))
-    if st != SS_OK:
-        _raise(st, "ss_bwd_varlen")
-    return out
+    return _bwd_call(desc, cu_seqlens, (u.shape[0],), (desc.batch, desc.dim, desc.dstate),
+                     u, delta, A, B, C, D, z, delta_bias, dy, h0, workspace, dB, dC,
+                     "ss_bwd_varlen")
 
 
 class _SelectiveScanFn(torch.autograd.Function):

@@ -91,6 +91,23 @@ bool overlap(const void* p, const void* q, int64_t bytes) {
   return bytes > 0 && a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes;
 }
 
+// Row strides of B / C (0 = N, the packed layout): at least N, and within
+// the 32-bit byte offsets that the tile kernels take inside one chunk
+// (rows_per_chunk rows, 0 for kernels with 64-bit addressing).
+int check_ld(int64_t* ldb, int64_t* ldc, int64_t N, int64_t es, int64_t rows_per_chunk,
+             const char* who) {
+  if (*ldb == 0) *ldb = N;
+  if (*ldc == 0) *ldc = N;
+  if (*ldb < N || *ldc < N)
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: B / C row strides must be 0 or >= dstate", who);
+  const int64_t ld = *ldb > *ldc ? *ldb : *ldc;
+  if (rows_per_chunk > 0 && (rows_per_chunk + ss::GL_MAX_TILE) * ld * es > 0x7fffffffLL)
+    return fail(SS_ERR_UNSUPPORTED, "%s: B / C row stride %lld is too large for chunks of "
+                "%lld steps (set a shorter desc->chunk_len)", who, (long long)ld,
+                (long long)rows_per_chunk);
+  return SS_OK;
+}
+
 int hip_status(hipError_t e, const char* who) {
   if (e == hipSuccess) return SS_OK;
   return fail(SS_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -134,7 +151,7 @@ namespace {
 // variable-length one (cu = cu_seqlens on the device, B sequences of at most
 // L steps in `total` rows).
 int fwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total,
-             const void* u, const void* delta, const void* A, const void* B, const void* C,
+             int64_t ldb, int64_t ldc, const void* u, const void* delta, const void* A, const void* B, const void* C,
              const void* Dskip, const void* z, const void* delta_bias, const void* h0, void* y,
              void* last_state, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
@@ -186,6 +203,8 @@ int fwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total
   if (in_place && p.K > 1)
     return fail(SS_ERR_UNSUPPORTED, "%s: an in-place state update (last_state == h0) needs a "
                 "single chunk, and this shape's rows exceed one chunk's 32-bit range", who);
+  st = check_ld(&ldb, &ldc, N, io, p.G == 8 ? p.chunk_len : 0, who);
+  if (st != SS_OK) return st;
   st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
   if (st != SS_OK) return st;
 
@@ -199,6 +218,7 @@ int fwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total
   a.Bn = Bn; a.L = L; a.D = D; a.N = N;
   a.chunk_len = p.chunk_len; a.K = p.K;
   a.cu = cu; a.Lt = rows;
+  a.ldb = ldb; a.ldc = ldc;
   a.softplus = d->delta_softplus;
   a.param_dtype = d->param_dtype;
   return hip_status(ss::launch_fwd(a, d->io_dtype, p.NS, p.G, s), who);
@@ -212,7 +232,7 @@ int ss_fwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A,
               const void* C, const void* Dskip, const void* z, const void* delta_bias,
               const void* h0, void* y, void* last_state, void* workspace,
               size_t workspace_bytes, void* stream) {
-  return fwd_impl(h0 ? "ss_fwd_h0" : "ss_fwd", d, nullptr, 0, u, delta, A, B, C, Dskip, z,
+  return fwd_impl(h0 ? "ss_fwd_h0" : "ss_fwd", d, nullptr, 0, 0, 0, u, delta, A, B, C, Dskip, z,
                   delta_bias, h0, y, last_state, workspace, workspace_bytes, stream);
 }
 
@@ -225,7 +245,7 @@ int ss_fwd_varlen(const ss_desc* d, const int32_t* cu_seqlens, int64_t total_len
     g_err[0] = 0;
     return fail(SS_ERR_INVALID_PROBLEM, "ss_fwd_varlen: cu_seqlens is NULL");
   }
-  return fwd_impl("ss_fwd_varlen", d, cu_seqlens, total_len, u, delta, A, B, C, Dskip, z,
+  return fwd_impl("ss_fwd_varlen", d, cu_seqlens, total_len, 0, 0, u, delta, A, B, C, Dskip, z,
                   delta_bias, h0, y, last_state, workspace, workspace_bytes, stream);
 }
 
@@ -243,7 +263,7 @@ namespace {
 
 // Backward of a dense (cu = NULL) or packed variable-length problem.
 int bwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total,
-             const void* u, const void* delta, const void* A, const void* B, const void* C,
+             int64_t ldb, int64_t ldc, const void* u, const void* delta, const void* A, const void* B, const void* C,
              const void* Dskip, const void* z, const void* delta_bias, const void* h0,
              const void* dy, void* du, void* ddelta, void* dA, void* dB, void* dC, void* dD,
              void* dz, void* ddelta_bias, void* dh0, void* workspace, size_t workspace_bytes,
@@ -289,6 +309,8 @@ int bwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total
   if (pc.status != SS_OK) return pc.status;
   if (h0 && overlap(h0, dh0, Bn * D * N * pa))
     return fail(SS_ERR_INVALID_PROBLEM, "%s: dh0 must not overlap h0", who);
+  st = check_ld(&ldb, &ldc, N, io, p.bwd_tile ? p.chunk_len : 0, who);
+  if (st != SS_OK) return st;
   st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
   if (st != SS_OK) return st;
   if (rows * D == 0 && D * N == 0 && rows * N == 0 && D == 0) return SS_OK;
@@ -305,6 +327,7 @@ int bwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total
   a.Bn = Bn; a.L = L; a.D = D; a.N = N;
   a.chunk_len = p.chunk_len; a.K = p.K;
   a.cu = cu; a.Lt = rows;
+  a.ldb = ldb; a.ldc = ldc;
   a.softplus = d->delta_softplus;
   a.param_dtype = d->param_dtype;
   a.io_dtype = d->io_dtype;
@@ -320,7 +343,7 @@ int ss_bwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A,
               const void* h0, const void* dy, void* du, void* ddelta, void* dA, void* dB,
               void* dC, void* dD, void* dz, void* ddelta_bias, void* dh0, void* workspace,
               size_t workspace_bytes, void* stream) {
-  return bwd_impl(h0 ? "ss_bwd_h0" : "ss_bwd", d, nullptr, 0, u, delta, A, B, C, Dskip, z,
+  return bwd_impl(h0 ? "ss_bwd_h0" : "ss_bwd", d, nullptr, 0, 0, 0, u, delta, A, B, C, Dskip, z,
                   delta_bias, h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
                   workspace, workspace_bytes, stream);
 }
@@ -335,9 +358,30 @@ int ss_bwd_varlen(const ss_desc* d, const int32_t* cu_seqlens, int64_t total_len
     g_err[0] = 0;
     return fail(SS_ERR_INVALID_PROBLEM, "ss_bwd_varlen: cu_seqlens is NULL");
   }
-  return bwd_impl("ss_bwd_varlen", d, cu_seqlens, total_len, u, delta, A, B, C, Dskip, z,
+  return bwd_impl("ss_bwd_varlen", d, cu_seqlens, total_len, 0, 0, u, delta, A, B, C, Dskip, z,
                   delta_bias, h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
                   workspace, workspace_bytes, stream);
+}
+
+int ss_fwd_strided(const ss_desc* d, const int32_t* cu_seqlens, int64_t total_len,
+                   int64_t ldb, int64_t ldc, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, void* y, void* last_state,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl("ss_fwd_strided", d, cu_seqlens, total_len, ldb, ldc, u, delta, A, B, C,
+                  Dskip, z, delta_bias, h0, y, last_state, workspace, workspace_bytes, stream);
+}
+
+int ss_bwd_strided(const ss_desc* d, const int32_t* cu_seqlens, int64_t total_len,
+                   int64_t ldb, int64_t ldc, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, const void* dy, void* du,
+                   void* ddelta, void* dA, void* dB, void* dC, void* dD, void* dz,
+                   void* ddelta_bias, void* dh0, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return bwd_impl("ss_bwd_strided", d, cu_seqlens, total_len, ldb, ldc, u, delta, A, B, C,
+                  Dskip, z, delta_bias, h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
+                  dh0, workspace, workspace_bytes, stream);
 }
 
 const char* ss_status_string(int status) {

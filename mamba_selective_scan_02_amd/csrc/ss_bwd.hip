@@ -42,15 +42,15 @@ constexpr int kRedStride = 257;        // LDS row stride of the dB/dC reduction 
 // are zero (their dt is zero too, so they are identity steps).
 template <typename Tio>
 __device__ __forceinline__ void load_bc_tile(float* sB, float* sC, const Tio* B, const Tio* C,
-                                             int64_t row0, int nt, int64_t N) {
+                                             int64_t row0, int nt, int64_t N, int64_t ldb,
+                                             int64_t ldc) {
   const int64_t total = N * T;
   for (int64_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
     const int64_t tt = idx / N, n = idx % N;   // n fastest: coalesced global reads
     float bv = 0.0f, cv = 0.0f;
     if (tt < nt) {
-      const int64_t g = (row0 + tt) * N + n;
-      bv = ld(B, g);
-      cv = ld(C, g);
+      bv = ld(B, (row0 + tt) * ldb + n);
+      cv = ld(C, (row0 + tt) * ldc + n);
     }
     sB[n * T + tt] = bv;
     sC[n * T + tt] = cv;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_summary(const BwdArgs a
   if (nt < 0) nt = 0;                        // a chunk past a short sequence's end
 
   load_bc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C),
-               sr.start + t0, nt, N);
+               sr.start + t0, nt, N, a.ldb, a.ldc);
 
   const float bv = a.bias ? ld_param(a.bias, d, a.param_dtype) : 0.0f;
   const bool has_z = a.z != nullptr, sp = a.softplus != 0;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
     if (nt < 0) nt = 0;                      // a chunk past a short sequence's end
     __syncthreads();  // previous chunk's tile readers are done
     load_bc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C),
-                 sr.start + t0, nt, N);
+                 sr.start + t0, nt, N, a.ldb, a.ldc);
 
     float uu[T], dl[T], xu[T], gg[T], gz[T], sx[T], oo[T], ddl[T], dua[T];
 #pragma unroll
@@ -353,8 +353,8 @@ __global__ void bwd_finalize_bc(const BwdArgs a) {
     sb += p[w * 2 * N];
     sc += p[w * 2 * N + N];
   }
-  static_cast<Tio*>(a.dB)[i] = from_f32<Tio>(sb);
-  static_cast<Tio*>(a.dC)[i] = from_f32<Tio>(sc);
+  static_cast<Tio*>(a.dB)[bt * a.ldb + n] = from_f32<Tio>(sb);
+  static_cast<Tio*>(a.dC)[bt * a.ldc + n] = from_f32<Tio>(sc);
 }
 
 // Fixed-order sum of `count` partials p[0], p[stride], ... (loads batched).
@@ -392,6 +392,23 @@ __global__ void bwd_finalize_d(const BwdArgs a) {
 __global__ void fill_zero_words(uint16_t* p, int64_t n) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
+}
+
+// Zero the first N elements of each of `rows` rows lying ld elements apart.
+template <typename W>
+__global__ void fill_zero_rows(W* p, int64_t rows, int64_t N, int64_t ld) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < rows * N) p[(i / N) * ld + i % N] = W(0);
+}
+
+static hipError_t zero_rows(void* p, int64_t rows, int64_t N, int64_t ld, int64_t es,
+                            hipStream_t s) {
+  const int64_t n = rows * N;
+  if (!p || n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (es == 4) fill_zero_rows<<<grid, dim3(256), 0, s>>>(static_cast<uint32_t*>(p), rows, N, ld);
+  else fill_zero_rows<<<grid, dim3(256), 0, s>>>(static_cast<uint16_t*>(p), rows, N, ld);
+  return hipGetLastError();
 }
 
 static hipError_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
@@ -462,8 +479,8 @@ hipError_t launch_bwd(const BwdArgs& a_in, const Plan& p, int io_dtype, hipStrea
     hipError_t e = zero_bytes(a.dA, D * N * pa, s);
     if (e == hipSuccess) e = zero_bytes(a.dD, D * pa, s);
     if (e == hipSuccess) e = zero_bytes(a.dbias, D * pa, s);
-    if (e == hipSuccess) e = zero_bytes(a.dB, rows * N * io, s);
-    if (e == hipSuccess) e = zero_bytes(a.dC, rows * N * io, s);
+    if (e == hipSuccess) e = zero_rows(a.dB, rows, N, a.ldb, io, s);
+    if (e == hipSuccess) e = zero_rows(a.dC, rows, N, a.ldc, io, s);
     if (e == hipSuccess) e = zero_bytes(a.dh0, Bn * D * N * pa, s);  // L = 0: y ignores h0
     return e;
   }

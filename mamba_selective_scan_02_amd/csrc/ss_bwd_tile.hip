@@ -113,15 +113,16 @@ __device__ __forceinline__ BTilePos btile_pos(const BwdArgs& a) {
 template <typename T, int NP>
 __device__ __forceinline__ void bstage(float (*sB)[BTS], float (*sC)[BTS], const T* B, const T* C,
                                        int64_t row0, int64_t nsteps,
-                                       int64_t N) {
+                                       int64_t N, int64_t ldb, int64_t ldc) {
   constexpr int ES = sizeof(T);
-  const auto rB = make_rsrc(B + row0 * N, nsteps * N * ES);
-  const auto rC = make_rsrc(C + row0 * N, nsteps * N * ES);
+  const auto rB = make_rsrc(B + row0 * ldb, rows_bytes(nsteps, ldb, N, ES));
+  const auto rC = make_rsrc(C + row0 * ldc, rows_bytes(nsteps, ldc, N, ES));
   for (int e = threadIdx.x; e < BTC * NP; e += kBT) {
     const int tt = e / NP, n = e % NP;
     const bool ok = n < N;
-    const int off = (tt * (int)N + (ok ? n : 0)) * ES;
-    const float vb = buf_ld<T>(rB, off, 0), vc = buf_ld<T>(rC, off, 0);
+    const int nn = ok ? n : 0;
+    const float vb = buf_ld<T>(rB, (tt * (int)ldb + nn) * ES, 0);
+    const float vc = buf_ld<T>(rC, (tt * (int)ldc + nn) * ES, 0);
     sB[n][tt] = ok ? vb : 0.0f;
     sC[n][tt] = ok ? vc : 0.0f;
   }
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
   const int64_t D = a.D, N = a.N, b = P.b, d = P.d;
   const int64_t nsteps = P.t1 - P.t0;
 
-  bstage<T, NP>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N);
+  bstage<T, NP>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N, a.ldb, a.ldc);
 
   // Sb is built two-level: per tile from its own start (E, sbl) and then
   // Sb += (decay of the chunk's earlier tiles) * sbl, the decay of a tile
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
   const int64_t D = a.D, N = a.N, K = a.K, b = P.b, d = P.d, k = P.k;
   const int64_t nsteps = P.t1 - P.t0;
 
-  bstage<T, NP>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N);
+  bstage<T, NP>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N, a.ldb, a.ldc);
 
   float A2[NS], An[NS], h[NS], dh[NS], dA_acc[NS];
 #pragma unroll

@@ -158,6 +158,12 @@ __device__ __forceinline__ SeqRows seq_rows(const int32_t* cu, int64_t b, int64_
   return {s, (e - s < L) ? e - s : L};
 }
 
+// Bytes from the first row of nrows rows of a [*, N] matrix whose rows lie
+// ld elements apart, to the end of the last row's N elements.
+__device__ __forceinline__ int64_t rows_bytes(int64_t nrows, int64_t ld, int64_t N, int es) {
+  return nrows > 0 ? ((nrows - 1) * ld + N) * es : 0;
+}
+
 // Chunk of sequence length len that holds its last step (0 when len = 0).
 __device__ __forceinline__ int64_t last_chunk(int64_t len, int64_t chunk_len) {
   return len > 0 ? (len - 1) / chunk_len : 0;
@@ -182,6 +188,7 @@ struct FwdArgs {
   int64_t chunk_len, K;    // chunk length and number of chunks
   const int32_t* cu;       // nullable: cu_seqlens [Bn+1] of a packed problem
   int64_t Lt;              // rows of the [rows, D] tensors (Bn*L when dense)
+  int64_t ldb, ldc;        // elements between consecutive rows of B / C (N when packed)
   int softplus;
   int param_dtype;
 };
@@ -227,6 +234,7 @@ struct BwdArgs {
   int64_t chunk_len, K, KG, nwgd;
   const int32_t* cu;       // nullable: cu_seqlens [Bn+1] of a packed problem
   int64_t Lt;              // rows of the [rows, D] tensors (Bn*L when dense)
+  int64_t ldb, ldc;        // elements between consecutive rows of B / C (N when packed)
   int softplus;
   int param_dtype;
   int io_dtype;

@@ -93,8 +93,9 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
   const T* dp = delta_in + sr.start * D + d;
   const T* zp = HAS_Z ? z_in + sr.start * D + d : up;
   T* yp = y_out + sr.start * D + d;
-  const T* Bp = B_in + sr.start * N + n0;
-  const T* Cp = C_in + sr.start * N + n0;
+  const int64_t ldb = a.ldb, ldc = a.ldc;
+  const T* Bp = B_in + sr.start * ldb + n0;
+  const T* Cp = C_in + sr.start * ldc + n0;
 
   // B / C rows, software-pipelined one step ahead (wave-uniform: SGPRs).
   // EXACT rows are prefetched as raw 32-bit words and converted at their use
@@ -105,8 +106,8 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
   using RowT = typename std::conditional<PAIRS, uint32_t, float>::type;
   auto fetch_rows = [&](int64_t t, RowT* Br, RowT* Cr) {
     if constexpr (PAIRS) {
-      const uint32_t* bw = reinterpret_cast<const uint32_t*>(Bp + t * N);
-      const uint32_t* cw = reinterpret_cast<const uint32_t*>(Cp + t * N);
+      const uint32_t* bw = reinterpret_cast<const uint32_t*>(Bp + t * ldb);
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(Cp + t * ldc);
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         Br[i] = bw[i];
@@ -116,8 +117,8 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const bool ok = EXACT || n0 + i < N;
-        Br[i] = ok ? ld(Bp, t * N + i) : 0.0f;
-        Cr[i] = (MODE == MODE_FULL && ok) ? ld(Cp, t * N + i) : 0.0f;
+        Br[i] = ok ? ld(Bp, t * ldb + i) : 0.0f;
+        Cr[i] = (MODE == MODE_FULL && ok) ? ld(Cp, t * ldc + i) : 0.0f;
       }
     }
   };
@@ -281,11 +282,12 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
 }
 
 // EXACT (N fills the bucket) reads whole B / C rows; for 16-bit types that
-// needs 4-byte aligned rows, i.e. 4-byte aligned B and C (N is even here).
+// needs 4-byte aligned rows: 4-byte aligned B and C and even row strides.
 template <typename T, int NS, int G>
 static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t s) {
   const bool rows_ok = sizeof(T) == 4 || ((reinterpret_cast<uintptr_t>(a.B) % 4 == 0) &&
-                                          (reinterpret_cast<uintptr_t>(a.C) % 4 == 0));
+                                          (reinterpret_cast<uintptr_t>(a.C) % 4 == 0) &&
+                                          a.ldb % 2 == 0 && a.ldc % 2 == 0);
   const bool exact = a.N == (int64_t)NS * G && rows_ok;
   if (a.z != nullptr)
     return exact ? launch_fwd_t<T, NS, G, true, true>(a, s) : launch_fwd_t<T, NS, G, false, true>(a, s);
@@ -384,8 +386,8 @@ __global__ __launch_bounds__(kBlock) void fwd_short(const T* __restrict__ u_in,
     const float x = ld(delta_in, i) + bv;
     const float dl = a.softplus ? softplus(x) : x;
     const float xu = dl * uu;
-    const T* Bt = B_in + (sr.start + t) * N;
-    const T* Ct = C_in + (sr.start + t) * N;
+    const T* Bt = B_in + (sr.start + t) * a.ldb;
+    const T* Ct = C_in + (sr.start + t) * a.ldc;
     float o = 0.0f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {

@@ -146,8 +146,9 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
   const auto rs_y = make_rsrc(y_out + row0, nsteps * D * ES);
   const int voff_own = (int)((g * D + d) * ES);
   const int soff_step = (int)(GL * D * ES);            // one 8-step tile
-  const auto rs_B = make_rsrc(B_in + (sr.start + t0) * N, nsteps * N * ES);
-  const auto rs_C = make_rsrc(C_in + (sr.start + t0) * N, nsteps * N * ES);
+  const auto rs_B = make_rsrc(B_in + (sr.start + t0) * a.ldb, rows_bytes(nsteps, a.ldb, N, ES));
+  const auto rs_C = make_rsrc(C_in + (sr.start + t0) * a.ldc, rows_bytes(nsteps, a.ldc, N, ES));
+  const int ldb = (int)a.ldb, ldc = (int)a.ldc;
 
   // ---- B / C staging (whole workgroup) ----
   float rb[RB], rc[RB];
@@ -158,11 +159,11 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
       const int e = tid + r * kBlockT;
       const int tt = e / NP, n = e % NP;
       const bool ok = n < N;                       // rows past the chunk read 0
-      const int off = ((trow + tt) * (int)N + (ok ? n : 0)) * ES;
-      const float vb = buf_ld<T>(rs_B, off, 0);
+      const int nn = ok ? n : 0;
+      const float vb = buf_ld<T>(rs_B, ((trow + tt) * ldb + nn) * ES, 0);
       rb[r] = ok ? vb : 0.0f;
       if (MODE == TMODE_FULL) {
-        const float vc = buf_ld<T>(rs_C, off, 0);
+        const float vc = buf_ld<T>(rs_C, ((trow + tt) * ldc + nn) * ES, 0);
         rc[r] = ok ? vc : 0.0f;
       }
     }
@@ -412,8 +413,8 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   rs_in[1] = make_rsrc(delta_in + row0, rbytes);
   if constexpr (NT == 3) rs_in[2] = make_rsrc(z_in + row0, rbytes);
   const auto rs_y = make_rsrc(y_out + row0, FULL ? rbytes : 0);
-  const auto rs_B = make_rsrc(B_in + (sr.start + t0) * N, nsteps * N * ES);
-  const auto rs_C = make_rsrc(C_in + (sr.start + t0) * N, nsteps * N * ES);
+  const auto rs_B = make_rsrc(B_in + (sr.start + t0) * a.ldb, rows_bytes(nsteps, a.ldb, N, ES));
+  const auto rs_C = make_rsrc(C_in + (sr.start + t0) * a.ldc, rows_bytes(nsteps, a.ldc, N, ES));
 
   // this thread's 16-byte piece of every stage: row pr, piece pq of the block's row
   const int pr = tid / W::LPR, pq = tid % W::LPR;
@@ -431,9 +432,10 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
     for (int r = 0; r < NPC; ++r) {
       const int pi = tid + r * kBlockT;
       const int q = pi % PB;                          // rows past the chunk read 0
-      const int off = (st * TB * NP + q * EPP) * ES;
       // PB is a multiple of 64, so B or C is a per-wave choice
       const bool isB = __builtin_amdgcn_readfirstlane(pi / PB) == 0;
+      const int ld = isB ? (int)a.ldb : (int)a.ldc;
+      const int off = ((st * TB + q / PPR) * ld + (q % PPR) * EPP) * ES;
       rbc[r] = __builtin_amdgcn_raw_buffer_load_b128(isB ? rs_B : rs_C, off, 0, 0);
     }
   };
@@ -573,7 +575,7 @@ hipError_t launch_fwd_carry(const FwdArgs& a, hipStream_t s);  // ss_fwd.hip
 static bool wide_ok(const FwdArgs& a, int es, int ns) {
   auto al = [](const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   return (a.D * es) % 16 == 0 && a.N == 8 * ns && al(a.u) && al(a.delta) && al(a.z) &&
-         al(a.y) && al(a.B) && al(a.C);
+         al(a.y) && al(a.B) && al(a.C) && (a.ldb * es) % 16 == 0 && (a.ldc * es) % 16 == 0;
 }
 
 template <typename T, int NS, bool HAS_Z>

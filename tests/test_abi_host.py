@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     lib = ss.load_library()
     names = _declared_functions()
     assert set(names) == {"ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0", "ss_bwd_h0",
-                          "ss_fwd_varlen", "ss_bwd_varlen", "ss_plan_query",
+                          "ss_fwd_varlen", "ss_bwd_varlen", "ss_fwd_strided",
+                          "ss_bwd_strided", "ss_plan_query",
                           "ss_status_string",
                           "ss_last_error"}
     for n in names:
@@ -120,6 +121,44 @@ def test_varlen_rules():
     # h0 / dh0 still come together
     assert ss.ss_bwd_varlen(d, P, 10, P, P, P, P, P, None, None, None, P, P, P, P, P, P, P,
                             None, None, None, None, P, 1 << 40, None) == ss.SS_ERR_INVALID_PROBLEM
+
+
+def test_strided_rules():
+    # every call below stops in validation (no launch): the workspace is
+    # always too small for shapes that pass the stride checks
+    q = ctypes.c_void_p(0x7F0000100000)
+
+    def fcall(d, ldb, ldc, cu=None, total=0):
+        return ss.ss_fwd_strided(d, cu, total, ldb, ldc, P, P, P, P, P, None, None, None, None,
+                                 P, None, q, 0, None)
+
+    def bcall(d, ldb, ldc):
+        return ss.ss_bwd_strided(d, None, 0, ldb, ldc, P, P, P, P, P, None, None, None, None, P,
+                                 P, P, P, P, P, None, None, None, None, P, 0, None)
+
+    d = _desc(B=1, L=4096, D=64, N=16)             # chunked: needs a forward workspace
+    assert ss.ss_workspace_size(d, 0) > 0
+    # strides below N
+    assert fcall(d, 15, 16) == ss.SS_ERR_INVALID_PROBLEM
+    assert "stride" in ss.ss_last_error()
+    assert fcall(d, 16, 8) == ss.SS_ERR_INVALID_PROBLEM
+    assert bcall(d, 16, 3) == ss.SS_ERR_INVALID_PROBLEM
+    # strides that fit pass validation up to the workspace check
+    assert fcall(d, 0, 0) == ss.SS_ERR_WORKSPACE_TOO_SMALL
+    assert fcall(d, 192, 200) == ss.SS_ERR_WORKSPACE_TOO_SMALL
+    assert bcall(d, 192, 192) == ss.SS_ERR_WORKSPACE_TOO_SMALL
+    # a single 4096-step chunk of a 2^20-element stride exceeds the tile
+    # kernels' 32-bit offsets; shorter forced chunks lift that
+    big = _desc(B=8, L=4096, D=5120, N=16, io=ss.SS_BF16)
+    assert ss.plan(big).n_chunks == 1
+    assert fcall(big, 1 << 20, 16) == ss.SS_ERR_UNSUPPORTED
+    assert "chunk_len" in ss.ss_last_error()
+    short = _desc(B=8, L=4096, D=5120, N=16, io=ss.SS_BF16, chunk=256)
+    assert fcall(short, 1 << 20, 16) == ss.SS_ERR_WORKSPACE_TOO_SMALL
+    # the varlen rules apply when cu_seqlens is given
+    assert fcall(d, 192, 192, P, -1) == ss.SS_ERR_INVALID_PROBLEM
+    assert "total_len" in ss.ss_last_error()
+    assert fcall(d, 192, 192, P, 4097) == ss.SS_ERR_INVALID_PROBLEM
 
 
 def test_status_strings():
