@@ -375,3 +375,7 @@ def np_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None, delta_so
     return {"du": du, "ddelta": dx, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz,
             "ddelta_bias": dx.sum(axis=(0, 1)) if delta_bias is not None else None,
             "dh0": carry if h0 is not None else None}
+
+
+# Complex-valued variant (numpy, complex128): see ``oracle/cplx.py``.
+from .cplx import bwd_complex, fwd_complex  # noqa: E402
