@@ -187,6 +187,35 @@ int ss_bwd_strided(const ss_desc* desc, const int32_t* cu_seqlens, int64_t total
                    void* ddelta_bias, void* dh0, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Complex-valued variant.  The scan page reserves complex variants without
+ * defining them (module docs, "Trailblazer scope"); here the recurrence of
+ * its "Algorithm summary" runs with A, B, C and the state complex and the
+ * rest real:
+ *     a = exp(dt * A[d,n])                      (complex; dt as above)
+ *     h = a * h + dt * u[b,t,d] * B[b,t,n]      (h = h0[b,d,n], or 0, before t = 0)
+ *     o = Re(sum_n C[b,t,n] * h[n]) + D[d] * u[b,t,d],   y = o * silu(z)
+ * Complex tensors are (re, im) pairs in a trailing axis of 2: A [D, N, 2] and
+ * h0 / last_state [B, D, N, 2] in param_dtype, B, C [B, L, N, 2] in io_dtype;
+ * the gradients dA, dB, dC, dh0 have the same layouts and hold
+ * (dL/dRe, dL/dIm) of each element.  Real tensors are as for ss_fwd_h0 /
+ * ss_bwd_h0.  A convention that keeps one state of each conjugate pair and
+ * doubles the real part is this operation with C scaled by 2.  The layouts
+ * are dense and packed (no cu_seqlens, no strides).  Workspace:
+ * ss_workspace_size_complex(desc, backward).  Validation, ownership,
+ * streams, determinism and the in-place state update (last_state == h0) are
+ * as for the real entry points. */
+size_t ss_workspace_size_complex(const ss_desc* desc, int32_t backward);
+int ss_fwd_complex(const ss_desc* desc, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, void* y, void* last_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int ss_bwd_complex(const ss_desc* desc, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, const void* dy, void* du,
+                   void* ddelta, void* dA, void* dB, void* dC, void* dD, void* dz,
+                   void* ddelta_bias, void* dh0, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* The schedule the library would use for a descriptor (informational). */
 typedef struct ss_plan {
   int32_t chunk_len;          /* time steps per chunk */

@@ -9,9 +9,11 @@ If the library is missing, every call raises: there is no fallback.
 Raw C entry points with the header's names: ``ss_workspace_size``,
 ``ss_fwd``, ``ss_bwd``, ``ss_fwd_h0``, ``ss_bwd_h0``, ``ss_fwd_varlen``,
 ``ss_bwd_varlen``, ``ss_fwd_strided``, ``ss_bwd_strided``,
+``ss_workspace_size_complex``, ``ss_fwd_complex``, ``ss_bwd_complex``,
 ``ss_plan_query``, ``ss_status_string``, ``ss_last_error``.  Tensor-level
 helpers: ``fwd``, ``bwd`` (both with an optional initial state ``h0``),
 ``fwd_varlen`` / ``bwd_varlen`` (packed variable-length sequences),
+``fwd_complex`` / ``bwd_complex`` (complex A, B, C and state),
 ``decode_step`` and the autograd function ``selective_scan``.  B and C (and
 the dB / dC outputs) may be row-strided views, e.g. column slices of the
 x-projection output; those calls go to the strided entry points.
@@ -27,7 +29,8 @@ import torch
 __all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "fwd_varlen", "bwd_varlen", "decode_step",
            "selective_scan", "plan", "workspace_size", "ss_workspace_size", "ss_fwd", "ss_bwd",
            "ss_fwd_h0", "ss_bwd_h0", "ss_fwd_varlen", "ss_bwd_varlen", "ss_fwd_strided",
-           "ss_bwd_strided",
+           "ss_bwd_strided", "ss_workspace_size_complex", "ss_fwd_complex", "ss_bwd_complex",
+           "fwd_complex", "bwd_complex",
            "ss_plan_query", "ss_status_string",
            "ss_last_error", "library_path", "load_library",
            "SS_OK", "SS_ERR_INVALID_PROBLEM", "SS_ERR_UNSUPPORTED",
@@ -91,6 +94,12 @@ def load_library(path: Optional[str] = None):
     lib.ss_fwd_strided.restype = ctypes.c_int
     lib.ss_bwd_strided.argtypes = [dp, vp, i64, i64, i64] + [vp] * 20 + [sz, vp]
     lib.ss_bwd_strided.restype = ctypes.c_int
+    lib.ss_workspace_size_complex.argtypes = [dp, ctypes.c_int32]
+    lib.ss_workspace_size_complex.restype = sz
+    lib.ss_fwd_complex.argtypes = [dp] + [vp] * 12 + [sz, vp]
+    lib.ss_fwd_complex.restype = ctypes.c_int
+    lib.ss_bwd_complex.argtypes = [dp] + [vp] * 20 + [sz, vp]
+    lib.ss_bwd_complex.restype = ctypes.c_int
     lib.ss_plan_query.argtypes = [dp, ctypes.c_int32, ctypes.POINTER(SsPlan)]
     lib.ss_plan_query.restype = ctypes.c_int
     lib.ss_status_string.argtypes = [ctypes.c_int]
@@ -168,6 +177,24 @@ def ss_bwd_strided(desc: SsDesc, cu_seqlens, total_len: int, ldb: int, ldc: int,
                                          int(ldc), u, delta, A, B, C, Dskip, z, delta_bias, h0,
                                          dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
                                          workspace, workspace_bytes, stream)
+
+
+def ss_workspace_size_complex(desc: SsDesc, backward: int) -> int:
+    return load_library().ss_workspace_size_complex(_ref(desc), int(backward))
+
+
+def ss_fwd_complex(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, h0, y, last_state,
+                   workspace, workspace_bytes: int, stream) -> int:
+    return load_library().ss_fwd_complex(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias,
+                                         h0, y, last_state, workspace, workspace_bytes, stream)
+
+
+def ss_bwd_complex(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, h0, dy, du, ddelta,
+                   dA, dB, dC, dD, dz, ddelta_bias, dh0, workspace, workspace_bytes: int,
+                   stream) -> int:
+    return load_library().ss_bwd_complex(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias,
+                                         h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
+                                         dh0, workspace, workspace_bytes, stream)
 
 
 def ss_plan_query(desc: SsDesc, backward: int, out: SsPlan) -> int:
@@ -393,6 +420,102 @@ def fwd_varlen(u, delta, A, B, C, cu_seqlens, max_seqlen: int, D=None, z=None,
     if st != SS_OK:
         _raise(st, who)
     return y, ls
+
+
+def _pairs(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    """A complex tensor as its (re, im) float pairs (a view); float tensors
+    with a trailing axis of 2 pass through."""
+    if t is None or not t.is_complex():
+        return t
+    return torch.view_as_real(t)
+
+
+def _complex_desc(u, A, delta_softplus, chunk_len) -> SsDesc:
+    if u.dim() != 3 or A.dim() != 3 or A.shape[-1] != 2:
+        raise ValueError("u must be [B, L, D] and A [D, N, 2] (re, im pairs) or complex [D, N]")
+    if u.dtype not in _DTYPE_ID or A.dtype not in _DTYPE_ID:
+        raise NotImplementedError("dtypes must be float32, float16 or bfloat16 (pairs)")
+    Bn, L, D = u.shape
+    return SsDesc(Bn, L, D, A.shape[1], 1 if delta_softplus else 0, _DTYPE_ID[u.dtype],
+                  _DTYPE_ID[A.dtype], int(chunk_len))
+
+
+def fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                delta_softplus: bool = True, h0=None, return_last_state: bool = False,
+                chunk_len: int = 0, last_state: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Complex-valued forward: A [D, N], B / C [B, L, N], h0 / last_state
+    [B, D, N] complex, given either as torch complex64 tensors or as float
+    tensors with a trailing (re, im) axis of 2; everything else as ``fwd``.
+    Returns (y [B, L, D] real, last_state as (re, im) pairs or None)."""
+    A, B, C, h0, last_state = (_pairs(t) for t in (A, B, C, h0, last_state))
+    desc = _complex_desc(u, A, delta_softplus, chunk_len)
+    dev, io, pa = u.device, u.dtype, A.dtype
+    Bn, L, Dd, N = desc.batch, desc.seqlen, desc.dim, desc.dstate
+    for t, name, shape, dt in ((u, "u", (Bn, L, Dd), io), (delta, "delta", (Bn, L, Dd), io),
+                               (A, "A", (Dd, N, 2), pa), (B, "B", (Bn, L, N, 2), io),
+                               (C, "C", (Bn, L, N, 2), io), (D, "D", (Dd,), pa),
+                               (z, "z", (Bn, L, Dd), io), (delta_bias, "delta_bias", (Dd,), pa),
+                               (h0, "h0", (Bn, Dd, N, 2), pa),
+                               (last_state, "last_state", (Bn, Dd, N, 2), pa)):
+        _check(t, name, shape, dt, dev)
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    y = torch.empty((Bn, L, Dd), dtype=io, device=dev)
+    ls = last_state
+    if ls is None and return_last_state:
+        ls = torch.empty((Bn, Dd, N, 2), dtype=pa, device=dev)
+    need = ss_workspace_size_complex(desc, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+    st = ss_fwd_complex(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                        _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls), _ptr(ws), need,
+                        _stream_of(dev))
+    if st != SS_OK:
+        _raise(st, "ss_fwd_complex")
+    return y, ls
+
+
+def bwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, dy=None,
+                delta_softplus: bool = True, h0=None, chunk_len: int = 0
+                ) -> Dict[str, Optional[torch.Tensor]]:
+    """Backward of ``fwd_complex`` for sum(dy * y): the dict of ``bwd`` with
+    dA / dB / dC / dh0 as (dL/dRe, dL/dIm) pairs in the layouts of A / B /
+    C / h0 (float pairs)."""
+    A, B, C, h0 = (_pairs(t) for t in (A, B, C, h0))
+    desc = _complex_desc(u, A, delta_softplus, chunk_len)
+    dev, io, pa = u.device, u.dtype, A.dtype
+    Bn, L, Dd, N = desc.batch, desc.seqlen, desc.dim, desc.dstate
+    for t, name, shape, dt in ((u, "u", (Bn, L, Dd), io), (delta, "delta", (Bn, L, Dd), io),
+                               (A, "A", (Dd, N, 2), pa), (B, "B", (Bn, L, N, 2), io),
+                               (C, "C", (Bn, L, N, 2), io), (D, "D", (Dd,), pa),
+                               (z, "z", (Bn, L, Dd), io), (delta_bias, "delta_bias", (Dd,), pa),
+                               (dy, "dy", (Bn, L, Dd), io), (h0, "h0", (Bn, Dd, N, 2), pa)):
+        _check(t, name, shape, dt, dev)
+    if dy is None:
+        raise ValueError("dy is required")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    out = {
+        "du": torch.empty((Bn, L, Dd), dtype=io, device=dev),
+        "ddelta": torch.empty((Bn, L, Dd), dtype=io, device=dev),
+        "dA": torch.empty((Dd, N, 2), dtype=pa, device=dev),
+        "dB": torch.empty((Bn, L, N, 2), dtype=io, device=dev),
+        "dC": torch.empty((Bn, L, N, 2), dtype=io, device=dev),
+        "dD": torch.empty((Dd,), dtype=pa, device=dev) if D is not None else None,
+        "dz": torch.empty((Bn, L, Dd), dtype=io, device=dev) if z is not None else None,
+        "ddelta_bias": torch.empty((Dd,), dtype=pa, device=dev) if delta_bias is not None else None,
+        "dh0": torch.empty((Bn, Dd, N, 2), dtype=pa, device=dev) if h0 is not None else None,
+    }
+    need = ss_workspace_size_complex(desc, 1)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = ss_bwd_complex(desc, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                        _ptr(delta_bias), _ptr(h0), _ptr(dy), _ptr(out["du"]),
+                        _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                        _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
+                        _ptr(out["dh0"]), _ptr(ws), ws.numel(), _stream_of(dev))
+    if st != SS_OK:
+        _raise(st, "ss_bwd_complex")
+    return out
 
 
 def decode_step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,

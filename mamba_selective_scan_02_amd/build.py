@@ -18,7 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libss.so")
-SOURCES = ["ss_api.cpp", "ss_fwd.hip", "ss_fwd_tile.hip", "ss_bwd.hip", "ss_bwd_tile.hip"]
+SOURCES = ["ss_api.cpp", "ss_fwd.hip", "ss_fwd_scan_f32.hip", "ss_fwd_scan_f16.hip",
+           "ss_fwd_scan_bf16.hip", "ss_fwd_tile.hip", "ss_bwd.hip", "ss_bwd_tile.hip",
+           "ss_cplx.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed FP32 instructions are disabled: the compiler would otherwise form

@@ -23,6 +23,8 @@ hipError_t launch_fwd(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_
 hipError_t launch_zero_param(void* p, int64_t n, int dtype, hipStream_t s);
 hipError_t launch_copy_param(void* dst, const void* src, int64_t n, int dtype, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, const Plan& p, int io_dtype, hipStream_t s);
+hipError_t launch_fwd_complex(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_t s);
+hipError_t launch_bwd_complex(const BwdArgs& a, const Plan& p, int io_dtype, hipStream_t s);
 }  // namespace ss
 
 namespace {
@@ -382,6 +384,133 @@ int ss_bwd_strided(const ss_desc* d, const int32_t* cu_seqlens, int64_t total_le
   return bwd_impl("ss_bwd_strided", d, cu_seqlens, total_len, ldb, ldc, u, delta, A, B, C,
                   Dskip, z, delta_bias, h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
                   dh0, workspace, workspace_bytes, stream);
+}
+
+size_t ss_workspace_size_complex(const ss_desc* d, int32_t backward) {
+  if (check_desc(d, "ss_workspace_size_complex") != SS_OK) return 0;
+  return ss::make_plan_complex(*d, backward != 0).ws_bytes;
+}
+
+int ss_fwd_complex(const ss_desc* d, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, void* y, void* last_state,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "ss_fwd_complex";
+  g_err[0] = 0;
+  int st = check_desc(d, who);
+  if (st != SS_OK) return st;
+  const int64_t Bn = d->batch, L = d->seqlen, D = d->dim, N = d->dstate;
+  const int64_t io = dtype_size(d->io_dtype), pa = dtype_size(d->param_dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PtrCheck pc{who};
+  pc.opt(last_state, "last_state", pa);
+  if (Bn * D * N > 0) pc.opt(h0, "h0", pa);
+  if (pc.status != SS_OK) return pc.status;
+  const int64_t state_elems = 2 * Bn * D * N;   // (re, im) pairs
+  const int64_t state_bytes = state_elems * pa;
+  const bool in_place = h0 && last_state == h0 && state_bytes > 0;
+  if (h0 && last_state && !in_place && overlap(h0, last_state, state_bytes))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: h0 and last_state must be the same buffer or "
+                "not overlap", who);
+  if (Bn * L * D == 0) {
+    if (L == 0 && last_state && state_bytes > 0)
+      return hip_status(h0 ? ss::launch_copy_param(last_state, h0, state_elems, d->param_dtype, s)
+                           : ss::launch_zero_param(last_state, state_elems, d->param_dtype, s),
+                        who);
+    return SS_OK;
+  }
+  pc.need(u, "u", io);
+  pc.need(delta, "delta", io);
+  pc.need(y, "y", io);
+  if (N > 0) {
+    pc.need(A, "A", pa);
+    pc.need(B, "B", io);
+    pc.need(C, "C", io);
+  }
+  pc.opt(Dskip, "D", pa);
+  pc.opt(z, "z", io);
+  pc.opt(delta_bias, "delta_bias", pa);
+  if (pc.status != SS_OK) return pc.status;
+  // In place (last_state == h0): one chunk, so that the only reader of an h0
+  // element is the lane that writes the same last_state element at its end.
+  ss_desc dd = *d;
+  if (in_place) dd.chunk_len = d->seqlen;
+  const ss::Plan p = ss::make_plan_complex(dd, false);
+  st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
+  if (st != SS_OK) return st;
+  ss::FwdArgs a{};
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C;
+  a.Dskip = Dskip; a.z = z; a.bias = delta_bias; a.y = y; a.last_state = last_state;
+  a.h0 = N > 0 ? h0 : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.chunk_state = p.K > 1 && N > 0 ? reinterpret_cast<float*>(ws + p.off_state) : nullptr;
+  a.Bn = Bn; a.L = L; a.D = D; a.N = N;
+  a.chunk_len = p.chunk_len; a.K = p.K;
+  a.Lt = Bn * L; a.ldb = 2 * N; a.ldc = 2 * N;
+  a.softplus = d->delta_softplus;
+  a.param_dtype = d->param_dtype;
+  return hip_status(ss::launch_fwd_complex(a, d->io_dtype, p.NS, p.G, s), who);
+}
+
+int ss_bwd_complex(const ss_desc* d, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, const void* dy, void* du,
+                   void* ddelta, void* dA, void* dB, void* dC, void* dD, void* dz,
+                   void* ddelta_bias, void* dh0, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  const char* who = "ss_bwd_complex";
+  g_err[0] = 0;
+  int st = check_desc(d, who);
+  if (st != SS_OK) return st;
+  if ((h0 == nullptr) != (dh0 == nullptr))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: h0 and dh0 must be both given or both omitted", who);
+  if ((Dskip == nullptr) != (dD == nullptr))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: D and dD must be both given or both omitted", who);
+  if ((z == nullptr) != (dz == nullptr))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: z and dz must be both given or both omitted", who);
+  if ((delta_bias == nullptr) != (ddelta_bias == nullptr))
+    return fail(SS_ERR_INVALID_PROBLEM,
+                "%s: delta_bias and ddelta_bias must be both given or both omitted", who);
+  const int64_t Bn = d->batch, L = d->seqlen, D = d->dim, N = d->dstate;
+  const int64_t io = dtype_size(d->io_dtype), pa = dtype_size(d->param_dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ss::Plan p = ss::make_plan_complex(*d, true);
+  PtrCheck pc{who};
+  if (Bn * L * D > 0) {
+    pc.need(u, "u", io); pc.need(delta, "delta", io); pc.need(dy, "dy", io);
+    pc.need(du, "du", io); pc.need(ddelta, "ddelta", io);
+    if (N > 0) {
+      pc.need(A, "A", pa); pc.need(B, "B", io); pc.need(C, "C", io);
+    }
+    pc.opt(z, "z", io); pc.opt(dz, "dz", io);
+  }
+  if (D * N > 0) pc.need(dA, "dA", pa);
+  if (Bn * L * N > 0) { pc.need(dB, "dB", io); pc.need(dC, "dC", io); }
+  pc.opt(Dskip, "D", pa); pc.opt(dD, "dD", pa);
+  pc.opt(delta_bias, "delta_bias", pa); pc.opt(ddelta_bias, "ddelta_bias", pa);
+  if (Bn * D * N > 0) { pc.opt(h0, "h0", pa); pc.opt(dh0, "dh0", pa); }
+  if (pc.status != SS_OK) return pc.status;
+  if (h0 && overlap(h0, dh0, 2 * Bn * D * N * pa))
+    return fail(SS_ERR_INVALID_PROBLEM, "%s: dh0 must not overlap h0", who);
+  st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
+  if (st != SS_OK) return st;
+  if (Bn * L * D == 0 && D * N == 0 && Bn * L * N == 0 && D == 0) return SS_OK;
+  const bool has_state = h0 && Bn * D * N > 0;
+  ss::BwdArgs a{};
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C;
+  a.Dskip = Dskip; a.z = z; a.bias = delta_bias; a.dy = dy;
+  a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC;
+  a.dD = dD; a.dz = dz; a.dbias = ddelta_bias;
+  a.h0 = has_state ? h0 : nullptr;
+  a.dh0 = has_state ? dh0 : nullptr;
+  a.ws = static_cast<char*>(workspace);
+  a.Bn = Bn; a.L = L; a.D = D; a.N = N;
+  a.chunk_len = p.chunk_len; a.K = p.K;
+  a.Lt = Bn * L; a.ldb = 2 * N; a.ldc = 2 * N;
+  a.softplus = d->delta_softplus;
+  a.param_dtype = d->param_dtype;
+  a.io_dtype = d->io_dtype;
+  return hip_status(ss::launch_bwd_complex(a, p, d->io_dtype, s), who);
 }
 
 const char* ss_status_string(int status) {

@@ -1,0 +1,728 @@
+// Complex-valued selective scan (forward and BPTT backward) for gfx950.
+//
+// The scan page (baracuda-kernels "src/attention/selective_scan.rs", module
+// docs, "Trailblazer scope") reserves complex variants without defining them.
+// The operation is its "Algorithm summary" with A, B, C and the state complex
+// and the output the real part of the readout:
+//   a = exp(dt A) = exp2(dt Re(A) log2 e) (cos(dt Im A), sin(dt Im A))
+//   h = a h + dt u B,   o = Re(sum_n C h) + D u,   y = o silu(z)
+// Complex tensors are (re, im) pairs in the last axis.  The backward is the
+// chain rule in real terms; with lam = dL/dRe(h) + i dL/dIm(h):
+//   lam_t = g_t conj(C_t) + conj(a_{t+1}) lam_{t+1}
+//   dB_t = dt u lam_t,   dC_t = g_t conj(h_t),   dw_t = conj(a_t) lam_t conj(h_{t-1})
+//   dA += dt dw_t,   ddt_t = sum_n Re(conj(A) dw_t) + u sum_n Re(conj(B_t) lam_t)
+//   du_t = dt sum_n Re(conj(B_t) lam_t) + D g_t,   dh0 = conj(a_0) lam_0
+// and gradients of complex inputs are returned as (dL/dRe, dL/dIm).
+//
+// Forward: G lanes per channel, each holding NS complex states in VGPRs; the
+// per-step scalar work is repeated on the G lanes; the readout is summed
+// across them with lane shuffles.  Long sequences with few channels use the
+// same two-level chunked scan as the real path (summaries from zero, a carry
+// over chunks, then a final pass), except that a chunk's decay is the running
+// product of its steps' decays rather than exp(A * sum dt): for complex A the
+// closed form turns the rounding of sum dt into a phase error |Im A| times as
+// large, which over long chunks exceeds the sequential scan's own rounding.
+// Backward: the same stages as the real general backward (summary, carry,
+// main, fixed-order finalizes) with one lane per channel, one state at a time,
+// 8-step chunks in registers, B / C of a chunk in LDS, and dB / dC summed over
+// the workgroup's 256 channels in LDS in a fixed order.  No atomics: every
+// output is bitwise reproducible.
+#include "ss_device.h"
+#include "ss_plan.h"
+
+namespace ss {
+
+namespace {
+
+constexpr int kCB = 256;               // threads per workgroup
+constexpr int CT = kCplxBwdTile;       // backward steps per chunk (max)
+constexpr int kCRedStride = 257;       // LDS row stride of the dB/dC reduction
+
+// a - 1 = exp(dt * (Ar + i Ai)) - 1 = (mr, mi), each part rounded once from
+// double.  The recurrences use a - 1 rather than a (h + ((a - 1) h + x)):
+// with small dt a is within a few ulps of 1, and rounding a itself would move
+// the effective decay rate coherently over every step of a state that decays
+// over thousands of steps.  The decay must also be unbiased: along slowly
+// decaying states the steps' errors accumulate coherently and a channel's
+// states interfere, so a tenth of an ulp of bias in |a| (what the float exp2
+// and sincos give together) triples the error of y on long sequences.
+// dt * Ar and dt * Ai are exact in double; exp and sincos are the device
+// library's double-precision functions.
+__device__ __forceinline__ void cexpm1_dt(float dt, float ar, float ai, float& mr, float& mi) {
+  const double m = exp((double)dt * (double)ar);
+  double s, c;
+  sincos((double)dt * (double)ai, &s, &c);
+  mr = (float)(m * c - 1.0);
+  mi = (float)(m * s);
+}
+
+// h <- a h + (xr, xi) = h + ((a - 1) h + x), with (mr, mi) = a - 1.
+__device__ __forceinline__ void cstep(float mr, float mi, float xr, float xi, float& hr,
+                                      float& hi) {
+  const float nr = hr + __builtin_fmaf(mr, hr, __builtin_fmaf(-mi, hi, xr));
+  const float ni = hi + __builtin_fmaf(mr, hi, __builtin_fmaf(mi, hr, xi));
+  hr = nr;
+  hi = ni;
+}
+
+// dt, sigmoid and the gate, each rounded once from double.  These are per
+// (step, channel), not per state, so double costs little here; a bias in dt
+// would shift the phase sum(dt Im A) of long-lived rotating states coherently.
+__device__ __forceinline__ float softplus_rn(float x) {
+  const double xd = x;
+  return (float)(xd > 0.0 ? xd + log1p(exp(-xd)) : log1p(exp(xd)));
+}
+__device__ __forceinline__ float sigmoid_rn(float x) { return (float)(1.0 / (1.0 + exp(-(double)x))); }
+__device__ __forceinline__ float silu_gate(float z) { return (float)((double)z / (1.0 + exp(-(double)z))); }
+
+// ------------------------------------------------------------------ forward
+
+// SUMMARY (FULL = false): chunk k < K-1 from a zero state, writes the chunk's
+// end state S and decay product P to chunk_state record k.  FULL: chunk k from
+// h0 (k = 0) or the carried state (record k-1), writes y and, on the last
+// chunk, last_state.
+template <typename T, int NS, int G, bool FULL>
+__global__ __launch_bounds__(kCB) void cfwd(const T* __restrict__ u_in,
+                                            const T* __restrict__ delta_in,
+                                            const T* __restrict__ B_in,
+                                            const T* __restrict__ C_in,
+                                            const T* __restrict__ z_in, T* __restrict__ y_out,
+                                            const FwdArgs a) {
+  constexpr int CPB = kCB / G;
+  const int64_t D = a.D, N = a.N, L = a.L, K = a.K;
+  const int64_t nbd = (D + CPB - 1) / CPB;
+  const int64_t nk = FULL ? K : K - 1;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t k = blk % nk;
+  const int64_t b = blk / nk;
+  const int g = (int)(threadIdx.x % G);
+  const int64_t d_raw = db * CPB + threadIdx.x / G;
+  const bool active = d_raw < D;
+  const int64_t d = active ? d_raw : D - 1;
+  const int n0 = g * NS;
+  const int pd = a.param_dtype;
+
+  // P: the chunk's decay product minus 1 (summary only)
+  float Ar[NS], Ai[NS], hr[NS], hi[NS], Pr[NS], Pi[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int64_t n = n0 + i;
+    const bool ok = n < N;
+    const int64_t ai = 2 * (d * N + n);
+    Ar[i] = ok ? ld_param(a.A, ai, pd) : 0.0f;
+    Ai[i] = ok ? ld_param(a.A, ai + 1, pd) : 0.0f;
+    hr[i] = 0.0f;
+    hi[i] = 0.0f;
+    Pr[i] = 0.0f;
+    Pi[i] = 0.0f;
+    if (FULL && ok) {
+      if (k > 0) {
+        const float* st = a.chunk_state + 4 * (((b * K + (k - 1)) * N + n) * D + d);
+        hr[i] = st[0];
+        hi[i] = st[1];
+      } else if (a.h0) {
+        const int64_t hidx = 2 * ((b * D + d) * N + n);
+        hr[i] = ld_param(a.h0, hidx, pd);
+        hi[i] = ld_param(a.h0, hidx + 1, pd);
+      }
+    }
+  }
+  const float bv = a.bias ? ld_param(a.bias, d, pd) : 0.0f;
+  const float Dv = a.Dskip ? ld_param(a.Dskip, d, pd) : 0.0f;
+  const bool has_z = z_in != nullptr, sp = a.softplus != 0;
+  const int64_t t0 = k * a.chunk_len;
+  const int64_t t1 = (t0 + a.chunk_len < L) ? t0 + a.chunk_len : L;
+  const T* up = u_in + b * L * D + d;
+  const T* dp = delta_in + b * L * D + d;
+  const T* zp = has_z ? z_in + b * L * D + d : up;
+  T* yp = y_out + b * L * D + d;
+
+  for (int64_t t = t0; t < t1; ++t) {
+    const float uu = ld(up, t * D);
+    const float x = ld(dp, t * D) + bv;
+    const float dt = sp ? softplus_rn(x) : x;
+    const float xu = dt * uu;
+    const T* Bt = B_in + 2 * ((b * L + t) * N + n0);
+    const T* Ct = C_in + 2 * ((b * L + t) * N + n0);
+    float o = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (n0 + i < N) {
+        const float br = ld(Bt, 2 * i), bi = ld(Bt, 2 * i + 1);
+        float mr, mi;
+        cexpm1_dt(dt, Ar[i], Ai[i], mr, mi);
+        cstep(mr, mi, xu * br, xu * bi, hr[i], hi[i]);
+        if (FULL) {
+          const float cr = ld(Ct, 2 * i), ci = ld(Ct, 2 * i + 1);
+          o = __builtin_fmaf(cr, hr[i], __builtin_fmaf(-ci, hi[i], o));
+        } else {
+          // (1 + P)(1 + m) - 1 = P + (P m + m)
+          cstep(mr, mi, mr, mi, Pr[i], Pi[i]);
+        }
+      }
+    }
+    if (FULL) {
+#pragma unroll
+      for (int s = 1; s < G; s <<= 1) o += __shfl_xor(o, s, 64);
+      if (g == 0 && active) {
+        float yv = __builtin_fmaf(Dv, uu, o);
+        if (has_z) yv *= silu_gate(ld(zp, t * D));
+        yp[t * D] = from_f32<T>(yv);
+      }
+    }
+  }
+  if (!active) return;
+  if (!FULL) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int64_t n = n0 + i;
+      if (n < N) {
+        float* st = a.chunk_state + 4 * (((b * K + k) * N + n) * D + d);
+        *reinterpret_cast<float4*>(st) = make_float4(hr[i], hi[i], Pr[i], Pi[i]);
+      }
+    }
+  } else if (a.last_state && k == K - 1) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int64_t n = n0 + i;
+      if (n < N) {
+        const int64_t o = 2 * ((b * D + d) * N + n);
+        st_param(a.last_state, o, pd, hr[i]);
+        st_param(a.last_state, o + 1, pd, hi[i]);
+      }
+    }
+  }
+}
+
+// Thread per (b, n, d), d fastest: the state part of chunk_state record k (the
+// chunk-k end state from zero) becomes the state entering chunk k+1:
+// h_in(k+1) = P_k h_in(k) + S_k,  h_in(0) = h0 or 0 (the record holds P_k - 1).
+__global__ __launch_bounds__(kCB) void cfwd_carry(const FwdArgs a) {
+  const int64_t D = a.D, N = a.N, K = a.K;
+  const int64_t nbd = (D + kCB - 1) / kCB;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t n = blk % N;
+  const int64_t b = blk / N;
+  const int64_t d = db * kCB + threadIdx.x;
+  if (d >= D) return;
+  const int pd = a.param_dtype;
+  float hr = 0.0f, hi = 0.0f;
+  if (a.h0) {
+    hr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
+    hi = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
+  }
+  for (int64_t k = 0; k < K - 1; ++k) {
+    float* st = a.chunk_state + 4 * (((b * K + k) * N + n) * D + d);
+    const float4 r = *reinterpret_cast<const float4*>(st);   // S, P - 1
+    cstep(r.z, r.w, r.x, r.y, hr, hi);
+    st[0] = hr;
+    st[1] = hi;
+  }
+}
+
+template <typename T, int NS, int G>
+hipError_t launch_cfwd_t(const FwdArgs& a, hipStream_t s) {
+  constexpr int CPB = kCB / G;
+  const int64_t nbd = (a.D + CPB - 1) / CPB;
+  const T* U = static_cast<const T*>(a.u);
+  const T* DL = static_cast<const T*>(a.delta);
+  const T* Bm = static_cast<const T*>(a.B);
+  const T* Cm = static_cast<const T*>(a.C);
+  const T* Z = static_cast<const T*>(a.z);
+  T* Y = static_cast<T*>(a.y);
+  hipError_t e;
+  if (a.K > 1) {
+    cfwd<T, NS, G, false><<<dim3((unsigned)(a.Bn * (a.K - 1) * nbd)), dim3(kCB), 0, s>>>(
+        U, DL, Bm, Cm, Z, Y, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.N > 0) {
+      const int64_t nc = (a.D + kCB - 1) / kCB;
+      cfwd_carry<<<dim3((unsigned)(a.Bn * a.N * nc)), dim3(kCB), 0, s>>>(a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  cfwd<T, NS, G, true><<<dim3((unsigned)(a.Bn * a.K * nbd)), dim3(kCB), 0, s>>>(
+      U, DL, Bm, Cm, Z, Y, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_cfwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s) {
+  if (gl == 1) {
+    switch (ns) {
+      case 1: return launch_cfwd_t<T, 1, 1>(a, s);
+      case 2: return launch_cfwd_t<T, 2, 1>(a, s);
+      case 4: return launch_cfwd_t<T, 4, 1>(a, s);
+      case 8: return launch_cfwd_t<T, 8, 1>(a, s);
+      case 16: return launch_cfwd_t<T, 16, 1>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (ns != 16) return hipErrorInvalidValue;
+  switch (gl) {
+    case 2: return launch_cfwd_t<T, 16, 2>(a, s);
+    case 4: return launch_cfwd_t<T, 16, 4>(a, s);
+    case 8: return launch_cfwd_t<T, 16, 8>(a, s);
+    case 16: return launch_cfwd_t<T, 16, 16>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ----------------------------------------------------------------- backward
+
+// B and C of one chunk as complex [n][tt] pairs in LDS; steps past the chunk
+// are zero (their dt is zero too, so they are identity steps).
+template <typename Tio>
+__device__ __forceinline__ void load_cbc_tile(float* sB, float* sC, const Tio* B, const Tio* C,
+                                              int64_t row0, int nt, int64_t N) {
+  const int64_t total = N * CT;
+  for (int64_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int64_t tt = idx / N, n = idx % N;   // n fastest: coalesced reads
+    float br = 0.0f, bi = 0.0f, cr = 0.0f, ci = 0.0f;
+    if (tt < nt) {
+      const int64_t gi = 2 * ((row0 + tt) * N + n);
+      br = ld(B, gi);
+      bi = ld(B, gi + 1);
+      cr = ld(C, gi);
+      ci = ld(C, gi + 1);
+    }
+    const int64_t li = 2 * (n * CT + tt);
+    sB[li] = br;
+    sB[li + 1] = bi;
+    sC[li] = cr;
+    sC[li + 1] = ci;
+  }
+}
+
+// Per chunk from zero: the end state S, E = prod conj(a_r) over the chunk (the
+// conjugate of its decay; stored as E - 1) and the reverse summary
+// Sb = sum_s (prod_{r<=s} conj(a_r)) g_s conj(C_s).
+template <typename Tio>
+__global__ __launch_bounds__(kChannelsPerBlock) void cbwd_summary(const BwdArgs a) {
+  extern __shared__ float smem[];
+  float* sB = smem;
+  float* sC = smem + 2 * a.N * CT;
+  const int64_t nbd = a.nwgd;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t k = blk % a.K;
+  const int64_t b = blk / a.K;
+  const int64_t L = a.L, D = a.D, N = a.N;
+  const int pd = a.param_dtype;
+  const int64_t d_raw = db * kChannelsPerBlock + threadIdx.x;
+  const bool active = d_raw < D;
+  const int64_t d = active ? d_raw : D - 1;
+  const int64_t t0 = k * a.chunk_len;
+  const int nt = (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
+
+  load_cbc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C), b * L + t0,
+                nt, N);
+
+  const float bv = a.bias ? ld_param(a.bias, d, pd) : 0.0f;
+  const bool has_z = a.z != nullptr, sp = a.softplus != 0;
+  const Tio* up = static_cast<const Tio*>(a.u) + b * L * D + d;
+  const Tio* dp = static_cast<const Tio*>(a.delta) + b * L * D + d;
+  const Tio* zp = has_z ? static_cast<const Tio*>(a.z) + b * L * D + d : up;
+  const Tio* yp = static_cast<const Tio*>(a.dy) + b * L * D + d;
+  float dl[CT], xu[CT], gg[CT];
+#pragma unroll
+  for (int tt = 0; tt < CT; ++tt) {
+    const bool ok = tt < nt;
+    const int64_t t = t0 + (ok ? tt : nt - 1);
+    const float uu = ld(up, t * D), x = ld(dp, t * D) + bv;
+    const float dlv = sp ? softplus_rn(x) : x;
+    float g = ld(yp, t * D);
+    if (has_z) g *= silu_gate(ld(zp, t * D));
+    dl[tt] = ok ? dlv : 0.0f;
+    xu[tt] = ok ? dlv * uu : 0.0f;
+    gg[tt] = ok ? g : 0.0f;
+  }
+  __syncthreads();
+
+  for (int64_t n = 0; n < N; ++n) {
+    const float ar = ld_param(a.A, 2 * (d * N + n), pd);
+    const float ai = ld_param(a.A, 2 * (d * N + n) + 1, pd);
+    const float* bn = sB + 2 * n * CT;
+    const float* cn = sC + 2 * n * CT;
+    // E is carried as E - 1
+    float hr = 0.0f, hi = 0.0f, Er = 0.0f, Ei = 0.0f, Sr = 0.0f, Si = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < CT; ++tt) {
+      float mr, mi;
+      cexpm1_dt(dl[tt], ar, ai, mr, mi);
+      cstep(mr, mi, xu[tt] * bn[2 * tt], xu[tt] * bn[2 * tt + 1], hr, hi);
+      // E <- E conj(a):  (1 + E)(1 + conj(m)) - 1
+      cstep(mr, -mi, mr, -mi, Er, Ei);
+      // Sb += E * w = w + (E - 1) w,  w = g conj(C)
+      const float wr = gg[tt] * cn[2 * tt], wi = -gg[tt] * cn[2 * tt + 1];
+      Sr += __builtin_fmaf(Er, wr, __builtin_fmaf(-Ei, wi, wr));
+      Si += __builtin_fmaf(Er, wi, __builtin_fmaf(Ei, wr, wi));
+    }
+    if (active) {
+      const int64_t o = ((b * a.K + k) * N + n) * D + d;
+      *reinterpret_cast<float4*>(a.fstate + 4 * o) = make_float4(hr, hi, Er, Ei);
+      a.bstate[2 * o] = Sr;
+      a.bstate[2 * o + 1] = Si;
+    }
+  }
+}
+
+// Thread per (b, n, d), d fastest.  Forward chain over k = 0 .. K-2 (the
+// state part of fstate record k becomes the state entering chunk k+1,
+// h = P_k h + S_k with P_k = conj(E_k)) and reverse chain over k = K-1 .. 1
+// (bstate slot k becomes the adjoint handed to the end of chunk k-1):
+// c_{k-1} = conj(P_k) c_k + Sb_k = E_k c_k + Sb_k.  Records hold E_k - 1.
+__global__ __launch_bounds__(kChannelsPerBlock) void cbwd_carry(const BwdArgs a) {
+  const int64_t D = a.D, N = a.N, K = a.K;
+  const int64_t nbd = (D + kChannelsPerBlock - 1) / kChannelsPerBlock;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t n = blk % N;
+  const int64_t b = blk / N;
+  const int64_t d = db * kChannelsPerBlock + threadIdx.x;
+  if (d >= D) return;
+  const int pd = a.param_dtype;
+  float hr = 0.0f, hi = 0.0f, cr = 0.0f, ci = 0.0f;
+  if (a.h0) {
+    hr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
+    hi = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
+  }
+  for (int64_t j = 0; j < K - 1; ++j) {
+    float* fs = a.fstate + 4 * (((b * K + j) * N + n) * D + d);
+    const float4 r = *reinterpret_cast<const float4*>(fs);   // S, E - 1 = conj(P) - 1
+    cstep(r.z, -r.w, r.x, r.y, hr, hi);                       // h = P h + S
+    fs[0] = hr;
+    fs[1] = hi;
+    const int64_t jj = K - 1 - j;
+    const float* fj = a.fstate + 4 * (((b * K + jj) * N + n) * D + d);
+    float* bs = a.bstate + 2 * (((b * K + jj) * N + n) * D + d);
+    cstep(fj[2], fj[3], bs[0], bs[1], cr, ci);                // c = E c + Sb
+    bs[0] = cr;
+    bs[1] = ci;
+  }
+}
+
+template <typename Tio>
+__global__ __launch_bounds__(kChannelsPerBlock) void cbwd_main(const BwdArgs a) {
+  extern __shared__ float smem[];
+  float* sB = smem;
+  float* sC = smem + 2 * a.N * CT;
+  float* red = smem + 4 * a.N * CT;  // [32][kCRedStride]
+  const int tid = threadIdx.x;
+  const int64_t nbd = a.nwgd;
+  int64_t blk = blockIdx.x;
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t kg = blk % a.KG;
+  const int64_t b = blk / a.KG;
+  const int64_t L = a.L, D = a.D, N = a.N, K = a.K;
+  const int pd = a.param_dtype;
+  const int64_t d_raw = db * kChannelsPerBlock + tid;
+  const bool active = d_raw < D;
+  const int64_t d = active ? d_raw : D - 1;
+  const float bv = a.bias ? ld_param(a.bias, d, pd) : 0.0f;
+  const float Dv = a.Dskip ? ld_param(a.Dskip, d, pd) : 0.0f;
+  const bool has_z = a.z != nullptr, has_D = a.Dskip != nullptr, sp = a.softplus != 0;
+  const Tio* up = static_cast<const Tio*>(a.u) + b * L * D + d;
+  const Tio* dp = static_cast<const Tio*>(a.delta) + b * L * D + d;
+  const Tio* zp = has_z ? static_cast<const Tio*>(a.z) + b * L * D + d : up;
+  const Tio* yp = static_cast<const Tio*>(a.dy) + b * L * D + d;
+  Tio* dup = static_cast<Tio*>(a.du) + b * L * D + d;
+  Tio* ddp = static_cast<Tio*>(a.ddelta) + b * L * D + d;
+  Tio* dzp = has_z ? static_cast<Tio*>(a.dz) + b * L * D + d : dup;
+
+  // reduction lane roles: row rv = which * CT + tt (which: dB re, dB im,
+  // dC re, dC im), channel slice rp
+  const int rv = tid >> 3, rp = tid & 7;
+  float dD_acc = 0.0f, db_acc = 0.0f;
+  const int64_t k_lo = kg * kBwdChunksPerGroup;
+  const int64_t k_hi = (k_lo + kBwdChunksPerGroup < K) ? k_lo + kBwdChunksPerGroup : K;
+
+  for (int64_t k = k_hi - 1; k >= k_lo; --k) {
+    const int64_t t0 = k * a.chunk_len;
+    const int nt = (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
+    __syncthreads();  // previous chunk's tile readers are done
+    load_cbc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C),
+                  b * L + t0, nt, N);
+
+    float uu[CT], dl[CT], xu[CT], gg[CT], gz[CT], sx[CT], oo[CT], ddl[CT], dua[CT];
+#pragma unroll
+    for (int tt = 0; tt < CT; ++tt) {
+      const bool ok = tt < nt;
+      const int64_t t = t0 + (ok ? tt : nt - 1);
+      const float u_ = ld(up, t * D), x = ld(dp, t * D) + bv, dy = ld(yp, t * D);
+      float dlv, sxv;
+      if (sp) { dlv = softplus_rn(x); sxv = sigmoid_rn(x); } else { dlv = x; sxv = 1.0f; }
+      float g = dy, gzv = 0.0f;
+      if (has_z) {
+        const float zz = ld(zp, t * D), s = sigmoid_rn(zz);
+        g = dy * zz * s;
+        gzv = dy * s * __builtin_fmaf(zz, 1.0f - s, 1.0f);
+      }
+      uu[tt] = ok ? u_ : 0.0f;
+      dl[tt] = ok ? dlv : 0.0f;
+      xu[tt] = ok ? dlv * u_ : 0.0f;
+      gg[tt] = ok ? g : 0.0f;
+      gz[tt] = gzv;
+      sx[tt] = sxv;
+      oo[tt] = 0.0f;
+      ddl[tt] = 0.0f;
+      dua[tt] = 0.0f;
+    }
+    __syncthreads();  // tile visible
+
+    for (int64_t n = 0; n < N; ++n) {
+      const int64_t ai_ = 2 * (d * N + n);
+      const float Ar = ld_param(a.A, ai_, pd), Ai = ld_param(a.A, ai_ + 1, pd);
+      float hinr = 0.0f, hini = 0.0f;
+      if (k > 0) {
+        const float* fs = a.fstate + 4 * (((b * K + (k - 1)) * N + n) * D + d);
+        hinr = fs[0];
+        hini = fs[1];
+      } else if (a.h0) {
+        hinr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
+        hini = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
+      }
+      float dhr = 0.0f, dhi = 0.0f;
+      if (k < K - 1) {
+        const float* bs = a.bstate + 2 * (((b * K + (k + 1)) * N + n) * D + d);
+        dhr = bs[0];
+        dhi = bs[1];
+      }
+      const float* bn = sB + 2 * n * CT;
+      const float* cn = sC + 2 * n * CT;
+      float hsr[CT], hsi[CT], ahr[CT], ahi[CT];   // states, a - 1
+      float pr = hinr, pi = hini;
+#pragma unroll
+      for (int tt = 0; tt < CT; ++tt) {
+        float mr, mi;
+        cexpm1_dt(dl[tt], Ar, Ai, mr, mi);
+        cstep(mr, mi, xu[tt] * bn[2 * tt], xu[tt] * bn[2 * tt + 1], pr, pi);
+        hsr[tt] = pr;
+        hsi[tt] = pi;
+        ahr[tt] = mr;
+        ahi[tt] = mi;
+        oo[tt] = __builtin_fmaf(cn[2 * tt], pr, __builtin_fmaf(-cn[2 * tt + 1], pi, oo[tt]));
+      }
+      float vBr[CT], vBi[CT], vCr[CT], vCi[CT];
+      float dAr = 0.0f, dAi = 0.0f;
+#pragma unroll
+      for (int tt = CT - 1; tt >= 0; --tt) {
+        // lam = dh + g conj(C)
+        const float lr = __builtin_fmaf(gg[tt], cn[2 * tt], dhr);
+        const float li = __builtin_fmaf(-gg[tt], cn[2 * tt + 1], dhi);
+        vCr[tt] = gg[tt] * hsr[tt];
+        vCi[tt] = -gg[tt] * hsi[tt];
+        vBr[tt] = lr * xu[tt];
+        vBi[tt] = li * xu[tt];
+        dua[tt] = __builtin_fmaf(bn[2 * tt], lr, __builtin_fmaf(bn[2 * tt + 1], li, dua[tt]));
+        // m = conj(a) lam = lam + conj(a - 1) lam
+        float mr = lr, mi = li;
+        cstep(ahr[tt], -ahi[tt], 0.0f, 0.0f, mr, mi);
+        // dw = m conj(h_{t-1})
+        const float qr = tt > 0 ? hsr[tt - 1] : hinr;
+        const float qi = tt > 0 ? hsi[tt - 1] : hini;
+        const float wr = __builtin_fmaf(mr, qr, mi * qi);
+        const float wi = __builtin_fmaf(mi, qr, -mr * qi);
+        ddl[tt] = __builtin_fmaf(Ar, wr, __builtin_fmaf(Ai, wi, ddl[tt]));
+        dAr = __builtin_fmaf(wr, dl[tt], dAr);
+        dAi = __builtin_fmaf(wi, dl[tt], dAi);
+        dhr = mr;
+        dhi = mi;
+      }
+      if (active) {
+        float* pa = a.part_dA + 2 * (((b * a.KG + kg) * N + n) * D + d);
+        if (k == k_hi - 1) {
+          pa[0] = dAr;
+          pa[1] = dAi;
+        } else {
+          pa[0] += dAr;
+          pa[1] += dAi;
+        }
+        // after step 0 of chunk 0, dh is dL/dh_{-1}
+        if (k == 0 && a.dh0) {
+          st_param(a.dh0, 2 * ((b * D + d) * N + n), pd, dhr);
+          st_param(a.dh0, 2 * ((b * D + d) * N + n) + 1, pd, dhi);
+        }
+      }
+      // dB / dC for this n: sums over the workgroup's channels in LDS.
+      // Inactive (tail) lanes contribute zero.
+#pragma unroll
+      for (int tt = 0; tt < CT; ++tt) {
+        red[(0 * CT + tt) * kCRedStride + tid] = active ? vBr[tt] : 0.0f;
+        red[(1 * CT + tt) * kCRedStride + tid] = active ? vBi[tt] : 0.0f;
+        red[(2 * CT + tt) * kCRedStride + tid] = active ? vCr[tt] : 0.0f;
+        red[(3 * CT + tt) * kCRedStride + tid] = active ? vCi[tt] : 0.0f;
+      }
+      __syncthreads();
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s += red[rv * kCRedStride + rp * 32 + ((i + 8 * rp) & 31)];
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      s += __shfl_xor(s, 4, 64);
+      if (rp == 0) {
+        const int which = rv / CT, tt = rv % CT;
+        if (tt < nt)
+          a.part_bc[(((b * L + t0 + tt) * a.nwgd + db) * 2 + (which >> 1)) * 2 * N + 2 * n +
+                    (which & 1)] = s;
+      }
+      __syncthreads();  // red free for the next n
+    }
+
+#pragma unroll
+    for (int tt = 0; tt < CT; ++tt) {
+      if (tt < nt && active) {
+        const int64_t t = t0 + tt;
+        const float du = __builtin_fmaf(dl[tt], dua[tt], has_D ? gg[tt] * Dv : 0.0f);
+        const float dde = __builtin_fmaf(uu[tt], dua[tt], ddl[tt]);
+        const float dx = dde * sx[tt];
+        dup[t * D] = from_f32<Tio>(du);
+        ddp[t * D] = from_f32<Tio>(dx);
+        if (has_z) dzp[t * D] = from_f32<Tio>(gz[tt] * __builtin_fmaf(Dv, uu[tt], oo[tt]));
+        db_acc += dx;
+        dD_acc = __builtin_fmaf(gg[tt], uu[tt], dD_acc);
+      }
+    }
+  }
+  if (active) {
+    a.part_dD[(b * a.KG + kg) * D + d] = dD_acc;
+    a.part_db[(b * a.KG + kg) * D + d] = db_acc;
+  }
+}
+
+// Fixed-order sum of `count` partials p[0], p[stride], ...
+__device__ __forceinline__ float csum_ordered(const float* p, int64_t count, int64_t stride) {
+  float s = 0.0f;
+  for (int64_t j = 0; j < count; ++j) s += p[j * stride];
+  return s;
+}
+
+// dB, dC [b, t, n, c] = sums over the channel blocks in block order.
+template <typename Tio>
+__global__ void cbwd_finalize_bc(const BwdArgs a) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // ((b*L + t)*N + n)*2 + c
+  const int64_t N = a.N;
+  if (i >= a.Bn * a.L * N * 2) return;
+  const int64_t c = i & 1, n = (i >> 1) % N, bt = (i >> 1) / N;
+  const float* p = a.part_bc + bt * a.nwgd * 4 * N + 2 * n + c;
+  static_cast<Tio*>(a.dB)[i] = from_f32<Tio>(csum_ordered(p, a.nwgd, 4 * N));
+  static_cast<Tio*>(a.dC)[i] = from_f32<Tio>(csum_ordered(p + 2 * N, a.nwgd, 4 * N));
+}
+
+// dA[d, n, c] = sum over (b, chunk group) in that order; dD, ddelta_bias
+// likewise.  Thread per (n', d), d fastest, n' < max(N, 1).
+__global__ void cbwd_finalize_d(const BwdArgs a) {
+  const int64_t N = a.N, D = a.D;
+  const int64_t nn = N > 0 ? N : 1;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= nn * D) return;
+  const int64_t n = i / D, d = i % D;
+  const int64_t cnt = a.Bn * a.KG;
+  const int pd = a.param_dtype;
+  if (N > 0) {
+    const float* p = a.part_dA + 2 * (n * D + d);
+    st_param(a.dA, 2 * (d * N + n), pd, csum_ordered(p, cnt, 2 * N * D));
+    st_param(a.dA, 2 * (d * N + n) + 1, pd, csum_ordered(p + 1, cnt, 2 * N * D));
+  }
+  if (n == 0) {
+    if (a.dD) st_param(a.dD, d, pd, csum_ordered(a.part_dD + d, cnt, D));
+    if (a.dbias) st_param(a.dbias, d, pd, csum_ordered(a.part_db + d, cnt, D));
+  }
+}
+
+__global__ void cfill_zero_words(uint16_t* p, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t czero_bytes(void* p, int64_t bytes, hipStream_t s) {
+  if (!p || bytes <= 0) return hipSuccess;
+  const int64_t n = bytes / 2;
+  cfill_zero_words<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+      static_cast<uint16_t*>(p), n);
+  return hipGetLastError();
+}
+
+template <typename Tio>
+hipError_t launch_cbwd_t(const BwdArgs& a, hipStream_t s) {
+  const int64_t Bn = a.Bn, N = a.N;
+  hipError_t e;
+  const size_t tile_bytes = sizeof(float) * 4 * (size_t)N * CT;
+  if (a.K > 1) {
+    cbwd_summary<Tio><<<dim3((unsigned)(Bn * a.K * a.nwgd)), dim3(kChannelsPerBlock),
+                        tile_bytes, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (N > 0) {
+      const int64_t nc = (a.D + kChannelsPerBlock - 1) / kChannelsPerBlock;
+      cbwd_carry<<<dim3((unsigned)(Bn * N * nc)), dim3(kChannelsPerBlock), 0, s>>>(a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  const size_t main_bytes = tile_bytes + sizeof(float) * 32 * kCRedStride;
+  if (main_bytes > 64 * 1024) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&cbwd_main<Tio>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)main_bytes);
+    if (e != hipSuccess) return e;
+  }
+  cbwd_main<Tio><<<dim3((unsigned)(Bn * a.KG * a.nwgd)), dim3(kChannelsPerBlock), main_bytes,
+                   s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (Bn * a.L * N > 0) {
+    const int64_t nb = Bn * a.L * N * 2;
+    cbwd_finalize_bc<Tio><<<dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t nd = (N > 0 ? N : 1) * a.D;
+  cbwd_finalize_d<<<dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_complex(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_t s) {
+  switch (io_dtype) {
+    case 0: return launch_cfwd_ty<float>(a, ns, gl, s);
+    case 1: return launch_cfwd_ty<f16_t>(a, ns, gl, s);
+    case 2: return launch_cfwd_ty<bf16_t>(a, ns, gl, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_complex(const BwdArgs& a_in, const Plan& p, int io_dtype, hipStream_t s) {
+  BwdArgs a = a_in;
+  const int64_t Bn = a.Bn, L = a.L, D = a.D, N = a.N;
+  const int64_t io = io_dtype == 0 ? 4 : 2, pa = a.param_dtype == 0 ? 4 : 2;
+  if (Bn * L * D == 0) {
+    // No (b, t, d) terms: every reduced gradient is an empty sum.
+    hipError_t e = czero_bytes(a.dA, 2 * D * N * pa, s);
+    if (e == hipSuccess) e = czero_bytes(a.dD, D * pa, s);
+    if (e == hipSuccess) e = czero_bytes(a.dbias, D * pa, s);
+    if (e == hipSuccess) e = czero_bytes(a.dB, 2 * Bn * L * N * io, s);
+    if (e == hipSuccess) e = czero_bytes(a.dC, 2 * Bn * L * N * io, s);
+    if (e == hipSuccess) e = czero_bytes(a.dh0, 2 * Bn * D * N * pa, s);
+    return e;
+  }
+  a.fstate = reinterpret_cast<float*>(a.ws + p.off_state);
+  a.bstate = reinterpret_cast<float*>(a.ws + p.off_bstate);
+  a.part_bc = reinterpret_cast<float*>(a.ws + p.off_part_bc);
+  a.part_dA = reinterpret_cast<float*>(a.ws + p.off_part_dA);
+  a.part_dD = reinterpret_cast<float*>(a.ws + p.off_part_dD);
+  a.part_db = reinterpret_cast<float*>(a.ws + p.off_part_db);
+  a.KG = p.KG;
+  a.nwgd = p.nwgd;
+  switch (io_dtype) {
+    case 0: return launch_cbwd_t<float>(a, s);
+    case 1: return launch_cbwd_t<f16_t>(a, s);
+    case 2: return launch_cbwd_t<bf16_t>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ss

@@ -34,7 +34,8 @@ def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert set(names) == {"ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0", "ss_bwd_h0",
                           "ss_fwd_varlen", "ss_bwd_varlen", "ss_fwd_strided",
-                          "ss_bwd_strided", "ss_plan_query",
+                          "ss_bwd_strided", "ss_workspace_size_complex", "ss_fwd_complex",
+                          "ss_bwd_complex", "ss_plan_query",
                           "ss_status_string",
                           "ss_last_error"}
     for n in names:
@@ -159,6 +160,30 @@ def test_strided_rules():
     assert fcall(d, 192, 192, P, -1) == ss.SS_ERR_INVALID_PROBLEM
     assert "total_len" in ss.ss_last_error()
     assert fcall(d, 192, 192, P, 4097) == ss.SS_ERR_INVALID_PROBLEM
+
+
+def test_complex_rules():
+    d = _desc(B=1, L=4096, D=64, N=16)
+    fcall = lambda ws_bytes, **kw: ss.ss_fwd_complex(
+        d, P, P, P, P, P, None, None, None, kw.get("h0"), P, kw.get("ls"), P, ws_bytes, None)
+    bcall = lambda **kw: ss.ss_bwd_complex(
+        d, P, P, P, P, P, kw.get("Dskip"), None, None, kw.get("h0"), P, P, P, P, P, P,
+        kw.get("dD"), None, None, kw.get("dh0"), P, 0, None)
+    # the complex workspace holds (re, im) states: larger than the real one
+    wf, wb = ss.ss_workspace_size_complex(d, 0), ss.ss_workspace_size_complex(d, 1)
+    assert wf > ss.ss_workspace_size(d, 0) > 0 and wb > 0
+    assert fcall(wf - 1) == ss.SS_ERR_WORKSPACE_TOO_SMALL
+    assert str(wf) in ss.ss_last_error()
+    assert bcall() == ss.SS_ERR_WORKSPACE_TOO_SMALL
+    assert bcall(h0=P) == ss.SS_ERR_INVALID_PROBLEM
+    assert "h0 and dh0" in ss.ss_last_error()
+    assert bcall(Dskip=P) == ss.SS_ERR_INVALID_PROBLEM
+    # h0 / last_state: same buffer or disjoint (a state is 2 * 64 * 16 floats)
+    assert fcall(wf, h0=P, ls=ctypes.c_void_p(0x7F0000000000 + 8)) == ss.SS_ERR_INVALID_PROBLEM
+    assert "overlap" in ss.ss_last_error()
+    assert ss.ss_workspace_size_complex(_desc(N=257), 0) == 0
+    assert ss.ss_fwd_complex(_desc(N=257), P, P, P, P, P, None, None, None, None, P, None, None,
+                             0, None) == ss.SS_ERR_UNSUPPORTED
 
 
 def test_status_strings():

@@ -675,3 +675,102 @@ def test_strided_bc_varlen_and_empty():
     ss.bwd(**args, dy=d["dy"], dB=dx[..., 3:7], dC=dx[..., 7:])
     torch.cuda.synchronize()
     assert torch.all(dx[..., :3] == 5.0) and torch.all(dx[..., 3:] == 0)
+
+
+# ------------------------------------------------------- complex A / B / C
+
+def _complex_inputs(Bn, L, D, N, seed, io="f32", pa="f32", backward=False):
+    """Real tensors from the seeded recipe plus complex A, B, C and h0 as
+    (re, im) pairs: Re A = -exp(N(0,1)), Im A = N(0, 2); B, C, h0 ~ N(0, 1)."""
+    inp = random_inputs(Bn, L, D, max(N, 1), seed=seed, io_dtype=io, param_dtype=pa,
+                        backward=backward)
+    g = torch.Generator().manual_seed(seed + 7)
+    iod, pad = inp["u"].dtype, inp["D"].dtype
+    A = torch.stack([-torch.exp(torch.randn(D, N, generator=g, dtype=torch.float64)),
+                     2.0 * torch.randn(D, N, generator=g, dtype=torch.float64)], -1)
+    inp["A"] = A.to(pad)
+    inp["B"] = torch.randn(Bn, L, N, 2, generator=g, dtype=torch.float64).to(iod)
+    inp["C"] = torch.randn(Bn, L, N, 2, generator=g, dtype=torch.float64).to(iod)
+    h0 = torch.randn(Bn, D, N, 2, generator=g, dtype=torch.float64).to(pad)
+    return inp, h0
+
+
+COMPLEX_CASES = [  # (B, L, D, N, io): N covers every lanes-per-channel bucket
+    (2, 70, 40, 1, "f32"), (2, 150, 72, 4, "f32"), (1, 300, 65, 16, "f32"),
+    (2, 90, 33, 17, "f32"), (1, 64, 20, 64, "f32"), (1, 40, 9, 130, "f32"),
+    (1, 33, 7, 256, "f32"), (2, 120, 96, 16, "bf16"), (1, 77, 40, 8, "f16"),
+    (1, 2048, 32, 16, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", COMPLEX_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fwd_complex(case):
+    Bn, L, D, N, io = case
+    inp, h0 = _complex_inputs(Bn, L, D, N, seed=3000 + L + N, io=io)
+    d = to_dev(inp)
+    tol = TOL[inp["u"].dtype]
+    for with_h0 in (False, True):
+        hh = h0 if with_h0 else None
+        yr, lsr = oracle.fwd_complex(**{k: inp[k] for k in KEYS}, h0=hh)
+        for chunk in (0, 24):
+            say("fwd complex", case, "chunk", chunk, "h0", with_h0)
+            y, ls = ss.fwd_complex(*[d[k] for k in KEYS], h0=None if hh is None else hh.to(DEV),
+                                   return_last_state=True, chunk_len=chunk)
+            torch.cuda.synchronize()
+            assert rel_err(to_np(y), yr) <= tol, f"y chunk {chunk}"
+            assert rel_err(to_np(ls), lsr) <= max(tol, TOL[inp["A"].dtype]), f"ls chunk {chunk}"
+
+
+@pytest.mark.parametrize("case", COMPLEX_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bwd_complex(case):
+    Bn, L, D, N, io = case
+    inp, h0 = _complex_inputs(Bn, L, D, N, seed=3100 + L + N, io=io, backward=True)
+    d = to_dev(inp)
+    tol = TOL[inp["u"].dtype]
+    for with_h0 in (False, True):
+        hh = h0 if with_h0 else None
+        r = oracle.bwd_complex(**{k: inp[k] for k in KEYS}, dy=inp["dy"], h0=hh)
+        for chunk in (0, 3):
+            say("bwd complex", case, "chunk", chunk, "h0", with_h0)
+            g = ss.bwd_complex(*[d[k] for k in KEYS], dy=d["dy"], chunk_len=chunk,
+                               h0=None if hh is None else hh.to(DEV))
+            torch.cuda.synchronize()
+            for k in GRADS + ("dh0",):
+                if r[k] is None:
+                    assert g[k] is None
+                    continue
+                e = rel_err(to_np(g[k]), r[k])
+                assert e <= tol, f"{k} chunk {chunk} h0 {with_h0}: {e:.3e}"
+
+
+def test_complex_decode_empty_and_determinism():
+    # an in-place L = 1 step on a carried complex state
+    inp, h0 = _complex_inputs(3, 1, 300, 16, seed=3201)
+    d = to_dev(inp)
+    state = h0.to(DEV).clone()
+    y, _ = ss.fwd_complex(*[d[k] for k in KEYS], h0=state, last_state=state)
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd_complex(**{k: inp[k] for k in KEYS}, h0=h0)
+    assert rel_err(to_np(y), yr) <= 1e-5 and rel_err(to_np(state), lsr) <= 1e-5
+    # L = 0: the final state is h0, every reduced gradient an empty sum
+    inp, h0 = _complex_inputs(2, 1, 20, 4, seed=3202, backward=True)
+    for k in ("u", "delta", "z", "B", "C", "dy"):
+        inp[k] = inp[k][:, :0].contiguous()
+    d = to_dev(inp)
+    _, ls = ss.fwd_complex(*[d[k] for k in KEYS], h0=h0.to(DEV), return_last_state=True)
+    g = ss.bwd_complex(*[d[k] for k in KEYS], dy=d["dy"], h0=h0.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(ls.cpu(), h0)
+    for k in ("dA", "dD", "ddelta_bias", "dh0"):
+        assert torch.all(g[k] == 0), k
+    # bitwise reproducible, torch complex64 inputs accepted
+    inp, h0 = _complex_inputs(2, 200, 64, 16, seed=3203, backward=True)
+    d = to_dev(inp)
+    args = [d[k] for k in KEYS]
+    g1 = ss.bwd_complex(*args, dy=d["dy"], h0=h0.to(DEV))
+    cargs = [torch.view_as_complex(x.contiguous()) if k in ("A", "B", "C") else x
+             for k, x in zip(KEYS, args)]
+    g2 = ss.bwd_complex(*cargs, dy=d["dy"], h0=torch.view_as_complex(h0.to(DEV)))
+    torch.cuda.synchronize()
+    for k in GRADS + ("dh0",):
+        assert torch.equal(g1[k], g2[k]), k
