@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_summary(const BwdArgs a
     // past the chunk: a step of it, or row 0 for an empty chunk (never used)
     const int64_t t = nt > 0 ? sr.start + t0 + (ok ? tt : nt - 1) : 0;
     const float uu = ld(up, t * D), x = ld(dp, t * D) + bv;
-    const float dlv = sp ? softplus(x) : x;
+    const float dlv = sp ? softplus_acc(x) : x;
     float g = ld(yp, t * D);
     if (has_z) { const float zz = ld(zp, t * D); g *= zz * sigmoid(zz); }
     dl[tt] = ok ? dlv : 0.0f;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
       const int64_t t = nt > 0 ? sr.start + t0 + (ok ? tt : nt - 1) : 0;   // row
       const float u_ = ld(up, t * D), x = ld(dp, t * D) + bv, dy = ld(yp, t * D);
       float dlv, sxv;
-      if (sp) { dlv = softplus(x); sxv = sigmoid(x); } else { dlv = x; sxv = 1.0f; }
+      if (sp) { dlv = softplus_acc(x); sxv = sigmoid_acc(x); } else { dlv = x; sxv = 1.0f; }
       float g = dy, gzv = 0.0f;
       if (has_z) {
         const float zz = ld(zp, t * D), s = sigmoid(zz);

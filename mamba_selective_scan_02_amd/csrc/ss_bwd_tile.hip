@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
     raw(j + 1, nu, nd, ny, nz);                       // past the chunk: reads 0
     const bool valid = (int64_t)j * BGL + g < nsteps;
     const float x = dr + bv;
-    float spx = softplus(x);
+    float spx = softplus_acc(x);
     __asm__ volatile("" : "+v"(spx));
     float dl = sp ? spx : x;
     float gg = HAS_Z ? dyv * zz * sigmoid(zz) : dyv;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
     const float dr = rw.dr;
     o.valid = (int64_t)j * BGL + g < nsteps;
     const float x = dr + bv;
-    float spx = softplus(x);
+    float spx = softplus_acc(x);
     __asm__ volatile("" : "+v"(spx));
     const float dl = sp ? spx : x;
     o.dl = o.valid ? dl : 0.0f;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
         o.gz = dyv * s * __builtin_fmaf(zz, 1.0f - s, 1.0f);
       }
       o.gg = o.valid ? gv : 0.0f;
-      float sxv = sigmoid(x);
+      float sxv = sigmoid_acc(x);
       __asm__ volatile("" : "+v"(sxv));
       o.sx = sp ? sxv : 1.0f;
     }

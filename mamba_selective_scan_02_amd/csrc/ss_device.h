@@ -95,7 +95,11 @@ __device__ __forceinline__ float log1p_pos(float w) {
   return __builtin_fmaf(fast_log2(s), kLn2, c);
 }
 
-// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^{-|x|}).
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^{-|x|}), the short
+// form used by the VALU-bound forward tile kernels: measured on gfx950 it is
+// within 0.6 ulp rms for |x| < 2 but errs by up to ~10 ulp (biased upwards by
+// about one ulp) for -10 < x < -2, where the transcendental unit's log of
+// s = 1 + w near 1 is inexact; softplus_acc below costs ~5% there.
 __device__ __forceinline__ float softplus(float x) {
   const float e = fast_exp2(-__builtin_fabsf(x) * kLog2e);
   return __builtin_fmaxf(x, 0.0f) + log1p_pos(e);
@@ -104,6 +108,49 @@ __device__ __forceinline__ float softplus(float x) {
 // sigmoid(x) = 1 / (1 + e^{-x}); exp overflow gives rcp(inf) = 0.
 __device__ __forceinline__ float sigmoid(float x) {
   return fast_rcp(1.0f + fast_exp2(-x * kLog2e));
+}
+
+// log2(e) as a float plus the float nearest to the remainder.
+constexpr float kLog2eHi = 1.44269502162933349609375f;
+constexpr float kLog2eLo = 1.925963033500011e-08f;
+
+// e^v for v <= 0 with the conversion to base 2 carried as yh + yl (the
+// product's rounding error from an FMA): rounding v * log2(e) to a float
+// alone errs by up to |v| / 2 ulp of the result (4 ulp at v = -8).
+__device__ __forceinline__ float exp_neg_acc(float v) {
+  const float yh = v * kLog2eHi;
+  const float yl = __builtin_fmaf(v, kLog2eHi, -yh) + v * kLog2eLo;
+  return fast_exp2(yh) * __builtin_fmaf(yl, kLn2, 1.0f);
+}
+
+// softplus to about an ulp and without bias, for the kernels where dt's
+// accuracy shows (the backward, the general and short-sequence forwards).
+// softplus(x) = max(x, 0) + log(1 + w), w = e^{-|x|}.  For w <= e^-2 the
+// logarithm is the Taylor series through w^9 (truncation below 2e-9
+// relative): the transcendental unit's log of s = 1 + w near 1 errs by up to
+// ~10 ulp of the small result and is biased upwards by about one ulp over
+// -10 < x < -2, the range of Mamba's dt initialisation (measured on gfx950).
+__device__ __forceinline__ float softplus_acc(float x) {
+  const float w = exp_neg_acc(-__builtin_fabsf(x));
+  float q = 1.0f / 9.0f;
+  q = __builtin_fmaf(q, w, -1.0f / 8.0f);
+  q = __builtin_fmaf(q, w, 1.0f / 7.0f);
+  q = __builtin_fmaf(q, w, -1.0f / 6.0f);
+  q = __builtin_fmaf(q, w, 1.0f / 5.0f);
+  q = __builtin_fmaf(q, w, -1.0f / 4.0f);
+  q = __builtin_fmaf(q, w, 1.0f / 3.0f);
+  q = __builtin_fmaf(q, w, -0.5f);
+  q = __builtin_fmaf(q, w, 1.0f);
+  const float lp = w <= 0.1353352832366127f ? w * q : log1p_pos(w);
+  return __builtin_fmaxf(x, 0.0f) + lp;
+}
+
+// sigmoid with the exponent's argument carried as in exp_neg_acc:
+// 1 / (1 + e^{-x}) for x >= 0, e^x / (1 + e^x) for x < 0.
+__device__ __forceinline__ float sigmoid_acc(float x) {
+  const float e = exp_neg_acc(-__builtin_fabsf(x));
+  const float r = fast_rcp(1.0f + e);
+  return x >= 0.0f ? r : e * r;
 }
 
 // Buffer resources (raw, stride 0) over a byte range: loads beyond the range

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kBlock) void fwd_short(const T* __restrict__ u_in,
     const int64_t i = (sr.start + t) * D + d;
     const float uu = ld(u_in, i);
     const float x = ld(delta_in, i) + bv;
-    const float dl = a.softplus ? softplus(x) : x;
+    const float dl = a.softplus ? softplus_acc(x) : x;
     const float xu = dl * uu;
     const T* Bt = B_in + (sr.start + t) * a.ldb;
     const T* Ct = C_in + (sr.start + t) * a.ldc;

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
     unpack_row(Bc, Bt);
     if (MODE == MODE_FULL) unpack_row(Cc, Ct);
     const float x = dr + bv;
-    float spx = softplus(x);
+    float spx = softplus_acc(x);
     // keep the select branch-free: the empty asm makes spx a computed value
     // the compiler cannot sink into a branch on the (uniform) flag
     __asm__ volatile("" : "+v"(spx));
