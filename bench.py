@@ -169,6 +169,104 @@ def cpu_baseline(w, inp, budget_s: float):
                       f"{dt:.1f} s on {cpu}"}
 
 
+def variant_legs(ss, w, dev, args_f, keys, steps):
+    """The strided-B/C, packed-sequence and complex variants, each timed on its
+    own workload (see each leg's "workload")."""
+    import torch
+    out = {}
+    B8, L8, D8, N8 = w.batch, w.seqlen, w.dim, w.dstate
+    io = dev["u"].dtype
+    ios = 2 if w.io_dtype != "f32" else 4
+    fbytes = algorithmic_bytes(w)
+
+    # B / C read in place from the x-projection output xdbl [B, L, dt_rank + 2N]
+    # (dt_rank = 160 for d_model 2560), against gathering them first.
+    R = 160
+    xdbl = torch.randn(B8, L8, R + 2 * N8, generator=torch.Generator().manual_seed(7)).to(io).cuda()
+    xdbl[..., R:R + N8] = dev["B"]
+    xdbl[..., R + N8:] = dev["C"]
+    y = torch.empty_like(dev["u"])
+    sargs = list(args_f)
+    sargs[keys.index("B")] = xdbl[..., R:R + N8]
+    sargs[keys.index("C")] = xdbl[..., R + N8:]
+
+    def s_step():
+        ss.fwd(*sargs, y=y)
+
+    def g_step():
+        gargs = list(sargs)
+        gargs[keys.index("B")] = sargs[keys.index("B")].contiguous()
+        gargs[keys.index("C")] = sargs[keys.index("C")].contiguous()
+        ss.fwd(*gargs, y=y)
+
+    log("timing strided B/C")
+    sms, _ = time_calls(s_step, steps, 2)
+    gms, _ = time_calls(g_step, steps, 2)
+    out["strided_bc"] = {
+        "workload": "the 2.8B-shaped forward with B, C as column slices of xdbl "
+                    f"[{B8}, {L8}, {R + 2 * N8}] (row stride {R + 2 * N8})",
+        "us_per_call": sms * 1e3, "state_updates_per_s": w.updates / (sms * 1e-3),
+        "us_per_call_gather_then_scan": gms * 1e3,
+    }
+    log(f"strided {sms * 1e3:.1f} us, gather + scan {gms * 1e3:.1f} us")
+    del xdbl, sargs
+
+    # packed sequences: the same 16384 rows cut into 14 sequences of 256..2048 steps
+    lens = [2048, 1024, 512, 2048, 1024, 512, 2048, 1024, 512, 2048, 1024, 512, 1024, 1024]
+    assert sum(lens) == B8 * L8
+    cu = torch.tensor([0] + list(torch.tensor(lens).cumsum(0)), dtype=torch.int32).cuda()
+    pk = {k: (None if dev[k] is None else
+              (dev[k].reshape(-1, dev[k].shape[-1]) if dev[k].dim() == 3 else dev[k]))
+          for k in keys}
+    yv = torch.empty_like(pk["u"])
+
+    def v_step():
+        ss.fwd_varlen(pk["u"], pk["delta"], pk["A"], pk["B"], pk["C"], cu, max(lens), pk["D"],
+                      pk["z"], pk["delta_bias"], y=yv)
+
+    log("timing packed sequences")
+    vms, _ = time_calls(v_step, steps, 2)
+    out["varlen"] = {
+        "workload": f"the 2.8B-shaped forward's {B8 * L8} rows as {len(lens)} packed sequences "
+                    f"of {min(lens)}..{max(lens)} steps (D=5120, N=16, bf16)",
+        "us_per_call": vms * 1e3, "state_updates_per_s": w.updates / (vms * 1e-3),
+        "hbm_gbs": fbytes / (vms * 1e-3) / 1e9,
+    }
+    log(f"varlen {vms * 1e3:.1f} us")
+    del pk, yv
+
+    # complex A, B, C: forward and backward, B=2, L=2048, D=1024, N=16, f32
+    Bc, Lc, Dc, Nc = 2, 2048, 1024, 16
+    g = torch.Generator().manual_seed(11)
+    f = lambda *sh: torch.randn(*sh, generator=g).cuda()
+    cu_ = f(Bc, Lc, Dc)
+    cdl = (f(Bc, Lc, Dc) * 0.5 - 1.0)
+    cA = torch.stack([-torch.exp(torch.randn(Dc, Nc, generator=g)),
+                      torch.randn(Dc, Nc, generator=g) * 2.0], -1).cuda()
+    cB, cC = f(Bc, Lc, Nc, 2), f(Bc, Lc, Nc, 2)
+    cD, cz, cbias, cdy = f(Dc), f(Bc, Lc, Dc), f(Dc) * 0.1 - 4.0, f(Bc, Lc, Dc)
+
+    def cf_step():
+        ss.fwd_complex(cu_, cdl, cA, cB, cC, cD, cz, cbias)
+
+    def cb_step():
+        ss.bwd_complex(cu_, cdl, cA, cB, cC, cD, cz, cbias, dy=cdy)
+
+    log("timing complex")
+    cfms, _ = time_calls(cf_step, steps, 2)
+    cbms, _ = time_calls(cb_step, max(3, steps // 2), 1)
+    upd = Bc * Lc * Dc * Nc
+    cfb = (4 * Bc * Lc * Dc + 4 * Bc * Lc * Nc + Dc * Nc * 2 + 2 * Dc) * 4
+    out["complex"] = {
+        "workload": f"complex A/B/C, B={Bc}, L={Lc}, D={Dc}, N={Nc}, f32, D/z/delta_bias",
+        "fwd_us_per_call": cfms * 1e3, "fwd_state_updates_per_s": upd / (cfms * 1e-3),
+        "fwd_hbm_gbs": cfb / (cfms * 1e-3) / 1e9,
+        "bwd_us_per_call": cbms * 1e3, "bwd_state_updates_per_s": upd / (cbms * 1e-3),
+    }
+    log(f"complex fwd {cfms * 1e3:.1f} us, bwd {cbms * 1e3:.1f} us")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,6 +277,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the strided-B/C, packed-sequence and complex legs")
+    ap.add_argument("--variants-only", action="store_true",
+                    help="time only those legs (for a kernel trace of them alone)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a plain 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
@@ -208,6 +310,9 @@ def main():
     def step():
         ss.fwd(*args_f, y=y, workspace=ws)
 
+    if args.variants_only:
+        print(json.dumps(variant_legs(ss, w, dev, args_f, keys, args.steps)), flush=True)
+        return
     log(f"timing forward: warmup {args.warmup}, steps {args.steps}")
     ms, wall = time_calls(step, args.steps, args.warmup)
     updates = w.updates
@@ -306,6 +411,9 @@ def main():
         }
         log(f"decode {dms * 1e3:.2f} us/step")
         del state
+
+    if not args.no_variants:
+        result.update(variant_legs(ss, w, dev, args_f, keys, max(5, args.steps // 2)))
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

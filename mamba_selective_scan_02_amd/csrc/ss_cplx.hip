@@ -393,18 +393,35 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_carry(const BwdArgs a)
     hr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
     hi = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
   }
-  for (int64_t j = 0; j < K - 1; ++j) {
-    float* fs = a.fstate + 4 * (((b * K + j) * N + n) * D + d);
-    const float4 r = *reinterpret_cast<const float4*>(fs);   // S, E - 1 = conj(P) - 1
-    cstep(r.z, -r.w, r.x, r.y, hr, hi);                       // h = P h + S
-    fs[0] = hr;
-    fs[1] = hi;
-    const int64_t jj = K - 1 - j;
-    const float* fj = a.fstate + 4 * (((b * K + jj) * N + n) * D + d);
-    float* bs = a.bstate + 2 * (((b * K + jj) * N + n) * D + d);
-    cstep(fj[2], fj[3], bs[0], bs[1], cr, ci);                // c = E c + Sb
-    bs[0] = cr;
-    bs[1] = ci;
+  // The records of KB chunks are loaded before the two dependent chains run
+  // through them (the chains alone would wait on every load).  The reverse
+  // chain reads the E parts of records the forward chain has not reached or
+  // only rewrote the state part of, so the loads never see a stale value.
+  float4* fs = reinterpret_cast<float4*>(a.fstate) + ((b * K) * N + n) * D + d;  // + j N D
+  float2* bs = reinterpret_cast<float2*>(a.bstate) + ((b * K) * N + n) * D + d;
+  const int64_t st = N * D;
+  constexpr int KB = 8;
+  for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
+    float4 rf[KB], rr[KB];
+    float2 rb[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int64_t jf = (j0 + j < K - 1) ? j0 + j : K - 2;
+      const int64_t jr = K - 1 - jf;
+      rf[j] = fs[jf * st];
+      rr[j] = fs[jr * st];
+      rb[j] = bs[jr * st];
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (j0 + j < K - 1) {
+        const int64_t jf = j0 + j, jr = K - 1 - jf;
+        cstep(rf[j].z, -rf[j].w, rf[j].x, rf[j].y, hr, hi);   // h = P h + S, P - 1 = conj(E - 1)
+        fs[jf * st] = make_float4(hr, hi, rf[j].z, rf[j].w);
+        cstep(rr[j].z, rr[j].w, rb[j].x, rb[j].y, cr, ci);    // c = E c + Sb
+        bs[jr * st] = make_float2(cr, ci);
+      }
+    }
   }
 }
 
@@ -597,10 +614,20 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_main(const BwdArgs a) 
   }
 }
 
-// Fixed-order sum of `count` partials p[0], p[stride], ...
+// Fixed-order sum of `count` partials p[0], p[stride], ... (loads issued in
+// batches of 8, the adds in index order).
 __device__ __forceinline__ float csum_ordered(const float* p, int64_t count, int64_t stride) {
+  constexpr int U = 8;
   float s = 0.0f;
-  for (int64_t j = 0; j < count; ++j) s += p[j * stride];
+  int64_t j = 0;
+  for (; j + U <= count; j += U) {
+    float v[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) v[q] = p[(j + q) * stride];
+#pragma unroll
+    for (int q = 0; q < U; ++q) s += v[q];
+  }
+  for (; j < count; ++j) s += p[j * stride];
   return s;
 }
 
