@@ -774,3 +774,111 @@ def test_complex_decode_empty_and_determinism():
     torch.cuda.synchronize()
     for k in GRADS + ("dh0",):
         assert torch.equal(g1[k], g2[k]), k
+
+
+# ------------------------------------- the bench's variant legs at full size
+
+def test_bench_strided_and_varlen_legs():
+    """The 2.8B-shaped forward with B/C read from xdbl [8, 2048, 192] equals the
+    packed call bit for bit; the same rows as 14 packed sequences match the
+    oracle on sampled (sequence, channel) pairs."""
+    w = WORKLOADS["m2p8b"]
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    say("bench legs: strided")
+    y0, _ = ss.fwd(*[d[k] for k in KEYS])
+    R, N = 160, w.dstate
+    x, Bv, Cv = _xdbl(d["B"], d["C"], R, 3301)
+    args = {k: d[k] for k in KEYS}
+    args.update(B=Bv, C=Cv)
+    y1, _ = ss.fwd(**args)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    del x, Bv, Cv, y1
+    say("bench legs: varlen")
+    lens = [2048, 1024, 512, 2048, 1024, 512, 2048, 1024, 512, 2048, 1024, 512, 1024, 1024]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pk = {k: (None if d[k] is None else (d[k].reshape(-1, d[k].shape[-1]) if d[k].dim() == 3
+                                          else d[k])) for k in KEYS}
+    yv, lsv = ss.fwd_varlen(cu_seqlens=torch.as_tensor(cu, device=DEV), max_seqlen=max(lens),
+                            return_last_state=True, **pk)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3302)
+    hp = {k: (None if inp[k] is None else (inp[k].reshape(-1, inp[k].shape[-1])
+                                           if inp[k].dim() == 3 else inp[k])) for k in KEYS}
+    for s in (0, 2, 8, 13):
+        a, b = int(cu[s]), int(cu[s + 1])
+        seg = {k: (None if hp[k] is None else (hp[k][a:b][None] if k in ("u", "delta", "z", "B", "C")
+                                               else hp[k])) for k in KEYS}
+        cd = np.concatenate([rng.integers(0, w.dim, 16), [0, 63, 64, w.dim - 1]])
+        yr, lsr = oracle.fwd_channels(**seg, chan_b=np.zeros_like(cd), chan_d=cd)
+        yg = yv[a:b][:, torch.as_tensor(cd)].T                 # [nchan, len]
+        assert rel_err(to_np(yg), yr) <= TOL[inp["u"].dtype], s
+        assert rel_err(to_np(lsv[s][torch.as_tensor(cd)]), lsr) <= 1e-5, s
+
+
+def test_bench_complex_leg():
+    """The complex leg's shape (2x2048x1024x16, f32, default schedule): the
+    whole forward against the oracle, and the backward's per-channel
+    gradients on a slice of channels (dB / dC sum over every channel and are
+    covered at the smaller sizes)."""
+    inp, h0 = _complex_inputs(2, 2048, 1024, 16, seed=3401, backward=True)
+    d = to_dev(inp)
+    say("bench legs: complex forward")
+    y, ls = ss.fwd_complex(*[d[k] for k in KEYS], return_last_state=True)
+    g = ss.bwd_complex(*[d[k] for k in KEYS], dy=d["dy"])
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd_complex(**{k: inp[k] for k in KEYS})
+    assert rel_err(to_np(y), yr) <= 1e-5 and rel_err(to_np(ls), lsr) <= 1e-5
+    say("bench legs: complex backward (channel slice)")
+    sl = slice(0, 96)
+    sub = {k: (None if inp[k] is None else
+               (inp[k][..., sl] if k in ("u", "delta", "z") else
+                inp[k][sl] if k in ("A", "D", "delta_bias") else inp[k])) for k in KEYS}
+    r = oracle.bwd_complex(**sub, dy=inp["dy"][..., sl])
+    for k, gk in (("du", g["du"][..., sl]), ("ddelta", g["ddelta"][..., sl]),
+                  ("dz", g["dz"][..., sl]), ("dA", g["dA"][sl]), ("dD", g["dD"][sl]),
+                  ("ddelta_bias", g["ddelta_bias"][sl])):
+        e = rel_err(to_np(gk), r[k])
+        assert e <= 1e-5, f"{k}: {e:.3e}"
+
+
+def test_graph_capture_replays():
+    """Forward, backward and an in-place decode step captured in one HIP graph:
+    every replay (with eager work between replays) matches the eager results
+    bit for bit (no memsets inside the library's launches)."""
+    inp = random_inputs(2, 300, 96, 16, seed=3501, backward=True)
+    d = to_dev(inp)
+    args = [d[k] for k in KEYS]
+    h0 = _state(inp, 3502).to(DEV)
+    y_e, _ = ss.fwd(*args, h0=h0)
+    g_e = ss.bwd(*args, dy=d["dy"], h0=h0)
+    st = h0.clone()
+    step = [None if t is None else (t[:, :1].contiguous() if t.dim() == 3 else t) for t in args]
+    ss.fwd(*step, h0=st, last_state=st)
+    st_e = st.clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    state = h0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ss.fwd(*args, h0=h0)                 # warm-up allocations outside the graph
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            y_g, _ = ss.fwd(*args, h0=h0)
+            g_g = ss.bwd(*args, dy=d["dy"], h0=h0)
+            ss.fwd(*step, h0=state, last_state=state)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(3):
+        say("graph replay", r)
+        state.copy_(h0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e)
+        for k in GRADS + ("dh0",):
+            if g_e[k] is not None:
+                assert torch.equal(g_g[k], g_e[k]), k
+        assert torch.equal(state, st_e)
+        ss.fwd(*args)                        # eager work between replays
+        torch.cuda.synchronize()
