@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
 // -------------------------------------------------------------------- main
 
 template <typename T, int NS, bool HAS_Z>
-__global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
+__global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_in,
                                                      const T* __restrict__ delta_in,
                                                      const T* __restrict__ B_in,
                                                      const T* __restrict__ C_in,
@@ -270,7 +270,8 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
   __shared__ __attribute__((aligned(16))) float sC[NP][BTS];
   __shared__ __attribute__((aligned(16))) float4 xch[BCPW][BXS];
   __shared__ __attribute__((aligned(16))) float hts[BNT][NS][kBT];  // tile-start states
-  __shared__ __attribute__((aligned(16))) float red[2][BCPW][RP];   // dB / dC of one tile
+  // dB / dC of one tile, per pair of channels (pre-summed across the pair)
+  __shared__ __attribute__((aligned(16))) float red[2][BCPW / 2][RP];
   const BTilePos P = btile_pos(a);
   const int tid = threadIdx.x;
   const int g = P.g, cl = P.cl, n0 = g * NS;
@@ -304,6 +305,10 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
   const auto ws_dd = make_rsrc(ddelta_out + row0, rbytes);
   const auto ws_dz = make_rsrc(HAS_Z ? dz_out + row0 : du_out + row0, HAS_Z ? rbytes : 0);
   const int voff = (int)((g * D + d) * ES);
+  // Tail channels (d >= D) compute a copy of channel D-1 with zero input
+  // drive and gradient (so they add nothing to the dB / dC sums); their
+  // stores go past the buffer range and are dropped.
+  const int voff_st = P.active ? voff : (int)rbytes;
   const int sstep = (int)(BGL * D * ES);
   const int ntile = (int)((nsteps + BGL - 1) / BGL);
   __syncthreads();
@@ -326,12 +331,13 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
     o.uu = rw.uu;
     const float dr = rw.dr;
     o.valid = (int64_t)j * BGL + g < nsteps;
+    const bool drive = o.valid && P.active;
     const float x = dr + bv;
     float spx = softplus_acc(x);
     __asm__ volatile("" : "+v"(spx));
     const float dl = sp ? spx : x;
     o.dl = o.valid ? dl : 0.0f;
-    o.xu = o.valid ? dl * o.uu : 0.0f;
+    o.xu = drive ? dl * o.uu : 0.0f;
     o.gg = 0.0f;
     o.sx = 1.0f;
     o.gz = 0.0f;
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
         gv = dyv * zz * s;
         o.gz = dyv * s * __builtin_fmaf(zz, 1.0f - s, 1.0f);
       }
-      o.gg = o.valid ? gv : 0.0f;
+      o.gg = drive ? gv : 0.0f;
       float sxv = sigmoid_acc(x);
       __asm__ volatile("" : "+v"(sxv));
       o.sx = sp ? sxv : 1.0f;
@@ -452,21 +458,24 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
       }
       pdua[s] = vdua;
       pddl[s] = vddl;
-      // dB / dC of (step s, these states) for the workgroup reduction
-      // (tail lanes duplicate channel D-1 and must add nothing)
+      // dB / dC of (step s, these states) for the workgroup reduction: the
+      // two channels of a 16-lane row (lanes g and g + 8) are summed first
+      // (tail lanes contribute exact zeros)
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        vb[i] = P.active ? vb[i] : 0.0f;
-        vc[i] = P.active ? vc[i] : 0.0f;
+        vb[i] += bdpp<0x128>(vb[i]);     // row_ror:8: the pair's other channel
+        vc[i] += bdpp<0x128>(vc[i]);
       }
-      if (NS == 2) {
-        *reinterpret_cast<float2*>(&red[0][cl][s * NP + n0]) = make_float2(vb[0], vb[NS - 1]);
-        *reinterpret_cast<float2*>(&red[1][cl][s * NP + n0]) = make_float2(vc[0], vc[NS - 1]);
-      } else {
+      if ((cl & 1) == 0) {
+        if (NS == 2) {
+          *reinterpret_cast<float2*>(&red[0][cl >> 1][s * NP + n0]) = make_float2(vb[0], vb[NS - 1]);
+          *reinterpret_cast<float2*>(&red[1][cl >> 1][s * NP + n0]) = make_float2(vc[0], vc[NS - 1]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          red[0][cl][s * NP + n0 + i] = vb[i];
-          red[1][cl][s * NP + n0 + i] = vc[i];
+          for (int i = 0; i < NS; ++i) {
+            red[0][cl >> 1][s * NP + n0 + i] = vb[i];
+            red[1][cl >> 1][s * NP + n0 + i] = vc[i];
+          }
         }
       }
     }
@@ -482,20 +491,20 @@ __global__ __launch_bounds__(kBT) void bwd_tile_main(const T* __restrict__ u_in,
     const float du = __builtin_fmaf(o.dl, dua_own, o.gg * Dv);
     const float dx = o.valid ? __builtin_fmaf(o.uu, dua_own, ddl_own) * o.sx : 0.0f;
     const int so = j * sstep;
-    buf_st<T>(du, ws_du, voff, so);          // steps past the chunk are dropped
-    buf_st<T>(dx, ws_dd, voff, so);
-    if (HAS_Z) buf_st<T>(o.gz * __builtin_fmaf(Dv, o.uu, o_own), ws_dz, voff, so);
+    buf_st<T>(du, ws_du, voff_st, so);       // steps past the chunk are dropped
+    buf_st<T>(dx, ws_dd, voff_st, so);
+    if (HAS_Z) buf_st<T>(o.gz * __builtin_fmaf(Dv, o.uu, o_own), ws_dz, voff_st, so);
     dD_acc = __builtin_fmaf(o.gg, o.uu, dD_acc);
     db_acc += dx;
 
-    // dB / dC of this tile: sum over the workgroup's 32 channels (fixed order)
+    // dB / dC of this tile: sum over the workgroup's 16 channel pairs (fixed order)
     __syncthreads();
     for (int v = tid; v < 2 * BGL * NP; v += kBT) {
       const int w = v / (BGL * NP), sn = v % (BGL * NP);
       const int s = sn / NP, n = sn % NP;
       float acc = 0.0f;
 #pragma unroll 8
-      for (int c = 0; c < BCPW; ++c) acc += red[w][c][sn];
+      for (int c = 0; c < BCPW / 2; ++c) acc += red[w][c][sn];
       const int64_t t = (int64_t)j * BGL + s;
       if (n < N && t < nsteps)
         a.part_bc[((P.start + P.t0 + t) * a.nwgd + P.db) * 2 * N + w * N + n] = acc;
