@@ -28,7 +28,8 @@
 //     from h_in into registers, sweep back from c, accumulate the per-t sums
 //     (ddt, du, o) in registers; dB and dC partials are summed over the 256
 //     channels of the workgroup through LDS in a fixed order.
-//  4. bwd_finalize_bc / bwd_finalize_d: fixed-order sums of the partials.
+//  4. bwd_finalize: fixed-order sums of the partials (dB / dC and dA / dD /
+//     ddelta_bias in one launch).
 #include "ss_device.h"
 #include "ss_plan.h"
 
@@ -330,8 +331,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
 // dB[b,t,n], dC[b,t,n] = sums over the channel blocks, in block order (loads
 // are issued in batches of 8, the adds stay in index order).
 template <typename Tio>
-__global__ void bwd_finalize_bc(const BwdArgs a) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // row * N + n
+__device__ __forceinline__ void finalize_bc(const BwdArgs& a, int64_t i) {  // i = row * N + n
   const int64_t N = a.N;
   if (i >= a.Lt * N) return;
   const int64_t bt = i / N, n = i % N;
@@ -375,10 +375,9 @@ __device__ __forceinline__ float ordered_sum(const float* p, int64_t count, int6
 
 // dA[d,n] = sum over (b, chunk group) in that order; dD, ddelta_bias likewise.
 // Thread per (n', d), d fastest, n' < max(N, 1); n' = 0 also does dD / dbias.
-__global__ void bwd_finalize_d(const BwdArgs a) {
+__device__ __forceinline__ void finalize_d(const BwdArgs& a, int64_t i) {
   const int64_t N = a.N, D = a.D;
   const int64_t nn = N > 0 ? N : 1;
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= nn * D) return;
   const int64_t n = i / D, d = i % D;
   const int64_t cnt = a.Bn * a.KG;
@@ -387,6 +386,16 @@ __global__ void bwd_finalize_d(const BwdArgs a) {
     if (a.dD) st_param(a.dD, d, a.param_dtype, ordered_sum(a.part_dD + d, cnt, D));
     if (a.dbias) st_param(a.dbias, d, a.param_dtype, ordered_sum(a.part_db + d, cnt, D));
   }
+}
+
+// Both finalizes in one launch: the first nbd blocks sum the per-channel
+// partials (few threads, each a chain of dependent-address loads, so they
+// start first), the rest the dB / dC partials.
+template <typename Tio>
+__global__ void bwd_finalize(const BwdArgs a, int64_t nbd) {
+  const int64_t blk = blockIdx.x;
+  if (blk < nbd) finalize_d(a, blk * blockDim.x + threadIdx.x);
+  else finalize_bc<Tio>(a, (blk - nbd) * blockDim.x + threadIdx.x);
 }
 
 __global__ void fill_zero_words(uint16_t* p, int64_t n) {
@@ -431,18 +440,15 @@ hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_finalize(const BwdArgs& a, hipStream_t s) {
-  hipError_t e;
-  if (a.Lt * a.N > 0) {
-    const int64_t n = a.Lt * a.N;
-    switch (a.io_dtype) {
-      case 0: bwd_finalize_bc<float><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a); break;
-      case 1: bwd_finalize_bc<f16_t><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a); break;
-      default: bwd_finalize_bc<bf16_t><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a); break;
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   const int64_t nd = (a.N > 0 ? a.N : 1) * a.D;
-  bwd_finalize_d<<<dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, s>>>(a);
+  const int64_t nbd = (nd + 255) / 256;
+  const int64_t nbc = (a.Lt * a.N + 255) / 256;
+  const dim3 grid((unsigned)(nbd + nbc));
+  switch (a.io_dtype) {
+    case 0: bwd_finalize<float><<<grid, dim3(256), 0, s>>>(a, nbd); break;
+    case 1: bwd_finalize<f16_t><<<grid, dim3(256), 0, s>>>(a, nbd); break;
+    default: bwd_finalize<bf16_t><<<grid, dim3(256), 0, s>>>(a, nbd); break;
+  }
   return hipGetLastError();
 }
 

@@ -151,7 +151,7 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
   p.off_part_db = off;
   off = align256(off + sizeof(float) * (size_t)(Bn * p.KG * D));
   p.ws_bytes = off;
-  p.n_launches = p.K > 1 ? 5 : 3;
+  p.n_launches = p.K > 1 ? 4 : 2;
   return p;
 }
 

@@ -289,9 +289,9 @@ def test_plan_is_a_function_of_shape():
     # the general kernels with chunks of 16 steps
     p = ss.plan(_desc(B=2, L=2048, D=2048, N=16), True)
     assert (p.chunk_len, p.n_chunks, p.n_launches, p.states_per_lane,
-            p.lanes_per_channel) == (64, 32, 5, 2, 8)
+            p.lanes_per_channel) == (64, 32, 4, 2, 8)
     p = ss.plan(_desc(B=2, L=2048, D=2048, N=17), True)
-    assert (p.chunk_len, p.n_chunks, p.n_launches) == (16, 128, 5)
+    assert (p.chunk_len, p.n_chunks, p.n_launches) == (16, 128, 4)
 
 
 def test_workspace_size_formula():
