@@ -14,9 +14,9 @@
 //   du_t = dt sum_n Re(conj(B_t) lam_t) + D g_t,   dh0 = conj(a_0) lam_0
 // and gradients of complex inputs are returned as (dL/dRe, dL/dIm).
 //
-// Forward: G lanes per channel, each holding NS complex states in VGPRs; the
-// per-step scalar work is repeated on the G lanes; the readout is summed
-// across them with lane shuffles.  Long sequences with few channels use the
+// Forward: G lanes per channel, each holding NS (at most 4 up to N = 64)
+// complex states in VGPRs; the per-step scalar work is repeated on the G
+// lanes; the readout is summed across them with lane shuffles.  Long sequences with few channels use the
 // same two-level chunked scan as the real path (summaries from zero, a carry
 // over chunks, then a final pass), except that a chunk's decay is the running
 // product of its steps' decays rather than exp(A * sum dt): for complex A the
@@ -285,16 +285,21 @@ hipError_t launch_cfwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s) {
       case 1: return launch_cfwd_t<T, 1, 1>(a, s);
       case 2: return launch_cfwd_t<T, 2, 1>(a, s);
       case 4: return launch_cfwd_t<T, 4, 1>(a, s);
-      case 8: return launch_cfwd_t<T, 8, 1>(a, s);
-      case 16: return launch_cfwd_t<T, 16, 1>(a, s);
     }
     return hipErrorInvalidValue;
   }
-  if (ns != 16) return hipErrorInvalidValue;
-  switch (gl) {
-    case 2: return launch_cfwd_t<T, 16, 2>(a, s);
-    case 4: return launch_cfwd_t<T, 16, 4>(a, s);
-    case 8: return launch_cfwd_t<T, 16, 8>(a, s);
+  if (ns == 4) {
+    switch (gl) {
+      case 2: return launch_cfwd_t<T, 4, 2>(a, s);
+      case 4: return launch_cfwd_t<T, 4, 4>(a, s);
+      case 8: return launch_cfwd_t<T, 4, 8>(a, s);
+      case 16: return launch_cfwd_t<T, 4, 16>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (gl != 16) return hipErrorInvalidValue;
+  switch (ns) {
+    case 8: return launch_cfwd_t<T, 8, 16>(a, s);
     case 16: return launch_cfwd_t<T, 16, 16>(a, s);
   }
   return hipErrorInvalidValue;

@@ -157,7 +157,7 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
 
 // Complex variant (A, B, C and the state complex, stored as (re, im) float
 // pairs).  Forward: G lanes per channel with NS complex states each
-// (NS * G >= N, NS <= 16), 256 / G channels per workgroup, chunks chosen as
+// (NS * G >= N, NS <= 4 up to N = 64), 256 / G channels per workgroup, chunks chosen as
 // for the real scan.  Backward: one lane per channel, chunks of at most
 // kCplxBwdTile steps, 256 channels per workgroup, partials per group of
 // kBwdChunksPerGroup chunks.  A chunk's decay is carried as the product of
@@ -169,12 +169,18 @@ constexpr int kCplxBwdTile = 8;
 inline Plan make_plan_complex(const ss_desc& d, bool backward) {
   Plan p;
   const int64_t Bn = d.batch, L = d.seqlen, D = d.dim, N = d.dstate;
-  if (N <= 16) {
+  // At most 4 states per lane up to N = 64: the complex step is long
+  // (double-precision exp and sincos per state), so more lanes per channel buy
+  // the waves that hide its latency at little cost in the readout sum.
+  if (N <= 4) {
     p.G = 1;
-    p.NS = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16;
+    p.NS = N <= 1 ? 1 : N <= 2 ? 2 : 4;
+  } else if (N <= 64) {
+    p.NS = 4;
+    p.G = N <= 8 ? 2 : N <= 16 ? 4 : N <= 32 ? 8 : 16;
   } else {
-    p.NS = 16;
-    p.G = N <= 32 ? 2 : N <= 64 ? 4 : N <= 128 ? 8 : 16;
+    p.G = 16;
+    p.NS = N <= 128 ? 8 : 16;
   }
   if (Bn * L * D == 0) {
     p.chunk_len = L;
