@@ -285,7 +285,7 @@ def main():
                     help="run a plain 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the "
+        print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}); the "
               "selective scan is timed at N=1.", file=sys.stderr)
         sys.exit(2)
 
