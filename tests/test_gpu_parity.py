@@ -882,3 +882,48 @@ def test_graph_capture_replays():
         assert torch.equal(state, st_e)
         ss.fwd(*args)                        # eager work between replays
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------ seeded random shapes
+
+def _random_case(seed):
+    rng = np.random.default_rng(seed)
+    Bn = int(rng.integers(1, 4))
+    L = int(rng.choice([1, 2, 5, 16, 17, 63, 64, 65, 130, 257, 700]))
+    D = int(rng.choice([1, 3, 8, 31, 32, 33, 64, 100, 257]))
+    N = int(rng.choice([1, 4, 8, 12, 16, 17, 32, 40, 64, 100]))
+    io = str(rng.choice(["f32", "f32", "bf16", "f16"]))
+    pa = "f32" if io == "f32" or rng.random() < 0.7 else io
+    opts = dict(has_D=bool(rng.random() < 0.8), has_z=bool(rng.random() < 0.8),
+                has_bias=bool(rng.random() < 0.8))
+    chunk = int(rng.choice([0, 0, 3, 8, 24, 64]))
+    return Bn, L, D, N, io, pa, opts, chunk, bool(rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(seed):
+    """Seeded random shapes, dtypes, options, forced chunk lengths and initial
+    states: forward and backward against the oracle."""
+    Bn, L, D, N, io, pa, opts, chunk, with_h0 = _random_case(4000 + seed)
+    say("random case", seed, (Bn, L, D, N), io, pa, opts, "chunk", chunk, "h0", with_h0)
+    inp = random_inputs(Bn, L, D, N, seed=4100 + seed, io_dtype=io, param_dtype=pa,
+                        backward=True, **opts)
+    h0 = _state(inp, 4200 + seed) if with_h0 else None
+    d = to_dev(inp)
+    hd = None if h0 is None else h0.to(DEV)
+    y, ls = ss.fwd(*[d[k] for k in KEYS], return_last_state=True, chunk_len=chunk, h0=hd)
+    g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"], chunk_len=chunk, h0=hd)
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+    r = oracle.bwd(**{k: inp[k] for k in KEYS}, dy=inp["dy"], h0=h0)
+    tol = TOL[inp["u"].dtype]
+    assert rel_err(to_np(y), yr) <= tol
+    assert rel_err(to_np(ls), lsr) <= max(tol, TOL[inp["A"].dtype])
+    for k in GRADS + ("dh0",):
+        if r[k] is None:
+            assert g[k] is None
+            continue
+        # parameter-dtype gradients are rounded to that dtype
+        t = max(tol, TOL[inp["A"].dtype]) if k in ("dA", "dD", "ddelta_bias", "dh0") else tol
+        e = rel_err(to_np(g[k]), r[k])
+        assert e <= t, f"{k}: {e:.3e}"
