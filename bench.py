@@ -28,6 +28,13 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (256 CUs x 2.4 GHz x 
 # Algorithmic flops of one state update: dt*A (1), exp (1), (dt*u)*B (1),
 # a*h + x (2), h*C accumulated (2).
 FLOPS_PER_UPDATE = 7
+# Backward, per state update: the forward recompute (7) plus the adjoint
+# g*C + a*dh (2), dB term dh*(dt*u) (1), du term dh*B (2), q = dh*a*h_prev (2),
+# ddt term q*A (2), dA term q*dt (2): 18.
+FLOPS_PER_UPDATE_BWD = 18
+# Complex forward, per complex state update: dt*A (2), exp and sincos (2),
+# (a - 1)*h + x + h (8), (dt*u)*B (2), Re(C*h) accumulated (4): 18.
+FLOPS_PER_UPDATE_COMPLEX = 18
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mamba_selective_scan_02_amd", "csrc")
 
@@ -126,6 +133,36 @@ def time_calls(fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps, wall
 
 
+def alu_roofline(updates_per_s: float, flops_per_update: int) -> dict:
+    achieved = updates_per_s * flops_per_update / 1e12
+    return {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+            "flops_per_update": flops_per_update}
+
+
+def cpu_oracle_rate(run, total_channels: int, updates_per_channel: int, budget_s: float,
+                    what: str):
+    """Rate of an oracle call `run(nchan)` over the first nchan channels,
+    grown until it takes ~1 s and then sized to ~budget_s."""
+    import oracle
+    n = 1
+    while True:
+        t0 = time.perf_counter()
+        run(n)
+        dt = time.perf_counter() - t0
+        if dt >= 1.0 or n >= total_channels:
+            break
+        n = min(total_channels, n * 4)
+    n = int(min(total_channels, max(1, n * budget_s / max(dt, 1e-9))))
+    t0 = time.perf_counter()
+    run(n)
+    dt = time.perf_counter() - t0
+    upd = n * updates_per_channel
+    return {"value": upd / dt, "unit": "state-updates/s", "cores": oracle.default_threads(),
+            "kind": "oracle", "sample": f"{what}: the first {n} of {total_channels} channels, "
+                                        f"{upd:.3e} updates in {dt:.1f} s"}
+
+
 def cpu_baseline(w, inp, budget_s: float):
     """The oracle (float64 C loop, threaded over channels) on the host cores,
     on a bounded sample of the same workload: the first channels of every
@@ -169,7 +206,7 @@ def cpu_baseline(w, inp, budget_s: float):
                       f"{dt:.1f} s on {cpu}"}
 
 
-def variant_legs(ss, w, dev, args_f, keys, steps):
+def variant_legs(ss, w, dev, args_f, keys, steps, with_cpu=False):
     """The strided-B/C, packed-sequence and complex variants, each timed on its
     own workload (see each leg's "workload")."""
     import torch
@@ -207,6 +244,7 @@ def variant_legs(ss, w, dev, args_f, keys, steps):
                     f"[{B8}, {L8}, {R + 2 * N8}] (row stride {R + 2 * N8})",
         "us_per_call": sms * 1e3, "state_updates_per_s": w.updates / (sms * 1e-3),
         "us_per_call_gather_then_scan": gms * 1e3,
+        "roofline": alu_roofline(w.updates / (sms * 1e-3), FLOPS_PER_UPDATE),
     }
     log(f"strided {sms * 1e3:.1f} us, gather + scan {gms * 1e3:.1f} us")
     del xdbl, sargs
@@ -231,6 +269,7 @@ def variant_legs(ss, w, dev, args_f, keys, steps):
                     f"of {min(lens)}..{max(lens)} steps (D=5120, N=16, bf16)",
         "us_per_call": vms * 1e3, "state_updates_per_s": w.updates / (vms * 1e-3),
         "hbm_gbs": fbytes / (vms * 1e-3) / 1e9,
+        "roofline": alu_roofline(w.updates / (vms * 1e-3), FLOPS_PER_UPDATE),
     }
     log(f"varlen {vms * 1e3:.1f} us")
     del pk, yv
@@ -262,7 +301,21 @@ def variant_legs(ss, w, dev, args_f, keys, steps):
         "fwd_us_per_call": cfms * 1e3, "fwd_state_updates_per_s": upd / (cfms * 1e-3),
         "fwd_hbm_gbs": cfb / (cfms * 1e-3) / 1e9,
         "bwd_us_per_call": cbms * 1e3, "bwd_state_updates_per_s": upd / (cbms * 1e-3),
+        "fwd_roofline": alu_roofline(upd / (cfms * 1e-3), FLOPS_PER_UPDATE_COMPLEX),
     }
+    if with_cpu:
+        import oracle
+        log("timing the CPU oracle complex forward")
+        cin = {"u": cu_.cpu(), "delta": cdl.cpu(), "A": cA.cpu(), "B": cB.cpu(), "C": cC.cpu(),
+               "D": cD.cpu(), "z": cz.cpu(), "delta_bias": cbias.cpu()}
+
+        def run_c(nd):
+            oracle.fwd_complex(**{k: (v[..., :nd] if k in ("u", "delta", "z") else
+                                      v[:nd] if k in ("A", "D", "delta_bias") else v)
+                                  for k, v in cin.items()})
+
+        out["complex"]["cpu_baseline"] = cpu_oracle_rate(
+            run_c, Dc, Bc * Lc * Nc, 3.0, "numpy complex128 forward, all batch rows and steps")
     log(f"complex fwd {cfms * 1e3:.1f} us, bwd {cbms * 1e3:.1f} us")
     return out
 
@@ -377,7 +430,22 @@ def main():
             "algorithmic_bytes": bb,
             "n_kernels": ss.plan(descb, True).n_launches,
             "traffic": stored_traffic("ss_bwd_bwd"),
+            "roofline": alu_roofline(wb.updates / (bms * 1e-3), FLOPS_PER_UPDATE_BWD),
         }
+        if not args.no_cpu_baseline:
+            import oracle
+            log("timing the CPU oracle backward")
+
+            def run_b(nd):
+                sub = {k: (None if ib[k] is None else
+                           (ib[k][..., :nd] if k in ("u", "delta", "z", "dy") else
+                            ib[k][:nd] if k in ("A", "D", "delta_bias") else ib[k]))
+                       for k in keys + ("dy",)}
+                oracle.bwd(**sub)
+
+            result["backward"]["cpu_baseline"] = cpu_oracle_rate(
+                run_b, wb.dim, wb.batch * wb.seqlen * wb.dstate, 5.0,
+                "float64 C backward, all batch rows and steps")
         log(f"backward {bms * 1e3:.1f} us/call")
         del wsb, db
 
@@ -428,7 +496,8 @@ def main():
         del state
 
     if not args.no_variants:
-        result.update(variant_legs(ss, w, dev, args_f, keys, max(5, args.steps // 2)))
+        result.update(variant_legs(ss, w, dev, args_f, keys, max(5, args.steps // 2),
+                                   with_cpu=not args.no_cpu_baseline))
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
