@@ -927,3 +927,47 @@ def test_random_shapes(seed):
         t = max(tol, TOL[inp["A"].dtype]) if k in ("dA", "dD", "ddelta_bias", "dh0") else tol
         e = rel_err(to_np(g[k]), r[k])
         assert e <= t, f"{k}: {e:.3e}"
+
+
+# ------------------------------------------- tensors beyond 2^31 bytes
+
+def test_tensors_beyond_2gib():
+    """u / delta / z / y of 4.3 GB each (2 x 262144 x 4096 bf16): the chunked
+    forward and the backward address them through per-chunk 32-bit ranges on
+    64-bit bases.  Checked on sampled channels (generated on the device with
+    a seeded generator; the oracle sees the sampled channels' slices)."""
+    Bn, L, D, N = 2, 262144, 4096, 16
+    g = torch.Generator(device=DEV).manual_seed(5001)
+    rn = lambda *sh: torch.randn(*sh, generator=g, device=DEV)
+    u = rn(Bn, L, D).to(torch.bfloat16)
+    delta = (rn(Bn, L, D) * 0.5 - 1.0).to(torch.bfloat16)
+    z = rn(Bn, L, D).to(torch.bfloat16)
+    B = rn(Bn, L, N).to(torch.bfloat16)
+    C = rn(Bn, L, N).to(torch.bfloat16)
+    A = -torch.exp(rn(D, N))
+    Dv = rn(D) * 0.1 + 1.0
+    bias = rn(D) * 0.1 - 4.0
+    assert u.numel() * u.element_size() >= (1 << 32)       # 4 GiB per stream
+    say("beyond 2 GiB: forward", (Bn, L, D, N), "plan", ss.plan(ss._desc_for(u, A, True, 0)).n_chunks)
+    y, ls = ss.fwd(u, delta, A, B, C, Dv, z, bias, return_last_state=True)
+    torch.cuda.synchronize()
+    cd = torch.tensor([0, 1, 255, 2048, 3000, D - 1], device=DEV)
+    sl = lambda t: t[..., cd].cpu()
+    sub = {"u": sl(u), "delta": sl(delta), "A": A[cd].cpu(), "B": B.cpu(), "C": C.cpu(),
+           "D": Dv[cd].cpu(), "z": sl(z), "delta_bias": bias[cd].cpu()}
+    yr, lsr = oracle.fwd(**sub, return_last_state=True)
+    assert rel_err(to_np(sl(y)), yr) <= 2e-2
+    assert rel_err(to_np(ls[:, cd].cpu()), lsr) <= 1e-5
+    del y
+    say("beyond 2 GiB: backward")
+    dy = rn(Bn, L, D).to(torch.bfloat16)
+    gr = ss.bwd(u, delta, A, B, C, Dv, z, bias, dy=dy)
+    torch.cuda.synchronize()
+    r = oracle.bwd(**sub, dy=sl(dy))
+    for k in ("du", "ddelta", "dz"):
+        e = rel_err(to_np(sl(gr[k])), r[k])
+        assert e <= 2e-2, f"{k}: {e:.3e}"
+    for k in ("dA", "dD", "ddelta_bias"):
+        e = rel_err(to_np(gr[k][cd].cpu()), r[k])
+        assert e <= 2e-2, f"{k}: {e:.3e}"
+        say(f"  {k} {e:.2e}")
