@@ -4,9 +4,10 @@
 // "src/attention/selective_scan.rs", module docs, "Algorithm summary"), for
 // N <= 32.  Mapping:
 //
-//   * 8 consecutive lanes own one channel d: lane g holds states
-//     n = g*NS .. g*NS+NS-1 (NS = 1, 2 or 4).  A wave covers 8 channels, a
-//     256-lane workgroup 32.  This gives 8x the waves of one-lane-per-channel,
+//   * 8 lanes own one channel d: lanes c, c+8, ..., c+56 of a wave hold
+//     channel c of the wave's 8, and lane g of the channel (wave lane c + 8g)
+//     holds states n = g*NS .. g*NS+NS-1 (NS = 1, 2 or 4).  A wave covers 8
+//     channels, a 256-lane workgroup 32.  This gives 8x the waves of one-lane-per-channel,
 //     which the wave-per-SIMD issue rate needs (a lone wave issues far below
 //     the VALU rate; several resident waves per SIMD are needed to fill it).
 //   * Per-(t, d) work is time-shared: in every tile of 8 steps, lane g loads
@@ -14,8 +15,9 @@
 //     dt*u and the gate silu(z) for that step only, and hands (dt, dt*u) to
 //     the other 7 lanes of its channel through a per-wave LDS exchange.
 //   * The readout sum over a channel's states is a sum over its 8 lanes, done
-//     once per 8-step tile as a DPP reduce-scatter: lane g ends with the sum of
-//     step t0+g and applies the skip term and the gate to it.
+//     once per 8-step tile as a reduce-scatter (lane swaps and DPP): lane g
+//     ends with the sum of step t0+g and applies the skip term and the gate
+//     to it.
 //   * B and C are staged per workgroup in LDS as f32, [n][t] per 64-step tile,
 //     double buffered, rows padded to 68 floats (16-byte aligned, conflict-free
 //     128-bit reads); states n >= N are zero rows, so padded states stay 0.
@@ -31,7 +33,7 @@ namespace ss {
 namespace {
 
 constexpr int kBlockT = 256;
-constexpr int GL = 8;                 // lanes per channel
+constexpr int GL = 8;                 // lanes per channel (the lane maps below assume 8)
 constexpr int CPW = kBlockT / GL;     // channels per workgroup (32)
 constexpr int TB = 64;                // steps per B/C staging tile
 constexpr int TS = 68;                // LDS row stride of a staged row (floats)
@@ -43,39 +45,72 @@ __device__ __forceinline__ float dpp(float v) {
                                                             0xf, 0xf, true));
 }
 
-// Reduce-scatter over each group of 8 consecutive lanes: lane g of the group
-// holds o[0..7]; on return it holds the group's sum of o[g].  Three butterfly
-// stages (partners g^7 via row_half_mirror, g^2, g^1): at each stage a lane
-// keeps the half of its values whose index bit matches its own lane bit and
-// sends the other half, so each stage is one DPP add per kept value plus two
-// selects.  21 VALU ops for 8 sums instead of 8 x (3 DPP adds + 1 select).
+// A channel's 8 lanes are 8 apart in the wave (lane c + 8g), so that its
+// butterfly partners are 32, 16 and 8 lanes away: the first two stages are
+// the gfx950 lane swaps, the last a DPP rotate within a row of 16.
+//   permlane32_swap(p, q) returns (p, p of lane + 32) in lanes 0-31 and
+//   (q of lane - 32, q) in lanes 32-63; permlane16_swap does the same between
+//   rows 0/1 and 2/3 of 16 lanes.  Summing the two results gives the pair's
+//   sum of p in the lower lane and of q in the upper one, with no selects.
+// (The halves are copied to scalars before the float casts: this compiler
+// turns __builtin_bit_cast of the second vector element into a read of the
+// first.)
+__device__ __forceinline__ void swap32(float p, float q, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(q), false,
+                                                  false);
+  const unsigned r0 = r[0], r1 = r[1];
+  lo = __uint_as_float(r0);
+  hi = __uint_as_float(r1);
+}
+__device__ __forceinline__ void swap16(float p, float q, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(q), false,
+                                                  false);
+  const unsigned r0 = r[0], r1 = r[1];
+  lo = __uint_as_float(r0);
+  hi = __uint_as_float(r1);
+}
+
+// Reduce-scatter over a channel's 8 lanes: lane g holds o[0..7]; on return it
+// holds the channel's sum of o[g].  Stage 1 (partner g ^ 4, 32 lanes away):
+// lanes with g < 4 keep indices 0-3, the others 4-7; stage 2 (g ^ 2, 16
+// away) halves that again; stage 3 (g ^ 1, 8 away, DPP row_ror:8) keeps one
+// value with a select pair.  15 VALU ops for 8 sums (4 + 2 swaps, 7 adds,
+// 2 selects).
 __device__ __forceinline__ float reduce_scatter8(const float (&o)[8], int g) {
-  const bool lo4 = (g & 4) == 0, lo2 = (g & 2) == 0, lo1 = (g & 1) == 0;
   float ra[4], rb[2];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float send = lo4 ? o[4 + k] : o[k];
-    const float keep = lo4 ? o[k] : o[4 + k];
-    ra[k] = keep + dpp<0x141>(send);    // row_half_mirror: lane g <-> 7 - g
+    float x, y;
+    swap32(o[k], o[4 + k], x, y);
+    ra[k] = x + y;
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const float send = lo2 ? ra[2 + k] : ra[k];
-    const float keep = lo2 ? ra[k] : ra[2 + k];
-    rb[k] = keep + dpp<0x4E>(send);     // quad_perm [2,3,0,1]: g <-> g ^ 2
+    float x, y;
+    swap16(ra[k], ra[2 + k], x, y);
+    rb[k] = x + y;
   }
+  const bool lo1 = (g & 1) == 0;
   const float send = lo1 ? rb[1] : rb[0];
   const float keep = lo1 ? rb[0] : rb[1];
-  return keep + dpp<0xB1>(send);        // quad_perm [1,0,3,2]: g <-> g ^ 1
+  return keep + dpp<0x128>(send);       // row_ror:8: lane i <-> i ^ 8 within a row
 }
 
-// Sum over each group of 8 consecutive lanes; every lane gets its group's sum.
+// Sum over a channel's 8 lanes; every lane gets the channel's sum (the two
+// addends of each stage are the same pair in both lanes, so both round alike).
 __device__ __forceinline__ float sum8(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp<0x141>(v);  // row_half_mirror: lane i <-> 7 - i within 8
-  return v;
+  v += dpp<0x128>(v);   // row_ror:8
+  float x, y;
+  swap16(v, v, x, y);
+  v = x + y;
+  swap32(v, v, x, y);
+  return x + y;
 }
+
+// Lane roles in a 256-lane workgroup: wave w's lane c + 8g is lane g of
+// channel 8w + c.
+__device__ __forceinline__ int lane_g(int tid) { return (tid >> 3) & 7; }
+__device__ __forceinline__ int lane_channel(int tid) { return ((tid >> 6) << 3) | (tid & 7); }
 
 }  // namespace
 
@@ -100,8 +135,8 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
   __shared__ __attribute__((aligned(16))) float2 xch[2][CPW][XS];
 
   const int tid = threadIdx.x;
-  const int g = tid % GL;
-  const int cl = tid / GL;
+  const int g = lane_g(tid);
+  const int cl = lane_channel(tid);
   const int64_t nbd = (a.D + CPW - 1) / CPW;
   int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
   const int64_t db = blk % nbd;
@@ -371,8 +406,8 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   __shared__ __attribute__((aligned(16))) float2 xch[CPW][XS];
 
   const int tid = threadIdx.x;
-  const int g = tid % GL;
-  const int cl = tid / GL;
+  const int g = lane_g(tid);
+  const int cl = lane_channel(tid);
   const int64_t nbd = (a.D + CPW - 1) / CPW;
   int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
   const int64_t db = blk % nbd;
