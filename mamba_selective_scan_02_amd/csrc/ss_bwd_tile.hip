@@ -6,11 +6,12 @@
 // "Algorithm summary"; gradient set of its SelectiveScanBackwardArgs;
 // per-channel reverse sweep and fixed-order partial reductions as in stage B3
 // of the mamba-rs page "mamba_ssm/gpu/backward.rs").  Mapping as in the
-// forward tile kernel: 8 lanes own a channel, lane g holds states
-// n = g*NS .. g*NS+NS-1 (NS = 1 or 2); a wave is 8 channels, a 256-lane
-// workgroup 32; per 8-step tile, lane g prepares the per-step scalars of step
-// t0 + 8j + g and hands them to the channel's lanes through LDS; sums over a
-// channel's states are DPP reduce-scatters over its 8 lanes.
+// forward tile kernel: 8 lanes own a channel (8 apart in the wave), lane g
+// holds states n = g*NS .. g*NS+NS-1 (NS = 1 or 2); a wave is 8 channels, a
+// 256-lane workgroup 32; per 8-step tile, lane g prepares the per-step
+// scalars of step t0 + 8j + g and hands them to the channel's lanes through
+// LDS; sums over a channel's states are reduce-scatters over its 8 lanes
+// (lane swaps and DPP).
 //
 // Time is cut into chunks of at most 64 steps (8 tiles):
 //   bwd_tile_sum   per chunk, from zero: forward end state S, reverse summary
@@ -42,42 +43,6 @@ constexpr int BNT = BTC / BGL;        // tiles per chunk (8)
 constexpr int BTS = 68;               // staged B/C row stride (floats)
 constexpr int BXS = 9;                // exchange row stride (float4) per channel
 
-template <int CTRL>
-__device__ __forceinline__ float bdpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
-                                                            0xf, 0xf, true));
-}
-
-// Sum over each group of 8 consecutive lanes; every lane gets the sum.
-__device__ __forceinline__ float bsum8(float v) {
-  v += bdpp<0xB1>(v);
-  v += bdpp<0x4E>(v);
-  v += bdpp<0x141>(v);
-  return v;
-}
-
-// Lane g of each 8-lane group ends with the group's sum of o[g] (butterfly
-// over partners g^7, g^2, g^1; see the forward tile kernel).
-__device__ __forceinline__ float brs8(const float (&o)[8], int g) {
-  const bool lo4 = (g & 4) == 0, lo2 = (g & 2) == 0, lo1 = (g & 1) == 0;
-  float ra[4], rb[2];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float send = lo4 ? o[4 + k] : o[k];
-    const float keep = lo4 ? o[k] : o[4 + k];
-    ra[k] = keep + bdpp<0x141>(send);
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float send = lo2 ? ra[2 + k] : ra[k];
-    const float keep = lo2 ? ra[k] : ra[2 + k];
-    rb[k] = keep + bdpp<0x4E>(send);
-  }
-  const float send = lo1 ? rb[1] : rb[0];
-  const float keep = lo1 ? rb[0] : rb[1];
-  return keep + bdpp<0xB1>(send);
-}
-
 }  // namespace
 
 // Decoded position of a workgroup / lane (shared by the two kernels).
@@ -90,8 +55,8 @@ struct BTilePos {
 __device__ __forceinline__ BTilePos btile_pos(const BwdArgs& a) {
   BTilePos p;
   const int tid = threadIdx.x;
-  p.g = tid % BGL;
-  p.cl = tid / BGL;
+  p.g = lane_g(tid);
+  p.cl = lane_channel(tid);
   int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
   p.db = blk % a.nwgd;
   blk /= a.nwgd;
@@ -199,7 +164,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
     gg = valid ? gg : 0.0f;
     dsum += dl;
     xch[cl][g] = make_float4(dl, xu, gg, 0.0f);
-    const float dst = bsum8(dl);       // the tile's sum of dt (same on the 8 lanes)
+    const float dst = sum8(dl);       // the tile's sum of dt (same on the 8 lanes)
     float4 ex[BGL];
 #pragma unroll
     for (int s = 0; s < BGL; ++s) ex[s] = xch[cl][s];
@@ -237,7 +202,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
       PP[i] *= fast_exp2(A2[i] * dst);
     }
   }
-  dsum = bsum8(dsum);
+  dsum = sum8(dsum);
   if (!P.active) return;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -401,7 +366,7 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
     const Raw cur = prv;
     prv = raw(j > 0 ? j - 1 : 0, true);
     const Own o = own(j, true, cur);
-    const float dst = bsum8(o.dl);
+    const float dst = sum8(o.dl);
     xch[cl][g] = make_float4(o.dl, o.xu, o.gg, 0.0f);
     float4 ex[BGL];
 #pragma unroll
@@ -459,12 +424,12 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
       pdua[s] = vdua;
       pddl[s] = vddl;
       // dB / dC of (step s, these states) for the workgroup reduction: the
-      // two channels of a 16-lane row (lanes g and g + 8) are summed first
-      // (tail lanes contribute exact zeros)
+      // channel pair (2m, 2m + 1), neighbouring lanes with the same g, is
+      // summed first (tail lanes contribute exact zeros)
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        vb[i] += bdpp<0x128>(vb[i]);     // row_ror:8: the pair's other channel
-        vc[i] += bdpp<0x128>(vc[i]);
+        vb[i] += dpp<0xB1>(vb[i]);       // quad_perm [1,0,3,2]: the pair's other channel
+        vc[i] += dpp<0xB1>(vc[i]);
       }
       if ((cl & 1) == 0) {
         if (NS == 2) {
@@ -485,9 +450,9 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
       dh[i] = cj[i];
     }
     // per-step sums over the channel's states: lane g gets its own step's
-    const float o_own = brs8(po, g);
-    const float dua_own = brs8(pdua, g);
-    const float ddl_own = brs8(pddl, g);
+    const float o_own = reduce_scatter8(po, g);
+    const float dua_own = reduce_scatter8(pdua, g);
+    const float ddl_own = reduce_scatter8(pddl, g);
     const float du = __builtin_fmaf(o.dl, dua_own, o.gg * Dv);
     const float dx = o.valid ? __builtin_fmaf(o.uu, dua_own, ddl_own) * o.sx : 0.0f;
     const int so = j * sstep;
@@ -513,8 +478,8 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
   }
   // tail channels (d >= D) duplicate channel D-1: they must not add to the sums
   if (!P.active) { dD_acc = 0.0f; db_acc = 0.0f; }
-  dD_acc = bsum8(dD_acc);
-  db_acc = bsum8(db_acc);
+  dD_acc = sum8(dD_acc);
+  db_acc = sum8(db_acc);
   if (!P.active) return;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {

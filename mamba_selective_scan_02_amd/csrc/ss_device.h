@@ -287,4 +287,81 @@ struct BwdArgs {
   int io_dtype;
 };
 
+
+// ---------------------------------------------------------------------------
+// Lane maps and cross-lane sums of the 8-lanes-per-channel tile kernels
+// (forward and backward).  In a 256-lane workgroup, wave w's lane c + 8g is
+// lane g of channel 8w + c, so a channel's 8 lanes sit 8 apart.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xf, 0xf, true));
+}
+
+// A channel's 8 lanes are 8 apart in the wave (lane c + 8g), so that its
+// butterfly partners are 32, 16 and 8 lanes away: the first two stages are
+// the gfx950 lane swaps, the last a DPP rotate within a row of 16.
+//   permlane32_swap(p, q) returns (p, p of lane + 32) in lanes 0-31 and
+//   (q of lane - 32, q) in lanes 32-63; permlane16_swap does the same between
+//   rows 0/1 and 2/3 of 16 lanes.  Summing the two results gives the pair's
+//   sum of p in the lower lane and of q in the upper one, with no selects.
+// (The halves are copied to scalars before the float casts: this compiler
+// turns __builtin_bit_cast of the second vector element into a read of the
+// first.)
+__device__ __forceinline__ void swap32(float p, float q, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(q), false,
+                                                  false);
+  const unsigned r0 = r[0], r1 = r[1];
+  lo = __uint_as_float(r0);
+  hi = __uint_as_float(r1);
+}
+__device__ __forceinline__ void swap16(float p, float q, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(q), false,
+                                                  false);
+  const unsigned r0 = r[0], r1 = r[1];
+  lo = __uint_as_float(r0);
+  hi = __uint_as_float(r1);
+}
+
+// Reduce-scatter over a channel's 8 lanes: lane g holds o[0..7]; on return it
+// holds the channel's sum of o[g].  Stage 1 (partner g ^ 4, 32 lanes away):
+// lanes with g < 4 keep indices 0-3, the others 4-7; stage 2 (g ^ 2, 16
+// away) halves that again; stage 3 (g ^ 1, 8 away, DPP row_ror:8) keeps one
+// value with a select pair.  15 VALU ops for 8 sums (4 + 2 swaps, 7 adds,
+// 2 selects).
+__device__ __forceinline__ float reduce_scatter8(const float (&o)[8], int g) {
+  float ra[4], rb[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float x, y;
+    swap32(o[k], o[4 + k], x, y);
+    ra[k] = x + y;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float x, y;
+    swap16(ra[k], ra[2 + k], x, y);
+    rb[k] = x + y;
+  }
+  const bool lo1 = (g & 1) == 0;
+  const float send = lo1 ? rb[1] : rb[0];
+  const float keep = lo1 ? rb[0] : rb[1];
+  return keep + dpp<0x128>(send);       // row_ror:8: lane i <-> i ^ 8 within a row
+}
+
+// Sum over a channel's 8 lanes; every lane gets the channel's sum (the two
+// addends of each stage are the same pair in both lanes, so both round alike).
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<0x128>(v);   // row_ror:8
+  float x, y;
+  swap16(v, v, x, y);
+  v = x + y;
+  swap32(v, v, x, y);
+  return x + y;
+}
+
+__device__ __forceinline__ int lane_g(int tid) { return (tid >> 3) & 7; }
+__device__ __forceinline__ int lane_channel(int tid) { return ((tid >> 6) << 3) | (tid & 7); }
+
 }  // namespace ss
