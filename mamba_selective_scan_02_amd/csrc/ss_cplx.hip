@@ -553,11 +553,14 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_carry(const BwdArgs a)
 }
 
 template <typename Tio>
-__global__ __launch_bounds__(kChannelsPerBlock) void cbwd_main(const BwdArgs a) {
+__global__ __launch_bounds__(kChannelsPerBlock, 2) void cbwd_main(const BwdArgs a) {
   extern __shared__ float smem[];
   float* sB = smem;
   float* sC = smem + 2 * a.N * CT;
   float* red = smem + 4 * a.N * CT;  // [32][kCRedStride]
+  // u, the gate factor dz / (C h + D u) and sigmoid(x) of each (step, lane):
+  // needed only at the chunk's end, so they wait in LDS, not in VGPRs
+  float* sst = red + 32 * kCRedStride;  // [3][CT][kChannelsPerBlock]
   const int tid = threadIdx.x;
   const int64_t nbd = a.nwgd;
   int64_t blk = blockIdx.x;
@@ -595,7 +598,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_main(const BwdArgs a) 
     load_cbc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C),
                   b * L + t0, nt, N);
 
-    float uu[CT], dl[CT], xu[CT], gg[CT], gz[CT], sx[CT], oo[CT], ddl[CT], dua[CT];
+    float dl[CT], xu[CT], gg[CT], oo[CT], ddl[CT], dua[CT];
 #pragma unroll
     for (int tt = 0; tt < CT; ++tt) {
       const bool ok = tt < nt;
@@ -609,12 +612,12 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_main(const BwdArgs a) 
         g = dy * zz * s;
         gzv = dy * s * __builtin_fmaf(zz, 1.0f - s, 1.0f);
       }
-      uu[tt] = ok ? u_ : 0.0f;
+      sst[(0 * CT + tt) * kChannelsPerBlock + tid] = ok ? u_ : 0.0f;
+      sst[(1 * CT + tt) * kChannelsPerBlock + tid] = gzv;
+      sst[(2 * CT + tt) * kChannelsPerBlock + tid] = sxv;
       dl[tt] = ok ? dlv : 0.0f;
       xu[tt] = ok ? dlv * u_ : 0.0f;
       gg[tt] = ok ? g : 0.0f;
-      gz[tt] = gzv;
-      sx[tt] = sxv;
       oo[tt] = 0.0f;
       ddl[tt] = 0.0f;
       dua[tt] = 0.0f;
@@ -654,17 +657,18 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_main(const BwdArgs a) 
         ahi[tt] = mi;
         oo[tt] = __builtin_fmaf(cn[2 * tt], pr, __builtin_fmaf(-cn[2 * tt + 1], pi, oo[tt]));
       }
-      float vBr[CT], vBi[CT], vCr[CT], vCi[CT];
+      // dB / dC of (step, this n) go straight to the LDS reduction rows;
+      // inactive (tail) lanes contribute zero
       float dAr = 0.0f, dAi = 0.0f;
 #pragma unroll
       for (int tt = CT - 1; tt >= 0; --tt) {
         // lam = dh + g conj(C)
         const float lr = __builtin_fmaf(gg[tt], cn[2 * tt], dhr);
         const float li = __builtin_fmaf(-gg[tt], cn[2 * tt + 1], dhi);
-        vCr[tt] = gg[tt] * hsr[tt];
-        vCi[tt] = -gg[tt] * hsi[tt];
-        vBr[tt] = lr * xu[tt];
-        vBi[tt] = li * xu[tt];
+        red[(0 * CT + tt) * kCRedStride + tid] = active ? lr * xu[tt] : 0.0f;
+        red[(1 * CT + tt) * kCRedStride + tid] = active ? li * xu[tt] : 0.0f;
+        red[(2 * CT + tt) * kCRedStride + tid] = active ? gg[tt] * hsr[tt] : 0.0f;
+        red[(3 * CT + tt) * kCRedStride + tid] = active ? -gg[tt] * hsi[tt] : 0.0f;
         dua[tt] = __builtin_fmaf(bn[2 * tt], lr, __builtin_fmaf(bn[2 * tt + 1], li, dua[tt]));
         // m = conj(a) lam = lam + conj(a - 1) lam
         float mr = lr, mi = li;
@@ -695,15 +699,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_main(const BwdArgs a) 
           st_param(a.dh0, 2 * ((b * D + d) * N + n) + 1, pd, dhi);
         }
       }
-      // dB / dC for this n: sums over the workgroup's channels in LDS.
-      // Inactive (tail) lanes contribute zero.
-#pragma unroll
-      for (int tt = 0; tt < CT; ++tt) {
-        red[(0 * CT + tt) * kCRedStride + tid] = active ? vBr[tt] : 0.0f;
-        red[(1 * CT + tt) * kCRedStride + tid] = active ? vBi[tt] : 0.0f;
-        red[(2 * CT + tt) * kCRedStride + tid] = active ? vCr[tt] : 0.0f;
-        red[(3 * CT + tt) * kCRedStride + tid] = active ? vCi[tt] : 0.0f;
-      }
+      // dB / dC for this n: sums over the workgroup's channels in LDS
       __syncthreads();
       float s = 0.0f;
 #pragma unroll
@@ -724,14 +720,17 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_main(const BwdArgs a) 
     for (int tt = 0; tt < CT; ++tt) {
       if (tt < nt && active) {
         const int64_t t = t0 + tt;
+        const float uu = sst[(0 * CT + tt) * kChannelsPerBlock + tid];
+        const float gz = sst[(1 * CT + tt) * kChannelsPerBlock + tid];
+        const float sx = sst[(2 * CT + tt) * kChannelsPerBlock + tid];
         const float du = __builtin_fmaf(dl[tt], dua[tt], has_D ? gg[tt] * Dv : 0.0f);
-        const float dde = __builtin_fmaf(uu[tt], dua[tt], ddl[tt]);
-        const float dx = dde * sx[tt];
+        const float dde = __builtin_fmaf(uu, dua[tt], ddl[tt]);
+        const float dx = dde * sx;
         dup[t * D] = from_f32<Tio>(du);
         ddp[t * D] = from_f32<Tio>(dx);
-        if (has_z) dzp[t * D] = from_f32<Tio>(gz[tt] * __builtin_fmaf(Dv, uu[tt], oo[tt]));
+        if (has_z) dzp[t * D] = from_f32<Tio>(gz * __builtin_fmaf(Dv, uu, oo[tt]));
         db_acc += dx;
-        dD_acc = __builtin_fmaf(gg[tt], uu[tt], dD_acc);
+        dD_acc = __builtin_fmaf(gg[tt], uu, dD_acc);
       }
     }
   }
@@ -819,7 +818,8 @@ hipError_t launch_cbwd_t(const BwdArgs& a, hipStream_t s) {
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  const size_t main_bytes = tile_bytes + sizeof(float) * 32 * kCRedStride;
+  const size_t main_bytes =
+      tile_bytes + sizeof(float) * (32 * kCRedStride + 3 * CT * kChannelsPerBlock);
   if (main_bytes > 64 * 1024) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&cbwd_main<Tio>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)main_bytes);
