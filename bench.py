@@ -113,6 +113,25 @@ def algorithmic_bytes_bwd(w) -> int:
     return nbytes
 
 
+def time_each(fn, reps: int, scratch=None):
+    """Per-call durations (ms) of `reps` calls of fn(), each bracketed by its
+    own HIP events on the launch stream.  With `scratch` (a 1 GiB device
+    buffer) every call is preceded by a write of the whole buffer, which
+    evicts L2 and the 256 MB MALL: the call then reads its inputs from HBM."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps):
+        if scratch is not None:
+            scratch.fill_(i)
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def time_calls(fn, steps: int, warmup: int):
     """Average duration of fn() over `steps` back-to-back calls, from HIP events
     recorded on the stream the kernels are launched on."""
@@ -320,6 +339,70 @@ def variant_legs(ss, w, dev, args_f, keys, steps, with_cpu=False):
     return out
 
 
+CONFIG_NAMES = ("tiny", "m130m", "m2p8b", "long", "bwd")
+
+
+def configs_leg(ss, reps: int, names=CONFIG_NAMES):
+    """Every forward workload and the backward one, each timed per call warm
+    (back to back) and cold (L2 and MALL evicted before every call): median,
+    min and max, with updates/s and algorithmic GB/s at the cold median."""
+    import statistics
+    import torch
+    from ss_inputs import WORKLOADS, make_inputs
+    keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    out = {}
+    for name in names:
+        w = WORKLOADS[name]
+        log(f"configs: {name}")
+        inp = make_inputs(w)
+        dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+        del inp
+        args_f = [dev[k] for k in keys]
+        io = {"f32": 0, "f16": 1, "bf16": 2}[w.io_dtype]
+        pa = {"f32": 0, "f16": 1, "bf16": 2}[w.param_dtype]
+        desc = ss.SsDesc(w.batch, w.seqlen, w.dim, w.dstate, 1, io, pa, 0)
+        if w.backward:
+            ws = torch.empty(max(1, ss.workspace_size(desc, True)), dtype=torch.uint8,
+                             device="cuda")
+
+            def fn():
+                ss.bwd(*args_f, dy=dev["dy"], workspace=ws)
+            nbytes = algorithmic_bytes_bwd(w)
+            launches = ss.plan(desc, True).n_launches
+        else:
+            ws = torch.empty(max(1, ss.workspace_size(desc)), dtype=torch.uint8, device="cuda")
+            y = torch.empty_like(dev["u"])
+            ls = (torch.empty(w.batch, w.dim, w.dstate, dtype=dev["A"].dtype, device="cuda")
+                  if w.last_state else None)
+
+            def fn():
+                ss.fwd(*args_f, y=y, workspace=ws, last_state=ls)
+            nbytes = algorithmic_bytes(w)
+            launches = ss.plan(desc).n_launches
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        warm = time_each(fn, reps)
+        cold = time_each(fn, reps, scratch)
+        med = statistics.median(cold)
+        out[name] = {
+            "shape": f"B={w.batch}, L={w.seqlen}, D={w.dim}, N={w.dstate}, {w.io_dtype} io",
+            "call": "ss_bwd" if w.backward else "ss_fwd", "launches": launches,
+            "warm_us": {"median": statistics.median(warm) * 1e3, "min": min(warm) * 1e3,
+                        "max": max(warm) * 1e3},
+            "cold_us": {"median": med * 1e3, "min": min(cold) * 1e3, "max": max(cold) * 1e3},
+            "state_updates_per_s_cold": w.updates / (med * 1e-3),
+            "hbm_gbs_cold": nbytes / (med * 1e-3) / 1e9,
+            "hbm_frac_cold": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": nbytes,
+        }
+        del dev, args_f, ws
+        torch.cuda.empty_cache()
+    del scratch
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -334,6 +417,11 @@ def main():
                     help="skip the strided-B/C, packed-sequence and complex legs")
     ap.add_argument("--variants-only", action="store_true",
                     help="time only those legs (for a kernel trace of them alone)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload warm / cold timings")
+    ap.add_argument("--configs-only", nargs="*", choices=CONFIG_NAMES, default=None,
+                    metavar="NAME",
+                    help="only the per-workload timings (of the named workloads, default all)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a plain 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
@@ -349,6 +437,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calib_copy:
         calibration_copy()
+    if args.configs_only is not None:
+        names = tuple(args.configs_only) or CONFIG_NAMES
+        print(json.dumps({"configs": configs_leg(ss, args.steps, names)}), flush=True)
+        return
     keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
     w = WORKLOADS["m2p8b"]
     log(f"generating {w.name} inputs")
@@ -498,6 +590,9 @@ def main():
     if not args.no_variants:
         result.update(variant_legs(ss, w, dev, args_f, keys, max(5, args.steps // 2),
                                    with_cpu=not args.no_cpu_baseline))
+
+    if not args.no_configs:
+        result["configs"] = configs_leg(ss, args.steps)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
