@@ -81,14 +81,16 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
       // waves to approach its VALU rate (a lone wave issues at about a third
       // of it), so below ~3 waves per SIMD (1024 SIMDs) the time axis is cut
       // into chunks until the grid reaches about 4 waves per SIMD, with chunks
-      // of at least 64 steps; the chunk summaries cost one extra sweep.
+      // of at least 128 steps; the chunk summaries cost one extra sweep and
+      // two more launches, which a sequence of fewer than 256 steps does not
+      // earn back (1x128x32x16: 17.8 us in 3 launches).
       const int64_t cpw = 64 / p.G;
       const int64_t waves = Bn * ((D + cpw - 1) / cpw);
       const int64_t target = 4096;
       int64_t K = 1;
       if (waves < 3072) {
         K = (target + waves - 1) / waves;
-        const int64_t kmax = (L + 63) / 64;
+        const int64_t kmax = L / 128;
         if (K > kmax) K = kmax;
         if (K < 1) K = 1;
       }
