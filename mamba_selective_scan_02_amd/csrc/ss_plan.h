@@ -174,8 +174,8 @@ constexpr int kCplxBwdTile = 8;
 inline Plan make_plan_complex(const ss_desc& d, bool backward) {
   Plan p;
   const int64_t Bn = d.batch, L = d.seqlen, D = d.dim, N = d.dstate;
-  // At most 4 states per lane up to N = 64: the complex step is long
-  // (double-precision exp and sincos per state), so more lanes per channel buy
+  // At most 4 states per lane up to N = 64: the complex step is long (exp
+  // and sin / cos from their series per state), so more lanes per channel buy
   // the waves that hide its latency at little cost in the readout sum.
   if (N <= 4) {
     p.G = 1;
