@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
   const int ntile = (int)((nsteps + BGL - 1) / BGL);
   // the lane's own-step inputs, loaded one tile ahead
   auto raw = [&](int j, float& uu, float& dr, float& dyv, float& zz) {
-    const int so = j * sstep;
+    const int so = __builtin_amdgcn_readfirstlane(j * sstep);
     uu = buf_ld<T>(rs_u, voff, so);
     dr = buf_ld<T>(rs_d, voff, so);
     dyv = buf_ld<T>(rs_y, voff, so);
@@ -275,14 +275,17 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
   // stores go past the buffer range and are dropped.
   const int voff_st = P.active ? voff : (int)rbytes;
   const int sstep = (int)(BGL * D * ES);
-  const int ntile = (int)((nsteps + BGL - 1) / BGL);
+  // (uniform, and kept in a scalar register: the tile index feeds the buffer
+  // instructions' scalar offsets, which the compiler otherwise fills through
+  // per-lane loops when it keeps the index in a vector register)
+  const int ntile = __builtin_amdgcn_readfirstlane((int)((nsteps + BGL - 1) / BGL));
   __syncthreads();
 
   // raw inputs of the lane's own step in tile j (loaded one tile ahead)
   struct Raw { float uu, dr, dyv, zz; };
   auto raw = [&](int j, bool full) {
     Raw r;
-    const int so = j * sstep;
+    const int so = __builtin_amdgcn_readfirstlane(j * sstep);
     r.uu = buf_ld<T>(rs_u, voff, so);
     r.dr = buf_ld<T>(rs_d, voff, so);
     r.dyv = full ? buf_ld<T>(rs_y, voff, so) : 0.0f;
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
   Raw prv = raw(ntile - 1, true);
   for (int j = ntile - 1; j >= 0; --j) {
     const Raw cur = prv;
-    prv = raw(j > 0 ? j - 1 : 0, true);
+    prv = raw(__builtin_amdgcn_readfirstlane(j > 0 ? j - 1 : 0), true);
     const Own o = own(j, true, cur);
     const float dst = sum8(o.dl);
     xch[cl][g] = make_float4(o.dl, o.xu, o.gg, 0.0f);
@@ -455,7 +458,7 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
     const float ddl_own = reduce_scatter8(pddl, g);
     const float du = __builtin_fmaf(o.dl, dua_own, o.gg * Dv);
     const float dx = o.valid ? __builtin_fmaf(o.uu, dua_own, ddl_own) * o.sx : 0.0f;
-    const int so = j * sstep;
+    const int so = __builtin_amdgcn_readfirstlane(j * sstep);
     buf_st<T>(du, ws_du, voff_st, so);       // steps past the chunk are dropped
     buf_st<T>(dx, ws_dd, voff_st, so);
     if (HAS_Z) buf_st<T>(o.gz * __builtin_fmaf(Dv, o.uu, o_own), ws_dz, voff_st, so);
