@@ -35,6 +35,23 @@ FLOPS_PER_UPDATE_BWD = 18
 # Complex forward, per complex state update: dt*A (2), exp and sincos (2),
 # (a - 1)*h + x + h (8), (dt*u)*B (2), Re(C*h) accumulated (4): 18.
 FLOPS_PER_UPDATE_COMPLEX = 18
+# Instruction-mix floor: the same work priced at the issue rates measured on
+# the box by microbench/rates.hip (profiles/hw_rates_mi355x.txt, 4 waves per
+# SIMD): one wave instruction per SIMD every 4.29 ns for v_exp_f32 and every
+# 1.246 ns for an FP32 FMA-class op, 1024 SIMDs, 64 lanes.  Per update, the
+# forward needs 1 exp + 4 ops (dt*A, (dt*u)*B, a*h + x, C*h); the backward
+# 3 exp + 20 ops (summary: exp + 5; pass 1: exp + 2; pass 2: exp + 2, the
+# readout 1 and the adjoint 10); the complex forward's decay is not an exp
+# instruction and is left out.
+EXP_NS, OP_NS, SIMDS = 4.29, 1.246, 1024
+
+
+def mix_floor(updates_per_s: float, n_exp: int, n_ops: int) -> dict:
+    floor = 64 * SIMDS / ((n_exp * EXP_NS + n_ops * OP_NS) * 1e-9)
+    return {"updates_per_s": floor, "frac": updates_per_s / floor, "exp_per_update": n_exp,
+            "ops_per_update": n_ops}
+
+
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mamba_selective_scan_02_amd", "csrc")
 
@@ -152,11 +169,14 @@ def time_calls(fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps, wall
 
 
-def alu_roofline(updates_per_s: float, flops_per_update: int) -> dict:
+def alu_roofline(updates_per_s: float, flops_per_update: int, mix=None) -> dict:
     achieved = updates_per_s * flops_per_update / 1e12
-    return {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
-            "flops_per_update": flops_per_update}
+    r = {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+         "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+         "flops_per_update": flops_per_update}
+    if mix is not None:
+        r["mix_floor"] = mix_floor(updates_per_s, *mix)
+    return r
 
 
 def cpu_oracle_rate(run, total_channels: int, updates_per_channel: int, budget_s: float,
@@ -263,7 +283,7 @@ def variant_legs(ss, w, dev, args_f, keys, steps, with_cpu=False):
                     f"[{B8}, {L8}, {R + 2 * N8}] (row stride {R + 2 * N8})",
         "us_per_call": sms * 1e3, "state_updates_per_s": w.updates / (sms * 1e-3),
         "us_per_call_gather_then_scan": gms * 1e3,
-        "roofline": alu_roofline(w.updates / (sms * 1e-3), FLOPS_PER_UPDATE),
+        "roofline": alu_roofline(w.updates / (sms * 1e-3), FLOPS_PER_UPDATE, (1, 4)),
     }
     log(f"strided {sms * 1e3:.1f} us, gather + scan {gms * 1e3:.1f} us")
     del xdbl, sargs
@@ -288,7 +308,7 @@ def variant_legs(ss, w, dev, args_f, keys, steps, with_cpu=False):
                     f"of {min(lens)}..{max(lens)} steps (D=5120, N=16, bf16)",
         "us_per_call": vms * 1e3, "state_updates_per_s": w.updates / (vms * 1e-3),
         "hbm_gbs": fbytes / (vms * 1e-3) / 1e9,
-        "roofline": alu_roofline(w.updates / (vms * 1e-3), FLOPS_PER_UPDATE),
+        "roofline": alu_roofline(w.updates / (vms * 1e-3), FLOPS_PER_UPDATE, (1, 4)),
     }
     log(f"varlen {vms * 1e3:.1f} us")
     del pk, yv
@@ -493,7 +513,8 @@ def main():
                      "frac": tflops / FP32_VECTOR_PEAK_TFLOPS,
                      "flops_per_update": FLOPS_PER_UPDATE,
                      "traffic": stored_traffic("fwd_wide_m2p8b"),
-                     "hbm_achieved_gbs": gbs, "hbm_peak_gbs": HBM_PEAK_GBS},
+                     "hbm_achieved_gbs": gbs, "hbm_peak_gbs": HBM_PEAK_GBS,
+                     "mix_floor": mix_floor(value, 1, 4)},
         "wall_s": wall,
     }
     del y, ws
@@ -522,7 +543,7 @@ def main():
             "algorithmic_bytes": bb,
             "n_kernels": ss.plan(descb, True).n_launches,
             "traffic": stored_traffic("ss_bwd_bwd"),
-            "roofline": alu_roofline(wb.updates / (bms * 1e-3), FLOPS_PER_UPDATE_BWD),
+            "roofline": alu_roofline(wb.updates / (bms * 1e-3), FLOPS_PER_UPDATE_BWD, (3, 20)),
         }
         if not args.no_cpu_baseline:
             import oracle
