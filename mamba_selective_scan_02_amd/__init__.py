@@ -221,7 +221,8 @@ def _raise(status: int, who: str):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # (a plain int: ctypes converts it for the c_void_p parameters)
+    return None if t is None else t.data_ptr()
 
 
 def _check(t: Optional[torch.Tensor], name: str, shape, dtype, device, contiguous=True):
@@ -229,7 +230,7 @@ def _check(t: Optional[torch.Tensor], name: str, shape, dtype, device, contiguou
         return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:                      # torch.Size compares equal to a tuple
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
