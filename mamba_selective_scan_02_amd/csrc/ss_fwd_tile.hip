@@ -1,6 +1,6 @@
 // Forward selective scan with a channel's states split over 8 lanes (gfx950).
 //
-// Same recurrence as ss_fwd.hip (baracuda-kernels page
+// Same recurrence as ss_fwd_scan.h (baracuda-kernels page
 // "src/attention/selective_scan.rs", module docs, "Algorithm summary"), for
 // N <= 32.  Mapping:
 //
@@ -23,7 +23,7 @@
 //     128-bit reads); states n >= N are zero rows, so padded states stay 0.
 //
 // Chunk summaries, the carry and the chunked final pass follow the same
-// two-level scheme as ss_fwd.hip and share its workspace layout.
+// two-level scheme as ss_fwd_scan.h and share its workspace layout.
 #include <type_traits>
 
 #include "ss_device.h"
