@@ -900,7 +900,7 @@ def _random_case(seed):
     return Bn, L, D, N, io, pa, opts, chunk, bool(rng.random() < 0.5)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_shapes(seed):
     """Seeded random shapes, dtypes, options, forced chunk lengths and initial
     states: forward and backward against the oracle."""
