@@ -743,6 +743,40 @@ def test_bwd_complex(case):
                 assert e <= tol, f"{k} chunk {chunk} h0 {with_h0}: {e:.3e}"
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_complex_random_shapes(seed):
+    """Seeded random complex cases (every lanes-per-channel bucket up to
+    N = 256, io dtypes, forced chunk lengths, h0): forward and backward
+    against the oracle."""
+    rng = np.random.default_rng(7000 + seed)
+    N = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 17, 24, 32, 40, 64, 65, 100, 128, 200, 256]))
+    L = int(rng.choice([1, 2, 7, 33, 64, 65, 130, 300]))
+    D = int(rng.integers(1, 130))
+    Bn = int(rng.integers(1, 4))
+    io = str(rng.choice(["f32", "f32", "bf16", "f16"]))
+    chunk = int(rng.choice([0, 0, 3, 8, 24]))
+    with_h0 = bool(rng.random() < 0.5)
+    say("complex random case", seed, (Bn, L, D, N), io, "chunk", chunk, "h0", with_h0)
+    inp, h0 = _complex_inputs(Bn, L, D, N, seed=7100 + seed, io=io, backward=True)
+    hh = h0 if with_h0 else None
+    d = to_dev(inp)
+    hd = None if hh is None else hh.to(DEV)
+    y, ls = ss.fwd_complex(*[d[k] for k in KEYS], h0=hd, return_last_state=True, chunk_len=chunk)
+    g = ss.bwd_complex(*[d[k] for k in KEYS], dy=d["dy"], chunk_len=chunk, h0=hd)
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd_complex(**{k: inp[k] for k in KEYS}, h0=hh)
+    r = oracle.bwd_complex(**{k: inp[k] for k in KEYS}, dy=inp["dy"], h0=hh)
+    tol = TOL[inp["u"].dtype]
+    assert rel_err(to_np(y), yr) <= tol
+    assert rel_err(to_np(ls), lsr) <= max(tol, TOL[inp["A"].dtype])
+    for k in GRADS + ("dh0",):
+        if r[k] is None:
+            assert g[k] is None
+            continue
+        e = rel_err(to_np(g[k]), r[k])
+        assert e <= tol, f"{k}: {e:.3e}"
+
+
 def test_complex_decode_empty_and_determinism():
     # an in-place L = 1 step on a carried complex state
     inp, h0 = _complex_inputs(3, 1, 300, 16, seed=3201)
