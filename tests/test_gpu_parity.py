@@ -551,6 +551,48 @@ def test_varlen_matches_dense_batch():
 
 # ---------------------------------------------- B / C as strided column slices
 
+@pytest.mark.parametrize("seed", range(16))
+def test_varlen_random(seed):
+    """Seeded random packed-sequence cases (1-6 sequences of 0-500 steps,
+    dtypes, N, forced chunk lengths, h0): forward and backward against the
+    oracle."""
+    rng = np.random.default_rng(8000 + seed)
+    S = int(rng.integers(1, 7))
+    lens = [int(rng.choice([0, 1, 2, 15, 16, 17, 63, 64, 65, 130, 257, 500])) for _ in range(S)]
+    if sum(lens) == 0:
+        lens[0] = 5
+    D = int(rng.integers(1, 130))
+    N = int(rng.choice([1, 4, 8, 16, 16, 17, 32, 64]))
+    io = str(rng.choice(["f32", "f32", "bf16", "f16"]))
+    chunk = int(rng.choice([0, 0, 3, 24, 64]))
+    with_h0 = bool(rng.random() < 0.5)
+    say("varlen random case", seed, lens, D, N, io, "chunk", chunk, "h0", with_h0)
+    p, cu, Lmax = _packed(S, lens, D, N, seed=8100 + seed, io=io, backward=True)
+    g = torch.Generator().manual_seed(8200 + seed)
+    h0 = (torch.randn(S, D, N, generator=g, dtype=torch.float64).to(p["A"].dtype)
+          if with_h0 else None)
+    d = to_dev(p)
+    cu_d = torch.as_tensor(cu, device=DEV)
+    hd = None if h0 is None else h0.to(DEV)
+    y, ls = ss.fwd_varlen(d["u"], d["delta"], d["A"], d["B"], d["C"], cu_d, Lmax, d["D"],
+                          d["z"], d["delta_bias"], chunk_len=chunk, h0=hd, return_last_state=True)
+    gr = ss.bwd_varlen(d["u"], d["delta"], d["A"], d["B"], d["C"], cu_d, Lmax, d["D"], d["z"],
+                       d["delta_bias"], d["dy"], chunk_len=chunk, h0=hd)
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd_varlen(**{k: p[k] for k in KEYS}, cu_seqlens=cu, h0=h0)
+    r = oracle.bwd_varlen(**{k: p[k] for k in KEYS}, dy=p["dy"], cu_seqlens=cu, h0=h0)
+    tol = TOL[p["u"].dtype]
+    ptol = max(tol, TOL[p["A"].dtype])
+    assert rel_err(to_np(y), yr) <= tol
+    assert rel_err(to_np(ls), lsr) <= ptol
+    for k in GRADS + ("dh0",):
+        if r[k] is None:
+            assert gr[k] is None
+            continue
+        e = rel_err(to_np(gr[k]), r[k])
+        assert e <= (ptol if k in ("dA", "dD", "ddelta_bias", "dh0") else tol), f"{k}: {e:.3e}"
+
+
 def _xdbl(B, C, R, seed):
     """A [..., R + 2N] x-projection-like matrix with B at column R and C at
     R + N (the dt columns hold seeded noise), on the device."""
