@@ -612,6 +612,41 @@ STRIDED_CASES = [  # (B, L, D, N, io, R): R = columns before B in each row
 ]
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_strided_random(seed):
+    """Seeded random shapes, dtypes, column offsets R and chunk lengths: B / C
+    read as column slices of an x-projection-like matrix give the packed
+    call's results bit for bit (forward and backward), dB / dC land in their
+    columns, and the other columns stay untouched."""
+    rng = np.random.default_rng(9000 + seed)
+    Bn = int(rng.integers(1, 4))
+    L = int(rng.choice([1, 5, 17, 64, 65, 200, 700]))
+    D = int(rng.integers(1, 300))
+    N = int(rng.choice([1, 4, 8, 16, 16, 17, 32, 64, 128]))
+    io = str(rng.choice(["f32", "bf16", "bf16", "f16"]))
+    R = int(rng.choice([1, 2, 3, 4, 7, 8, 160]))
+    chunk = int(rng.choice([0, 0, 3, 24]))
+    say("strided random case", seed, (Bn, L, D, N), io, "R", R, "chunk", chunk)
+    inp = random_inputs(Bn, L, D, N, seed=9100 + seed, io_dtype=io, backward=True)
+    h0 = _state(inp, 9200 + seed).to(DEV)
+    d = to_dev(inp)
+    x, Bv, Cv = _xdbl(d["B"], d["C"], R, 9300 + seed)
+    args = {k: d[k] for k in KEYS}
+    y0, ls0 = ss.fwd(**args, return_last_state=True, chunk_len=chunk, h0=h0)
+    g0 = ss.bwd(**args, dy=d["dy"], chunk_len=chunk, h0=h0)
+    args.update(B=Bv, C=Cv)
+    y1, ls1 = ss.fwd(**args, return_last_state=True, chunk_len=chunk, h0=h0)
+    dx = torch.full_like(x, 7.0)
+    g1 = ss.bwd(**args, dy=d["dy"], chunk_len=chunk, h0=h0, dB=dx[..., R:R + N],
+                dC=dx[..., R + N:])
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(ls0, ls1)
+    assert torch.all(dx[..., :R] == 7.0)
+    for k in GRADS + ("dh0",):
+        if g0[k] is not None:
+            assert torch.equal(g0[k], g1[k]), k
+
+
 @pytest.mark.parametrize("case", STRIDED_CASES, ids=lambda c: "x".join(map(str, c)))
 def test_fwd_strided_bc(case):
     Bn, L, D, N, io, R = case
