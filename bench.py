@@ -35,6 +35,11 @@ FLOPS_PER_UPDATE_BWD = 18
 # Complex forward, per complex state update: dt*A (2), exp and sincos (2),
 # (a - 1)*h + x + h (8), (dt*u)*B (2), Re(C*h) accumulated (4): 18.
 FLOPS_PER_UPDATE_COMPLEX = 18
+# Complex backward, per complex state update: the forward recompute (18) plus
+# the adjoint lam = g*conj(C) + dh (4), dB = (dt*u)*lam (2), dC = g*conj(h)
+# (2), m = conj(a)*lam (6), dw = m*conj(h_prev) (6), Re(conj(A)*dw) (3),
+# dA += dt*dw (4), Re(conj(B)*lam) (3): 48.
+FLOPS_PER_UPDATE_COMPLEX_BWD = 48
 # Instruction-mix floor: the same work priced at the issue rates measured on
 # the box by microbench/rates.hip (profiles/hw_rates_mi355x.txt, 4 waves per
 # SIMD): one wave instruction per SIMD every 4.29 ns for v_exp_f32 and every
@@ -341,6 +346,7 @@ def variant_legs(ss, w, dev, args_f, keys, steps, with_cpu=False):
         "fwd_hbm_gbs": cfb / (cfms * 1e-3) / 1e9,
         "bwd_us_per_call": cbms * 1e3, "bwd_state_updates_per_s": upd / (cbms * 1e-3),
         "fwd_roofline": alu_roofline(upd / (cfms * 1e-3), FLOPS_PER_UPDATE_COMPLEX),
+        "bwd_roofline": alu_roofline(upd / (cbms * 1e-3), FLOPS_PER_UPDATE_COMPLEX_BWD),
     }
     if with_cpu:
         import oracle
