@@ -152,6 +152,42 @@ def test_fwd_degenerate():
         assert y.numel() == 0
 
 
+def test_extreme_inputs():
+    """Softplus and decay extremes: pre-softplus delta at +-30 (dt = 30, a
+    state reset each step; dt ~ 1e-13, a state held), A = 0 on some states
+    (a running sum), u = 0 on some channels: forward and backward against
+    the oracle."""
+    Bn, L, D, N = 2, 97, 40, 16
+    inp = random_inputs(Bn, L, D, N, seed=5101, backward=True)
+    g = torch.Generator().manual_seed(5102)
+    pick = torch.randint(0, 5, (Bn, L, D), generator=g)
+    vals = torch.tensor([-30.0, -10.0, 0.0, 10.0, 30.0], dtype=torch.float64)
+    inp["delta"] = vals[pick].to(inp["delta"].dtype)
+    inp["delta_bias"] = torch.zeros_like(inp["delta_bias"])
+    A = inp["A"].clone()
+    A[:, ::4] = 0.0
+    inp["A"] = A
+    u = inp["u"].clone()
+    u[:, :, ::5] = 0.0
+    inp["u"] = u
+    h0 = _state(inp, 5103)
+    d = to_dev(inp)
+    for chunk in (0, 16):
+        say("extreme inputs, chunk", chunk)
+        y, ls = ss.fwd(*[d[k] for k in KEYS], return_last_state=True, chunk_len=chunk,
+                       h0=h0.to(DEV))
+        gr = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"], chunk_len=chunk, h0=h0.to(DEV))
+        torch.cuda.synchronize()
+        yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+        r = oracle.bwd(**{k: inp[k] for k in KEYS}, dy=inp["dy"], h0=h0)
+        assert rel_err(to_np(y), yr) <= 1e-5
+        assert rel_err(to_np(ls), lsr) <= 1e-5
+        for k in GRADS + ("dh0",):
+            if r[k] is not None:
+                e = rel_err(to_np(gr[k]), r[k])
+                assert e <= 1e-5, f"{k} chunk {chunk}: {e:.3e}"
+
+
 def test_fwd_workloads_tiny_and_m130m():
     for name in ("tiny", "m130m"):
         w = WORKLOADS[name]
@@ -852,6 +888,44 @@ def test_complex_random_shapes(seed):
             continue
         e = rel_err(to_np(g[k]), r[k])
         assert e <= tol, f"{k}: {e:.3e}"
+
+
+def test_complex_extreme_inputs():
+    """The complex decay's edge branches: dt up to 30 with Im A up to ~1e4
+    (angles dt Im A past 4096 take the double-precision reduction), Re A at
+    -80 (e^w below the float range: a clamps to 0), and A = 0 on some states:
+    forward and backward against the oracle.  dt is taken without softplus,
+    so both sides use the same float dt: a float-rounded dt would itself move
+    such angles by more than the tolerance (|dt Im A| ~ 1e5 times 6e-8)."""
+    Bn, L, D, N = 2, 61, 24, 16
+    inp, h0 = _complex_inputs(Bn, L, D, N, seed=5201, backward=True)
+    g = torch.Generator().manual_seed(5202)
+    pick = torch.randint(0, 5, (Bn, L, D), generator=g)
+    vals = torch.tensor([1e-3, 0.3, 2.0, 9.0, 30.0], dtype=torch.float64)
+    inp["delta"] = vals[pick].to(inp["delta"].dtype)
+    inp["delta_bias"] = torch.zeros_like(inp["delta_bias"])
+    A = inp["A"].to(torch.float64).clone()
+    A[:, 1::4, 1] *= 3000.0                   # fast rotations
+    A[:, 2::4, 0] = -80.0                     # decays past the float range at dt = 30
+    A[:, ::4] = 0.0                           # a = 1
+    inp["A"] = A.to(inp["A"].dtype)
+    d = to_dev(inp)
+    for chunk in (0, 8):
+        say("complex extreme inputs, chunk", chunk)
+        y, ls = ss.fwd_complex(*[d[k] for k in KEYS], delta_softplus=False, h0=h0.to(DEV),
+                               return_last_state=True, chunk_len=chunk)
+        gr = ss.bwd_complex(*[d[k] for k in KEYS], dy=d["dy"], delta_softplus=False,
+                            chunk_len=chunk, h0=h0.to(DEV))
+        torch.cuda.synchronize()
+        yr, lsr = oracle.fwd_complex(**{k: inp[k] for k in KEYS}, delta_softplus=False, h0=h0)
+        r = oracle.bwd_complex(**{k: inp[k] for k in KEYS}, dy=inp["dy"], delta_softplus=False,
+                               h0=h0)
+        assert rel_err(to_np(y), yr) <= 1e-5
+        assert rel_err(to_np(ls), lsr) <= 1e-5
+        for k in GRADS + ("dh0",):
+            if r[k] is not None:
+                e = rel_err(to_np(gr[k]), r[k])
+                assert e <= 1e-5, f"{k} chunk {chunk}: {e:.3e}"
 
 
 def test_complex_decode_empty_and_determinism():
