@@ -610,6 +610,11 @@ def main():
             "state_updates_per_s": B8 * D8 * N8 / (dms * 1e-3),
             "algorithmic_bytes": dbytes, "hbm_gbs": dbytes / (dms * 1e-3) / 1e9,
             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            # one step moves 5.9 MB in a few microseconds: bound by HBM and
+            # launch latency, priced here against HBM at the graph-replay rate
+            "roofline": {"bound": "hbm", "achieved": dbytes / (gms * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         }
         log(f"decode {dms * 1e3:.2f} us/step, {gms * 1e3:.2f} us/step from a graph")
         del state
