@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) 
   const int64_t d = db * kChannelsPerBlock + threadIdx.x;
   if (d >= a.D) return;
   const int64_t D = a.D, N = a.N, K = a.K;
-  const float A2 = ld_param(a.A, d * N + n, a.param_dtype) * kLog2e;
+  const float Av = ld_param(a.A, d * N + n, a.param_dtype);
   float* fs = a.fstate + (b * K * N + n) * D + d;   // + k * N * D
   float* bs = a.bstate + (b * K * N + n) * D + d;
   const float* ds = a.dsum + b * K * D + d;         // + k * D
@@ -164,9 +164,9 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) 
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (j0 + j < K - 1) {
-        hc = __builtin_fmaf(fast_exp2(A2 * df[j]), hc, sf[j]);
+        hc = __builtin_fmaf(chunk_decay(Av, df[j]), hc, sf[j]);
         fs[(j0 + j) * N * D] = hc;
-        cc = __builtin_fmaf(fast_exp2(A2 * dbk[j]), cc, sb[j]);
+        cc = __builtin_fmaf(chunk_decay(Av, dbk[j]), cc, sb[j]);
         bs[(K - 1 - (j0 + j)) * N * D] = cc;
       }
     }

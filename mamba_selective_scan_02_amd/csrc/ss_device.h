@@ -105,6 +105,17 @@ __device__ __forceinline__ float softplus(float x) {
   return __builtin_fmaxf(x, 0.0f) + log1p_pos(e);
 }
 
+// Decay of a whole chunk for the carries across chunks: exp(A * sum of the
+// chunk's dt), the closed form of the product of its per-step decays.  It is
+// taken in double precision (A and the sum exact in double, one rounding to
+// float at the end) because every chunk boundary of a long sequence passes
+// through it: a float exp2 of a rounded A * log2(e) adds one to two ulps per
+// boundary, which accumulate along slowly decaying states.  The carries run
+// once per (b, chunk, n, d), a small share of a call.
+__device__ __forceinline__ float chunk_decay(float A, float dsum) {
+  return static_cast<float>(exp(static_cast<double>(A) * static_cast<double>(dsum)));
+}
+
 // sigmoid(x) = 1 / (1 + e^{-x}); exp overflow gives rcp(inf) = 0.
 __device__ __forceinline__ float sigmoid(float x) {
   return fast_rcp(1.0f + fast_exp2(-x * kLog2e));

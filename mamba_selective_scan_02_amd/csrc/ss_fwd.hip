@@ -19,6 +19,7 @@
 //   1. fwd_scan<SUMMARY>: every chunk but the last runs from h = 0 and writes
 //      its end state S_k[n] and sum_k = sum of dt over the chunk;
 //   2. fwd_carry: per (b, d, n), h_in(k+1) = exp(A * sum_k) * h_in(k) + S_k,
+//      the decay in double precision (chunk_decay),
 //      the composition (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) of the chunk
 //      summaries, folded over k (the product of a chunk's decays is
 //      exp(A * sum of its dt) in closed form);
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
   const int64_t d = db * kBlock + threadIdx.x;
   if (d >= a.D) return;
   const int64_t D = a.D, N = a.N, K = a.K;
-  const float A2 = ld_param(a.A, d * N + n, a.param_dtype) * kLog2e;
+  const float Av = ld_param(a.A, d * N + n, a.param_dtype);
   float* __restrict__ st = a.chunk_state + (b * K * N + n) * D + d;  // + k * N * D
   const float* __restrict__ ds = a.chunk_dsum + b * K * D + d;       // + k * D
   float hc = a.h0 ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0f;  // h_in(0)
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (k0 + j < K - 1) {
-        hc = __builtin_fmaf(fast_exp2(A2 * dv[j]), hc, sv[j]);
+        hc = __builtin_fmaf(chunk_decay(Av, dv[j]), hc, sv[j]);
         st[(k0 + j) * N * D] = hc;
       }
     }

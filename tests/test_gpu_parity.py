@@ -4,9 +4,7 @@ Every call goes through the C ABI (mamba_selective_scan_02_amd wraps it with
 ctypes).  Outputs are compared element by element with the float64 oracle on
 the same seeded inputs; the bound is the one the target states (1e-5 f32,
 2e-2 f16/bf16) on max |x - r| / max(|r|, rms(r)).  The five workloads run
-in the schedule the bench times (chunk_len = 0); the large ones are checked
-on sampled channels (all time steps of those channels) where the oracle would
-take too long in full.
+in the schedule the bench times (chunk_len = 0) and are compared in full.
 """
 import os
 
@@ -196,31 +194,24 @@ def test_fwd_workloads_tiny_and_m130m():
         _check_fwd(inp, label=name)
 
 
-def _sampled_channels(Bn, D, count, seed):
-    rng = np.random.default_rng(seed)
-    bs = list(rng.integers(0, Bn, size=count))
-    ds = list(rng.integers(0, D, size=count))
-    # workgroup and wave edges
-    for d in (0, 63, 64, 255, 256, D - 1):
-        if d < D:
-            bs.append(Bn - 1)
-            ds.append(d)
-    return np.array(bs), np.array(ds)
-
-
 @pytest.mark.parametrize("name", ["m2p8b", "long"])
-def test_fwd_workloads_sampled(name):
+def test_fwd_workloads_full(name):
+    """The Mamba-2.8B-shaped (bf16) and the long-sequence workloads, every
+    element of y and of last_state against the float64 oracle, in the schedule
+    the bench times (single pass for the 2.8B shape, 128 chunks for the long
+    one)."""
     w = WORKLOADS[name]
     inp = make_inputs(w)
-    say("workload", name, "sampled")
+    say("workload", name, "full")
     y, ls = _run_fwd(inp)
-    cb, cd = _sampled_channels(w.batch, w.dim, 24 if name == "long" else 64, w.seed)
-    yr, lsr = oracle.fwd_channels(**{k: inp[k] for k in KEYS}, chan_b=cb, chan_d=cd)
-    yg = y[torch.as_tensor(cb), :, torch.as_tensor(cd)]          # [nchan, L]
-    lg = ls[torch.as_tensor(cb), torch.as_tensor(cd)]             # [nchan, N]
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True)
     tol = TOL[inp["u"].dtype]
-    assert rel_err(to_np(yg), yr) <= tol
-    assert rel_err(to_np(lg), lsr) <= max(tol, 1e-5)
+    e_y = rel_err(to_np(y), yr)
+    del yr
+    e_s = rel_err(to_np(ls), lsr)
+    say(f"  {name}: y err {e_y:.3e}, last_state err {e_s:.3e} (bound {tol})")
+    assert e_y <= tol, f"{name} y err {e_y:.3e}"
+    assert e_s <= max(tol, 1e-5), f"{name} last_state err {e_s:.3e}"
 
 
 def test_fwd_deterministic():
@@ -716,7 +707,6 @@ def test_bwd_strided_bc(case):
     x, Bv, Cv = _xdbl(d["B"], d["C"], R, 2802 + R)
     r = oracle.bwd(**{k: inp[k] for k in KEYS}, dy=inp["dy"], h0=h0)
     tol = TOL[inp["u"].dtype]
-    floor = {}
     for chunk in (0, 5):
         say("bwd strided", case, "chunk", chunk)
         args = {k: d[k] for k in KEYS}
@@ -735,22 +725,38 @@ def test_bwd_strided_bc(case):
                 continue
             assert torch.equal(g0[k], g1[k]), k
             e = rel_err(to_np(g1[k]), r[k])
-            if e > tol and io == "f32":
-                # Some f32 outputs are ill-conditioned sums (dz at L = 2048
-                # here): where the sequential f32 scan itself misses the
-                # bound, the kernels must be no worse than it.
-                if not floor:
-                    floor.update(oracle.bwd_f32(**{q: inp[q] for q in KEYS}, dy=inp["dy"],
-                                                h0=h0))
-                fe = rel_err(floor[k], r[k])
-                say(f"  {k}: {e:.3e} above {tol}; f32 sequential floor {fe:.3e}")
-                assert fe > tol and e <= fe, f"{k} chunk {chunk}: {e:.3e} (floor {fe:.3e})"
-                continue
             assert e <= tol, f"{k} chunk {chunk}: {e:.3e}"
         # freshly allocated strided outputs keep B's layout
         g2 = ss.bwd(**args, dy=d["dy"], chunk_len=chunk, h0=h0.to(DEV))
         torch.cuda.synchronize()
         assert g2["dB"].stride() == Bv.stride() and torch.equal(g2["dB"], g0["dB"])
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3, 5, 8])
+def test_bwd_long_memory_short_chunks(chunk):
+    """f32, L = 2048 with an initial state and slowly decaying states, cut into
+    very short chunks: every chunk boundary passes the states through the
+    carry's closed-form decay, so errors there add up along the sequence (dz,
+    an ill-conditioned readout here, is where it shows first: the sequential
+    f32 loop itself reaches 2.4e-5 on it).  Every gradient stays within the
+    f32 bound at every chunk length."""
+    inp = random_inputs(1, 2048, 64, 8, seed=2800 + 2048 + 8, backward=True)
+    h0 = _state(inp, 2801 + 64)
+    d = to_dev(inp)
+    say("bwd long memory", "chunk", chunk)
+    g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"], chunk_len=chunk, h0=h0.to(DEV))
+    y, ls = ss.fwd(*[d[k] for k in KEYS], return_last_state=True, chunk_len=chunk,
+                   h0=h0.to(DEV))
+    torch.cuda.synchronize()
+    r = oracle.bwd(**{k: inp[k] for k in KEYS}, dy=inp["dy"], h0=h0)
+    errs = {k: rel_err(to_np(g[k]), r[k]) for k in GRADS + ("dh0",) if r[k] is not None}
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+    errs["last_state"] = rel_err(to_np(ls), lsr)
+    if chunk > 1:
+        errs["y"] = rel_err(to_np(y), yr)
+    say("  ", {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if not v <= 1e-5}
+    assert not bad, bad
 
 
 def test_strided_bc_varlen_and_empty():

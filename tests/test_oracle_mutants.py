@@ -4,7 +4,10 @@ Each case copies the oracle's C source, plants one mistake in the copy (a
 dropped term, a wrong sign, a wrong index, a transposed operand, a missing
 factor in the backward), builds it into a temporary library and runs the pin
 suite (tests/test_oracle_pins.py) against it through SS_ORACLE_LIB.  The suite
-must fail for every mutant.  The oracle source itself is never modified.
+must fail for every mutant.  Each mutant is also planted in the float
+instantiation alone (the single-precision build behind fwd_f32 / bwd_f32),
+which the suite must catch through its float-build pins.  The oracle source
+itself is never modified.
 """
 import concurrent.futures as cf
 import os
@@ -61,15 +64,31 @@ def _mutate(text, old, new, occ):
     return old.join(parts[:occ + 1]) + new + old.join(parts[occ + 1:])
 
 
-def _run_mutant(case, tmp):
+def _run_mutant(case, tmp, f32_only=False):
+    """Build the mutant and run the pins against it.  f32_only plants the
+    mistake in the float instantiation alone (fwd_f32 / bwd_f32), leaving the
+    double one intact: the pins must then catch it through the float build."""
     name, old, new, occ = case
-    d = os.path.join(tmp, name.replace(" ", "_"))
+    d = os.path.join(tmp, ("f32_" if f32_only else "") + name.replace(" ", "_"))
     os.makedirs(d)
-    shutil.copy(os.path.join(ORACLE, "ss_oracle.c"), d)
     with open(os.path.join(ORACLE, "ss_oracle_impl.h")) as f:
         text = f.read()
-    with open(os.path.join(d, "ss_oracle_impl.h"), "w") as f:
-        f.write(_mutate(text, old, new, occ))
+    with open(os.path.join(ORACLE, "ss_oracle.c")) as f:
+        csrc = f.read()
+    if f32_only:
+        inc = '#include "ss_oracle_impl.h"'
+        assert csrc.count(inc) == 2, "expected the double and the float instantiation"
+        first = csrc.index(inc) + len(inc)
+        csrc = csrc[:first] + csrc[first:].replace(inc, '#include "ss_oracle_impl_f32.h"')
+        with open(os.path.join(d, "ss_oracle_impl.h"), "w") as f:
+            f.write(text)
+        with open(os.path.join(d, "ss_oracle_impl_f32.h"), "w") as f:
+            f.write(_mutate(text, old, new, occ))
+    else:
+        with open(os.path.join(d, "ss_oracle_impl.h"), "w") as f:
+            f.write(_mutate(text, old, new, occ))
+    with open(os.path.join(d, "ss_oracle.c"), "w") as f:
+        f.write(csrc)
     lib = os.path.join(d, "libmut.so")
     subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-pthread",
                     "-ffp-contract=off", os.path.join(d, "ss_oracle.c"), "-o", lib, "-lm"],
@@ -81,9 +100,10 @@ def _run_mutant(case, tmp):
     return name, r.returncode
 
 
-def test_pins_catch_every_mutant():
+@pytest.mark.parametrize("f32_only", [False, True], ids=["both_builds", "float_build_only"])
+def test_pins_catch_every_mutant(f32_only):
     with tempfile.TemporaryDirectory() as tmp:
         with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-            results = list(ex.map(lambda c: _run_mutant(c, tmp), MUTANTS))
+            results = list(ex.map(lambda c: _run_mutant(c, tmp, f32_only), MUTANTS))
     survivors = [name for name, rc in results if rc == 0]
     assert not survivors, f"pins did not catch: {survivors}"

@@ -522,3 +522,48 @@ def test_f32_floor_is_close():
     y32 = oracle.fwd_f32(**a)[0]
     err = np.max(np.abs(y32 - y64)) / np.sqrt(np.mean(y64 ** 2))
     assert err < 1e-5
+
+
+def _rel(x, r):
+    """max |x - r| / max(|r|, rms(r)) over a tensor."""
+    rms = float(np.sqrt(np.mean(r * r)))
+    return float(np.max(np.abs(x - r) / np.maximum(np.abs(r), rms)))
+
+
+# Shapes short enough that every output is well conditioned in single
+# precision: each step rounds a few times at 2^-24 ~ 6e-8 relative, so over
+# L <= 64 steps the float loop stays within ~1e-6 of the double one (measured
+# 1e-7 .. 2.3e-6); F32_BOUND = 2e-5 leaves a margin of about 10, while any
+# mistake in the loop (a dropped term, a wrong sign or index) moves some
+# output by far more than 1e-3.
+F32_BOUND = 2e-5
+
+
+@pytest.mark.parametrize("sp", [True, False])
+@pytest.mark.parametrize("seed,shape", [(1, (2, 24, 6, 4)), (2, (1, 40, 5, 8)),
+                                        (3, (2, 16, 7, 16)), (4, (1, 64, 3, 2))])
+def test_f32_build_tracks_f64(seed, shape, sp):
+    """The float instantiation of the loop (fwd_f32 / bwd_f32, the single-
+    precision floor) against the pinned double one, every output including the
+    initial-state gradient, with and without softplus."""
+    Bn, L, D, N = shape
+    a = _rand(700 + seed, Bn=Bn, L=L, D=D, N=N)
+    if not sp:  # keep dt positive without softplus (a decaying recurrence)
+        a["delta"] = np.abs(a["delta"]) * 0.3
+        a["delta_bias"] = np.abs(a["delta_bias"]) * 0.01
+    rng = np.random.default_rng(710 + seed)
+    dy = rng.normal(size=(Bn, L, D)).astype(np.float32).astype(np.float64)
+    h0 = rng.normal(size=(Bn, D, N)).astype(np.float32).astype(np.float64)
+    y, ls = oracle.fwd(**a, delta_softplus=sp, return_last_state=True, h0=h0)
+    y3, ls3 = oracle.fwd_f32(**a, delta_softplus=sp, return_last_state=True, h0=h0)
+    assert y3.dtype == np.float32
+    errs = {"y": _rel(y3, y), "last_state": _rel(ls3, ls)}
+    g = oracle.bwd(**a, dy=dy, delta_softplus=sp, h0=h0)
+    g3 = oracle.bwd_f32(**a, dy=dy, delta_softplus=sp, h0=h0)
+    for k, v in g.items():
+        assert (v is None) == (g3[k] is None), k
+        if v is not None:
+            assert g3[k].dtype == np.float32, k
+            errs[k] = _rel(g3[k], v)
+    bad = {k: e for k, e in errs.items() if not e <= F32_BOUND}
+    assert not bad, bad
