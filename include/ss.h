@@ -18,7 +18,9 @@
  *
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers owned by the caller (workspace included).
- *    The library allocates no memory, keeps no state between calls, is
+ *    The library allocates no memory, keeps no state between calls (two
+ *    exceptions, both stated where they are declared: the per-thread message
+ *    of ss_last_error, and the static scratch of ss_bwd_noalloc), is
  *    reentrant, enqueues work only on the given stream (a hipStream_t; NULL
  *    means the default stream) and never synchronises.  Calls return after
  *    enqueueing; results are ready when the stream reaches that point.
@@ -215,6 +217,26 @@ int ss_bwd_complex(const ss_desc* desc, const void* u, const void* delta, const 
                    void* ddelta, void* dA, void* dB, void* dC, void* dD, void* dz,
                    void* ddelta_bias, void* dh0, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/* Backward for callers that cannot allocate (code under HIP graph capture,
+ * tight serving or training loops, harnesses that forbid hipMalloc): ss_bwd_h0
+ * without the workspace arguments.  Its scratch is a static device array of
+ * SS_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * first call on that GPU until the process ends; the call itself allocates
+ * nothing.  A problem whose ss_workspace_size(desc, 1) exceeds
+ * SS_NOALLOC_SCRATCH_BYTES returns SS_ERR_UNSUPPORTED before anything is
+ * enqueued (the backward workload B=2, L=2048, D=2048, N=16 needs 57.5 MiB).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads, other host processes' contexts
+ * excepted) race and give undefined results; serialise them on one stream.
+ * The first call on a GPU looks the array's address up (a mutex guards that
+ * lookup).  Everything else, including the results bit for bit, as ss_bwd_h0. */
+#define SS_NOALLOC_SCRATCH_BYTES (64u << 20)
+int ss_bwd_noalloc(const ss_desc* desc, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, const void* dy, void* du,
+                   void* ddelta, void* dA, void* dB, void* dC, void* dD, void* dz,
+                   void* ddelta_bias, void* dh0, void* stream);
 
 /* The schedule the library would use for a descriptor (informational). */
 typedef struct ss_plan {

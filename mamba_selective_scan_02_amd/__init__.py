@@ -7,7 +7,7 @@ on the tensors' device and passes raw pointers plus the current HIP stream.
 If the library is missing, every call raises: there is no fallback.
 
 Raw C entry points with the header's names: ``ss_workspace_size``,
-``ss_fwd``, ``ss_bwd``, ``ss_fwd_h0``, ``ss_bwd_h0``, ``ss_fwd_varlen``,
+``ss_fwd``, ``ss_bwd``, ``ss_fwd_h0``, ``ss_bwd_h0``, ``ss_bwd_noalloc``, ``ss_fwd_varlen``,
 ``ss_bwd_varlen``, ``ss_fwd_strided``, ``ss_bwd_strided``,
 ``ss_workspace_size_complex``, ``ss_fwd_complex``, ``ss_bwd_complex``,
 ``ss_plan_query``, ``ss_status_string``, ``ss_last_error``.  Tensor-level
@@ -28,7 +28,7 @@ import torch
 
 __all__ = ["SsDesc", "SsPlan", "fwd", "bwd", "fwd_varlen", "bwd_varlen", "decode_step",
            "selective_scan", "plan", "workspace_size", "ss_workspace_size", "ss_fwd", "ss_bwd",
-           "ss_fwd_h0", "ss_bwd_h0", "ss_fwd_varlen", "ss_bwd_varlen", "ss_fwd_strided",
+           "ss_fwd_h0", "ss_bwd_h0", "ss_bwd_noalloc", "ss_fwd_varlen", "ss_bwd_varlen", "ss_fwd_strided",
            "ss_bwd_strided", "ss_workspace_size_complex", "ss_fwd_complex", "ss_bwd_complex",
            "fwd_complex", "bwd_complex",
            "ss_plan_query", "ss_status_string",
@@ -85,6 +85,8 @@ def load_library(path: Optional[str] = None):
     lib.ss_fwd_h0.restype = ctypes.c_int
     lib.ss_bwd_h0.argtypes = [dp] + [vp] * 20 + [sz, vp]
     lib.ss_bwd_h0.restype = ctypes.c_int
+    lib.ss_bwd_noalloc.argtypes = [dp] + [vp] * 20
+    lib.ss_bwd_noalloc.restype = ctypes.c_int
     lib.ss_fwd_varlen.argtypes = [dp, vp, ctypes.c_int64] + [vp] * 12 + [sz, vp]
     lib.ss_fwd_varlen.restype = ctypes.c_int
     lib.ss_bwd_varlen.argtypes = [dp, vp, ctypes.c_int64] + [vp] * 20 + [sz, vp]
@@ -144,6 +146,13 @@ def ss_bwd_h0(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, h0, dy, du,
     return load_library().ss_bwd_h0(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias, h0,
                                     dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
                                     workspace, workspace_bytes, stream)
+
+
+def ss_bwd_noalloc(desc: SsDesc, u, delta, A, B, C, Dskip, z, delta_bias, h0, dy, du, ddelta,
+                   dA, dB, dC, dD, dz, ddelta_bias, dh0, stream) -> int:
+    return load_library().ss_bwd_noalloc(_ref(desc), u, delta, A, B, C, Dskip, z, delta_bias,
+                                         h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
+                                         dh0, stream)
 
 
 def ss_fwd_varlen(desc: SsDesc, cu_seqlens, total_len: int, u, delta, A, B, C, Dskip, z,

@@ -10,9 +10,11 @@
 // become descriptor checks; null and misaligned pointers are rejected here.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/ss.h"
 #include "ss_device.h"
@@ -348,6 +350,80 @@ int ss_bwd_h0(const ss_desc* d, const void* u, const void* delta, const void* A,
   return bwd_impl(h0 ? "ss_bwd_h0" : "ss_bwd", d, nullptr, 0, 0, 0, u, delta, A, B, C, Dskip, z,
                   delta_bias, h0, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
                   workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch of ss_bwd_noalloc: the workspace of callers that cannot allocate.
+// Each GPU the library runs on holds its own copy until the process ends; in
+// host code `scratch` only names the symbol, and its device address is looked
+// up once per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the device the work is enqueued on (the
+// stream's device, or the current one for the NULL stream).
+int scratch_address(hipStream_t s, void** out, const char* who) {
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess) {
+    dev = cur;
+    if (s) e = hipStreamGetDevice(s, &dev);
+  }
+  if (e != hipSuccess) return fail(SS_ERR_HIP, "%s: no device: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SS_ERR_UNSUPPORTED, "%s: device %d is beyond the %d the scratch table holds",
+                who, dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+        return fail(SS_ERR_HIP, "%s: cannot select device %d: %s", who, dev, hipGetErrorString(e));
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (dev != cur) (void)hipSetDevice(cur);
+      if (e != hipSuccess || !p)
+        return fail(SS_ERR_HIP, "%s: no address for the static scratch on device %d: %s", who,
+                    dev, hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss_bwd_noalloc(const ss_desc* d, const void* u, const void* delta, const void* A,
+                   const void* B, const void* C, const void* Dskip, const void* z,
+                   const void* delta_bias, const void* h0, const void* dy, void* du,
+                   void* ddelta, void* dA, void* dB, void* dC, void* dD, void* dz,
+                   void* ddelta_bias, void* dh0, void* stream) {
+  const char* who = "ss_bwd_noalloc";
+  g_err[0] = 0;
+  int st = check_desc(d, who);
+  if (st != SS_OK) return st;
+  const size_t need = ss::make_plan(*d, true).ws_bytes;
+  if (need > (size_t)SS_NOALLOC_SCRATCH_BYTES)
+    return fail(SS_ERR_UNSUPPORTED, "%s: this problem needs %zu bytes of scratch, above the %zu "
+                "of the static scratch (call ss_bwd_h0 with a workspace instead)", who, need,
+                (size_t)SS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(static_cast<hipStream_t>(stream), &ws, who);
+    if (st != SS_OK) return st;
+  }
+  return bwd_impl(who, d, nullptr, 0, 0, 0, u, delta, A, B, C, Dskip, z, delta_bias, h0, dy, du,
+                  ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, ws,
+                  need > 0 ? (size_t)SS_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int ss_bwd_varlen(const ss_desc* d, const int32_t* cu_seqlens, int64_t total_len,

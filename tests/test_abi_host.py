@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     lib = ss.load_library()
     names = _declared_functions()
     assert set(names) == {"ss_workspace_size", "ss_fwd", "ss_bwd", "ss_fwd_h0", "ss_bwd_h0",
-                          "ss_fwd_varlen", "ss_bwd_varlen", "ss_fwd_strided",
+                          "ss_bwd_noalloc", "ss_fwd_varlen", "ss_bwd_varlen", "ss_fwd_strided",
                           "ss_bwd_strided", "ss_workspace_size_complex", "ss_fwd_complex",
                           "ss_bwd_complex", "ss_plan_query",
                           "ss_status_string",
@@ -301,3 +301,22 @@ def test_workspace_size_formula():
     K = p.n_chunks
     al = lambda x: (x + 255) // 256 * 256
     assert ss.ss_workspace_size(d, 0) == al(4 * B * K * D) + al(4 * B * K * N * D)
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """ss_bwd_noalloc refuses a problem whose workspace exceeds its static
+    scratch (64 MiB) before touching the device, and names both sizes."""
+    big = _desc(B=8, L=2048, D=5120, N=16)
+    need = ss.ss_workspace_size(big, 1)
+    assert need > 64 << 20
+    st = ss.ss_bwd_noalloc(big, P, P, P, P, P, None, None, None, None, P, P, P, P, P, P, None,
+                           None, None, None, None)
+    assert st == ss.SS_ERR_UNSUPPORTED
+    msg = ss.ss_last_error()
+    assert "ss_bwd_noalloc" in msg and str(need) in msg and str(64 << 20) in msg
+    # invalid descriptors are reported as by the other entry points
+    st = ss.ss_bwd_noalloc(_desc(B=-1), P, P, P, P, P, None, None, None, None, P, P, P, P, P,
+                           P, None, None, None, None, None)
+    assert st == ss.SS_ERR_INVALID_PROBLEM
+    # the backward workload's workspace fits the scratch
+    assert ss.ss_workspace_size(_desc(B=2, L=2048, D=2048, N=16), 1) <= 64 << 20
