@@ -49,6 +49,33 @@ enum { TMODE_FULL = 0, TMODE_SUMMARY = 1 };
 template <int NS>
 constexpr int tile_waves_per_simd() { return NS <= 2 ? 5 : 3; }
 
+// 2^x in place for 4, 8 or 16 values as one run of v_exp_f32 (a run costs the
+// SIMD about 4.3 ns per exp, one exp between dependent FP32 operations about
+// 5.3 ns: measured).  The compiler schedules independent work between exps,
+// so the run is one asm statement; it ends with s_nop 1 because a VALU
+// operation that reads a transcendental result needs a wait state on gfx950,
+// which the compiler's hazard check cannot see inside the statement.
+__device__ __forceinline__ void exp2_run(float (&e)[4]) {
+  __asm__ volatile(
+      "v_exp_f32 %0, %0\n\tv_exp_f32 %1, %1\n\tv_exp_f32 %2, %2\n\tv_exp_f32 %3, %3\n\t"
+      "s_nop 1"
+      : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]));
+}
+__device__ __forceinline__ void exp2_run(float (&e)[8]) {
+  __asm__ volatile(
+      "v_exp_f32 %0, %0\n\tv_exp_f32 %1, %1\n\tv_exp_f32 %2, %2\n\tv_exp_f32 %3, %3\n\t"
+      "v_exp_f32 %4, %4\n\tv_exp_f32 %5, %5\n\tv_exp_f32 %6, %6\n\tv_exp_f32 %7, %7\n\t"
+      "s_nop 1"
+      : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]), "+v"(e[6]),
+        "+v"(e[7]));
+}
+__device__ __forceinline__ void exp2_run(float (&e)[16]) {
+  float (&lo)[8] = *reinterpret_cast<float(*)[8]>(&e[0]);
+  float (&hi)[8] = *reinterpret_cast<float(*)[8]>(&e[8]);
+  exp2_run(lo);
+  exp2_run(hi);
+}
+
 template <typename T, int NS, int MODE, bool HAS_Z>
 __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(const T* __restrict__ u_in,
                                                     const T* __restrict__ delta_in,
@@ -224,15 +251,22 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
           if (MODE == TMODE_FULL)
             cq[i] = *reinterpret_cast<const float4*>(&sBC[buf][1][n0 + i][pt * GL + jh]);
         }
+        // the half tile's decays as one run of exps (exp2_run)
+        float ea[4 * NS];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int i = 0; i < NS; ++i) ea[jj * NS + i] = ex[jh + jj].x * A2[i];
+        exp2_run(ea);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int j = jh + jj;
-          const float dlj = ex[j].x, xuj = ex[j].y;
+          const float xuj = ex[j].y;
           float o = 0.0f;
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
             const float bvj = jj == 0 ? bq[i].x : jj == 1 ? bq[i].y : jj == 2 ? bq[i].z : bq[i].w;
-            const float dA = fast_exp2(dlj * A2[i]);
+            const float dA = ea[jj * NS + i];
             h[i] = __builtin_fmaf(dA, h[i], xuj * bvj);
             if (MODE == TMODE_FULL) {
               const float cvj = jj == 0 ? cq[i].x : jj == 1 ? cq[i].y : jj == 2 ? cq[i].z : cq[i].w;
@@ -327,10 +361,12 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   constexpr int NBC = FULL ? 2 : 1;
   constexpr int NPC = (NBC * PB + kBlockT - 1) / kBlockT;
   static_assert(PB % 64 == 0, "a wave's pieces come from one tensor");
+  // u, delta[, z] rows of the stage; y of row t replaces delta of row t once
+  // the lane that owns (t, channel) has prepared that step (it is delta's
+  // only reader), so the stage's y leaves from sIn[1].
   __shared__ __attribute__((aligned(16))) uint8_t sIn[NT][TB * RS];
-  __shared__ __attribute__((aligned(16))) uint8_t sY[FULL ? TB * RS : 16];
   __shared__ __attribute__((aligned(16))) float sBC[FULL ? 2 : 1][NP][TSW];
-  __shared__ __attribute__((aligned(16))) float2 xch[CPW][XS];
+  __shared__ __attribute__((aligned(16))) float2 xch[2][CPW][XS];
 
   const int tid = threadIdx.x;
   const int g = lane_g(tid);
@@ -424,16 +460,18 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   // y of the stage just finished leaves in 16-byte pieces; the last channel
   // block of a row, where the block runs past D, stores element by element.
   const bool full_row = d0 + CPW <= D;
+  // Full rows: each thread drains exactly the 16-byte piece it commits next,
+  // so drain and commit need no barrier between them.
   auto drain_y = [&](int st) {
     if (full_row) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&sY[lds_piece]);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&sIn[1][lds_piece]);
       __builtin_amdgcn_raw_buffer_store_b128(v, rs_y, voff_piece, st * soff_stage, 0);
     } else {
       const int rowb = (int)(D * ES), colb = (int)(d0 * ES);
       for (int e = tid; e < TB * CPW; e += kBlockT) {
         const int r = e / CPW, c = e % CPW;
         if (d0 + c < D) {
-          const float v = lds_elem<T>(&sY[r * RS + c * ES]);
+          const float v = lds_elem<T>(&sIn[1][r * RS + c * ES]);
           buf_st<T>(v, rs_y, r * rowb + colb + c * ES, st * soff_stage);
         }
       }
@@ -444,35 +482,58 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   commit_loads();
   __syncthreads();
 
+  // Per-step inputs of this lane's own step (stage row `row`): dt, dt*u
+  // (handed to the channel's 8 lanes through xch), u and the gate (kept for
+  // the output).  Rows past the chunk (masked stages only) get dt = dt*u = 0.
+  struct Prep { float dl, xu, uu, gate; };
+  auto prep = [&](int row, bool valid) {
+    const uint8_t* own = &sIn[0][row * RS + lds_own_col];
+    const float uu = lds_elem<T>(own);
+    const float x = lds_elem<T>(own + TB * RS) + bv;
+    float spx = softplus(x);
+    __asm__ volatile("" : "+v"(spx));
+    const float dl0 = sp ? spx : x;
+    Prep r;
+    r.dl = valid ? dl0 : 0.0f;
+    r.xu = valid ? dl0 * uu : 0.0f;
+    r.uu = uu;
+    r.gate = 1.0f;
+    if constexpr (FULL && HAS_Z) {
+      const float zz = lds_elem<T>(own + 2 * TB * RS);
+      r.gate = zz * sigmoid(zz);
+    }
+    return r;
+  };
+
   float dsum = 0.0f;
   const int nstage = (int)((nsteps + TB - 1) / TB);
-  for (int st = 0; st < nstage; ++st) {
-    const bool has_next = st + 1 < nstage;
-    if (has_next) issue_loads(st + 1);
+  // One stage of tiles.  The lane's step of tile pt+1 is prepared while tile
+  // pt runs (xch double buffered: one wave's LDS operations complete in
+  // program order), so the exchange's LDS round trip overlaps the updates.
+  // MASKED: the chunk ends inside this stage; otherwise no step is checked.
+  auto run_stage = [&](int st, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int left = (int)nsteps - st * TB;          // steps of the chunk from this stage on
+    Prep cur = prep(g, !MASKED || g < left);
+    xch[0][cl][g] = make_float2(cur.dl, cur.xu);
     constexpr int kUnroll = FULL ? NTILE : 1;
 #pragma unroll kUnroll
     for (int pt = 0; pt < NTILE; ++pt) {
-      if (pt * GL >= (int)nsteps - st * TB) break;   // tiles past the chunk (uniform)
-      const int row = pt * GL + g;                    // this lane's own step in the stage
-      const uint8_t* own = &sIn[0][row * RS + lds_own_col];
-      const float uu = lds_elem<T>(own);
-      const float dr = lds_elem<T>(own + TB * RS);
-      const float x = dr + bv;
-      float spx = softplus(x);
-      __asm__ volatile("" : "+v"(spx));
-      const bool valid = st * TB + row < (int)nsteps;
-      const float dl0 = sp ? spx : x;
-      const float dl = valid ? dl0 : 0.0f;
-      const float xu = valid ? dl0 * uu : 0.0f;
-      if (!FULL) dsum += dl;
-      xch[cl][g] = make_float2(dl, xu);
+      if (MASKED && pt * GL >= left) break;          // tiles past the chunk (uniform)
       float2 ex[GL];
 #pragma unroll
       for (int j = 0; j < GL; j += 2) {
-        const float4 v = *reinterpret_cast<const float4*>(&xch[cl][j]);
+        const float4 v = *reinterpret_cast<const float4*>(&xch[pt & 1][cl][j]);
         ex[j] = make_float2(v.x, v.y);
         ex[j + 1] = make_float2(v.z, v.w);
       }
+      Prep nxt = cur;
+      if (pt + 1 < NTILE) {
+        const int row = (pt + 1) * GL + g;
+        nxt = prep(row, !MASKED || row < left);
+        xch[(pt + 1) & 1][cl][g] = make_float2(nxt.dl, nxt.xu);
+      }
+      if (!FULL) dsum += cur.dl;
       float ot[GL];
 #pragma unroll
       for (int jh = 0; jh < GL; jh += 4) {
@@ -482,15 +543,22 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
           bq[i] = *reinterpret_cast<const float4*>(&sBC[0][n0 + i][pt * GL + jh]);
           if (FULL) cq[i] = *reinterpret_cast<const float4*>(&sBC[FULL ? 1 : 0][n0 + i][pt * GL + jh]);
         }
+        // the half tile's decays as one run of exps (exp2_run)
+        float ea[4 * NS];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int i = 0; i < NS; ++i) ea[jj * NS + i] = ex[jh + jj].x * A2[i];
+        exp2_run(ea);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int j = jh + jj;
-          const float dlj = ex[j].x, xuj = ex[j].y;
+          const float xuj = ex[j].y;
           float o = 0.0f;
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
             const float bvj = jj == 0 ? bq[i].x : jj == 1 ? bq[i].y : jj == 2 ? bq[i].z : bq[i].w;
-            const float dA = fast_exp2(dlj * A2[i]);
+            const float dA = ea[jj * NS + i];
             h[i] = __builtin_fmaf(dA, h[i], xuj * bvj);
             if (FULL) {
               const float cvj = jj == 0 ? cq[i].x : jj == 1 ? cq[i].y : jj == 2 ? cq[i].z : cq[i].w;
@@ -501,18 +569,24 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
         }
       }
       if constexpr (FULL) {
-        float gate = 1.0f;
-        if constexpr (HAS_Z) {
-          const float zz = lds_elem<T>(own + 2 * TB * RS);
-          gate = zz * sigmoid(zz);
-        }
         const float o_own = reduce_scatter8(ot, g);   // full readout of this lane's step
-        lds_put<T>(&sY[row * RS + lds_own_col], __builtin_fmaf(Dv, uu, o_own) * gate);
+        lds_put<T>(&sIn[1][(pt * GL + g) * RS + lds_own_col],
+                   __builtin_fmaf(Dv, cur.uu, o_own) * cur.gate);
       }
+      cur = nxt;
     }
+  };
+  for (int st = 0; st < nstage; ++st) {
+    const bool has_next = st + 1 < nstage;
+    if (has_next) issue_loads(st + 1);
+    if ((st + 1) * TB <= (int)nsteps) run_stage(st, std::false_type{});
+    else run_stage(st, std::true_type{});
     __syncthreads();
+    if (FULL) {
+      drain_y(st);                                  // steps past the chunk are dropped
+      if (!full_row && has_next) __syncthreads();   // element-wise drain reads others' pieces
+    }
     if (has_next) commit_loads();
-    if (FULL) drain_y(st);                          // steps past the chunk are dropped
     __syncthreads();
   }
 

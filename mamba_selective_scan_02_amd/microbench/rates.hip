@@ -16,6 +16,13 @@
 //              (4 FP32 VALU + 1 exp per update), B and C in VGPRs
 //   update_s   the same with B and C wave-uniform (SGPR operands)
 //   upd_nexp   the update without its exp (a = dt * A), for the VALU share
+//   upd_clust  the update with its 16 exps issued back to back (empty asm
+//              fences order: 16 dt*A products, 16 exps, then the 48 other
+//              operations), against the compiler's interleaved order
+//   perm32     8 v_permlane32_swap per iteration (8 independent pairs) plus
+//              16 FMAs; perm16 the same with v_permlane16_swap; dpp_add 16
+//              v_add_f32 with a DPP row rotation plus 16 FMAs: the cross-lane
+//              steps of the readout's sum over a channel's lanes
 //
 // Each line gives ns and shader-clock cycles per wave-instruction per SIMD
 // (the SIMD's issue cost of one 64-lane instruction), the clock the kernel
@@ -54,13 +61,14 @@ __global__ void read_k(const float4* __restrict__ in, float* __restrict__ out, s
   out[blockIdx.x * (size_t)blockDim.x + threadIdx.x] = acc.x + acc.y + acc.z + acc.w;
 }
 
-enum { M_FMA = 0, M_EXP, M_MIX, M_UPD, M_UPD_S, M_UPD_NEXP, M_COUNT };
+enum { M_FMA = 0, M_EXP, M_MIX, M_UPD, M_UPD_S, M_UPD_NEXP, M_UPD_CL, M_PERM32, M_PERM16,
+       M_DPP, M_COUNT };
 static const char* kModeName[M_COUNT] = {"fma", "exp", "fma+exp", "update", "update_s",
-                                         "upd_nexp"};
+                                         "upd_nexp", "upd_clust", "perm32", "perm16", "dpp_add"};
 // counted wave-instructions per iteration of each mode
-static const int kInstr[M_COUNT] = {16, 16, 20, 80, 80, 64};
+static const int kInstr[M_COUNT] = {16, 16, 20, 80, 80, 64, 80, 24, 24, 32};
 // state updates per lane per iteration (update kernels)
-static const int kUpd[M_COUNT] = {0, 0, 0, 16, 16, 16};
+static const int kUpd[M_COUNT] = {0, 0, 0, 16, 16, 16, 16, 0, 0, 0};
 
 // Keeps v in a VGPR and opaque to the optimiser without emitting code.
 #define OPAQUE(v) __asm__ volatile("" : "+v"(v))
@@ -113,6 +121,63 @@ __global__ __launch_bounds__(256, 8) void alu_k(float* __restrict__ out, long lo
       // 4 exp chains on their own registers: no data flow to or from the FMAs
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_exp2f(-o[j]);
+    }
+    if (MODE == M_PERM32 || MODE == M_PERM16) {
+      // 8 pairs (x[2k], x[2k+1]) swapped across lanes, then each pair summed back
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const auto r = MODE == M_PERM32
+            ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[2 * k]),
+                                               __float_as_uint(x[2 * k + 1]), false, false)
+            : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[2 * k]),
+                                               __float_as_uint(x[2 * k + 1]), false, false);
+        const unsigned r0 = r[0], r1 = r[1];
+        x[2 * k] = __builtin_fmaf(__uint_as_float(r0), c0, c1);
+        x[2 * k + 1] = __builtin_fmaf(__uint_as_float(r1), c0, c1);
+      }
+    }
+    if (MODE == M_DPP) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float d = __builtin_bit_cast(
+            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[j]), 0x128, 0xf, 0xf, true));
+        x[j] = __builtin_fmaf(d + x[j], c0, c1);
+      }
+    }
+    if (MODE == M_UPD_CL) {
+      float e[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        OPAQUE(dt[i]);
+        OPAQUE(xu[i]);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[4 * s + i] = dt[s] * A2[i];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) OPAQUE(e[j]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(e[j]);
+      // the other operations read xu, B, C only after this fence
+#pragma unroll
+      for (int j = 0; j < 16; ++j) OPAQUE(e[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        OPAQUE(xu[i]);
+        OPAQUE(Bv[i]);
+        OPAQUE(Cv[i]);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float acc = o[s];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[i] = __builtin_fmaf(e[4 * s + i], h[i], xu[s] * Bv[i]);
+          acc = __builtin_fmaf(Cv[i], h[i], acc);
+        }
+        o[s] = acc;
+      }
     }
     if (MODE == M_UPD || MODE == M_UPD_S || MODE == M_UPD_NEXP) {
 #pragma unroll
@@ -246,6 +311,10 @@ int main() {
   CK(hipFuncSetAttribute((const void*)alu_k<M_UPD>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds));
   CK(hipFuncSetAttribute((const void*)alu_k<M_UPD_S>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds));
   CK(hipFuncSetAttribute((const void*)alu_k<M_UPD_NEXP>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds));
+  CK(hipFuncSetAttribute((const void*)alu_k<M_UPD_CL>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds));
+  CK(hipFuncSetAttribute((const void*)alu_k<M_PERM32>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds));
+  CK(hipFuncSetAttribute((const void*)alu_k<M_PERM16>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds));
+  CK(hipFuncSetAttribute((const void*)alu_k<M_DPP>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds));
   const int iters = 2048;
   for (int wps : {1, 2, 3, 4, 5, 6, 8}) {
     // the largest 1 KiB multiple that lets wps workgroups, but not wps + 1, share a CU
@@ -257,6 +326,10 @@ int main() {
     report<M_UPD>(red, clk, uni, wps, lds, iters);
     report<M_UPD_S>(red, clk, uni, wps, lds, iters);
     report<M_UPD_NEXP>(red, clk, uni, wps, lds, iters);
+    report<M_UPD_CL>(red, clk, uni, wps, lds, iters);
+    report<M_PERM32>(red, clk, uni, wps, lds, iters);
+    report<M_PERM16>(red, clk, uni, wps, lds, iters);
+    report<M_DPP>(red, clk, uni, wps, lds, iters);
   }
   CK(hipDeviceSynchronize());
   CK(hipFree(red));
