@@ -74,7 +74,15 @@ typedef struct ss_desc {
 
 /* Workspace bytes that ss_fwd (backward = 0) or ss_bwd (backward = 1) needs
  * for this descriptor: pure arithmetic, no device access.  Returns 0 for an
- * invalid descriptor (ss_fwd / ss_bwd then report the error). */
+ * invalid descriptor (ss_fwd / ss_bwd then report the error).  This is the
+ * query the scan page asks callers to make before a launch (module docs,
+ * "Workspace"; SelectiveScanPlan::workspace_size and
+ * SelectiveScanBackwardPlan::workspace_size).  The sizes differ from the
+ * page's: its forward needs none and its backward records every state,
+ * B*D*L*N elements.  Here a single-pass forward needs none, a forward cut
+ * into time chunks needs the chunk summaries, and the backward needs f32
+ * chunk checkpoints, carried adjoints and fixed-order reduction partials
+ * (each sub-buffer 256-byte aligned). */
 size_t ss_workspace_size(const ss_desc* desc, int32_t backward);
 
 /* Forward.  u, delta, A, B, C, y are required; Dskip, z, delta_bias and
@@ -251,11 +259,19 @@ typedef struct ss_plan {
  * status like the entry points (no device access). */
 int ss_plan_query(const ss_desc* desc, int32_t backward, ss_plan* out);
 
-/* Static text for a status code. */
+/* Static text for a status code, naming the scan page's error
+ * variants (Error::InvalidProblem, Error::Unsupported,
+ * Error::WorkspaceTooSmall, returned by SelectiveScanPlan::select /
+ * can_implement and the backward plan's run) and of a failed launch, which
+ * the page maps from the kernel's return code (map_status).  Unknown codes
+ * give "unknown status".  Never NULL; the text is static. */
 const char* ss_status_string(int status);
 
 /* Message describing the calling thread's most recent failed call ("" if
- * none).  The pointer stays valid until that thread's next call. */
+ * none): which entry point, which argument and why.  This is the library's
+ * one piece of per-thread state: a thread-local buffer of 512 bytes that
+ * every entry point clears on entry and fills on failure.  The pointer stays
+ * valid until the same thread's next call into the library. */
 const char* ss_last_error(void);
 
 #ifdef __cplusplus

@@ -64,11 +64,13 @@ _lib = None
 
 
 def load_library(path: Optional[str] = None):
-    """Load libss.so (once).  Raises if it has not been built."""
+    """Load libss.so (once).  Raises if it has not been built.  The
+    SS_LIBRARY environment variable names another build of the same library
+    (the sanitizer build of the host code, tests/test_sanitizers.py)."""
     global _lib
     if _lib is not None:
         return _lib
-    p = path or library_path
+    p = path or os.environ.get("SS_LIBRARY") or library_path
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with "
                            "`python -m mamba_selective_scan_02_amd.build`")

@@ -182,6 +182,12 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
         bq[i] = *reinterpret_cast<const float4*>(&sB[n0 + i][j * BGL + sh]);
         cq[i] = *reinterpret_cast<const float4*>(&sC[n0 + i][j * BGL + sh]);
       }
+      float ea[4 * NS];                    // the half tile's decays as one run
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+        for (int i = 0; i < NS; ++i) ea[ss * NS + i] = ex[sh + ss].x * A2[i];
+      exp2_run(ea);
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss) {
         const float4 e = ex[sh + ss];
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
         for (int i = 0; i < NS; ++i) {
           const float bvs = ss == 0 ? bq[i].x : ss == 1 ? bq[i].y : ss == 2 ? bq[i].z : bq[i].w;
           const float cvs = ss == 0 ? cq[i].x : ss == 1 ? cq[i].y : ss == 2 ? cq[i].z : cq[i].w;
-          const float av = fast_exp2(e.x * A2[i]);
+          const float av = ea[ss * NS + i];
           h[i] = __builtin_fmaf(av, h[i], e.y * bvs);
           E[i] *= av;
           sbl[i] = __builtin_fmaf(E[i], e.z * cvs, sbl[i]);
@@ -344,13 +350,19 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
 #pragma unroll
       for (int i = 0; i < NS; ++i)
         bq[i] = *reinterpret_cast<const float4*>(&sB[n0 + i][j * BGL + sh]);
+      float ea[4 * NS];                    // the half tile's decays as one run
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+        for (int i = 0; i < NS; ++i) ea[ss * NS + i] = ex[sh + ss].x * A2[i];
+      exp2_run(ea);
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss) {
         const float4 e = ex[sh + ss];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
           const float bvs = ss == 0 ? bq[i].x : ss == 1 ? bq[i].y : ss == 2 ? bq[i].z : bq[i].w;
-          h[i] = __builtin_fmaf(fast_exp2(e.x * A2[i]), h[i], e.y * bvs);
+          h[i] = __builtin_fmaf(ea[ss * NS + i], h[i], e.y * bvs);
         }
       }
     }
@@ -391,12 +403,24 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
       }
     }
 #pragma unroll
+    for (int sh = 0; sh < BGL; sh += 4) {   // the tile's decays in runs of exps
+      float ea[4 * NS];
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+        for (int i = 0; i < NS; ++i) ea[ss * NS + i] = ex[sh + ss].x * A2[i];
+      exp2_run(ea);
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+        for (int i = 0; i < NS; ++i) aa[sh + ss][i] = ea[ss * NS + i];
+    }
+#pragma unroll
     for (int s = 0; s < BGL; ++s) {
       float ov = 0.0f;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const float prev = s > 0 ? hh[s - 1][i] : h0[i];
-        aa[s][i] = fast_exp2(ex[s].x * A2[i]);
         hh[s][i] = __builtin_fmaf(aa[s][i], prev, ex[s].y * bt[s][i]);
         ov = __builtin_fmaf(ct[s][i], hh[s][i], ov);
       }

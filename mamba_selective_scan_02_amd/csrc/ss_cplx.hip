@@ -49,7 +49,10 @@ constexpr int kCRedStride = 257;       // LDS row stride of the dB/dC reduction
 // |a| (what the hardware exp2 and sin/cos approximations give together)
 // triples the error of y on long sequences.
 //
-// So exp and sin/cos are built here from the mathematics, in float:
+// So exp and sin/cos are built here from the mathematics, in float.  The
+// argument reductions are Cody and Waite's (1980): the constant (ln 2, pi/2)
+// is split into a short leading part, whose products with the small integer
+// multiple are exact, and trailing parts that carry the rest.
 //   * w = dt Ar and theta = dt Ai are carried as exact head + tail pairs
 //     (the tail from an fma), so the arguments are not rounded;
 //   * exp: w = k ln2 + r with |r| <= ln2 / 2 (ln2 in two parts, the high one
