@@ -4,11 +4,15 @@
 
 A step is one ss_fwd call over the Mamba-2.8B-shaped batch (B=8, L=2048,
 D=5120, N=16, bf16 u/delta/B/C/z/y, f32 A/D/delta_bias), inputs resident in
-HBM.  The value is forward state-updates/s (B*L*D*N per step / step time).
+HBM.  The value is forward state-updates/s (B*L*D*N per step / step time) at
+the median of K steps, each timed by HIP events on the launch stream with L2
+and the MALL evicted before it; back-to-back timings are reported beside it.
 The same line carries the HBM rate of the algorithmic bytes, the roofline of
-the scan kernel, the backward (ss_bwd on the B=2, L=2048, D=2048, N=16 f32
-workload), and the CPU oracle's rate on the host cores.  Prints ONE JSON line
-on stdout; progress goes to stderr.
+the scan kernel (bound by the ALU: the update's instruction mix), the
+backward (ss_bwd on the B=2, L=2048, D=2048, N=16 f32 workload), the decode
+step, the strided, packed-sequence and complex variants, every workload's
+timings with its parity against the float64 oracle, and the oracle's rate on
+the host cores.  Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -17,6 +21,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -40,19 +45,36 @@ FLOPS_PER_UPDATE_COMPLEX = 18
 # (2), m = conj(a)*lam (6), dw = m*conj(h_prev) (6), Re(conj(A)*dw) (3),
 # dA += dt*dw (4), Re(conj(B)*lam) (3): 48.
 FLOPS_PER_UPDATE_COMPLEX_BWD = 48
-# Instruction-mix floor: the same work priced at the issue rates measured on
-# the box by microbench/rates.hip (profiles/hw_rates_mi355x.txt, 4 waves per
-# SIMD): one wave instruction per SIMD every 4.29 ns for v_exp_f32 and every
-# 1.246 ns for an FP32 FMA-class op, 1024 SIMDs, 64 lanes.  Per update, the
-# forward needs 1 exp + 4 ops (dt*A, (dt*u)*B, a*h + x, C*h); the backward
-# 3 exp + 20 ops (summary: exp + 5; pass 1: exp + 2; pass 2: exp + 2, the
-# readout 1 and the adjoint 10); the complex forward's decay is not an exp
-# instruction and is left out.
-EXP_NS, OP_NS, SIMDS = 4.29, 1.246, 1024
+# The scan is bound by VALU issue, not by HBM (profiles/hw_rates_mi355x.txt):
+# a state update is 1 transcendental (v_exp_f32) + 4 FP32 operations (dt*A,
+# (dt*u)*B, a*h + x, C*h), and on gfx950 the transcendental takes the same
+# issue slots as the FP32 operations (no co-issue, measured).
+#
+# ALU peak of that instruction mix, from the chip's unit counts and clock:
+# 256 CUs x 4 SIMDs = 1024 SIMDs at 2.4 GHz; the FP32 vector peak of 157.3
+# TFLOP/s is 32 FMA lanes per SIMD per clock, i.e. one 64-lane FP32
+# instruction every 2 clocks; transcendentals run at a quarter of that rate,
+# 8 clocks.  One update per lane therefore costs a SIMD 4 x 2 + 8 = 16 clocks
+# per 64 updates: 1024 x 64 x 2.4e9 / 16 = 9.83e12 updates/s, 68.8 TFLOP/s
+# at 7 flops per update.  (The bare update mix, with no other instruction,
+# measures 6.6-7.1e12 updates/s on the box: the clock under this load sits
+# below 2.4 GHz.)
+SIMDS, CLOCK_HZ = 1024, 2.4e9
+OP_CLK, TRANS_CLK = 2, 8        # SIMD clocks per 64-lane FP32 / transcendental instruction
+
+
+def mix_peak_updates(n_trans: int, n_ops: int) -> float:
+    """Updates/s at the ALU peak for n_trans + n_ops instructions per update."""
+    return SIMDS * 64 * CLOCK_HZ / (n_trans * TRANS_CLK + n_ops * OP_CLK)
+
+
+# Measured issue cost of the bare update mix (microbenchmark "upd_clust" at 5
+# waves/SIMD, the 2.8B-shaped grid): the floor a real kernel can approach.
+MEASURED_UPDATE_MIX = 7.15e12
 
 
 def mix_floor(updates_per_s: float, n_exp: int, n_ops: int) -> dict:
-    floor = 64 * SIMDS / ((n_exp * EXP_NS + n_ops * OP_NS) * 1e-9)
+    floor = mix_peak_updates(n_exp, n_ops)
     return {"updates_per_s": floor, "frac": updates_per_s / floor, "exp_per_update": n_exp,
             "ops_per_update": n_ops}
 
@@ -175,12 +197,17 @@ def time_calls(fn, steps: int, warmup: int):
 
 
 def alu_roofline(updates_per_s: float, flops_per_update: int, mix=None) -> dict:
+    """ALU roofline of a leg.  With mix = (transcendentals, FP32 operations)
+    per update, the peak is that instruction mix's ALU peak (mix_peak_updates
+    x flops per update); without, the FP32 vector peak."""
     achieved = updates_per_s * flops_per_update / 1e12
-    r = {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
-         "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
-         "flops_per_update": flops_per_update}
+    peak = (mix_peak_updates(*mix) * flops_per_update / 1e12 if mix is not None
+            else FP32_VECTOR_PEAK_TFLOPS)
+    r = {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+         "frac": achieved / peak, "flops_per_update": flops_per_update,
+         "fp32_vector_frac": achieved / FP32_VECTOR_PEAK_TFLOPS}
     if mix is not None:
-        r["mix_floor"] = mix_floor(updates_per_s, *mix)
+        r["mix"] = {"transcendentals_per_update": mix[0], "fp32_ops_per_update": mix[1]}
     return r
 
 
@@ -368,11 +395,71 @@ def variant_legs(ss, w, dev, args_f, keys, steps, with_cpu=False):
 CONFIG_NAMES = ("tiny", "m130m", "m2p8b", "long", "bwd")
 
 
-def configs_leg(ss, reps: int, names=CONFIG_NAMES):
+def rel_err(x, r) -> float:
+    """max_i |x_i - r_i| / max(|r_i|, rms(r)) over one tensor (the parity metric)."""
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(r * r)))
+    if rms == 0.0:
+        return float(np.max(np.abs(x - r)))
+    return float(np.max(np.abs(x - r) / np.maximum(np.abs(r), rms)))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def config_parity(ss, w, inp, args_f, dy, gpu_s: float) -> dict:
+    """One workload against the float64 oracle: the max error per output, run-
+    to-run bit-exactness (two calls compared bit for bit), and the oracle's
+    time on the host cores (the whole workload, compute only)."""
+    import torch
+    import oracle
+    keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
+    tol = 1e-5 if w.io_dtype == "f32" else 2e-2
+    to64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
+    if w.backward:
+        g1 = ss.bwd(*args_f, dy=dy)
+        g2 = ss.bwd(*args_f, dy=dy)
+        torch.cuda.synchronize()
+        exact = all(torch.equal(g1[k], g2[k]) for k in g1 if g1[k] is not None)
+        t0 = time.perf_counter()
+        ref = oracle.bwd(**{k: inp[k] for k in keys}, dy=inp["dy"])
+        osec = time.perf_counter() - t0
+        errs = {k: rel_err(to64(g1[k]), ref[k]) for k in ref if ref[k] is not None}
+    else:
+        y1, l1 = ss.fwd(*args_f, return_last_state=True)
+        y2, l2 = ss.fwd(*args_f, return_last_state=True)
+        torch.cuda.synchronize()
+        exact = torch.equal(y1, y2) and torch.equal(l1, l2)
+        t0 = time.perf_counter()
+        yr, lr = oracle.fwd(**{k: inp[k] for k in keys}, return_last_state=True)
+        osec = time.perf_counter() - t0
+        errs = {"y": rel_err(to64(y1), yr), "last_state": rel_err(to64(l1), lr)}
+        del yr
+    worst = max(errs.values())
+    return {"max_rel_err": errs, "worst_rel_err": worst, "bound": tol, "within_bound": worst <= tol,
+            "bit_exact_run_to_run": bool(exact),
+            "oracle": {"seconds": osec, "cores": oracle.default_threads(), "cpu": cpu_model(),
+                       "state_updates_per_s": w.updates / osec, "kind": "float64 C loop",
+                       "gpu_speedup": osec / gpu_s}}
+
+
+def configs_leg(ss, reps: int, names=CONFIG_NAMES, with_oracle: bool = True):
     """Every forward workload and the backward one, each timed per call warm
     (back to back) and cold (L2 and MALL evicted before every call): median,
-    min and max, with updates/s and algorithmic GB/s at the cold median."""
-    import statistics
+    min and max, with updates/s and algorithmic GB/s at the cold median; with
+    with_oracle, also each workload's parity record (config_parity)."""
     import torch
     from ss_inputs import WORKLOADS, make_inputs
     keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
@@ -383,7 +470,6 @@ def configs_leg(ss, reps: int, names=CONFIG_NAMES):
         log(f"configs: {name}")
         inp = make_inputs(w)
         dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
-        del inp
         args_f = [dev[k] for k in keys]
         io = {"f32": 0, "f16": 1, "bf16": 2}[w.io_dtype]
         pa = {"f32": 0, "f16": 1, "bf16": 2}[w.param_dtype]
@@ -423,7 +509,10 @@ def configs_leg(ss, reps: int, names=CONFIG_NAMES):
             "hbm_frac_cold": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": nbytes,
         }
-        del dev, args_f, ws
+        if with_oracle:
+            log(f"configs: {name} against the oracle")
+            out[name].update(config_parity(ss, w, inp, args_f, dev.get("dy"), med * 1e-3))
+        del dev, args_f, ws, inp
         torch.cuda.empty_cache()
     del scratch
     return out
@@ -465,7 +554,8 @@ def main():
         calibration_copy()
     if args.configs_only is not None:
         names = tuple(args.configs_only) or CONFIG_NAMES
-        print(json.dumps({"configs": configs_leg(ss, args.steps, names)}), flush=True)
+        print(json.dumps({"configs": configs_leg(ss, args.steps, names,
+                                                 not args.no_cpu_baseline)}), flush=True)
         return
     keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
     w = WORKLOADS["m2p8b"]
@@ -484,14 +574,28 @@ def main():
     if args.variants_only:
         print(json.dumps(variant_legs(ss, w, dev, args_f, keys, args.steps)), flush=True)
         return
+    # The headline step: warmup, then K calls each timed by its own HIP events
+    # on the launch stream, with L2 and the 256 MB MALL evicted before every
+    # call (a 1 GiB write), so each call reads its inputs from HBM; the value
+    # is taken at the median.  The same K calls back to back ("warm") are
+    # reported beside it.
     log(f"timing forward: warmup {args.warmup}, steps {args.steps}")
-    ms, wall = time_calls(step, args.steps, args.warmup)
+    for _ in range(args.warmup):
+        step()
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    cold = time_each(step, args.steps, scratch)
+    wall = time.perf_counter() - t_wall
+    del scratch
+    warm_ms, _ = time_calls(step, args.steps, 1)
+    ms = statistics.median(cold)
     updates = w.updates
     value = updates / (ms * 1e-3)
     abytes = algorithmic_bytes(w)
     gbs = abytes / (ms * 1e-3) / 1e9
-    tflops = FLOPS_PER_UPDATE * value / 1e12
-    log(f"forward {ms * 1e3:.1f} us/step, {value:.3e} updates/s, {gbs:.0f} GB/s")
+    log(f"forward {ms * 1e3:.1f} us/step (median, cold), {value:.3e} updates/s, {gbs:.0f} GB/s; "
+        f"back to back {warm_ms * 1e3:.1f} us")
 
     result = {
         "metric": "selective_scan fwd state-updates/s and HBM GB/s (% of peak), 1 MI355X",
@@ -511,16 +615,26 @@ def main():
                    "batch": w.batch, "seq_len": w.seqlen, "dim": w.dim, "dstate": w.dstate,
                    "io_dtype": w.io_dtype, "param_dtype": w.param_dtype,
                    "n_chunks": plan.n_chunks, "kernels_per_step": plan.n_launches},
+        "timing": {"protocol": "median of K calls, L2 and MALL evicted before each call",
+                   "us_min": min(cold) * 1e3, "us_max": max(cold) * 1e3,
+                   "us_per_call_back_to_back": warm_ms * 1e3,
+                   "state_updates_per_s_back_to_back": updates / (warm_ms * 1e-3)},
         "hbm_gbs": gbs,
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "algorithmic_bytes": abytes,
-        "roofline": {"bound": "alu", "kernel": "fwd_wide (single pass, 8 lanes per channel, LDS-staged streams)",
-                     "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / FP32_VECTOR_PEAK_TFLOPS,
-                     "flops_per_update": FLOPS_PER_UPDATE,
-                     "traffic": stored_traffic("fwd_wide_m2p8b"),
-                     "hbm_achieved_gbs": gbs, "hbm_peak_gbs": HBM_PEAK_GBS,
-                     "mix_floor": mix_floor(value, 1, 4)},
+        # binding roofline: the update's instruction mix (1 transcendental +
+        # 4 FP32 ops) at the ALU peak; the HBM and FP32-vector fractions beside it
+        "roofline": dict(alu_roofline(value, FLOPS_PER_UPDATE, (1, 4)),
+                         kernel="fwd_wide (single pass, 8 lanes per channel, LDS-staged streams)",
+                         traffic=stored_traffic("fwd_wide_m2p8b"),
+                         hbm_achieved_gbs=gbs, hbm_peak_gbs=HBM_PEAK_GBS,
+                         hbm_frac=gbs / HBM_PEAK_GBS,
+                         floors_us={"hbm": abytes / (HBM_PEAK_GBS * 1e9) * 1e6,
+                                    "fp32_vector": updates * FLOPS_PER_UPDATE
+                                    / (FP32_VECTOR_PEAK_TFLOPS * 1e12) * 1e6,
+                                    "alu_mix": updates / mix_peak_updates(1, 4) * 1e6,
+                                    "measured_update_mix": updates / MEASURED_UPDATE_MIX * 1e6},
+                         measured_mix_frac=value / MEASURED_UPDATE_MIX),
         "wall_s": wall,
     }
     del y, ws
@@ -624,7 +738,7 @@ def main():
                                    with_cpu=not args.no_cpu_baseline))
 
     if not args.no_configs:
-        result["configs"] = configs_leg(ss, args.steps)
+        result["configs"] = configs_leg(ss, args.steps, with_oracle=not args.no_cpu_baseline)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
