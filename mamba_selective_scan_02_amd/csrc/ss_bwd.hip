@@ -161,12 +161,19 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) 
       sb[j] = bs[(K - 1 - jj) * N * D];
       dbk[j] = ds[(K - 1 - jj) * D];
     }
+    // the batch's decays first (independent of the chains), then the chains
+    float pf[KB], pb[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      pf[j] = chunk_decay(Av, df[j]);
+      pb[j] = chunk_decay(Av, dbk[j]);
+    }
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (j0 + j < K - 1) {
-        hc = __builtin_fmaf(chunk_decay(Av, df[j]), hc, sf[j]);
+        hc = __builtin_fmaf(pf[j], hc, sf[j]);
         fs[(j0 + j) * N * D] = hc;
-        cc = __builtin_fmaf(chunk_decay(Av, dbk[j]), cc, sb[j]);
+        cc = __builtin_fmaf(pb[j], cc, sb[j]);
         bs[(K - 1 - (j0 + j)) * N * D] = cc;
       }
     }

@@ -57,10 +57,14 @@ __global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
       sv[j] = st[kk * N * D];
       dv[j] = ds[kk * D];
     }
+    // the batch's decays first (independent of the chain), then the chain
+    float pv[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) pv[j] = chunk_decay(Av, dv[j]);
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (k0 + j < K - 1) {
-        hc = __builtin_fmaf(chunk_decay(Av, dv[j]), hc, sv[j]);
+        hc = __builtin_fmaf(pv[j], hc, sv[j]);
         st[(k0 + j) * N * D] = hc;
       }
     }

@@ -77,21 +77,22 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
     if (d.chunk_len > 0) {
       lc = d.chunk_len < L ? d.chunk_len : L;
     } else {
-      // Waves that one chunk index provides.  A SIMD needs several resident
-      // waves to approach its VALU rate (a lone wave issues at about a third
-      // of it), so below ~3 waves per SIMD (1024 SIMDs) the time axis is cut
-      // into chunks until the grid reaches about 8 waves per SIMD (5 are
-      // resident at a time; the rest even out the tail), with chunks of at
-      // least 128 steps; the chunk summaries cost one extra sweep and two
-      // more launches, which a sequence of fewer than 256 steps does not earn
-      // back (1x128x32x16: 17.8 us in 3 launches).  Measured against the
-      // chunk length: 1x262144x512x16 takes 1037 / 972 / 963 us with chunks
-      // of 4096 / 2048 / 1024 steps, 4x1024x1536x16 79 / 76 us with 172 / 128.
+      // Waves that one chunk index provides.  The chunked schedule sweeps
+      // the data twice (the summaries cost about as many exps as the final
+      // pass) and adds two launches, so it pays only when the grid leaves
+      // most SIMDs (1024) idle: below 640 waves the time axis is cut into
+      // chunks until the grid reaches about 8 waves per SIMD, with chunks of
+      // at least 128 steps (a sequence of fewer than 256 steps does not earn
+      // the extra launches back: 1x128x32x16 takes 17.8 us in 3 launches).
+      // Measured (cold medians): 4x1024x1536x16 (768 waves) 66.6 us in one
+      // pass, 69.2 / 84.5 / 72.6 us with chunks of 256 / 512 / 128 steps;
+      // 1x262144x512x16 (64 waves) 1037 / 972 / 963 us with chunks of
+      // 4096 / 2048 / 1024 steps.
       const int64_t cpw = 64 / p.G;
       const int64_t waves = Bn * ((D + cpw - 1) / cpw);
       const int64_t target = 8192;
       int64_t K = 1;
-      if (waves < 3072) {
+      if (waves < 640) {
         K = (target + waves - 1) / waves;
         const int64_t kmax = L / 128;
         if (K > kmax) K = kmax;
