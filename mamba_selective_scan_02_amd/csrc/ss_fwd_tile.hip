@@ -4,20 +4,21 @@
 // "src/attention/selective_scan.rs", module docs, "Algorithm summary"), for
 // N <= 32.  Mapping:
 //
-//   * 8 lanes own one channel d: lanes c, c+8, ..., c+56 of a wave hold
-//     channel c of the wave's 8, and lane g of the channel (wave lane c + 8g)
-//     holds states n = g*NS .. g*NS+NS-1 (NS = 1, 2 or 4).  A wave covers 8
-//     channels, a 256-lane workgroup 32.  This gives 8x the waves of one-lane-per-channel,
-//     which the wave-per-SIMD issue rate needs (a lone wave issues far below
-//     the VALU rate; several resident waves per SIMD are needed to fill it).
+//   * 8 lanes own one channel d, all in one row of 16 lanes of the wave
+//     (tile_g / tile_channel), and lane g of the channel holds states
+//     n = g*NS .. g*NS+NS-1 (NS = 1, 2 or 4).  A wave covers 8 channels, a
+//     256-lane workgroup 32.  This gives 8x the waves of one lane per
+//     channel, which the wave-per-SIMD issue rate needs (a lone wave issues
+//     far below the VALU rate; several resident waves per SIMD are needed).
 //   * Per-(t, d) work is time-shared: in every tile of 8 steps, lane g loads
 //     u / delta / z of step t0+g, computes dt = softplus(delta + bias),
 //     dt*u and the gate silu(z) for that step only, and hands (dt, dt*u) to
 //     the other 7 lanes of its channel through a per-wave LDS exchange.
 //   * The readout sum over a channel's states is a sum over its 8 lanes, done
-//     once per 8-step tile as a reduce-scatter (lane swaps and DPP): lane g
-//     ends with the sum of step t0+g and applies the skip term and the gate
-//     to it.
+//     once per 8-step tile as a reduce-scatter through DPP moves within the
+//     row: lane g ends with the sum of step t0+g and applies the skip term
+//     and the gate to it.
+//   * The decays of each half tile issue as one run of exps (exp2_run).
 //   * B and C are staged per workgroup in LDS as f32, [n][t] per 64-step tile,
 //     double buffered, rows padded to 68 floats (16-byte aligned, conflict-free
 //     128-bit reads); states n >= N are zero rows, so padded states stay 0.
@@ -49,6 +50,41 @@ enum { TMODE_FULL = 0, TMODE_SUMMARY = 1 };
 template <int NS>
 constexpr int tile_waves_per_simd() { return NS <= 2 ? 5 : 3; }
 
+// Lane map of the forward tile kernels: a channel's 8 lanes lie in one row of 16 lanes, so
+// that every stage of the readout's reduce-scatter is a DPP move within the
+// row.  Wave lane l = 16 r + 8 q + 4 s + p holds lane g = 4 q + p of channel
+// c = 2 r + s (of the wave's 8).  Butterfly partners: g ^ 4 is lane l ^ 8
+// (row rotation by 8), g ^ 2 is l ^ 2 and g ^ 1 is l ^ 1 (quad permutations).
+__device__ __forceinline__ int tile_g(int tid) { return (tid & 3) | ((tid >> 1) & 4); }
+__device__ __forceinline__ int tile_channel(int tid) {
+  return ((tid >> 6) << 3) | ((tid >> 2) & 1) | ((tid >> 3) & 6);
+}
+
+// Reduce-scatter over a channel's 8 lanes (this lane map): lane g holds o[0..7]
+// and ends with the channel's sum of o[g].  Each stage keeps half of the
+// values (chosen by one bit of g) and adds the partner's matching half, sent
+// through DPP: 14 selects and 7 DPP adds, no lane swaps (a v_permlane*_swap
+// costs the SIMD about as much as two DPP adds: measured).
+__device__ __forceinline__ float reduce_scatter8_dpp(const float (&o)[8], int g) {
+  const bool hi = (g & 4) != 0, b1 = (g & 2) != 0, b0 = (g & 1) != 0;
+  float a[4], b[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = hi ? o[4 + k] : o[k];
+    const float send = hi ? o[k] : o[4 + k];
+    a[k] = keep + dpp<0x128>(send);       // row_ror:8: lane l ^ 8
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float keep = b1 ? a[2 + k] : a[k];
+    const float send = b1 ? a[k] : a[2 + k];
+    b[k] = keep + dpp<0x4E>(send);        // quad_perm [2,3,0,1]: lane l ^ 2
+  }
+  const float keep = b0 ? b[1] : b[0];
+  const float send = b0 ? b[0] : b[1];
+  return keep + dpp<0xB1>(send);          // quad_perm [1,0,3,2]: lane l ^ 1
+}
+
 template <typename T, int NS, int MODE, bool HAS_Z>
 __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(const T* __restrict__ u_in,
                                                     const T* __restrict__ delta_in,
@@ -62,8 +98,8 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
   __shared__ __attribute__((aligned(16))) float2 xch[2][CPW][XS];
 
   const int tid = threadIdx.x;
-  const int g = lane_g(tid);
-  const int cl = lane_channel(tid);
+  const int g = tile_g(tid);
+  const int cl = tile_channel(tid);
   const int64_t nbd = (a.D + CPW - 1) / CPW;
   int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
   const int64_t db = blk % nbd;
@@ -250,7 +286,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
         }
       }
       if (MODE == TMODE_FULL) {
-        const float o_own = reduce_scatter8(ot, g);   // full readout of step t0 + p*8 + g
+        const float o_own = reduce_scatter8_dpp(ot, g);   // full readout of step t0 + p*8 + g
         const float yv = __builtin_fmaf(Dv, cur.uu, o_own) * cur.gate;
         // tail lanes (d >= D) store channel D-1's value to channel D-1's
         // address; steps past the chunk fall outside the buffer and are dropped
@@ -262,7 +298,11 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
     __syncthreads();
   }
 
-  if (MODE == TMODE_SUMMARY) dsum = sum8(dsum);
+  if (MODE == TMODE_SUMMARY) {                     // the channel's sum over its 8 lanes
+    dsum += dpp<0x128>(dsum);
+    dsum += dpp<0x4E>(dsum);
+    dsum += dpp<0xB1>(dsum);
+  }
   if (!active) return;
   if (MODE == TMODE_SUMMARY) {
 #pragma unroll
@@ -342,8 +382,8 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   __shared__ __attribute__((aligned(16))) float2 xch[2][CPW][XS];
 
   const int tid = threadIdx.x;
-  const int g = lane_g(tid);
-  const int cl = lane_channel(tid);
+  const int g = tile_g(tid);
+  const int cl = tile_channel(tid);
   const int64_t nbd = (a.D + CPW - 1) / CPW;
   int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
   const int64_t db = blk % nbd;
@@ -542,7 +582,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
         }
       }
       if constexpr (FULL) {
-        const float o_own = reduce_scatter8(ot, g);   // full readout of this lane's step
+        const float o_own = reduce_scatter8_dpp(ot, g);   // full readout of this lane's step
         lds_put<T>(&sIn[1][(pt * GL + g) * RS + lds_own_col],
                    __builtin_fmaf(Dv, cur.uu, o_own) * cur.gate);
       }
@@ -563,7 +603,11 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
     __syncthreads();
   }
 
-  if (!FULL) dsum = sum8(dsum);
+  if (!FULL) {                                      // the channel's sum over its 8 lanes
+    dsum += dpp<0x128>(dsum);
+    dsum += dpp<0x4E>(dsum);
+    dsum += dpp<0xB1>(dsum);
+  }
   if (!active) return;
   if (!FULL) {
 #pragma unroll
