@@ -18,7 +18,8 @@
 // the scheme here (no atomics anywhere, so every output is bitwise
 // reproducible).
 //
-// Schedule.  Time is cut into chunks of at most 16 steps (one register tile).
+// Schedule.  Time is cut into chunks of at most kBwdTile = 8 steps (one
+// register tile).
 //  1. bwd_summary: per chunk, from zero: S (forward end state), Sb (the
 //     adjoint the chunk hands to the step before it, sum_s (prod_{r<=s} a_r)
 //     g_s C_s, accumulated forward with a running decay product) and sum dt.
@@ -35,7 +36,7 @@
 
 namespace ss {
 
-constexpr int T = kBwdTile;            // 16 steps per chunk (max)
+constexpr int T = kBwdTile;            // steps per chunk (max)
 constexpr int kRedStride = 257;        // LDS row stride of the dB/dC reduction buffer
 
 // Per-chunk inputs shared by all channels of a workgroup: B and C for the
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
   Tio* ddp = static_cast<Tio*>(a.ddelta) + d;
   Tio* dzp = has_z ? static_cast<Tio*>(a.dz) + d : dup;
 
-  // reduction lane roles: value v (0..15 dB, 16..31 dC), channel slice p
+  // reduction lane roles: value v (0..T-1 dB, T..2T-1 dC), channel slice p
   const int rv = tid >> 3, rp = tid & 7;
   float dD_acc = 0.0f, db_acc = 0.0f;
   const int64_t k_lo = kg * kBwdChunksPerGroup;
@@ -298,14 +299,17 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
         red[(T + tt) * kRedStride + tid] = active ? vC[tt] : 0.0f;
       }
       __syncthreads();
+      // 2T values (T of dB, T of dC), 8 threads each; rows rv >= 2T are unused
       float s = 0.0f;
+      if (rv < 2 * T) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) s += red[rv * kRedStride + rp * 32 + ((i + 8 * rp) & 31)];
+        for (int i = 0; i < 32; ++i) s += red[rv * kRedStride + rp * 32 + ((i + 8 * rp) & 31)];
+      }
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
       s += __shfl_xor(s, 4, 64);
-      if (rp == 0) {
-        const int tt = rv & (T - 1), which = rv >> 4;
+      if (rp == 0 && rv < 2 * T) {
+        const int tt = rv % T, which = rv / T;
         if (tt < nt)
           a.part_bc[((sr.start + t0 + tt) * a.nwgd + db) * 2 * N + which * N + n] = s;
       }

@@ -11,8 +11,11 @@
 
 namespace ss {
 
-// Backward register tile: time steps one lane holds per chunk (general path).
-constexpr int kBwdTile = 16;
+// Backward register tile: time steps one lane holds per chunk (general path,
+// N > 16).  8 steps keep the main kernel at 208 VGPRs (2 waves per SIMD);
+// 16 steps took 336 (1 wave): 2x2048x2048 backward, N = 32 982 -> 894 us,
+// N = 64 1794 -> 1584 us (twice the chunk records, but twice the waves).
+constexpr int kBwdTile = 8;
 // Backward chunk length of the tile path (N <= 16): 8 tiles of 8 steps.
 constexpr int kBwdTileChunk = 64;
 // Chunks of one channel block handled by one backward workgroup (their dA /
@@ -120,7 +123,7 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
   }
   // backward.  N <= 16: tile kernels, chunks of up to 64 steps, 32 channels
   // per workgroup, per-chunk partials.  Otherwise the general kernels: chunks
-  // of up to 16 steps (one register tile), 256 channels per workgroup,
+  // of up to kBwdTile steps (one register tile), 256 channels per workgroup,
   // partials per group of 4 chunks.
   p.bwd_tile = N <= 16;
   int64_t lc = p.bwd_tile ? kBwdTileChunk : kBwdTile;

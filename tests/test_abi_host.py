@@ -286,12 +286,12 @@ def test_plan_is_a_function_of_shape():
         p = ss.plan(_desc(N=n))
         assert (p.states_per_lane, p.lanes_per_channel) == (ns, g), n
     # backward: N <= 16 uses the tile kernels with chunks of 64 steps, larger N
-    # the general kernels with chunks of 16 steps
+    # the general kernels with chunks of 8 steps
     p = ss.plan(_desc(B=2, L=2048, D=2048, N=16), True)
     assert (p.chunk_len, p.n_chunks, p.n_launches, p.states_per_lane,
             p.lanes_per_channel) == (64, 32, 4, 2, 8)
     p = ss.plan(_desc(B=2, L=2048, D=2048, N=17), True)
-    assert (p.chunk_len, p.n_chunks, p.n_launches) == (16, 128, 4)
+    assert (p.chunk_len, p.n_chunks, p.n_launches) == (8, 256, 4)
 
 
 def test_workspace_size_formula():
