@@ -37,6 +37,7 @@
 namespace ss {
 
 constexpr int T = kBwdTile;            // steps per chunk (max)
+static_assert(4 * T <= 32, "two states' dB / dC rows fill the 32-row reduction buffer");
 constexpr int kRedStride = 257;        // LDS row stride of the dB/dC reduction buffer
 
 // Per-chunk inputs shared by all channels of a workgroup: B and C for the
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
   extern __shared__ float smem[];
   float* sB = smem;
   float* sC = smem + a.N * T;
-  float* red = smem + 2 * a.N * T;  // [32][kRedStride]
+  float* red = smem + 2 * a.N * T;  // [32][kRedStride]: 4T rows (two states) used
   const int tid = threadIdx.x;
   const int64_t nbd = a.nwgd;
   int64_t blk = blockIdx.x;
@@ -212,7 +213,8 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
   Tio* ddp = static_cast<Tio*>(a.ddelta) + d;
   Tio* dzp = has_z ? static_cast<Tio*>(a.dz) + d : dup;
 
-  // reduction lane roles: value v (0..T-1 dB, T..2T-1 dC), channel slice p
+  // reduction lane roles: value v (per state of a round: T of dB, T of dC),
+  // channel slice p
   const int rv = tid >> 3, rp = tid & 7;
   float dD_acc = 0.0f, db_acc = 0.0f;
   const int64_t k_lo = kg * kBwdChunksPerGroup;
@@ -291,29 +293,35 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
         // after step 0 of chunk 0, dh is dL/dh_{-1}
         if (k == 0 && a.dh0) st_param(a.dh0, (b * D + d) * N + n, a.param_dtype, dh);
       }
-      // dB / dC for this n: sum over the workgroup's channels in LDS.
-      // Inactive (tail) lanes contribute zero.
+      // dB / dC for this n: sum over the workgroup's channels in LDS, two
+      // states per round (rows [2T * (n % 2), 2T * (n % 2) + 2T) of red:
+      // T of dB, then T of dC).  Inactive (tail) lanes contribute zero.
+      const int half = (int)(n & 1) * 2 * T;
 #pragma unroll
       for (int tt = 0; tt < T; ++tt) {
-        red[tt * kRedStride + tid] = active ? vB[tt] : 0.0f;
-        red[(T + tt) * kRedStride + tid] = active ? vC[tt] : 0.0f;
+        red[(half + tt) * kRedStride + tid] = active ? vB[tt] : 0.0f;
+        red[(half + T + tt) * kRedStride + tid] = active ? vC[tt] : 0.0f;
       }
+      if ((n & 1) == 0 && n + 1 < N) continue;   // the round's second state first
       __syncthreads();
-      // 2T values (T of dB, T of dC), 8 threads each; rows rv >= 2T are unused
+      // 4T values (two states), 8 threads each; rows rv >= 4T are unused
+      const int64_t nb = n & ~int64_t(1);        // the round's first state
+      const int rows = (n & 1) ? 4 * T : 2 * T;  // an odd last state rounds alone
       float s = 0.0f;
-      if (rv < 2 * T) {
+      if (rv < rows) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) s += red[rv * kRedStride + rp * 32 + ((i + 8 * rp) & 31)];
       }
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
       s += __shfl_xor(s, 4, 64);
-      if (rp == 0 && rv < 2 * T) {
-        const int tt = rv % T, which = rv / T;
+      if (rp == 0 && rv < rows) {
+        const int ns = rv / (2 * T), w = rv % (2 * T);
+        const int tt = w % T, which = w / T;
         if (tt < nt)
-          a.part_bc[((sr.start + t0 + tt) * a.nwgd + db) * 2 * N + which * N + n] = s;
+          a.part_bc[((sr.start + t0 + tt) * a.nwgd + db) * 2 * N + which * N + nb + ns] = s;
       }
-      __syncthreads();  // red free for the next n
+      __syncthreads();  // red free for the next round
     }
 
 #pragma unroll
