@@ -23,8 +23,22 @@
 //     double buffered, rows padded to 68 floats (16-byte aligned, conflict-free
 //     128-bit reads); states n >= N are zero rows, so padded states stay 0.
 //
-// Chunk summaries, the carry and the chunked final pass follow the same
-// two-level scheme as ss_fwd_scan.h and share its workspace layout.
+// Chunked sequences share the workspace layout and the carry of ss_fwd_scan.h.
+// fwd_tile follows its two-level scheme (summaries from zero, carry, a final
+// pass from the carried states).  fwd_wide writes y in its first pass:
+//   LOCAL  runs every chunk from h = 0 and writes y, the chunk end states and
+//          the chunks' dt sums;
+//   carry  turns them into the true state entering each chunk;
+//   FIXUP  reruns each chunk from that state beside a copy of the LOCAL
+//          recurrence, writing y, and stops at the first stage end (every 32
+//          or 64 steps) at which all states of the workgroup equal the copy's
+//          bit for bit.
+// From that step on the two passes perform the same operations on the same
+// values, so the LOCAL pass's y of the rest of the chunk is exactly what the
+// rerun would write: the result is that of a full final pass.  Decaying states
+// forget their start within tens to hundreds of steps, so FIXUP usually
+// covers a few stages per chunk; states that never forget it (A = 0) make it a
+// full second pass.
 #include <type_traits>
 
 #include "ss_device.h"
@@ -42,13 +56,19 @@ constexpr int XS = 10;                // exchange row stride (float2) per channe
 
 }  // namespace
 
-enum { TMODE_FULL = 0, TMODE_SUMMARY = 1 };
+// FULL: one pass from h0 (or, after a carry, from the carried state).
+// SUMMARY: chunk end state and dt sum from h = 0 (fwd_tile's chunked scheme).
+// LOCAL / FIXUP: fwd_wide's chunked scheme (see launch_tile_t).
+enum { TMODE_FULL = 0, TMODE_SUMMARY = 1, TMODE_LOCAL = 2, TMODE_FIXUP = 3 };
 
 // Resident waves per SIMD the register budget is held to: a 2.8B-shaped grid
 // (5120 waves of 8 channels) is exactly 5 waves on each of the 1024 SIMDs, and
 // 5 waves fit 96 VGPRs.  NS = 4 needs more registers and gets 3.
-template <int NS>
-constexpr int tile_waves_per_simd() { return NS <= 2 ? 5 : 3; }
+// The fix-up pass carries a second set of states and is short: 4 waves.
+template <int NS, int MODE = TMODE_FULL>
+constexpr int tile_waves_per_simd() {
+  return NS <= 2 ? (MODE == TMODE_FIXUP ? 4 : 5) : 3;
+}
 
 // Lane map of the forward tile kernels: a channel's 8 lanes lie in one row of 16 lanes, so
 // that every stage of the readout's reduce-scatter is a DPP move within the
@@ -357,29 +377,33 @@ __device__ __forceinline__ void lds_put(uint8_t* p, float v) {
 }
 
 template <typename T, int NS, int MODE, bool HAS_Z>
-__global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
+__global__ __launch_bounds__(kBlockT, (tile_waves_per_simd<NS, MODE>())) void fwd_wide(
     const T* __restrict__ u_in, const T* __restrict__ delta_in, const T* __restrict__ B_in,
     const T* __restrict__ C_in, const T* __restrict__ z_in, T* __restrict__ y_out,
     const FwdArgs a) {
   using W = WideCfg<T>;
   constexpr int ES = W::ES, TB = W::TB, RS = W::RS, TSW = W::TSW;
   constexpr int NP = NS * GL;                          // == N on this path
-  constexpr bool FULL = MODE == TMODE_FULL;
-  constexpr int NT = (FULL && HAS_Z) ? 3 : 2;          // streamed inputs: u, delta[, z]
+  constexpr bool OUT = MODE != TMODE_SUMMARY;          // readout and y
+  constexpr bool SUMM = MODE == TMODE_SUMMARY || MODE == TMODE_LOCAL;  // chunk summaries
+  constexpr bool CARRIED = MODE == TMODE_FULL || MODE == TMODE_FIXUP;  // starts from h_in
+  constexpr bool FIX = MODE == TMODE_FIXUP;
+  constexpr int NT = (OUT && HAS_Z) ? 3 : 2;           // streamed inputs: u, delta[, z]
   constexpr int NTILE = TB / GL;
   // B / C of a stage in 16-byte pieces: PPR per row, PB per tensor, NPC per thread
   constexpr int EPP = 16 / ES;
   constexpr int PPR = NP * ES / 16;
   constexpr int PB = TB * PPR;
-  constexpr int NBC = FULL ? 2 : 1;
+  constexpr int NBC = OUT ? 2 : 1;
   constexpr int NPC = (NBC * PB + kBlockT - 1) / kBlockT;
   static_assert(PB % 64 == 0, "a wave's pieces come from one tensor");
   // u, delta[, z] rows of the stage; y of row t replaces delta of row t once
   // the lane that owns (t, channel) has prepared that step (it is delta's
   // only reader), so the stage's y leaves from sIn[1].
   __shared__ __attribute__((aligned(16))) uint8_t sIn[NT][TB * RS];
-  __shared__ __attribute__((aligned(16))) float sBC[FULL ? 2 : 1][NP][TSW];
+  __shared__ __attribute__((aligned(16))) float sBC[OUT ? 2 : 1][NP][TSW];
   __shared__ __attribute__((aligned(16))) float2 xch[2][CPW][XS];
+  __shared__ int vote[2][kBlockT / 64];                // FIXUP: per-wave "all states agree"
 
   const int tid = threadIdx.x;
   const int g = tile_g(tid);
@@ -388,8 +412,10 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
   const int64_t db = blk % nbd;
   blk /= nbd;
-  const int64_t Kg = FULL ? a.K : a.K - 1;
-  const int64_t k = blk % Kg;
+  // FIXUP skips chunk 0 when there is no h0 (its LOCAL pass was exact)
+  const int64_t kf = (FIX && a.h0 == nullptr) ? 1 : 0;
+  const int64_t Kg = MODE == TMODE_SUMMARY ? a.K - 1 : a.K - kf;
+  const int64_t k = kf + blk % Kg;
   const int64_t b = blk / Kg;
   const int64_t d0 = db * CPW;
   const int64_t d_raw = d0 + cl;
@@ -402,14 +428,15 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   if (t1 < t0) t1 = t0;                         // a chunk past a short sequence's end
   const int n0 = g * NS;
 
-  float A2[NS], h[NS];
+  float A2[NS], h[NS], hl[NS];   // hl: FIXUP's copy of the LOCAL pass's states
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int n = n0 + i;
     A2[i] = n < N ? ld_param(a.A, d * N + n, a.param_dtype) * kLog2e : 0.0f;
     h[i] = 0.0f;
-    if (FULL && k > 0 && n < N) h[i] = a.chunk_state[((b * a.K + (k - 1)) * N + n) * D + d];
-    else if (FULL && k == 0 && n < N && a.h0)
+    hl[i] = 0.0f;
+    if (CARRIED && k > 0 && n < N) h[i] = a.chunk_state[((b * a.K + (k - 1)) * N + n) * D + d];
+    else if (CARRIED && k == 0 && n < N && a.h0)
       h[i] = ld_param(a.h0, (b * D + d) * N + n, a.param_dtype);
   }
   const float Dv = a.Dskip ? ld_param(a.Dskip, d, a.param_dtype) : 0.0f;
@@ -423,7 +450,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
   rs_in[0] = make_rsrc(u_in + row0, rbytes);
   rs_in[1] = make_rsrc(delta_in + row0, rbytes);
   if constexpr (NT == 3) rs_in[2] = make_rsrc(z_in + row0, rbytes);
-  const auto rs_y = make_rsrc(y_out + row0, FULL ? rbytes : 0);
+  const auto rs_y = make_rsrc(y_out + row0, OUT ? rbytes : 0);
   const auto rs_B = make_rsrc(B_in + (sr.start + t0) * a.ldb, rows_bytes(nsteps, a.ldb, N, ES));
   const auto rs_C = make_rsrc(C_in + (sr.start + t0) * a.ldc, rows_bytes(nsteps, a.ldc, N, ES));
 
@@ -511,7 +538,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
     r.xu = valid ? dl0 * uu : 0.0f;
     r.uu = uu;
     r.gate = 1.0f;
-    if constexpr (FULL && HAS_Z) {
+    if constexpr (OUT && HAS_Z) {
       const float zz = lds_elem<T>(own + 2 * TB * RS);
       r.gate = zz * sigmoid(zz);
     }
@@ -529,7 +556,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
     const int left = (int)nsteps - st * TB;          // steps of the chunk from this stage on
     Prep cur = prep(g, !MASKED || g < left);
     xch[0][cl][g] = make_float2(cur.dl, cur.xu);
-    constexpr int kUnroll = FULL ? NTILE : 1;
+    constexpr int kUnroll = OUT ? NTILE : 1;
 #pragma unroll kUnroll
     for (int pt = 0; pt < NTILE; ++pt) {
       if (MASKED && pt * GL >= left) break;          // tiles past the chunk (uniform)
@@ -546,7 +573,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
         nxt = prep(row, !MASKED || row < left);
         xch[(pt + 1) & 1][cl][g] = make_float2(nxt.dl, nxt.xu);
       }
-      if (!FULL) dsum += cur.dl;
+      if (SUMM) dsum += cur.dl;
       float ot[GL];
 #pragma unroll
       for (int jh = 0; jh < GL; jh += 4) {
@@ -554,7 +581,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
           bq[i] = *reinterpret_cast<const float4*>(&sBC[0][n0 + i][pt * GL + jh]);
-          if (FULL) cq[i] = *reinterpret_cast<const float4*>(&sBC[FULL ? 1 : 0][n0 + i][pt * GL + jh]);
+          if (OUT) cq[i] = *reinterpret_cast<const float4*>(&sBC[OUT ? 1 : 0][n0 + i][pt * GL + jh]);
         }
         // the half tile's decays as one run of exps (exp2_run)
         float ea[4 * NS];
@@ -572,8 +599,10 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
           for (int i = 0; i < NS; ++i) {
             const float bvj = jj == 0 ? bq[i].x : jj == 1 ? bq[i].y : jj == 2 ? bq[i].z : bq[i].w;
             const float dA = ea[jj * NS + i];
-            h[i] = __builtin_fmaf(dA, h[i], xuj * bvj);
-            if (FULL) {
+            const float xb = xuj * bvj;
+            h[i] = __builtin_fmaf(dA, h[i], xb);
+            if (FIX) hl[i] = __builtin_fmaf(dA, hl[i], xb);   // the LOCAL pass's operations
+            if (OUT) {
               const float cvj = jj == 0 ? cq[i].x : jj == 1 ? cq[i].y : jj == 2 ? cq[i].z : cq[i].w;
               o = __builtin_fmaf(cvj, h[i], o);
             }
@@ -581,7 +610,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
           ot[j] = o;
         }
       }
-      if constexpr (FULL) {
+      if constexpr (OUT) {
         const float o_own = reduce_scatter8_dpp(ot, g);   // full readout of this lane's step
         lds_put<T>(&sIn[1][(pt * GL + g) * RS + lds_own_col],
                    __builtin_fmaf(Dv, cur.uu, o_own) * cur.gate);
@@ -589,32 +618,56 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_wide(
       cur = nxt;
     }
   };
+  bool stopped = false;   // FIXUP: left before the chunk's end (states had converged)
   for (int st = 0; st < nstage; ++st) {
     const bool has_next = st + 1 < nstage;
     if (has_next) issue_loads(st + 1);
     if ((st + 1) * TB <= (int)nsteps) run_stage(st, std::false_type{});
     else run_stage(st, std::true_type{});
+    if constexpr (FIX) {
+      // bitwise equality of every state of the workgroup with the LOCAL
+      // pass's: from here on both passes compute the same values, and the
+      // LOCAL pass's y of the rest of the chunk is already in place
+      bool same = true;
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        same = same && __builtin_bit_cast(uint32_t, h[i]) == __builtin_bit_cast(uint32_t, hl[i]);
+      const bool wave_same = __builtin_amdgcn_ballot_w64(!same) == 0;
+      if ((tid & 63) == 0) vote[st & 1][tid >> 6] = wave_same ? 1 : 0;
+    }
     __syncthreads();
-    if (FULL) {
+    if constexpr (FIX) {
+      int all = 1;
+#pragma unroll
+      for (int w = 0; w < kBlockT / 64; ++w) all &= vote[st & 1][w];
+      stopped = all != 0 && has_next;                 // (vote[st & 1] is rewritten two stages on)
+    }
+    if (OUT) {
       drain_y(st);                                  // steps past the chunk are dropped
       if (!full_row && has_next) __syncthreads();   // element-wise drain reads others' pieces
     }
+    if (stopped) break;                             // uniform over the workgroup
     if (has_next) commit_loads();
     __syncthreads();
   }
 
-  if (!FULL) {                                      // the channel's sum over its 8 lanes
+  if (SUMM) {                                       // the channel's sum over its 8 lanes
     dsum += dpp<0x128>(dsum);
     dsum += dpp<0x4E>(dsum);
     dsum += dpp<0xB1>(dsum);
   }
   if (!active) return;
-  if (!FULL) {
+  if (SUMM) {
 #pragma unroll
     for (int i = 0; i < NS; ++i)
       if (n0 + i < N) a.chunk_state[((b * a.K + k) * N + n0 + i) * D + d] = h[i];
     if (g == 0) a.chunk_dsum[(b * a.K + k) * D + d] = dsum;
-  } else if (a.last_state != nullptr && k == last_chunk(sr.len, a.chunk_len)) {
+  }
+  // last_state: FULL, and LOCAL from its zero start (exact for chunk 0 without
+  // h0, and what FIXUP converges to when it stops early); FIXUP rewrites it
+  // when it ran to the chunk's end
+  if (MODE != TMODE_SUMMARY && !stopped && a.last_state != nullptr &&
+      k == last_chunk(sr.len, a.chunk_len)) {
 #pragma unroll
     for (int i = 0; i < NS; ++i)
       if (n0 + i < N) st_param(a.last_state, (b * D + d) * N + n0 + i, a.param_dtype, h[i]);
@@ -642,12 +695,29 @@ static hipError_t launch_tile_t(const FwdArgs& a, hipStream_t s) {
   const int64_t nbd = (a.D + CPW - 1) / CPW;
   const bool wide = wide_ok(a, (int)sizeof(T), NS);
   hipError_t e;
+  if (wide && a.K > 1) {
+    // Chunked, fwd_wide: LOCAL runs every chunk from h = 0 (chunk 0 from 0
+    // too), writing y, the chunk end states and dt sums; the carry turns the
+    // summaries into each chunk's true starting state; FIXUP reruns each
+    // chunk from that state next to a copy of the LOCAL recurrence and stops
+    // at the first stage end where the two agree bit for bit in every state
+    // of the workgroup: the rest of the chunk's y is then exactly what FIXUP
+    // would write.  Where the states forget their start quickly, FIXUP
+    // covers a few stages per chunk instead of the whole sequence again.
+    fwd_wide<T, NS, TMODE_LOCAL, HAS_Z><<<dim3((unsigned)(a.Bn * a.K * nbd)), dim3(kBlockT), 0,
+                                         s>>>(U, DL, Bm, Cm, Z, Y, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_fwd_carry(a, s)) != hipSuccess) return e;
+    const int64_t kf = a.h0 ? 0 : 1;
+    fwd_wide<T, NS, TMODE_FIXUP, HAS_Z><<<dim3((unsigned)(a.Bn * (a.K - kf) * nbd)),
+                                         dim3(kBlockT), 0, s>>>(U, DL, Bm, Cm, Z, Y, a);
+    return hipGetLastError();
+  }
   if (a.K > 1) {
-    const dim3 gs((unsigned)(a.Bn * (a.K - 1) * nbd));
-    if (wide)
-      fwd_wide<T, NS, TMODE_SUMMARY, false><<<gs, dim3(kBlockT), 0, s>>>(U, DL, Bm, Cm, Z, Y, a);
-    else
-      fwd_tile<T, NS, TMODE_SUMMARY, false><<<gs, dim3(kBlockT), 0, s>>>(U, DL, Bm, Cm, Z, Y, a);
+    // Chunked, fwd_tile: summaries from h = 0, the carry, then every chunk
+    // again from its carried-in state.
+    fwd_tile<T, NS, TMODE_SUMMARY, false><<<dim3((unsigned)(a.Bn * (a.K - 1) * nbd)),
+                                           dim3(kBlockT), 0, s>>>(U, DL, Bm, Cm, Z, Y, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_fwd_carry(a, s)) != hipSuccess) return e;
   }

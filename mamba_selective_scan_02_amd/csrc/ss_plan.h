@@ -80,17 +80,19 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
     if (d.chunk_len > 0) {
       lc = d.chunk_len < L ? d.chunk_len : L;
     } else {
-      // Waves that one chunk index provides.  The chunked schedule sweeps
-      // the data twice (the summaries cost about as many exps as the final
-      // pass) and adds two launches, so it pays only when the grid leaves
-      // most SIMDs (1024) idle: below 640 waves the time axis is cut into
-      // chunks until the grid reaches about 8 waves per SIMD, with chunks of
-      // at least 128 steps (a sequence of fewer than 256 steps does not earn
-      // the extra launches back: 1x128x32x16 takes 17.8 us in 3 launches).
-      // Measured (cold medians): 4x1024x1536x16 (768 waves) 66.6 us in one
-      // pass, 69.2 / 84.5 / 72.6 us with chunks of 256 / 512 / 128 steps;
-      // 1x262144x512x16 (64 waves) 1037 / 972 / 963 us with chunks of
-      // 4096 / 2048 / 1024 steps.
+      // Waves that one chunk index provides.  Chunking adds two launches and,
+      // where states forget their start slowly, a second sweep over the data
+      // (the fix-up pass of the 16-byte-row kernel runs until the carried-in
+      // states have decayed into the zero-start ones, and the general kernels
+      // always sweep twice), so it pays only when the grid leaves most SIMDs
+      // (1024) idle: below 640 waves the time axis is cut into chunks until
+      // the grid reaches about 8 waves per SIMD, with chunks of at least 128
+      // steps (a sequence of fewer than 256 steps does not earn the extra
+      // launches back: 1x128x32x16 takes 17.8 us in 3 launches).
+      // Measured (cold medians): 4x1024x1536x16 (768 waves, dt down to 1e-3:
+      // slow decay) 67.8 us in one pass, 75.9 / 79.4 / 92.5 us with chunks of
+      // 128 / 256 / 512 steps; 1x262144x512x16 (64 waves) 559 / 530 / 539 /
+      // 636 us with chunks of 1024 / 2048 / 4096 / 8192 steps.
       const int64_t cpw = 64 / p.G;
       const int64_t waves = Bn * ((D + cpw - 1) / cpw);
       const int64_t target = 8192;

@@ -119,6 +119,37 @@ def test_fwd_wide_path(io, N):
         assert torch.equal(y1, y2) and torch.equal(l1, l2), f"{io}/N{N}/chunk{chunk}"
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_fwd_chunk_fixup_exit(io):
+    """The chunked LDS-staged forward reruns each chunk from its carried state
+    only until every state of the workgroup equals, bit for bit, the state of
+    the pass that ran the chunk from zero.  Channels whose states forget fast
+    (A = -4 (n+1)) sit beside channels that never forget (A = 0) in different
+    waves and lanes of the same workgroups (32 channels each), so an exit vote
+    that missed one lane or one wave would leave the zero-start outputs in the
+    tails of their chunks.  With h0, chunk 0 is rerun as well."""
+    inp = random_inputs(1, 600, 64, 16, seed=470, io_dtype=io)
+    A = inp["A"].clone()
+    n = torch.arange(1, 17, dtype=A.dtype)
+    A[:] = -4.0 * n
+    for d in (5, 30, 33, 63):               # waves 0 and 3 of block 0, waves 0 and 3 of block 1
+        A[d] = 0.0
+    inp["A"] = A
+    h0 = _state(inp, 471)
+    d = to_dev(inp)
+    for chunk in (100, 256):
+        for with_h0 in (False, True):
+            say("fwd fixup", io, "chunk", chunk, "h0", with_h0)
+            y, ls = ss.fwd(*[d[k] for k in KEYS], return_last_state=True, chunk_len=chunk,
+                           h0=h0.to(DEV) if with_h0 else None)
+            torch.cuda.synchronize()
+            yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True,
+                                 h0=h0 if with_h0 else None)
+            tol = TOL[inp["u"].dtype]
+            assert rel_err(to_np(y), yr) <= tol, f"y chunk {chunk} h0 {with_h0}"
+            assert rel_err(to_np(ls), lsr) <= max(tol, TOL[inp["A"].dtype])
+
+
 def test_fwd_misaligned_16bit_rows():
     """bf16 B / C at an odd element offset take the element-wise load path."""
     inp = random_inputs(1, 40, 64, 16, seed=401, io_dtype="bf16")
