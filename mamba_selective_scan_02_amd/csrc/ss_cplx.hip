@@ -502,11 +502,16 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_summary(const BwdArgs 
   }
 }
 
-// Thread per (b, n, d), d fastest.  Forward chain over k = 0 .. K-2 (the
-// state part of fstate record k becomes the state entering chunk k+1,
-// h = P_k h + S_k with P_k = conj(E_k)) and reverse chain over k = K-1 .. 1
-// (bstate slot k becomes the adjoint handed to the end of chunk k-1):
-// c_{k-1} = conj(P_k) c_k + Sb_k = E_k c_k + Sb_k.  Records hold E_k - 1.
+// Thread per (chain, b, n, d), d fastest; the two chains are independent and
+// run in separate threads.  Forward chain over k = 0 .. K-2: the state part of
+// fstate record k becomes the state entering chunk k+1, h = P_k h + S_k with
+// P_k = conj(E_k).  Reverse chain over k = K-1 .. 1: bstate slot k becomes the
+// adjoint handed to the end of chunk k-1, c_{k-1} = conj(P_k) c_k + Sb_k =
+// E_k c_k + Sb_k.  Records hold E_k - 1.  The forward chain rewrites only the
+// state half of each record and the reverse chain reads only the E half, so
+// the two never touch the same words.  Each chain loads the records of KB
+// chunks before it runs through them (the chain alone would wait on every
+// load).
 __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_carry(const BwdArgs a) {
   const int64_t D = a.D, N = a.N, K = a.K;
   const int64_t nbd = (D + kChannelsPerBlock - 1) / kChannelsPerBlock;
@@ -514,42 +519,50 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_carry(const BwdArgs a)
   const int64_t db = blk % nbd;
   blk /= nbd;
   const int64_t n = blk % N;
-  const int64_t b = blk / N;
+  blk /= N;
+  const int64_t b = blk % a.Bn;
+  const bool reverse = blk / a.Bn != 0;
   const int64_t d = db * kChannelsPerBlock + threadIdx.x;
   if (d >= D) return;
   const int pd = a.param_dtype;
-  float hr = 0.0f, hi = 0.0f, cr = 0.0f, ci = 0.0f;
-  if (a.h0) {
-    hr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
-    hi = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
-  }
-  // The records of KB chunks are loaded before the two dependent chains run
-  // through them (the chains alone would wait on every load).  The reverse
-  // chain reads the E parts of records the forward chain has not reached or
-  // only rewrote the state part of, so the loads never see a stale value.
-  float4* fs = reinterpret_cast<float4*>(a.fstate) + ((b * K) * N + n) * D + d;  // + j N D
+  float4* fs = reinterpret_cast<float4*>(a.fstate) + ((b * K) * N + n) * D + d;  // + k N D
   float2* bs = reinterpret_cast<float2*>(a.bstate) + ((b * K) * N + n) * D + d;
   const int64_t st = N * D;
-  constexpr int KB = 8;
-  for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
-    float4 rf[KB], rr[KB];
-    float2 rb[KB];
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int64_t jf = (j0 + j < K - 1) ? j0 + j : K - 2;
-      const int64_t jr = K - 1 - jf;
-      rf[j] = fs[jf * st];
-      rr[j] = fs[jr * st];
-      rb[j] = bs[jr * st];
+  constexpr int KB = 16;
+  if (!reverse) {
+    float hr = 0.0f, hi = 0.0f;
+    if (a.h0) {
+      hr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
+      hi = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
     }
+    for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
+      float4 rf[KB];
 #pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      if (j0 + j < K - 1) {
-        const int64_t jf = j0 + j, jr = K - 1 - jf;
-        cstep(rf[j].z, -rf[j].w, rf[j].x, rf[j].y, hr, hi);   // h = P h + S, P - 1 = conj(E - 1)
-        fs[jf * st] = make_float4(hr, hi, rf[j].z, rf[j].w);
-        cstep(rr[j].z, rr[j].w, rb[j].x, rb[j].y, cr, ci);    // c = E c + Sb
-        bs[jr * st] = make_float2(cr, ci);
+      for (int j = 0; j < KB; ++j) rf[j] = fs[((j0 + j < K - 1) ? j0 + j : K - 2) * st];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (j0 + j < K - 1) {
+          cstep(rf[j].z, -rf[j].w, rf[j].x, rf[j].y, hr, hi);   // P - 1 = conj(E - 1)
+          *reinterpret_cast<float2*>(fs + (j0 + j) * st) = make_float2(hr, hi);
+        }
+      }
+    }
+  } else {
+    float cr = 0.0f, ci = 0.0f;
+    for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
+      float2 re[KB], rb[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const int64_t jr = K - 1 - ((j0 + j < K - 1) ? j0 + j : K - 2);
+        re[j] = *(reinterpret_cast<const float2*>(fs + jr * st) + 1);
+        rb[j] = bs[jr * st];
+      }
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (j0 + j < K - 1) {
+          cstep(re[j].x, re[j].y, rb[j].x, rb[j].y, cr, ci);    // c = E c + Sb
+          bs[(K - 1 - (j0 + j)) * st] = make_float2(cr, ci);
+        }
       }
     }
   }
@@ -627,37 +640,51 @@ __global__ __launch_bounds__(kChannelsPerBlock, 2) void cbwd_main(const BwdArgs 
     }
     __syncthreads();  // tile visible
 
-    for (int64_t n = 0; n < N; ++n) {
+    // the next state's A, incoming state and incoming adjoint are loaded one
+    // iteration ahead, so their latency hides behind this state's work
+    auto load_state = [&](int64_t n, float& ar, float& ai, float& hr, float& hi, float& cr,
+                          float& ci) {
       const int64_t ai_ = 2 * (d * N + n);
-      const float Ar = ld_param(a.A, ai_, pd), Ai = ld_param(a.A, ai_ + 1, pd);
-      float hinr = 0.0f, hini = 0.0f;
+      ar = ld_param(a.A, ai_, pd);
+      ai = ld_param(a.A, ai_ + 1, pd);
+      hr = 0.0f;
+      hi = 0.0f;
       if (k > 0) {
-        const float* fs = a.fstate + 4 * (((b * K + (k - 1)) * N + n) * D + d);
-        hinr = fs[0];
-        hini = fs[1];
+        const float2 f = *reinterpret_cast<const float2*>(
+            a.fstate + 4 * (((b * K + (k - 1)) * N + n) * D + d));
+        hr = f.x;
+        hi = f.y;
       } else if (a.h0) {
-        hinr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
-        hini = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
+        hr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
+        hi = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
       }
-      float dhr = 0.0f, dhi = 0.0f;
+      cr = 0.0f;
+      ci = 0.0f;
       if (k < K - 1) {
-        const float* bs = a.bstate + 2 * (((b * K + (k + 1)) * N + n) * D + d);
-        dhr = bs[0];
-        dhi = bs[1];
+        const float2 c = *reinterpret_cast<const float2*>(
+            a.bstate + 2 * (((b * K + (k + 1)) * N + n) * D + d));
+        cr = c.x;
+        ci = c.y;
       }
+    };
+    float nAr = 0.0f, nAi = 0.0f, nhr = 0.0f, nhi = 0.0f, ndr = 0.0f, ndi = 0.0f;
+    if (N > 0) load_state(0, nAr, nAi, nhr, nhi, ndr, ndi);
+    for (int64_t n = 0; n < N; ++n) {
+      const float Ar = nAr, Ai = nAi, hinr = nhr, hini = nhi;
+      float dhr = ndr, dhi = ndi;
+      if (n + 1 < N) load_state(n + 1, nAr, nAi, nhr, nhi, ndr, ndi);
       const float* bn = sB + 2 * n * CT;
       const float* cn = sC + 2 * n * CT;
       float hsr[CT], hsi[CT], ahr[CT], ahi[CT];   // states, a - 1
+      // the decays first (independent of one another), then the state chain
+#pragma unroll
+      for (int tt = 0; tt < CT; ++tt) cexpm1_dt(dl[tt], Ar, Ai, ahr[tt], ahi[tt]);
       float pr = hinr, pi = hini;
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt) {
-        float mr, mi;
-        cexpm1_dt(dl[tt], Ar, Ai, mr, mi);
-        cstep(mr, mi, xu[tt] * bn[2 * tt], xu[tt] * bn[2 * tt + 1], pr, pi);
+        cstep(ahr[tt], ahi[tt], xu[tt] * bn[2 * tt], xu[tt] * bn[2 * tt + 1], pr, pi);
         hsr[tt] = pr;
         hsi[tt] = pi;
-        ahr[tt] = mr;
-        ahi[tt] = mi;
         oo[tt] = __builtin_fmaf(cn[2 * tt], pr, __builtin_fmaf(-cn[2 * tt + 1], pi, oo[tt]));
       }
       // dB / dC of (step, this n) go straight to the LDS reduction rows;
@@ -705,7 +732,7 @@ __global__ __launch_bounds__(kChannelsPerBlock, 2) void cbwd_main(const BwdArgs 
       // dB / dC for this n: sums over the workgroup's channels in LDS
       __syncthreads();
       float s = 0.0f;
-#pragma unroll
+#pragma unroll 4   // (unrolled whole, its 32 loads in flight spilled registers)
       for (int i = 0; i < 32; ++i) s += red[rv * kCRedStride + rp * 32 + ((i + 8 * rp) & 31)];
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
@@ -817,7 +844,7 @@ hipError_t launch_cbwd_t(const BwdArgs& a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (N > 0) {
       const int64_t nc = (a.D + kChannelsPerBlock - 1) / kChannelsPerBlock;
-      cbwd_carry<<<dim3((unsigned)(Bn * N * nc)), dim3(kChannelsPerBlock), 0, s>>>(a);
+      cbwd_carry<<<dim3((unsigned)(2 * Bn * N * nc)), dim3(kChannelsPerBlock), 0, s>>>(a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
