@@ -132,51 +132,48 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_summary(const BwdArgs a
 
 // ------------------------------------------------------------------ carry
 
-// Thread per (b, n, d), d fastest.  Forward chain over k = 0 .. K-2 (fstate
-// slot k becomes the state entering chunk k+1) and reverse chain over
-// k = K-1 .. 1 (bstate slot k becomes the adjoint at the end of chunk k-1),
-// interleaved so both chains' loads are in flight together.
+// Thread per (chain, b, n, d), d fastest: the forward chain over k = 0 .. K-2
+// (fstate slot k becomes the state entering chunk k+1) and the reverse chain
+// over k = K-1 .. 1 (bstate slot k becomes the adjoint at the end of chunk
+// k-1) run in separate threads.  Each loads the summaries and dt sums of KB
+// chunks, computes their decays (independent of the chain), then runs the
+// chain through them.
 __global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) {
   const int64_t nbd = a.nwgd;
   int64_t blk = blockIdx.x;
   const int64_t db = blk % nbd;
   blk /= nbd;
   const int64_t n = blk % a.N;
-  const int64_t b = blk / a.N;
+  blk /= a.N;
+  const int64_t b = blk % a.Bn;
+  const bool reverse = blk / a.Bn != 0;
   const int64_t d = db * kChannelsPerBlock + threadIdx.x;
   if (d >= a.D) return;
   const int64_t D = a.D, N = a.N, K = a.K;
   const float Av = ld_param(a.A, d * N + n, a.param_dtype);
-  float* fs = a.fstate + (b * K * N + n) * D + d;   // + k * N * D
-  float* bs = a.bstate + (b * K * N + n) * D + d;
-  const float* ds = a.dsum + b * K * D + d;         // + k * D
-  float hc = a.h0 ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0f;  // h_in(0)
-  float cc = 0.0f;
-  constexpr int KB = 8;
+  // the forward chain walks slots 0, 1, .. of fstate, the reverse chain slots
+  // K-1, K-2, .. of bstate: step j touches slot kj = j or K-1-j
+  float* st = (reverse ? a.bstate : a.fstate) + (b * K * N + n) * D + d;   // + k * N * D
+  const float* ds = a.dsum + b * K * D + d;                                // + k * D
+  float c = (!reverse && a.h0) ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0f;
+  constexpr int KB = 16;
   for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
-    float sf[KB], df[KB], sb[KB], dbk[KB];
+    float sv[KB], dv[KB];
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const int64_t jj = (j0 + j < K - 1) ? j0 + j : K - 2;
-      sf[j] = fs[jj * N * D];
-      df[j] = ds[jj * D];
-      sb[j] = bs[(K - 1 - jj) * N * D];
-      dbk[j] = ds[(K - 1 - jj) * D];
+      const int64_t kj = reverse ? K - 1 - jj : jj;
+      sv[j] = st[kj * N * D];
+      dv[j] = ds[kj * D];
     }
-    // the batch's decays first (independent of the chains), then the chains
-    float pf[KB], pb[KB];
+    float pv[KB];
 #pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      pf[j] = chunk_decay(Av, df[j]);
-      pb[j] = chunk_decay(Av, dbk[j]);
-    }
+    for (int j = 0; j < KB; ++j) pv[j] = chunk_decay(Av, dv[j]);
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (j0 + j < K - 1) {
-        hc = __builtin_fmaf(pf[j], hc, sf[j]);
-        fs[(j0 + j) * N * D] = hc;
-        cc = __builtin_fmaf(pb[j], cc, sb[j]);
-        bs[(K - 1 - (j0 + j)) * N * D] = cc;
+        c = __builtin_fmaf(pv[j], c, sv[j]);
+        st[(reverse ? K - 1 - (j0 + j) : j0 + j) * N * D] = c;
       }
     }
   }
@@ -348,7 +345,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
 // --------------------------------------------------------------- finalize
 
 // dB[b,t,n], dC[b,t,n] = sums over the channel blocks, in block order (loads
-// are issued in batches of 8, the adds stay in index order).
+// are issued in batches of 16, the adds stay in index order).
 template <typename Tio>
 __device__ __forceinline__ void finalize_bc(const BwdArgs& a, int64_t i) {  // i = row * N + n
   const int64_t N = a.N;
@@ -356,7 +353,7 @@ __device__ __forceinline__ void finalize_bc(const BwdArgs& a, int64_t i) {  // i
   const int64_t bt = i / N, n = i % N;
   const float* p = a.part_bc + bt * a.nwgd * 2 * N + n;
   float sb = 0.0f, sc = 0.0f;
-  constexpr int U = 8;
+  constexpr int U = 16;
   int64_t w = 0;
   for (; w + U <= a.nwgd; w += U) {
     float vb[U], vc[U];
@@ -379,7 +376,7 @@ __device__ __forceinline__ void finalize_bc(const BwdArgs& a, int64_t i) {  // i
 // Fixed-order sum of `count` partials p[0], p[stride], ... (loads batched).
 __device__ __forceinline__ float ordered_sum(const float* p, int64_t count, int64_t stride) {
   float s = 0.0f;
-  constexpr int U = 8;
+  constexpr int U = 16;
   int64_t j = 0;
   for (; j + U <= count; j += U) {
     float v[U];
@@ -454,7 +451,7 @@ hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t s) {
   const int64_t nbd = (a.D + kChannelsPerBlock - 1) / kChannelsPerBlock;
   BwdArgs c = a;
   c.nwgd = nbd;  // the carry's own channel blocking (256 per workgroup)
-  bwd_carry<<<dim3((unsigned)(a.Bn * a.N * nbd)), dim3(kChannelsPerBlock), 0, s>>>(c);
+  bwd_carry<<<dim3((unsigned)(2 * a.Bn * a.N * nbd)), dim3(kChannelsPerBlock), 0, s>>>(c);
   return hipGetLastError();
 }
 
