@@ -452,22 +452,24 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
       pddl[s] = vddl;
       // dB / dC of (step s, these states) for the workgroup reduction: the
       // channel pair (2m, 2m + 1), neighbouring lanes with the same g, is
-      // summed first (tail lanes contribute exact zeros)
+      // summed first (tail lanes contribute exact zeros).  Both lanes of the
+      // pair hold the same sum (the two addends swapped), so both store it to
+      // the pair's slot: no branch, and the DPP move fuses into the add.
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
+        // (rounded products first: an fma would round the two lanes' sums differently)
+        __asm__ volatile("" : "+v"(vb[i]), "+v"(vc[i]));
         vb[i] += dpp<0xB1>(vb[i]);       // quad_perm [1,0,3,2]: the pair's other channel
         vc[i] += dpp<0xB1>(vc[i]);
       }
-      if ((cl & 1) == 0) {
-        if (NS == 2) {
-          *reinterpret_cast<float2*>(&red[0][cl >> 1][s * NP + n0]) = make_float2(vb[0], vb[NS - 1]);
-          *reinterpret_cast<float2*>(&red[1][cl >> 1][s * NP + n0]) = make_float2(vc[0], vc[NS - 1]);
-        } else {
+      if (NS == 2) {
+        *reinterpret_cast<float2*>(&red[0][cl >> 1][s * NP + n0]) = make_float2(vb[0], vb[NS - 1]);
+        *reinterpret_cast<float2*>(&red[1][cl >> 1][s * NP + n0]) = make_float2(vc[0], vc[NS - 1]);
+      } else {
 #pragma unroll
-          for (int i = 0; i < NS; ++i) {
-            red[0][cl >> 1][s * NP + n0 + i] = vb[i];
-            red[1][cl >> 1][s * NP + n0 + i] = vc[i];
-          }
+        for (int i = 0; i < NS; ++i) {
+          red[0][cl >> 1][s * NP + n0 + i] = vb[i];
+          red[1][cl >> 1][s * NP + n0 + i] = vc[i];
         }
       }
     }
