@@ -7,13 +7,13 @@
 // per-channel reverse sweep and fixed-order partial reductions as in stage B3
 // of the mamba-rs page "mamba_ssm/gpu/backward.rs").  Mapping as in the
 // forward tile kernel: 8 lanes own a channel (8 apart in the wave), lane g
-// holds states n = g*NS .. g*NS+NS-1 (NS = 1 or 2); a wave is 8 channels, a
+// holds states n = g*NS .. g*NS+NS-1 (NS = 1, 2 or 4); a wave is 8 channels, a
 // 256-lane workgroup 32; per 8-step tile, lane g prepares the per-step
 // scalars of step t0 + 8j + g and hands them to the channel's lanes through
 // LDS; sums over a channel's states are reduce-scatters over its 8 lanes
 // (lane swaps and DPP).
 //
-// Time is cut into chunks of at most 64 steps (8 tiles):
+// Time is cut into chunks of at most 64 steps (8 tiles; 32 steps with NS = 4):
 //   bwd_tile_sum   per chunk, from zero: forward end state S, reverse summary
 //                  Sb = sum_s (prod_{r<=s} a_r) g_s C_s (built per 8-step tile
 //                  and combined with the tiles' decays), and sum of dt;
@@ -38,9 +38,12 @@ namespace {
 constexpr int kBT = 256;              // threads per workgroup
 constexpr int BGL = 8;                // lanes per channel
 constexpr int BCPW = kBT / BGL;       // channels per workgroup (32)
-constexpr int BTC = 64;               // max steps per chunk
-constexpr int BNT = BTC / BGL;        // tiles per chunk (8)
-constexpr int BTS = 68;               // staged B/C row stride (floats)
+// Steps per chunk (at most): 64 (8 tiles) with NS <= 2 states per lane; 32
+// with NS = 4, whose tile-start states and dB/dC rows take twice the LDS per
+// step (two workgroups per CU either way).
+template <int NS> constexpr int btc() { return NS <= 2 ? 64 : 32; }
+// Resident waves per SIMD the main kernel's registers are held to.
+template <int NS> constexpr int bmain_waves() { return NS <= 2 ? 3 : 2; }
 constexpr int BXS = 9;                // exchange row stride (float4) per channel
 
 }  // namespace
@@ -75,7 +78,7 @@ __device__ __forceinline__ BTilePos btile_pos(const BwdArgs& a) {
 
 // Stage the chunk's B and C rows as f32, [n][t], rows padded; states n >= N
 // and steps past the chunk are zero.
-template <typename T, int NP>
+template <typename T, int NP, int BTC, int BTS>
 __device__ __forceinline__ void bstage(float (*sB)[BTS], float (*sC)[BTS], const T* B, const T* C,
                                        int64_t row0, int64_t nsteps,
                                        int64_t N, int64_t ldb, int64_t ldc) {
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
                                                     const T* __restrict__ dy_in, const BwdArgs a) {
   constexpr int NP = NS * BGL;
   constexpr int ES = sizeof(T);
+  constexpr int BTC = btc<NS>(), BTS = BTC + 4;
   __shared__ __attribute__((aligned(16))) float sB[NP][BTS];
   __shared__ __attribute__((aligned(16))) float sC[NP][BTS];
   __shared__ __attribute__((aligned(16))) float4 xch[BCPW][BXS];
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
   const int64_t D = a.D, N = a.N, b = P.b, d = P.d;
   const int64_t nsteps = P.t1 - P.t0;
 
-  bstage<T, NP>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N, a.ldb, a.ldc);
+  bstage<T, NP, BTC, BTS>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N, a.ldb, a.ldc);
 
   // Sb is built two-level: per tile from its own start (E, sbl) and then
   // Sb += (decay of the chunk's earlier tiles) * sbl, the decay of a tile
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
 // -------------------------------------------------------------------- main
 
 template <typename T, int NS, bool HAS_Z>
-__global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_in,
+__global__ __launch_bounds__(kBT, bmain_waves<NS>()) void bwd_tile_main(const T* __restrict__ u_in,
                                                      const T* __restrict__ delta_in,
                                                      const T* __restrict__ B_in,
                                                      const T* __restrict__ C_in,
@@ -237,6 +241,7 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
   constexpr int NP = NS * BGL;
   constexpr int ES = sizeof(T);
   constexpr int RP = BGL * NP + 4;      // reduction row (one channel: 8 steps x NP) + pad
+  constexpr int BTC = btc<NS>(), BNT = BTC / BGL, BTS = BTC + 4;
   __shared__ __attribute__((aligned(16))) float sB[NP][BTS];
   __shared__ __attribute__((aligned(16))) float sC[NP][BTS];
   __shared__ __attribute__((aligned(16))) float4 xch[BCPW][BXS];
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
   const int64_t D = a.D, N = a.N, K = a.K, b = P.b, d = P.d, k = P.k;
   const int64_t nsteps = P.t1 - P.t0;
 
-  bstage<T, NP>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N, a.ldb, a.ldc);
+  bstage<T, NP, BTC, BTS>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N, a.ldb, a.ldc);
 
   float A2[NS], An[NS], h[NS], dh[NS], dA_acc[NS];
 #pragma unroll
@@ -462,9 +467,14 @@ __global__ __launch_bounds__(kBT, 3) void bwd_tile_main(const T* __restrict__ u_
         vb[i] += dpp<0xB1>(vb[i]);       // quad_perm [1,0,3,2]: the pair's other channel
         vc[i] += dpp<0xB1>(vc[i]);
       }
-      if (NS == 2) {
-        *reinterpret_cast<float2*>(&red[0][cl >> 1][s * NP + n0]) = make_float2(vb[0], vb[NS - 1]);
-        *reinterpret_cast<float2*>(&red[1][cl >> 1][s * NP + n0]) = make_float2(vc[0], vc[NS - 1]);
+      if constexpr (NS == 4) {
+        *reinterpret_cast<float4*>(&red[0][cl >> 1][s * NP + n0]) =
+            make_float4(vb[0], vb[1], vb[2], vb[3]);
+        *reinterpret_cast<float4*>(&red[1][cl >> 1][s * NP + n0]) =
+            make_float4(vc[0], vc[1], vc[2], vc[3]);
+      } else if constexpr (NS == 2) {
+        *reinterpret_cast<float2*>(&red[0][cl >> 1][s * NP + n0]) = make_float2(vb[0], vb[1]);
+        *reinterpret_cast<float2*>(&red[1][cl >> 1][s * NP + n0]) = make_float2(vc[0], vc[1]);
       } else {
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
@@ -553,6 +563,7 @@ static hipError_t launch_btile_ty(const BwdArgs& a, int ns, hipStream_t s) {
   const bool z = a.z != nullptr;
   if (ns == 1) return z ? launch_btile_t<T, 1, true>(a, s) : launch_btile_t<T, 1, false>(a, s);
   if (ns == 2) return z ? launch_btile_t<T, 2, true>(a, s) : launch_btile_t<T, 2, false>(a, s);
+  if (ns == 4) return z ? launch_btile_t<T, 4, true>(a, s) : launch_btile_t<T, 4, false>(a, s);
   return hipErrorInvalidValue;
 }
 

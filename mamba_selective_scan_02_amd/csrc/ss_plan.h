@@ -16,8 +16,11 @@ namespace ss {
 // 16 steps took 336 (1 wave): 2x2048x2048 backward, N = 32 982 -> 894 us,
 // N = 64 1794 -> 1584 us (twice the chunk records, but twice the waves).
 constexpr int kBwdTile = 8;
-// Backward chunk length of the tile path (N <= 16): 8 tiles of 8 steps.
+// Backward chunk length of the tile path: 8 tiles of 8 steps (N <= 16), 4
+// tiles with 4 states per lane (N <= 32: the tile-start states and dB/dC rows
+// take twice the LDS per step).
 constexpr int kBwdTileChunk = 64;
+constexpr int kBwdTileChunk4 = 32;
 // Chunks of one channel block handled by one backward workgroup (their dA /
 // dD / ddelta_bias partials are summed in registers / in place).
 constexpr int kBwdChunksPerGroup = 4;
@@ -37,7 +40,7 @@ struct Plan {
          off_part_dD = 0, off_part_db = 0;
   size_t ws_bytes = 0;
   int64_t KG = 0, nwgd = 0;   // backward: chunk groups, channel blocks
-  bool bwd_tile = false;      // backward: 8-lanes-per-channel tile kernels (N <= 16)
+  bool bwd_tile = false;      // backward: 8-lanes-per-channel tile kernels (N <= 32)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -123,12 +126,12 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
     p.n_launches = p.K > 1 ? (N > 0 ? 3 : 2) : 1;
     return p;
   }
-  // backward.  N <= 16: tile kernels, chunks of up to 64 steps, 32 channels
-  // per workgroup, per-chunk partials.  Otherwise the general kernels: chunks
-  // of up to kBwdTile steps (one register tile), 256 channels per workgroup,
-  // partials per group of 4 chunks.
-  p.bwd_tile = N <= 16;
-  int64_t lc = p.bwd_tile ? kBwdTileChunk : kBwdTile;
+  // backward.  N <= 32: tile kernels, chunks of up to 64 steps (32 above
+  // N = 16), 32 channels per workgroup, per-chunk partials.  Otherwise the
+  // general kernels: chunks of up to kBwdTile steps (one register tile), 256
+  // channels per workgroup, partials per group of 4 chunks.
+  p.bwd_tile = N <= 32;
+  int64_t lc = !p.bwd_tile ? kBwdTile : N <= 16 ? kBwdTileChunk : kBwdTileChunk4;
   if (d.chunk_len > 0 && d.chunk_len < lc) lc = d.chunk_len;
   if (lc > L) lc = L;
   const int64_t lc_cap = (int64_t)0x7fffffff / ((D > 0 ? D : 1) * 4) - GL_MAX_TILE;
@@ -136,7 +139,7 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
   p.chunk_len = lc;
   p.K = (L + lc - 1) / lc;
   if (p.bwd_tile) {
-    p.NS = N <= 8 ? 1 : 2;
+    p.NS = N <= 8 ? 1 : N <= 16 ? 2 : 4;
     p.G = 8;
     p.KG = p.K;
     p.nwgd = (D + 31) / 32;

@@ -285,12 +285,17 @@ def test_plan_is_a_function_of_shape():
                        256: (64, 4)}.items():
         p = ss.plan(_desc(N=n))
         assert (p.states_per_lane, p.lanes_per_channel) == (ns, g), n
-    # backward: N <= 16 uses the tile kernels with chunks of 64 steps, larger N
+    # backward: N <= 16 uses the tile kernels with chunks of 64 steps, N <= 32
+    # the tile kernels with 4 states per lane and chunks of 32 steps, larger N
     # the general kernels with chunks of 8 steps
     p = ss.plan(_desc(B=2, L=2048, D=2048, N=16), True)
     assert (p.chunk_len, p.n_chunks, p.n_launches, p.states_per_lane,
             p.lanes_per_channel) == (64, 32, 4, 2, 8)
-    p = ss.plan(_desc(B=2, L=2048, D=2048, N=17), True)
+    for n in (17, 32):
+        p = ss.plan(_desc(B=2, L=2048, D=2048, N=n), True)
+        assert (p.chunk_len, p.n_chunks, p.n_launches, p.states_per_lane,
+                p.lanes_per_channel) == (32, 64, 4, 4, 8), n
+    p = ss.plan(_desc(B=2, L=2048, D=2048, N=33), True)
     assert (p.chunk_len, p.n_chunks, p.n_launches) == (8, 256, 4)
 
 

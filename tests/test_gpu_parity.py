@@ -293,7 +293,9 @@ def _check_bwd(inp, sp=True, chunk_len=0, label=""):
 
 BWD_SHAPES = [(1, 1, 1, 1), (1, 5, 3, 4), (2, 16, 64, 16), (2, 17, 65, 16), (1, 100, 300, 16),
               (3, 63, 31, 8), (1, 47, 20, 17), (1, 33, 10, 64), (1, 20, 9, 130), (1, 18, 5, 256),
-              (2, 300, 257, 16), (2, 2048, 512, 16)]
+              (2, 300, 257, 16), (2, 2048, 512, 16),
+              # 4 states per lane (N = 17 .. 32): 32-step chunks, ragged tails, padded states
+              (2, 300, 72, 32), (1, 129, 40, 24), (2, 2048, 512, 32)]
 
 
 @pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
