@@ -110,6 +110,12 @@ __device__ __forceinline__ void exp2_run(float (&e)[16]) {
   exp2_run(lo);
   exp2_run(hi);
 }
+__device__ __forceinline__ void exp2_run(float (&e)[32]) {
+  float (&lo)[16] = *reinterpret_cast<float(*)[16]>(&e[0]);
+  float (&hi)[16] = *reinterpret_cast<float(*)[16]>(&e[16]);
+  exp2_run(lo);
+  exp2_run(hi);
+}
 
 // log(1 + w) for 0 <= w <= 1, accurate in relative terms also for tiny w.
 // With s = 1 + w rounded, c = w - (s - 1) is the rounding error of s, computed

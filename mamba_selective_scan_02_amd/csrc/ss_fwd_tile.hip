@@ -67,7 +67,7 @@ enum { TMODE_FULL = 0, TMODE_SUMMARY = 1, TMODE_LOCAL = 2, TMODE_FIXUP = 3 };
 // The fix-up pass carries a second set of states and is short: 4 waves.
 template <int NS, int MODE = TMODE_FULL>
 constexpr int tile_waves_per_simd() {
-  return NS <= 2 ? (MODE == TMODE_FIXUP ? 4 : 5) : 3;
+  return NS <= 2 ? (MODE == TMODE_FIXUP ? 4 : 5) : NS <= 4 ? 3 : 2;
 }
 
 // Lane map of the forward tile kernels: a channel's 8 lanes lie in one row of 16 lanes, so
@@ -740,6 +740,7 @@ static hipError_t launch_tile_ty(const FwdArgs& a, int ns, hipStream_t s) {
     case 1: return launch_tile_ns<T, 1>(a, s);
     case 2: return launch_tile_ns<T, 2>(a, s);
     case 4: return launch_tile_ns<T, 4>(a, s);
+    case 8: return launch_tile_ns<T, 8>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -45,14 +45,14 @@ struct Plan {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Forward mapping by state count: N <= 32 uses 8 lanes per channel with NS
-// states each (the tile kernel); larger N one lane per channel with 64 states
-// (G = 2 or 4 lanes above 64 states).
+// Forward mapping by state count: N <= 64 uses 8 lanes per channel with NS
+// states each (the tile kernels; NS = 8 runs 2 waves per SIMD); larger N one
+// lane per channel with 64 states (G = 2 or 4 lanes above 64 states).
 inline void pick_bucket(int64_t N, int* NS, int* G) {
   if (N <= 8) { *NS = 1; *G = 8; }
   else if (N <= 16) { *NS = 2; *G = 8; }
   else if (N <= 32) { *NS = 4; *G = 8; }
-  else if (N <= 64) { *NS = 64; *G = 1; }
+  else if (N <= 64) { *NS = 8; *G = 8; }
   else if (N <= 128) { *NS = 64; *G = 2; }
   else { *NS = 64; *G = 4; }
 }

@@ -281,7 +281,7 @@ def test_plan_is_a_function_of_shape():
     assert (p.chunk_len, p.n_chunks) == (7, 15)
     # N buckets
     for n, (ns, g) in {0: (1, 8), 1: (1, 8), 5: (1, 8), 9: (2, 8), 16: (2, 8), 17: (4, 8),
-                       32: (4, 8), 33: (64, 1), 64: (64, 1), 65: (64, 2), 200: (64, 4),
+                       32: (4, 8), 33: (8, 8), 64: (8, 8), 65: (64, 2), 200: (64, 4),
                        256: (64, 4)}.items():
         p = ss.plan(_desc(N=n))
         assert (p.states_per_lane, p.lanes_per_channel) == (ns, g), n

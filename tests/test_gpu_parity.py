@@ -55,6 +55,8 @@ SHAPES = [  # (B, L, D, N)
     (1, 1, 1, 1), (1, 2, 31, 4), (3, 63, 64, 16), (2, 64, 65, 16), (1, 65, 300, 16),
     (2, 1000, 33, 16), (1, 300, 257, 8), (2, 129, 70, 17), (1, 77, 40, 32), (1, 50, 20, 64),
     (1, 40, 20, 65), (1, 33, 10, 128), (1, 21, 9, 200), (1, 19, 7, 256), (2, 17, 5, 3),
+    # 8 states per lane (N = 33 .. 64), chunked: several stages, ragged tails, padded states
+    (2, 600, 72, 64), (1, 300, 40, 48),
 ]
 
 
@@ -100,9 +102,9 @@ def _offset_copy(x, elems=1):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("N", [8, 16, 32])
+@pytest.mark.parametrize("N", [8, 16, 32, 64])
 def test_fwd_wide_path(io, N):
-    """Rows of a multiple of 16 bytes with N = 8, 16, 32 take the LDS-staged
+    """Rows of a multiple of 16 bytes with N = 8, 16, 32, 64 take the LDS-staged
     kernel (D = 72: two full channel blocks and a partial one; L = 150: partial
     stages).  It must match the oracle, and match bit for bit the element-wise
     kernel that misaligned inputs take, since both do the same arithmetic."""
