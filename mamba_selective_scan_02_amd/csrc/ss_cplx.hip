@@ -38,7 +38,9 @@ namespace {
 
 constexpr int kCB = 256;               // threads per workgroup
 constexpr int CT = kCplxBwdTile;       // backward steps per chunk (max)
-constexpr int kCRedStride = 257;       // LDS row stride of the dB/dC reduction
+// LDS row stride of the dB/dC reduction: with the read rotation below, each
+// read of a wave hits distinct banks whether the LDS has 32 or 64 banks
+constexpr int kCRedStride = 264;
 
 // a - 1 = exp(dt * (Ar + i Ai)) - 1 = (mr, mi).  The recurrences use a - 1
 // rather than a (h + ((a - 1) h + x)): with small dt a is within a few ulps of
@@ -737,7 +739,7 @@ __global__ __launch_bounds__(kChannelsPerBlock, 2) void cbwd_main(const BwdArgs 
       __syncthreads();
       float s = 0.0f;
 #pragma unroll 4   // (unrolled whole, its 32 loads in flight spilled registers)
-      for (int i = 0; i < 32; ++i) s += red[rv * kCRedStride + rp * 32 + ((i + 8 * rp) & 31)];
+      for (int i = 0; i < 32; ++i) s += red[rv * kCRedStride + rp * 32 + ((i + rp) & 31)];
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
       s += __shfl_xor(s, 4, 64);
