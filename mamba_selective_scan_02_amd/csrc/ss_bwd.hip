@@ -155,7 +155,8 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) 
   // K-1, K-2, .. of bstate: step j touches slot kj = j or K-1-j
   float* st = (reverse ? a.bstate : a.fstate) + (b * K * N + n) * D + d;   // + k * N * D
   const float* ds = a.dsum + b * K * D + d;                                // + k * D
-  float c = (!reverse && a.h0) ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0f;
+  // the chain runs in double; each carried value is rounded to float once
+  double c = (!reverse && a.h0) ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0;
   constexpr int KB = 16;
   for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
     float sv[KB], dv[KB];
@@ -166,14 +167,14 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) 
       sv[j] = st[kj * N * D];
       dv[j] = ds[kj * D];
     }
-    float pv[KB];
+    double pv[KB];
 #pragma unroll
     for (int j = 0; j < KB; ++j) pv[j] = chunk_decay(Av, dv[j]);
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (j0 + j < K - 1) {
-        c = __builtin_fmaf(pv[j], c, sv[j]);
-        st[(reverse ? K - 1 - (j0 + j) : j0 + j) * N * D] = c;
+        c = __builtin_fma(pv[j], c, static_cast<double>(sv[j]));
+        st[(reverse ? K - 1 - (j0 + j) : j0 + j) * N * D] = static_cast<float>(c);
       }
     }
   }

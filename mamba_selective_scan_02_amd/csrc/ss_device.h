@@ -150,7 +150,7 @@ __device__ __forceinline__ float softplus(float x) {
 // r with |r| <= ln2 / 2 (Cody and Waite's reduction, ln 2 in two parts whose
 // first part times k is exact), e^r by its Taylor series through r^10
 // (truncation below 3e-13 relative), then 2^k by ldexp; far below the one
-// float rounding that follows.  The carries run it once per chunk and state
+// float rounding of the carried state that follows.  The carries run it once per chunk and state
 // on a sequential chain, where a library exp's latency showed (long sequence:
 // 27.8 us for the forward carry).
 __device__ __forceinline__ double exp_dbl(double x) {
@@ -176,8 +176,11 @@ __device__ __forceinline__ double exp_dbl(double x) {
   p = __builtin_fma(p, r, 1.0);
   return __builtin_ldexp(p, static_cast<int>(kd));
 }
-__device__ __forceinline__ float chunk_decay(float A, float dsum) {
-  return static_cast<float>(exp_dbl(static_cast<double>(A) * static_cast<double>(dsum)));
+// A chunk's decay exp(A * sum of its dt), in double: the carries fold their
+// chains in double and round each carried state to float once, so that a
+// state passed through many chunks does not collect a float rounding per chunk.
+__device__ __forceinline__ double chunk_decay(float A, float dsum) {
+  return exp_dbl(static_cast<double>(A) * static_cast<double>(dsum));
 }
 
 // sigmoid(x) = 1 / (1 + e^{-x}); exp overflow gives rcp(inf) = 0.

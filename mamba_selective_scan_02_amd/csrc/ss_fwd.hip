@@ -19,7 +19,8 @@
 //   1. fwd_scan<SUMMARY>: every chunk but the last runs from h = 0 and writes
 //      its end state S_k[n] and sum_k = sum of dt over the chunk;
 //   2. fwd_carry: per (b, d, n), h_in(k+1) = exp(A * sum_k) * h_in(k) + S_k,
-//      the decay in double precision (chunk_decay),
+//      the decay and the chain in double precision (chunk_decay), each
+//      carried state rounded to float once,
 //      the composition (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) of the chunk
 //      summaries, folded over k (the product of a chunk's decays is
 //      exp(A * sum of its dt) in closed form);
@@ -47,7 +48,8 @@ __global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
   const float Av = ld_param(a.A, d * N + n, a.param_dtype);
   float* __restrict__ st = a.chunk_state + (b * K * N + n) * D + d;  // + k * N * D
   const float* __restrict__ ds = a.chunk_dsum + b * K * D + d;       // + k * D
-  float hc = a.h0 ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0f;  // h_in(0)
+  // the chain runs in double; each carried state is rounded to float once
+  double hc = a.h0 ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0;  // h_in(0)
   constexpr int KB = 16;
   for (int64_t k0 = 0; k0 < K - 1; k0 += KB) {
     float sv[KB], dv[KB];
@@ -58,14 +60,14 @@ __global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
       dv[j] = ds[kk * D];
     }
     // the batch's decays first (independent of the chain), then the chain
-    float pv[KB];
+    double pv[KB];
 #pragma unroll
     for (int j = 0; j < KB; ++j) pv[j] = chunk_decay(Av, dv[j]);
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (k0 + j < K - 1) {
-        hc = __builtin_fmaf(pv[j], hc, sv[j]);
-        st[(k0 + j) * N * D] = hc;
+        hc = __builtin_fma(pv[j], hc, static_cast<double>(sv[j]));
+        st[(k0 + j) * N * D] = static_cast<float>(hc);
       }
     }
   }

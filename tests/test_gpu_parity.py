@@ -773,12 +773,10 @@ def test_bwd_long_memory_short_chunks(chunk):
     very short chunks: every chunk boundary passes the states through the
     carry's closed-form decay, so errors there add up along the sequence (dz,
     an ill-conditioned readout here, is where it shows first: the sequential
-    f32 loop itself reaches 2.4e-5 on it).  Every gradient and last_state stay
-    within the f32 bound at every chunk length.  y is held to it from 2-step
-    chunks on: its readout cancels here too, and the sequential f32 loop is
-    1.75e-5 from the f64 result on these inputs; with 1-step chunks every
-    state passes through the carry's own float fma, as in that loop, and y
-    reaches ~1.4e-5 (measured on the box)."""
+    f32 loop itself reaches 2.4e-5 on it, and 1.75e-5 on y).  The carries
+    fold their chains in double and round each carried state once, so every
+    output stays within the f32 bound at every chunk length, 1-step chunks
+    (every state through the carry) included."""
     inp = random_inputs(1, 2048, 64, 8, seed=2800 + 2048 + 8, backward=True)
     h0 = _state(inp, 2801 + 64)
     d = to_dev(inp)
@@ -791,8 +789,7 @@ def test_bwd_long_memory_short_chunks(chunk):
     errs = {k: rel_err(to_np(g[k]), r[k]) for k in GRADS + ("dh0",) if r[k] is not None}
     yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
     errs["last_state"] = rel_err(to_np(ls), lsr)
-    if chunk > 1:
-        errs["y"] = rel_err(to_np(y), yr)
+    errs["y"] = rel_err(to_np(y), yr)
     say("  ", {k: f"{v:.2e}" for k, v in errs.items()})
     bad = {k: v for k, v in errs.items() if not v <= 1e-5}
     assert not bad, bad
