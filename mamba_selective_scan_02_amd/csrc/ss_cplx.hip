@@ -22,6 +22,8 @@
 // product of its steps' decays rather than exp(A * sum dt): for complex A the
 // closed form turns the rounding of sum dt into a phase error |Im A| times as
 // large, which over long chunks exceeds the sequential scan's own rounding.
+// The carry over chunks (forward and both backward chains) runs in double
+// and rounds each carried value to float once.
 // Backward: the same stages as the real general backward (summary, carry,
 // main, fixed-order finalizes) with one lane per channel, one state at a time,
 // 8-step chunks in registers, B / C of a chunk in LDS, and dB / dC summed over
@@ -334,7 +336,8 @@ __global__ __launch_bounds__(kCB) void cfwd_carry(const FwdArgs a) {
   const int64_t d = db * kCB + threadIdx.x;
   if (d >= D) return;
   const int pd = a.param_dtype;
-  float hr = 0.0f, hi = 0.0f;
+  // the chain runs in double; each carried state is rounded to float once
+  double hr = 0.0, hi = 0.0;
   if (a.h0) {
     hr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
     hi = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
@@ -342,9 +345,9 @@ __global__ __launch_bounds__(kCB) void cfwd_carry(const FwdArgs a) {
   for (int64_t k = 0; k < K - 1; ++k) {
     float* st = a.chunk_state + 4 * (((b * K + k) * N + n) * D + d);
     const float4 r = *reinterpret_cast<const float4*>(st);   // S, P - 1
-    cstep(r.z, r.w, r.x, r.y, hr, hi);
-    st[0] = hr;
-    st[1] = hi;
+    cstep_d(r.z, r.w, r.x, r.y, hr, hi);
+    st[0] = (float)hr;
+    st[1] = (float)hi;
   }
 }
 
@@ -535,8 +538,9 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_carry(const BwdArgs a)
   float2* bs = reinterpret_cast<float2*>(a.bstate) + ((b * K) * N + n) * D + d;
   const int64_t st = N * D;
   constexpr int KB = 16;
+  // the chains run in double; each carried value is rounded to float once
   if (!reverse) {
-    float hr = 0.0f, hi = 0.0f;
+    double hr = 0.0, hi = 0.0;
     if (a.h0) {
       hr = ld_param(a.h0, 2 * ((b * D + d) * N + n), pd);
       hi = ld_param(a.h0, 2 * ((b * D + d) * N + n) + 1, pd);
@@ -548,13 +552,13 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_carry(const BwdArgs a)
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
         if (j0 + j < K - 1) {
-          cstep(rf[j].z, -rf[j].w, rf[j].x, rf[j].y, hr, hi);   // P - 1 = conj(E - 1)
-          *reinterpret_cast<float2*>(fs + (j0 + j) * st) = make_float2(hr, hi);
+          cstep_d(rf[j].z, -rf[j].w, rf[j].x, rf[j].y, hr, hi);   // P - 1 = conj(E - 1)
+          *reinterpret_cast<float2*>(fs + (j0 + j) * st) = make_float2((float)hr, (float)hi);
         }
       }
     }
   } else {
-    float cr = 0.0f, ci = 0.0f;
+    double cr = 0.0, ci = 0.0;
     for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
       float2 re[KB], rb[KB];
 #pragma unroll
@@ -566,8 +570,8 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_carry(const BwdArgs a)
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
         if (j0 + j < K - 1) {
-          cstep(re[j].x, re[j].y, rb[j].x, rb[j].y, cr, ci);    // c = E c + Sb
-          bs[(K - 1 - (j0 + j)) * st] = make_float2(cr, ci);
+          cstep_d(re[j].x, re[j].y, rb[j].x, rb[j].y, cr, ci);    // c = E c + Sb
+          bs[(K - 1 - (j0 + j)) * st] = make_float2((float)cr, (float)ci);
         }
       }
     }
