@@ -408,10 +408,10 @@ hipError_t launch_cfwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s) {
 
 // B and C of one chunk as complex [n][tt] pairs in LDS; steps past the chunk
 // are zero (their dt is zero too, so they are identity steps).
-template <typename Tio>
+template <int CTS, typename Tio>
 __device__ __forceinline__ void load_cbc_tile(float* sB, float* sC, const Tio* B, const Tio* C,
                                               int64_t row0, int nt, int64_t N) {
-  const int64_t total = N * CT;
+  const int64_t total = N * CTS;
   for (int64_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
     const int64_t tt = idx / N, n = idx % N;   // n fastest: coalesced reads
     float br = 0.0f, bi = 0.0f, cr = 0.0f, ci = 0.0f;
@@ -422,7 +422,7 @@ __device__ __forceinline__ void load_cbc_tile(float* sB, float* sC, const Tio* B
       cr = ld(C, gi);
       ci = ld(C, gi + 1);
     }
-    const int64_t li = 2 * (n * CT + tt);
+    const int64_t li = 2 * (n * CTS + tt);
     sB[li] = br;
     sB[li + 1] = bi;
     sC[li] = cr;
@@ -433,12 +433,12 @@ __device__ __forceinline__ void load_cbc_tile(float* sB, float* sC, const Tio* B
 // Per chunk from zero: the end state S, E = prod conj(a_r) over the chunk (the
 // conjugate of its decay; stored as E - 1) and the reverse summary
 // Sb = sum_s (prod_{r<=s} conj(a_r)) g_s conj(C_s).
-template <typename Tio>
+template <typename Tio, int CT>
 __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_summary(const BwdArgs a) {
   extern __shared__ float smem[];
   float* sB = smem;
   float* sC = smem + 2 * a.N * CT;
-  const int64_t nbd = a.nwgd;
+  const int64_t nbd = (a.D + kChannelsPerBlock - 1) / kChannelsPerBlock;
   int64_t blk = blockIdx.x;
   const int64_t db = blk % nbd;
   blk /= nbd;
@@ -452,8 +452,8 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_summary(const BwdArgs 
   const int64_t t0 = k * a.chunk_len;
   const int nt = (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
 
-  load_cbc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C), b * L + t0,
-                nt, N);
+  load_cbc_tile<CT>(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C),
+                    b * L + t0, nt, N);
 
   const float bv = a.bias ? ld_param(a.bias, d, pd) : 0.0f;
   const bool has_z = a.z != nullptr, sp = a.softplus != 0;
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_summary(const BwdArgs 
     const float* cn = sC + 2 * n * CT;
     // E is carried as E - 1 and accumulates in double (rounded once): the
     // chunk's decay product is what the carry multiplies through every later
-    // chunk.  S and Sb cover only the chunk's 8 steps and stay in float
+    // chunk.  S and Sb cover only the chunk's 8 or 16 steps and stay in float
     // (measured: the gradients' errors against the oracle unchanged).
     float hr = 0.0f, hi = 0.0f, Sr = 0.0f, Si = 0.0f;
     double Er = 0.0, Ei = 0.0;
@@ -621,8 +621,8 @@ __global__ __launch_bounds__(kChannelsPerBlock, 2) void cbwd_main(const BwdArgs 
     const int64_t t0 = k * a.chunk_len;
     const int nt = (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
     __syncthreads();  // previous chunk's tile readers are done
-    load_cbc_tile(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C),
-                  b * L + t0, nt, N);
+    load_cbc_tile<CT>(sB, sC, static_cast<const Tio*>(a.B), static_cast<const Tio*>(a.C),
+                      b * L + t0, nt, N);
 
     float dl[CT], xu[CT], gg[CT], oo[CT], ddl[CT], dua[CT];
 #pragma unroll
@@ -780,6 +780,427 @@ __global__ __launch_bounds__(kChannelsPerBlock, 2) void cbwd_main(const BwdArgs 
   }
 }
 
+// ------------------------------------------------- backward, N <= 16: lanes
+//
+// One lane per (channel, state): lane n of row r of wave w (lane 16 r + n)
+// holds state n of channel c = 4 w + r, 16 channels per 256-lane workgroup.
+// The chunk group's chunks (at most kLCL = 16 steps each) are walked
+// backwards; per chunk:
+//   prep     thread (t, c) = (tid / 16, tid % 16) reads step t of channel c,
+//            forms dt, dt u, the gated output gradient and the gate terms as
+//            cbwd_main does, and puts them in LDS; B / C of the chunk go to
+//            LDS as one (B, C) quadruple per (t, n);
+//   states   lane (c, n) runs the chunk forward from its carried-in state and
+//            keeps the 16 states and decays in registers;
+//   adjoint  it runs the chunk backward from the carried-in adjoint.  dB / dC
+//            of each (step, state) are summed over the wave's 4 channels with
+//            lane swaps, then over the 4 waves in LDS (fixed order);
+//   sums over a channel's states (readout, dt and u gradients) are
+//            reduce-scatters over the 16 lanes of a row: lane n ends with
+//            step n's sums.  The outputs leave through LDS, written by the
+//            prep threads in rows of the workgroup's 16 channels.
+// The next chunk's inputs and carried values are loaded while this chunk
+// computes.  States n >= N are zero lanes (A = 0, B = C = 0, zero carries);
+// tail channels (d >= D) copy channel D-1 with zero drive and gradient.
+constexpr int kLCL = kCplxBwdLanesTile;
+constexpr int kLCPW = kCplxLanesCPW;
+static_assert(kLCL == 16 && kLCPW * 16 == 256, "lane maps below assume 16 x 16");
+
+// Reduce-scatter over the 16 lanes of a row (lane n = lane % 16): lane n
+// holds o[0..15] and returns the row's sum of o[n].  Partners per stage:
+// n ^ 15 (row_mirror), n ^ 7 (row_half_mirror), n ^ 2 and n ^ 1 (quad
+// permutations), a basis of the row, so the four stages sum over all 16
+// lanes; at each stage a lane keeps the half of its values picked by one bit
+// of n (3, 2, 1, 0), which its partner sends.  15 DPP adds, 30 selects.
+__device__ __forceinline__ float reduce_scatter16(const float (&o)[16], int n) {
+  const bool b3 = (n & 8) != 0, b2 = (n & 4) != 0, b1 = (n & 2) != 0, b0 = (n & 1) != 0;
+  float a[8], b[4], c[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float keep = b3 ? o[8 + k] : o[k];
+    const float send = b3 ? o[k] : o[8 + k];
+    a[k] = keep + dpp<0x140>(send);     // row_mirror
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = b2 ? a[4 + k] : a[k];
+    const float send = b2 ? a[k] : a[4 + k];
+    b[k] = keep + dpp<0x141>(send);     // row_half_mirror
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float keep = b1 ? b[2 + k] : b[k];
+    const float send = b1 ? b[k] : b[2 + k];
+    c[k] = keep + dpp<0x4E>(send);      // quad_perm [2,3,0,1]
+  }
+  const float keep = b0 ? c[1] : c[0];
+  const float send = b0 ? c[0] : c[1];
+  return keep + dpp<0xB1>(send);        // quad_perm [1,0,3,2]
+}
+
+// Sum of v[r] over the wave's 4 rows, returned in row r (r = lane / 16):
+// rows 0-1 and 2-3 exchange through permlane32_swap (v0 with v2, v1 with
+// v3), then rows 0/1 and 2/3 through permlane16_swap.
+__device__ __forceinline__ float rows_sum4(float v0, float v1, float v2, float v3) {
+  float x, y;
+  swap32(v0, v2, x, y);
+  const float p = x + y;    // rows 0-1: v0 over rows r, r ^ 2; rows 2-3: v2
+  swap32(v1, v3, x, y);
+  const float q = x + y;    // rows 0-1: v1; rows 2-3: v3
+  swap16(p, q, x, y);
+  return x + y;             // rows 0, 2: p over all rows; rows 1, 3: q
+}
+
+// Per-(step, channel) terms of the backward (as cbwd_main forms them): dt,
+// the gated output gradient g, dz's factor gz and sigmoid(x) for ddelta.  Not
+// inlined: inside a chunk loop the compiler would keep the double-precision
+// series constants in registers across the whole loop.
+struct CPrep { float dl, g, gz, sx; };
+__device__ __attribute__((noinline)) CPrep cprep(float x, float dy, float z, bool has_z,
+                                                 bool sp) {
+  CPrep r;
+  if (sp) { r.dl = softplus_rn(x); r.sx = sigmoid_rn(x); } else { r.dl = x; r.sx = 1.0f; }
+  r.g = dy;
+  r.gz = 0.0f;
+  if (has_z) {
+    const float s = sigmoid_rn(z);
+    r.g = dy * z * s;
+    r.gz = dy * s * __builtin_fmaf(z, 1.0f - s, 1.0f);
+  }
+  return r;
+}
+
+// Chunk summaries (as cbwd_summary) in the lanes layout: one workgroup per
+// (b, chunk, 16 channels), lane (c, n) runs state n of channel c over the
+// chunk from zero.
+template <typename Tio>
+__global__ __launch_bounds__(256) void cbwd_summary_lanes(const BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float4 sBC[kLCL][16];        // (Br, Bi, Cr, Ci)
+  __shared__ __attribute__((aligned(16))) float4 xs[kLCPW][kLCL + 1];  // (dt, dt u, g, -)
+  constexpr int ES = sizeof(Tio);
+  const int tid = threadIdx.x;
+  const int64_t nbd = a.nwgd;
+  int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t k = blk % a.K;
+  const int64_t b = blk / a.K;
+  const int64_t L = a.L, D = a.D, N = a.N, K = a.K;
+  const int pd = a.param_dtype;
+  const int64_t d0 = db * kLCPW;
+  const int lc = tid >> 4, n = tid & 15;
+  const int pt = tid >> 4, pc = tid & 15;
+  const bool l_active = d0 + lc < D, p_active = d0 + pc < D;
+  const int64_t ld_ = l_active ? d0 + lc : D - 1;
+  const int64_t pd_ = p_active ? d0 + pc : D - 1;
+  const bool has_z = a.z != nullptr, sp = a.softplus != 0;
+  const bool sn = n < N;
+  const int64_t t0 = k * a.chunk_len;
+  const int nt = (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
+
+  {
+    // prep of step pt of channel pc; (B, C) of (step pt, state pc)
+    const int64_t row0 = (b * L + t0) * D + d0;
+    const int64_t avail = ((int64_t)nt * D - d0) * ES;
+    const int voff_in = (int)(((int64_t)pt * D + pc) * ES);
+    const float u = buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.u) + row0, avail), voff_in, 0);
+    const float x = buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.delta) + row0, avail), voff_in, 0);
+    const float dy = buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.dy) + row0, avail), voff_in, 0);
+    const float z = has_z ? buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.z) + row0, avail),
+                                        voff_in, 0)
+                          : 0.0f;
+    float4 bc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (pt < nt && pc < N) {
+      const int voff_bc = (int)(((int64_t)pt * N + pc) * 2 * ES);
+      const int64_t bo = 2 * (b * L + t0) * N;
+      const int64_t bb = (int64_t)nt * N * 2 * ES;
+      const auto rB = make_rsrc(static_cast<const Tio*>(a.B) + bo, bb);
+      const auto rC = make_rsrc(static_cast<const Tio*>(a.C) + bo, bb);
+      bc = make_float4(buf_ld<Tio>(rB, voff_bc, 0), buf_ld<Tio>(rB, voff_bc + ES, 0),
+                       buf_ld<Tio>(rC, voff_bc, 0), buf_ld<Tio>(rC, voff_bc + ES, 0));
+    }
+    const float pbv = a.bias ? ld_param(a.bias, pd_, pd) : 0.0f;
+    const bool drive = pt < nt && p_active;
+    const CPrep pr = cprep(x + pbv, dy, z, has_z, sp);
+    xs[pc][pt] = make_float4(drive ? pr.dl : 0.0f, drive ? pr.dl * u : 0.0f,
+                             drive ? pr.g : 0.0f, 0.0f);
+    sBC[pt][pc] = bc;
+  }
+  const float ar = sn ? ld_param(a.A, 2 * (ld_ * N + n), pd) : 0.0f;
+  const float ai = sn ? ld_param(a.A, 2 * (ld_ * N + n) + 1, pd) : 0.0f;
+  __syncthreads();
+
+  // S from zero, E - 1 = prod conj(a) - 1 in double (rounded once), and
+  // Sb = sum_s E_s g_s conj(C_s), as cbwd_summary
+  float hr = 0.0f, hi = 0.0f, Sr = 0.0f, Si = 0.0f;
+  double Er = 0.0, Ei = 0.0;
+#pragma unroll
+  for (int t = 0; t < kLCL; ++t) {
+    const float4* xrow = &xs[lc][0];
+    const float4* brow = &sBC[0][n];
+    __asm__ volatile("" : "+v"(xrow), "+v"(brow));
+    const float4 e = xrow[t];
+    const float4 bc = brow[16 * t];
+    float fr, fi;
+    cexpm1_dt(e.x, ar, ai, fr, fi);
+    cstep(fr, fi, e.y * bc.x, e.y * bc.y, hr, hi);
+    const double mr = fr, mi = fi;
+    cstep_d(mr, -mi, mr, -mi, Er, Ei);
+    const float wr = e.z * bc.z, wi = -e.z * bc.w;
+    const float er = (float)Er, ei = (float)Ei;
+    Sr += __builtin_fmaf(er, wr, __builtin_fmaf(-ei, wi, wr));
+    Si += __builtin_fmaf(er, wi, __builtin_fmaf(ei, wr, wi));
+    __asm__ volatile("" : "+v"(hr), "+v"(hi), "+v"(Sr), "+v"(Si));
+  }
+  if (l_active && sn) {
+    const int64_t o = ((b * K + k) * N + n) * D + ld_;
+    *reinterpret_cast<float4*>(a.fstate + 4 * o) =
+        make_float4(hr, hi, (float)Er, (float)Ei);
+    *reinterpret_cast<float2*>(a.bstate + 2 * o) = make_float2(Sr, Si);
+  }
+}
+
+template <typename Tio>
+__global__ __launch_bounds__(256, 3) void cbwd_lanes(const BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float4 sBC[kLCL][16];        // (Br, Bi, Cr, Ci)
+  // rows padded by one element: the row-wise writes of the prep threads and
+  // the per-step writes of dB / dC hit distinct banks
+  __shared__ __attribute__((aligned(16))) float4 xs[kLCPW][kLCL + 1];  // (dt, dt u, g, -)
+  __shared__ __attribute__((aligned(16))) float4 sst[kLCPW][kLCL + 1]; // (u, gz, sx, -)
+  __shared__ float red[4][4][16][kLCL + 1];                           // [wave][which][n][t]
+  __shared__ float ob[3][kLCL][kLCPW + 1];                            // du, ddelta, dz
+  __shared__ float fin[2][kLCL][kLCPW + 1];                           // dD, dbias per (t, c)
+  constexpr int ES = sizeof(Tio);
+  const int tid = threadIdx.x;
+  const int64_t nbd = a.nwgd;
+  int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t kg = blk % a.KG;
+  const int64_t b = blk / a.KG;
+  const int64_t L = a.L, D = a.D, N = a.N, K = a.K;
+  const int pd = a.param_dtype;
+  const int64_t d0 = db * kLCPW;
+  // compute role: channel lc, state n; prep / output role: step pt, channel pc
+  const int lc = tid >> 4, n = tid & 15;
+  const int pt = tid >> 4, pc = tid & 15;
+  const int wv = tid >> 6, row = (tid >> 4) & 3;
+  const bool l_active = d0 + lc < D, p_active = d0 + pc < D;
+  const int64_t ld_ = l_active ? d0 + lc : D - 1;
+  const int64_t pd_ = p_active ? d0 + pc : D - 1;
+  const bool has_z = a.z != nullptr, has_D = a.Dskip != nullptr, sp = a.softplus != 0;
+  const float pbv = a.bias ? ld_param(a.bias, pd_, pd) : 0.0f;
+  const float lDv = a.Dskip ? ld_param(a.Dskip, ld_, pd) : 0.0f;
+  const bool sn = n < N;
+  const float ar = sn ? ld_param(a.A, 2 * (ld_ * N + n), pd) : 0.0f;
+  const float ai = sn ? ld_param(a.A, 2 * (ld_ * N + n) + 1, pd) : 0.0f;
+  // 32-bit offsets within a chunk: step pt of channel pc of the [t][d] rows,
+  // (step pt, state pc) of the [t][n] complex rows, (n, channel lc) of a chunk
+  // record [n][d]
+  const int voff_in = (int)(((int64_t)pt * D + pc) * ES);
+  const int voff_bc = (int)(((int64_t)pt * N + pc) * 2 * ES);
+  const uint32_t roff = (uint32_t)(n * D + ld_);
+  const int64_t k_lo = kg * kBwdChunksPerGroup;
+  const int64_t k_hi = (k_lo + kBwdChunksPerGroup < K) ? k_lo + kBwdChunksPerGroup : K;
+  auto chunk_rows = [&](int64_t k) {
+    const int64_t t0 = k * a.chunk_len;
+    return (int)((t0 + a.chunk_len < L ? t0 + a.chunk_len : L) - t0);
+  };
+
+  // h0 of lane (lc, n), used by chunk 0
+  float h0r = 0.0f, h0i = 0.0f;
+  if (a.h0 && k_lo == 0 && sn) {
+    h0r = ld_param(a.h0, 2 * ((b * D + ld_) * N + n), pd);
+    h0i = ld_param(a.h0, 2 * ((b * D + ld_) * N + n) + 1, pd);
+  }
+  // raw inputs of one chunk: step pt of channel pc, (B, C) of (step pt, state
+  // pc), and lane (lc, n)'s carried-in state and adjoint
+  struct Raw { float u, x, dy, z; float4 bc; float hr, hi, cr, ci; };
+  auto load_raw = [&](int64_t k) {
+    Raw r;
+    const int64_t t0 = k * a.chunk_len;
+    const int nt = chunk_rows(k);
+    const int64_t row0 = (b * L + t0) * D + d0;
+    const int64_t avail = ((int64_t)nt * D - d0) * ES;    // bytes to the chunk's end
+    r.u = buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.u) + row0, avail), voff_in, 0);
+    r.x = buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.delta) + row0, avail), voff_in, 0);
+    r.dy = buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.dy) + row0, avail), voff_in, 0);
+    r.z = has_z ? buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.z) + row0, avail), voff_in, 0)
+                : 0.0f;
+    r.bc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (pt < nt && pc < N) {
+      const int64_t bo = 2 * (b * L + t0) * N;
+      const int64_t bb = (int64_t)nt * N * 2 * ES;
+      const auto rB = make_rsrc(static_cast<const Tio*>(a.B) + bo, bb);
+      const auto rC = make_rsrc(static_cast<const Tio*>(a.C) + bo, bb);
+      r.bc = make_float4(buf_ld<Tio>(rB, voff_bc, 0), buf_ld<Tio>(rB, voff_bc + ES, 0),
+                         buf_ld<Tio>(rC, voff_bc, 0), buf_ld<Tio>(rC, voff_bc + ES, 0));
+    }
+    r.hr = 0.0f; r.hi = 0.0f; r.cr = 0.0f; r.ci = 0.0f;
+    if (sn) {
+      if (k > 0) {
+        const float* fb = a.fstate + 4 * ((b * K + (k - 1)) * N * D);
+        const float2 f = *reinterpret_cast<const float2*>(fb + 4 * roff);
+        r.hr = f.x;
+        r.hi = f.y;
+      } else {
+        r.hr = h0r;
+        r.hi = h0i;
+      }
+      if (k < K - 1) {
+        const float* bb = a.bstate + 2 * ((b * K + (k + 1)) * N * D);
+        const float2 c = *reinterpret_cast<const float2*>(bb + 2 * roff);
+        r.cr = c.x;
+        r.ci = c.y;
+      }
+    }
+    return r;
+  };
+
+  float dAr = 0.0f, dAi = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
+  float dh_last_r = 0.0f, dh_last_i = 0.0f;   // the adjoint after the last chunk walked
+  Raw nx = load_raw(k_hi - 1);
+  for (int64_t k = k_hi - 1; k >= k_lo; --k) {
+    const int64_t t0 = k * a.chunk_len;
+    const int nt = chunk_rows(k);
+    const Raw cur = nx;
+    // ---- prep: step pt of channel pc (as cbwd_main; tail channels and steps
+    // past the chunk get zero dt, drive and gradient)
+    const bool drive = pt < nt && p_active;
+    const CPrep pr = cprep(cur.x + pbv, cur.dy, cur.z, has_z, sp);
+    const float p_gg = drive ? pr.g : 0.0f, p_uu = drive ? cur.u : 0.0f;
+    xs[pc][pt] = make_float4(drive ? pr.dl : 0.0f, drive ? pr.dl * cur.u : 0.0f, p_gg, 0.0f);
+    sst[pc][pt] = make_float4(p_uu, pr.gz, pr.sx, 0.0f);
+    sBC[pt][pc] = cur.bc;
+    __syncthreads();                                  // (A) the chunk's inputs are in LDS
+    if (k > k_lo) nx = load_raw(k - 1);
+
+    // ---- states: the chunk forward from the carried-in state
+    float amr[kLCL], ami[kLCL], hsr[kLCL], hsi[kLCL], po[kLCL];
+    // the decays one after another (fenced): interleaved, their temporaries
+    // alone would exceed the register budget
+#pragma unroll
+    for (int t = 0; t < kLCL; ++t) {
+      float dlt = xs[lc][t].x;
+      __asm__ volatile("" : "+v"(dlt));
+      cexpm1_dt(dlt, ar, ai, amr[t], ami[t]);
+      __asm__ volatile("" : "+v"(amr[t]), "+v"(ami[t]));
+    }
+    {
+      float hr = cur.hr, hi = cur.hi;
+#pragma unroll
+      for (int t = 0; t < kLCL; ++t) {
+        // (row pointers through an empty asm: the loads of a step issue at
+        //  most one step early instead of all at once)
+        const float4* xrow = &xs[lc][0];
+        const float4* brow = &sBC[0][n];
+        __asm__ volatile("" : "+v"(xrow), "+v"(brow));
+        const float xu = xrow[t].y;
+        const float4 bc = brow[16 * t];
+        cstep(amr[t], ami[t], xu * bc.x, xu * bc.y, hr, hi);
+        hsr[t] = hr;
+        hsi[t] = hi;
+        po[t] = __builtin_fmaf(bc.z, hr, -bc.w * hi);   // Re(C h)
+      }
+    }
+    const float o_own = reduce_scatter16(po, n);
+
+    // ---- adjoint: the chunk backward from the carried-in adjoint
+    float pdua[kLCL], pddl[kLCL];
+    float dhr = cur.cr, dhi = cur.ci;
+#pragma unroll
+    for (int t = kLCL - 1; t >= 0; --t) {
+      const float4* xrow = &xs[lc][0];
+      const float4* brow = &sBC[0][n];
+      __asm__ volatile("" : "+v"(xrow), "+v"(brow));
+      const float4 e = xrow[t];
+      const float4 bc = brow[16 * t];
+      // lam = dh + g conj(C)
+      const float lr = __builtin_fmaf(e.z, bc.z, dhr);
+      const float li = __builtin_fmaf(-e.z, bc.w, dhi);
+      // dB = lam dt u, dC = g conj(h): summed over the wave's channels
+      red[wv][row][n][t] = rows_sum4(lr * e.y, li * e.y, e.z * hsr[t], -e.z * hsi[t]);
+      pdua[t] = __builtin_fmaf(bc.x, lr, bc.y * li);  // Re(conj(B) lam)
+      // m = conj(a) lam = lam + conj(a - 1) lam
+      float mr = lr, mi = li;
+      cstep(amr[t], -ami[t], 0.0f, 0.0f, mr, mi);
+      // dw = m conj(h_{t-1})
+      const float qr = t > 0 ? hsr[t - 1] : cur.hr;
+      const float qi = t > 0 ? hsi[t - 1] : cur.hi;
+      const float wr = __builtin_fmaf(mr, qr, mi * qi);
+      const float wi = __builtin_fmaf(mi, qr, -mr * qi);
+      pddl[t] = __builtin_fmaf(ar, wr, ai * wi);
+      dAr = __builtin_fmaf(wr, e.x, dAr);
+      dAi = __builtin_fmaf(wi, e.x, dAi);
+      __asm__ volatile("" : "+v"(dAr), "+v"(dAi));   // accumulated step by step
+      dhr = mr;
+      dhi = mi;
+    }
+    dh_last_r = dhr;
+    dh_last_i = dhi;
+    const float dua_own = reduce_scatter16(pdua, n);
+    const float ddl_own = reduce_scatter16(pddl, n);
+    {
+      // outputs of step n of channel lc
+      const float4 e = xs[lc][n];
+      const float4 q = sst[lc][n];
+      ob[0][n][lc] = __builtin_fmaf(e.x, dua_own, has_D ? e.z * lDv : 0.0f);
+      ob[1][n][lc] = __builtin_fmaf(q.x, dua_own, ddl_own) * q.z;
+      ob[2][n][lc] = q.y * __builtin_fmaf(lDv, q.x, o_own);
+    }
+    __syncthreads();                                  // (B) red and ob complete
+
+    // ---- the outputs of step pt, channel pc; dB / dC summed over the 4 waves
+    if (drive) {
+      const int64_t row0 = (b * L + t0) * D + d0;
+      const float dx = ob[1][pt][pc];
+      const int64_t bytes = ((int64_t)nt * D - d0) * ES;
+      buf_st<Tio>(ob[0][pt][pc], make_rsrc(static_cast<Tio*>(a.du) + row0, bytes), voff_in, 0);
+      buf_st<Tio>(dx, make_rsrc(static_cast<Tio*>(a.ddelta) + row0, bytes), voff_in, 0);
+      if (has_z)
+        buf_st<Tio>(ob[2][pt][pc], make_rsrc(static_cast<Tio*>(a.dz) + row0, bytes), voff_in, 0);
+      db_acc += dx;
+      dD_acc = __builtin_fmaf(p_gg, p_uu, dD_acc);
+    }
+    float* pbc = a.part_bc + ((b * L + t0) * a.nwgd + db) * 4 * N;
+    const uint32_t tstride = (uint32_t)(a.nwgd * 4 * N);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int t = idx >> 6, j = idx & 63;
+      const int bcw = j >> 5, nn = (j >> 1) & 15, ri = j & 1;
+      const int which = 2 * bcw + ri;
+      const float v = ((red[0][which][nn][t] + red[1][which][nn][t]) + red[2][which][nn][t]) +
+                      red[3][which][nn][t];
+      if (t < nt && nn < N) pbc[t * tstride + (uint32_t)(bcw * 2 * N + 2 * nn + ri)] = v;
+    }
+  }
+  if (l_active && sn) {
+    float* pa = a.part_dA + 2 * (((b * a.KG + kg) * N + n) * D + ld_);
+    pa[0] = dAr;
+    pa[1] = dAi;
+    // after step 0 of chunk 0 (the group's last), dh is dL/dh_{-1}
+    if (k_lo == 0 && a.dh0) {
+      st_param(a.dh0, 2 * ((b * D + ld_) * N + n), pd, dh_last_r);
+      st_param(a.dh0, 2 * ((b * D + ld_) * N + n) + 1, pd, dh_last_i);
+    }
+  }
+  // dD / dbias of channel pc: its 16 step threads' sums, added in step order
+  fin[0][pt][pc] = dD_acc;
+  fin[1][pt][pc] = db_acc;
+  __syncthreads();
+  if (tid < kLCPW && d0 + tid < D) {
+    float sD = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kLCL; ++t) {
+      sD += fin[0][t][tid];
+      sb += fin[1][t][tid];
+    }
+    a.part_dD[(b * a.KG + kg) * D + d0 + tid] = sD;
+    a.part_db[(b * a.KG + kg) * D + d0 + tid] = sb;
+  }
+}
+
 // Fixed-order sum of `count` partials p[0], p[stride], ... (loads issued in
 // batches of 8, the adds in index order).
 __device__ __forceinline__ float csum_ordered(const float* p, int64_t count, int64_t stride) {
@@ -865,28 +1286,37 @@ hipError_t czero_bytes(void* p, int64_t bytes, hipStream_t s) {
 template <typename Tio>
 hipError_t launch_cbwd_t(const BwdArgs& a, hipStream_t s) {
   const int64_t Bn = a.Bn, N = a.N;
+  const bool lanes = N <= 16;
   hipError_t e;
-  const size_t tile_bytes = sizeof(float) * 4 * (size_t)N * CT;
+  const int64_t nc = (a.D + kChannelsPerBlock - 1) / kChannelsPerBlock;
+  const size_t tile_bytes = sizeof(float) * 4 * (size_t)N * CT;   // the N > 16 kernels
   if (a.K > 1) {
-    cbwd_summary<Tio><<<dim3((unsigned)(Bn * a.K * a.nwgd)), dim3(kChannelsPerBlock),
-                        tile_bytes, s>>>(a);
+    if (lanes)
+      cbwd_summary_lanes<Tio><<<dim3((unsigned)(Bn * a.K * a.nwgd)), dim3(256), 0, s>>>(a);
+    else
+      cbwd_summary<Tio, CT><<<dim3((unsigned)(Bn * a.K * nc)), dim3(kChannelsPerBlock),
+                              tile_bytes, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (N > 0) {
-      const int64_t nc = (a.D + kChannelsPerBlock - 1) / kChannelsPerBlock;
       cbwd_carry<<<dim3((unsigned)(2 * Bn * N * nc)), dim3(kChannelsPerBlock), 0, s>>>(a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  const size_t main_bytes =
-      tile_bytes + sizeof(float) * (32 * kCRedStride + 3 * CT * kChannelsPerBlock);
-  if (main_bytes > 64 * 1024) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&cbwd_main<Tio>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)main_bytes);
-    if (e != hipSuccess) return e;
+  if (lanes) {
+    cbwd_lanes<Tio><<<dim3((unsigned)(Bn * a.KG * a.nwgd)), dim3(256), 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    const size_t main_bytes =
+        tile_bytes + sizeof(float) * (32 * kCRedStride + 3 * CT * kChannelsPerBlock);
+    if (main_bytes > 64 * 1024) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&cbwd_main<Tio>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)main_bytes);
+      if (e != hipSuccess) return e;
+    }
+    cbwd_main<Tio><<<dim3((unsigned)(Bn * a.KG * a.nwgd)), dim3(kChannelsPerBlock), main_bytes,
+                     s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  cbwd_main<Tio><<<dim3((unsigned)(Bn * a.KG * a.nwgd)), dim3(kChannelsPerBlock), main_bytes,
-                   s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (Bn * a.L * N > 0) {
     const int64_t nb = Bn * a.L * N * 2;
     cbwd_finalize_bc<Tio><<<dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s>>>(a);

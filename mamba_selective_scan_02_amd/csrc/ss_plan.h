@@ -172,13 +172,17 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
 // Complex variant (A, B, C and the state complex, stored as (re, im) float
 // pairs).  Forward: G lanes per channel with NS complex states each
 // (NS * G >= N, NS <= 4 up to N = 64), 256 / G channels per workgroup, chunks chosen as
-// for the real scan.  Backward: one lane per channel, chunks of at most
-// kCplxBwdTile steps, 256 channels per workgroup, partials per group of
-// kBwdChunksPerGroup chunks.  A chunk's decay is carried as the product of
-// its steps' decays, stored beside its end state (4 floats per (b, k, n, d)):
-// the closed form exp(A * sum dt) would turn the rounding of the sum into a
-// phase error of |Im A| times it.
+// for the real scan.  Backward, N <= 16: one lane per (channel, state), 16
+// channels per workgroup, chunks of at most kCplxBwdLanesTile steps.  N > 16:
+// one lane per channel looping over the states, chunks of at most
+// kCplxBwdTile steps, 256 channels per workgroup.  Both write partials per
+// group of kBwdChunksPerGroup chunks.  A chunk's decay is carried as the
+// product of its steps' decays, stored beside its end state (4 floats per
+// (b, k, n, d)): the closed form exp(A * sum dt) would turn the rounding of
+// the sum into a phase error of |Im A| times it.
 constexpr int kCplxBwdTile = 8;
+constexpr int kCplxBwdLanesTile = 16;
+constexpr int kCplxLanesCPW = 16;      // channels per workgroup of the N <= 16 backward
 
 inline Plan make_plan_complex(const ss_desc& d, bool backward) {
   Plan p;
@@ -229,15 +233,17 @@ inline Plan make_plan_complex(const ss_desc& d, bool backward) {
     p.n_launches = p.K > 1 ? (N > 0 ? 3 : 2) : 1;
     return p;
   }
-  int64_t lc = kCplxBwdTile;
+  const bool lanes = N <= 16;
+  int64_t lc = lanes ? kCplxBwdLanesTile : kCplxBwdTile;
   if (d.chunk_len > 0 && d.chunk_len < lc) lc = d.chunk_len;
   if (lc > L) lc = L;
   p.chunk_len = lc;
   p.K = (L + lc - 1) / lc;
   p.NS = 1;
-  p.G = 1;
+  p.G = lanes ? 16 : 1;
   p.KG = (p.K + kBwdChunksPerGroup - 1) / kBwdChunksPerGroup;
-  p.nwgd = (D + kChannelsPerBlock - 1) / kChannelsPerBlock;
+  const int64_t cpw = lanes ? kCplxLanesCPW : kChannelsPerBlock;
+  p.nwgd = (D + cpw - 1) / cpw;
   size_t off = 0;
   p.off_state = off;   // (S re, S im, E re, E im), E = product of conj(a)
   off = align256(off + 4 * sizeof(float) * (size_t)(Bn * p.K * N * D));
