@@ -796,9 +796,10 @@ __global__ __launch_bounds__(kChannelsPerBlock, 2) void cbwd_main(const BwdArgs 
 //            of each (step, state) are summed over the wave's 4 channels with
 //            lane swaps, then over the 4 waves in LDS (fixed order);
 //   sums over a channel's states (readout, dt and u gradients) are
-//            reduce-scatters over the 16 lanes of a row: lane n ends with
-//            step n's sums.  The outputs leave through LDS, written by the
-//            prep threads in rows of the workgroup's 16 channels.
+//            reduce-scatters over the 16 lanes of a row, fed step by step:
+//            lane n ends with the sums of step rev4(n).  The outputs leave
+//            through LDS, written by the prep threads in rows of the
+//            workgroup's 16 channels.
 // The next chunk's inputs and carried values are loaded while this chunk
 // computes.  States n >= N are zero lanes (A = 0, B = C = 0, zero carries);
 // tail channels (d >= D) copy channel D-1 with zero drive and gradient.
@@ -806,37 +807,54 @@ constexpr int kLCL = kCplxBwdLanesTile;
 constexpr int kLCPW = kCplxLanesCPW;
 static_assert(kLCL == 16 && kLCPW * 16 == 256, "lane maps below assume 16 x 16");
 
-// Reduce-scatter over the 16 lanes of a row (lane n = lane % 16): lane n
-// holds o[0..15] and returns the row's sum of o[n].  Partners per stage:
-// n ^ 15 (row_mirror), n ^ 7 (row_half_mirror), n ^ 2 and n ^ 1 (quad
-// permutations), a basis of the row, so the four stages sum over all 16
-// lanes; at each stage a lane keeps the half of its values picked by one bit
-// of n (3, 2, 1, 0), which its partner sends.  15 DPP adds, 30 selects.
-__device__ __forceinline__ float reduce_scatter16(const float (&o)[16], int n) {
-  const bool b3 = (n & 8) != 0, b2 = (n & 4) != 0, b1 = (n & 2) != 0, b0 = (n & 1) != 0;
-  float a[8], b[4], c[2];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float keep = b3 ? o[8 + k] : o[k];
-    const float send = b3 ? o[k] : o[8 + k];
-    a[k] = keep + dpp<0x140>(send);     // row_mirror
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float keep = b2 ? a[4 + k] : a[k];
-    const float send = b2 ? a[k] : a[4 + k];
-    b[k] = keep + dpp<0x141>(send);     // row_half_mirror
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float keep = b1 ? b[2 + k] : b[k];
-    const float send = b1 ? b[k] : b[2 + k];
-    c[k] = keep + dpp<0x4E>(send);      // quad_perm [2,3,0,1]
-  }
-  const float keep = b0 ? c[1] : c[0];
-  const float send = b0 ? c[0] : c[1];
-  return keep + dpp<0xB1>(send);        // quad_perm [1,0,3,2]
+// Reduce-scatter over the 16 lanes of a row (lane n = lane % 16), fed one
+// step at a time.  Stage j combines the pair of partial sums whose step
+// indices differ in bit j - 1; the partner lanes are n ^ 15 (row_mirror),
+// n ^ 7 (row_half_mirror), n ^ 2 and n ^ 1 (quad permutations), a basis of
+// the row, and at stage j a lane keeps the partial whose index bit equals its
+// lane bit 4 - j (bits 3, 2, 1, 0 of n), which the partner sends.  After the
+// 16 steps lane n holds the row's sum for step rev4(n) (n's 4 bits reversed).
+// Pairs combine as soon as both halves exist, so at most a few partial sums
+// are live.  15 DPP adds and 30 selects per 16 steps.
+__device__ __forceinline__ int rev4(int n) {
+  return ((n & 1) << 3) | ((n & 2) << 1) | ((n & 4) >> 1) | ((n & 8) >> 3);
 }
+template <int CTRL>
+__device__ __forceinline__ float pair_sum(float x0, float x1, bool bit) {
+  const float keep = bit ? x1 : x0;
+  const float send = bit ? x0 : x1;
+  return keep + dpp<CTRL>(send);
+}
+struct RowScatter16 {
+  float hold, p1[8], p2[4], p3[2], own;
+  bool b3, b2, b1, b0;
+  __device__ __forceinline__ explicit RowScatter16(int n)
+      : b3((n & 8) != 0), b2((n & 4) != 0), b1((n & 2) != 0), b0((n & 1) != 0) {}
+  // step t's value, steps in ascending order
+  __device__ __forceinline__ void up(int t, float v) {
+    if ((t & 1) == 0) { hold = v; return; }
+    const int m = t >> 1;
+    p1[m] = pair_sum<0x140>(hold, v, b3);
+    if ((m & 1) == 0) return;
+    p2[m >> 1] = pair_sum<0x141>(p1[m - 1], p1[m], b2);
+    if (((m >> 1) & 1) == 0) return;
+    p3[m >> 2] = pair_sum<0x4E>(p2[(m >> 1) - 1], p2[m >> 1], b1);
+    if (((m >> 2) & 1) == 0) return;
+    own = pair_sum<0xB1>(p3[0], p3[1], b0);
+  }
+  // step t's value, steps in descending order
+  __device__ __forceinline__ void down(int t, float v) {
+    if (t & 1) { hold = v; return; }
+    const int m = t >> 1;
+    p1[m] = pair_sum<0x140>(v, hold, b3);
+    if (m & 1) return;
+    p2[m >> 1] = pair_sum<0x141>(p1[m], p1[m + 1], b2);
+    if ((m >> 1) & 1) return;
+    p3[m >> 2] = pair_sum<0x4E>(p2[m >> 1], p2[(m >> 1) + 1], b1);
+    if ((m >> 2) & 1) return;
+    own = pair_sum<0xB1>(p3[0], p3[1], b0);
+  }
+};
 
 // Sum of v[r] over the wave's 4 rows, returned in row r (r = lane / 16):
 // rows 0-1 and 2-3 exchange through permlane32_swap (v0 with v2, v1 with
@@ -851,19 +869,59 @@ __device__ __forceinline__ float rows_sum4(float v0, float v1, float v2, float v
   return x + y;             // rows 0, 2: p over all rows; rows 1, 3: q
 }
 
-// Per-(step, channel) terms of the backward (as cbwd_main forms them): dt,
-// the gated output gradient g, dz's factor gz and sigmoid(x) for ddelta.  Not
-// inlined: inside a chunk loop the compiler would keep the double-precision
-// series constants in registers across the whole loop.
+// Per-(step, channel) terms of the N <= 16 backward: dt, the gated output
+// gradient g, dz's factor gz and sigmoid(x) for ddelta, formed as cbwd_main
+// does but in float: the double-rounded versions cost ~800 VALU slots per
+// (step, channel), a third of these kernels' work.  dt must not inherit the
+// transcendental unit's exp bias (with softplus_acc, dA of the
+// 2x2048x1024x16 backward erred by 1.3e-5 against 4.6e-6 with the double
+// version), so softplus_cw builds e^{-|x|} from its series; the sigmoids use
+// sigmoid_acc (measured no worse than double).
+// softplus(x) = max(x, 0) + log(1 + w), w = e^{-|x|}, in float without the
+// transcendental unit: w by Cody and Waite's reduction and the Taylor series
+// of e^r - 1 through r^8 (as in cexpm1_dt), log(1 + w) by its series through
+// w^9 for w <= e^-2 and log1p_pos above.
+__device__ __forceinline__ float softplus_cw(float x) {
+  float v = -__builtin_fabsf(x);
+  v = v < -110.0f ? -110.0f : v;                 // (e^v is 0 in float from -104 on)
+  const float k = __builtin_rintf(v * kInvLn2);
+  const float r = __builtin_fmaf(-k, kLn2Lo, __builtin_fmaf(-k, kLn2Hi, v));
+  float p = 1.0f / 40320.0f;
+  p = __builtin_fmaf(p, r, 1.0f / 5040.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  const float sc = __builtin_ldexpf(1.0f, (int)k);
+  const float w = __builtin_fmaf(p * r, sc, sc);
+  float q = 1.0f / 9.0f;
+  q = __builtin_fmaf(q, w, -1.0f / 8.0f);
+  q = __builtin_fmaf(q, w, 1.0f / 7.0f);
+  q = __builtin_fmaf(q, w, -1.0f / 6.0f);
+  q = __builtin_fmaf(q, w, 1.0f / 5.0f);
+  q = __builtin_fmaf(q, w, -1.0f / 4.0f);
+  q = __builtin_fmaf(q, w, 1.0f / 3.0f);
+  q = __builtin_fmaf(q, w, -0.5f);
+  q = __builtin_fmaf(q, w, 1.0f);
+  const float lp = w <= 0.1353352832366127f ? w * q : log1p_pos(w);
+  return __builtin_fmaxf(x, 0.0f) + lp;
+}
 struct CPrep { float dl, g, gz, sx; };
-__device__ __attribute__((noinline)) CPrep cprep(float x, float dy, float z, bool has_z,
-                                                 bool sp) {
+__device__ __forceinline__ CPrep cprep(float x, float dy, float z, bool has_z, bool sp) {
   CPrep r;
-  if (sp) { r.dl = softplus_rn(x); r.sx = sigmoid_rn(x); } else { r.dl = x; r.sx = 1.0f; }
+  if (sp) {
+    r.dl = softplus_cw(x);
+    r.sx = sigmoid_acc(x);
+  } else {
+    r.dl = x;
+    r.sx = 1.0f;
+  }
   r.g = dy;
   r.gz = 0.0f;
   if (has_z) {
-    const float s = sigmoid_rn(z);
+    const float s = sigmoid_acc(z);
     r.g = dy * z * s;
     r.gz = dy * s * __builtin_fmaf(z, 1.0f - s, 1.0f);
   }
@@ -1076,7 +1134,8 @@ __global__ __launch_bounds__(256, 3) void cbwd_lanes(const BwdArgs a) {
     if (k > k_lo) nx = load_raw(k - 1);
 
     // ---- states: the chunk forward from the carried-in state
-    float amr[kLCL], ami[kLCL], hsr[kLCL], hsi[kLCL], po[kLCL];
+    float amr[kLCL], ami[kLCL], hsr[kLCL], hsi[kLCL];
+    RowScatter16 ro(n), rdua(n), rddl(n);
     // the decays one after another (fenced): interleaved, their temporaries
     // alone would exceed the register budget
 #pragma unroll
@@ -1100,13 +1159,11 @@ __global__ __launch_bounds__(256, 3) void cbwd_lanes(const BwdArgs a) {
         cstep(amr[t], ami[t], xu * bc.x, xu * bc.y, hr, hi);
         hsr[t] = hr;
         hsi[t] = hi;
-        po[t] = __builtin_fmaf(bc.z, hr, -bc.w * hi);   // Re(C h)
+        ro.up(t, __builtin_fmaf(bc.z, hr, -bc.w * hi));   // Re(C h)
       }
     }
-    const float o_own = reduce_scatter16(po, n);
 
     // ---- adjoint: the chunk backward from the carried-in adjoint
-    float pdua[kLCL], pddl[kLCL];
     float dhr = cur.cr, dhi = cur.ci;
 #pragma unroll
     for (int t = kLCL - 1; t >= 0; --t) {
@@ -1120,7 +1177,7 @@ __global__ __launch_bounds__(256, 3) void cbwd_lanes(const BwdArgs a) {
       const float li = __builtin_fmaf(-e.z, bc.w, dhi);
       // dB = lam dt u, dC = g conj(h): summed over the wave's channels
       red[wv][row][n][t] = rows_sum4(lr * e.y, li * e.y, e.z * hsr[t], -e.z * hsi[t]);
-      pdua[t] = __builtin_fmaf(bc.x, lr, bc.y * li);  // Re(conj(B) lam)
+      rdua.down(t, __builtin_fmaf(bc.x, lr, bc.y * li));  // Re(conj(B) lam)
       // m = conj(a) lam = lam + conj(a - 1) lam
       float mr = lr, mi = li;
       cstep(amr[t], -ami[t], 0.0f, 0.0f, mr, mi);
@@ -1129,7 +1186,7 @@ __global__ __launch_bounds__(256, 3) void cbwd_lanes(const BwdArgs a) {
       const float qi = t > 0 ? hsi[t - 1] : cur.hi;
       const float wr = __builtin_fmaf(mr, qr, mi * qi);
       const float wi = __builtin_fmaf(mi, qr, -mr * qi);
-      pddl[t] = __builtin_fmaf(ar, wr, ai * wi);
+      rddl.down(t, __builtin_fmaf(ar, wr, ai * wi));
       dAr = __builtin_fmaf(wr, e.x, dAr);
       dAi = __builtin_fmaf(wi, e.x, dAi);
       __asm__ volatile("" : "+v"(dAr), "+v"(dAi));   // accumulated step by step
@@ -1138,15 +1195,14 @@ __global__ __launch_bounds__(256, 3) void cbwd_lanes(const BwdArgs a) {
     }
     dh_last_r = dhr;
     dh_last_i = dhi;
-    const float dua_own = reduce_scatter16(pdua, n);
-    const float ddl_own = reduce_scatter16(pddl, n);
     {
-      // outputs of step n of channel lc
-      const float4 e = xs[lc][n];
-      const float4 q = sst[lc][n];
-      ob[0][n][lc] = __builtin_fmaf(e.x, dua_own, has_D ? e.z * lDv : 0.0f);
-      ob[1][n][lc] = __builtin_fmaf(q.x, dua_own, ddl_own) * q.z;
-      ob[2][n][lc] = q.y * __builtin_fmaf(lDv, q.x, o_own);
+      // outputs of step tn of channel lc (the step whose sums this lane holds)
+      const int tn = rev4(n);
+      const float4 e = xs[lc][tn];
+      const float4 q = sst[lc][tn];
+      ob[0][tn][lc] = __builtin_fmaf(e.x, rdua.own, has_D ? e.z * lDv : 0.0f);
+      ob[1][tn][lc] = __builtin_fmaf(q.x, rdua.own, rddl.own) * q.z;
+      ob[2][tn][lc] = q.y * __builtin_fmaf(lDv, q.x, ro.own);
     }
     __syncthreads();                                  // (B) red and ob complete
 
