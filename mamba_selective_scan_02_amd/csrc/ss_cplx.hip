@@ -179,15 +179,44 @@ __device__ __forceinline__ void cstep(float mr, float mi, float xr, float xi, fl
   hi = ni;
 }
 
-// dt, sigmoid and the gate, each rounded once from double.  These are per
-// (step, channel), not per state, so double costs little here; a bias in dt
-// would shift the phase sum(dt Im A) of long-lived rotating states coherently.
-__device__ __forceinline__ float softplus_rn(float x) {
-  const double xd = x;
-  return (float)(xd > 0.0 ? xd + log1p(exp(-xd)) : log1p(exp(xd)));
+// dt, sigmoid and the gate in float.  dt must not inherit the transcendental
+// unit's exp bias: along slowly decaying, rotating states a bias in dt shifts
+// the phase sum(dt Im A) coherently (the hardware-exp softplus_acc put dA of
+// the 2x2048x1024x16 backward at 1.3e-5 against the oracle, a softplus
+// rounded once from double at 4.6e-6, this one at 2.4e-6).  The sigmoids use
+// sigmoid_acc (measured as close as double).
+// softplus(x) = max(x, 0) + log(1 + w), w = e^{-|x|}, in float without the
+// transcendental unit: w by Cody and Waite's reduction and the Taylor series
+// of e^r - 1 through r^8 (as in cexpm1_dt), log(1 + w) by its series through
+// w^9 for w <= e^-2 and log1p_pos above.
+__device__ __forceinline__ float softplus_cw(float x) {
+  float v = -__builtin_fabsf(x);
+  v = v < -110.0f ? -110.0f : v;                 // (e^v is 0 in float from -104 on)
+  const float k = __builtin_rintf(v * kInvLn2);
+  const float r = __builtin_fmaf(-k, kLn2Lo, __builtin_fmaf(-k, kLn2Hi, v));
+  float p = 1.0f / 40320.0f;
+  p = __builtin_fmaf(p, r, 1.0f / 5040.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  const float sc = __builtin_ldexpf(1.0f, (int)k);
+  const float w = __builtin_fmaf(p * r, sc, sc);
+  float q = 1.0f / 9.0f;
+  q = __builtin_fmaf(q, w, -1.0f / 8.0f);
+  q = __builtin_fmaf(q, w, 1.0f / 7.0f);
+  q = __builtin_fmaf(q, w, -1.0f / 6.0f);
+  q = __builtin_fmaf(q, w, 1.0f / 5.0f);
+  q = __builtin_fmaf(q, w, -1.0f / 4.0f);
+  q = __builtin_fmaf(q, w, 1.0f / 3.0f);
+  q = __builtin_fmaf(q, w, -0.5f);
+  q = __builtin_fmaf(q, w, 1.0f);
+  const float lp = w <= 0.1353352832366127f ? w * q : log1p_pos(w);
+  return __builtin_fmaxf(x, 0.0f) + lp;
 }
-__device__ __forceinline__ float sigmoid_rn(float x) { return (float)(1.0 / (1.0 + exp(-(double)x))); }
-__device__ __forceinline__ float silu_gate(float z) { return (float)((double)z / (1.0 + exp(-(double)z))); }
+__device__ __forceinline__ float silu_gate(float z) { return z * sigmoid_acc(z); }
 
 // ------------------------------------------------------------------ forward
 
@@ -263,7 +292,7 @@ __global__ __launch_bounds__(kCB) void cfwd(const T* __restrict__ u_in,
   for (int64_t t = t0; t < t1; ++t) {
     const float uu = ld(up, t * D);
     const float x = ld(dp, t * D) + bv;
-    const float dt = sp ? softplus_rn(x) : x;
+    const float dt = sp ? softplus_cw(x) : x;
     const float xu = dt * uu;
     const T* Bt = B_in + 2 * ((b * L + t) * N + n0);
     const T* Ct = C_in + 2 * ((b * L + t) * N + n0);
@@ -467,7 +496,7 @@ __global__ __launch_bounds__(kChannelsPerBlock) void cbwd_summary(const BwdArgs 
     const bool ok = tt < nt;
     const int64_t t = t0 + (ok ? tt : nt - 1);
     const float uu = ld(up, t * D), x = ld(dp, t * D) + bv;
-    const float dlv = sp ? softplus_rn(x) : x;
+    const float dlv = sp ? softplus_cw(x) : x;
     float g = ld(yp, t * D);
     if (has_z) g *= silu_gate(ld(zp, t * D));
     dl[tt] = ok ? dlv : 0.0f;
@@ -631,10 +660,10 @@ __global__ __launch_bounds__(kChannelsPerBlock, 2) void cbwd_main(const BwdArgs 
       const int64_t t = t0 + (ok ? tt : nt - 1);
       const float u_ = ld(up, t * D), x = ld(dp, t * D) + bv, dy = ld(yp, t * D);
       float dlv, sxv;
-      if (sp) { dlv = softplus_rn(x); sxv = sigmoid_rn(x); } else { dlv = x; sxv = 1.0f; }
+      if (sp) { dlv = softplus_cw(x); sxv = sigmoid_acc(x); } else { dlv = x; sxv = 1.0f; }
       float g = dy, gzv = 0.0f;
       if (has_z) {
-        const float zz = ld(zp, t * D), s = sigmoid_rn(zz);
+        const float zz = ld(zp, t * D), s = sigmoid_acc(zz);
         g = dy * zz * s;
         gzv = dy * s * __builtin_fmaf(zz, 1.0f - s, 1.0f);
       }
@@ -870,44 +899,7 @@ __device__ __forceinline__ float rows_sum4(float v0, float v1, float v2, float v
 }
 
 // Per-(step, channel) terms of the N <= 16 backward: dt, the gated output
-// gradient g, dz's factor gz and sigmoid(x) for ddelta, formed as cbwd_main
-// does but in float: the double-rounded versions cost ~800 VALU slots per
-// (step, channel), a third of these kernels' work.  dt must not inherit the
-// transcendental unit's exp bias (with softplus_acc, dA of the
-// 2x2048x1024x16 backward erred by 1.3e-5 against 4.6e-6 with the double
-// version), so softplus_cw builds e^{-|x|} from its series; the sigmoids use
-// sigmoid_acc (measured no worse than double).
-// softplus(x) = max(x, 0) + log(1 + w), w = e^{-|x|}, in float without the
-// transcendental unit: w by Cody and Waite's reduction and the Taylor series
-// of e^r - 1 through r^8 (as in cexpm1_dt), log(1 + w) by its series through
-// w^9 for w <= e^-2 and log1p_pos above.
-__device__ __forceinline__ float softplus_cw(float x) {
-  float v = -__builtin_fabsf(x);
-  v = v < -110.0f ? -110.0f : v;                 // (e^v is 0 in float from -104 on)
-  const float k = __builtin_rintf(v * kInvLn2);
-  const float r = __builtin_fmaf(-k, kLn2Lo, __builtin_fmaf(-k, kLn2Hi, v));
-  float p = 1.0f / 40320.0f;
-  p = __builtin_fmaf(p, r, 1.0f / 5040.0f);
-  p = __builtin_fmaf(p, r, 1.0f / 720.0f);
-  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
-  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
-  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
-  p = __builtin_fmaf(p, r, 0.5f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  const float sc = __builtin_ldexpf(1.0f, (int)k);
-  const float w = __builtin_fmaf(p * r, sc, sc);
-  float q = 1.0f / 9.0f;
-  q = __builtin_fmaf(q, w, -1.0f / 8.0f);
-  q = __builtin_fmaf(q, w, 1.0f / 7.0f);
-  q = __builtin_fmaf(q, w, -1.0f / 6.0f);
-  q = __builtin_fmaf(q, w, 1.0f / 5.0f);
-  q = __builtin_fmaf(q, w, -1.0f / 4.0f);
-  q = __builtin_fmaf(q, w, 1.0f / 3.0f);
-  q = __builtin_fmaf(q, w, -0.5f);
-  q = __builtin_fmaf(q, w, 1.0f);
-  const float lp = w <= 0.1353352832366127f ? w * q : log1p_pos(w);
-  return __builtin_fmaxf(x, 0.0f) + lp;
-}
+// gradient g, dz's factor gz and sigmoid(x) for ddelta (as cbwd_main).
 struct CPrep { float dl, g, gz, sx; };
 __device__ __forceinline__ CPrep cprep(float x, float dy, float z, bool has_z, bool sp) {
   CPrep r;
