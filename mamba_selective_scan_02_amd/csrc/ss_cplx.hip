@@ -407,7 +407,11 @@ hipError_t launch_cfwd_t(const FwdArgs& a, hipStream_t s) {
 }
 
 template <typename T>
+hipError_t launch_cfwd_lanes(const FwdArgs& a, hipStream_t s);   // below
+
+template <typename T>
 hipError_t launch_cfwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s) {
+  if (gl == 16 && ns == 1) return launch_cfwd_lanes<T>(a, s);
   if (gl == 1) {
     switch (ns) {
       case 1: return launch_cfwd_t<T, 1, 1>(a, s);
@@ -1247,6 +1251,172 @@ __global__ __launch_bounds__(256, 3) void cbwd_lanes(const BwdArgs a) {
     a.part_dD[(b * a.KG + kg) * D + d0 + tid] = sD;
     a.part_db[(b * a.KG + kg) * D + d0 + tid] = sb;
   }
+}
+
+// Forward for 8 < N <= 16 in the lanes layout of cbwd_lanes: lane (c, n)
+// holds state n of channel c, 16 channels per workgroup, and a chunk runs in
+// tiles of 16 steps.  Per tile the prep threads (t, c) put dt, dt u, u and
+// the gate of step t in LDS, with (B, C) of (t, n); each lane runs the 16
+// steps.  FULL (every chunk, from h0 or its carried-in state) sums Re(C h)
+// over the row with the step-fed reduce-scatter and writes y through LDS;
+// SUMMARY (chunks k < K-1, from zero) accumulates the state and the decay
+// product minus 1 in double and writes the chunk record rounded once, as
+// cfwd does.
+template <typename Tio, bool FULL>
+__global__ __launch_bounds__(256) void cfwd_lanes(const FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float4 sBC[kLCL][16];        // (Br, Bi, Cr, Ci)
+  __shared__ __attribute__((aligned(16))) float4 xs[kLCPW][kLCL + 1];  // (dt, dt u, u, gate)
+  __shared__ float ob[kLCL][kLCPW + 1];                               // y of (t, c)
+  constexpr int ES = sizeof(Tio);
+  const int tid = threadIdx.x;
+  const int64_t nbd = (a.D + kLCPW - 1) / kLCPW;
+  const int64_t nk = FULL ? a.K : a.K - 1;
+  int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
+  const int64_t db = blk % nbd;
+  blk /= nbd;
+  const int64_t k = blk % nk;
+  const int64_t b = blk / nk;
+  const int64_t L = a.L, D = a.D, N = a.N, K = a.K;
+  const int pd = a.param_dtype;
+  const int64_t d0 = db * kLCPW;
+  // compute role: channel lc, state n; prep / output role: step pt, channel pc
+  const int lc = tid >> 4, n = tid & 15;
+  const int pt = tid >> 4, pc = tid & 15;
+  const bool l_active = d0 + lc < D, p_active = d0 + pc < D;
+  const int64_t ld_ = l_active ? d0 + lc : D - 1;
+  const int64_t pd_ = p_active ? d0 + pc : D - 1;
+  const bool has_z = a.z != nullptr, sp = a.softplus != 0;
+  const bool sn = n < N;
+  const float ar = sn ? ld_param(a.A, 2 * (ld_ * N + n), pd) : 0.0f;
+  const float ai = sn ? ld_param(a.A, 2 * (ld_ * N + n) + 1, pd) : 0.0f;
+  const float pbv = a.bias ? ld_param(a.bias, pd_, pd) : 0.0f;
+  const float lDv = a.Dskip ? ld_param(a.Dskip, ld_, pd) : 0.0f;
+  const int64_t t0 = k * a.chunk_len;
+  const int64_t t1 = (t0 + a.chunk_len < L) ? t0 + a.chunk_len : L;
+  const int ntile = (int)((t1 - t0 + kLCL - 1) / kLCL);
+
+  using ST = typename std::conditional<FULL, float, double>::type;
+  ST hr = 0.0f, hi = 0.0f;
+  double Pr = 0.0, Pi = 0.0;
+  if (FULL && sn) {
+    if (k > 0) {
+      const float* st = a.chunk_state + 4 * (((b * K + (k - 1)) * N + n) * D + ld_);
+      hr = st[0];
+      hi = st[1];
+    } else if (a.h0) {
+      hr = ld_param(a.h0, 2 * ((b * D + ld_) * N + n), pd);
+      hi = ld_param(a.h0, 2 * ((b * D + ld_) * N + n) + 1, pd);
+    }
+  }
+  const int voff_in = (int)(((int64_t)pt * D + pc) * ES);
+  const int voff_bc = (int)(((int64_t)pt * N + pc) * 2 * ES);
+  auto tile_rows = [&](int j) {
+    const int64_t ts = t0 + (int64_t)kLCL * j;
+    return (int)((ts + kLCL < t1 ? ts + kLCL : t1) - ts);
+  };
+  // raw inputs of tile j: step pt of channel pc, (B, C) of (step pt, state pc)
+  struct Raw { float u, x, z; float4 bc; };
+  auto load_raw = [&](int j) {
+    Raw r;
+    const int64_t ts = t0 + (int64_t)kLCL * j;
+    const int nt = tile_rows(j);
+    const int64_t row0 = (b * L + ts) * D + d0;
+    const int64_t avail = ((int64_t)nt * D - d0) * ES;
+    r.u = buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.u) + row0, avail), voff_in, 0);
+    r.x = buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.delta) + row0, avail), voff_in, 0);
+    r.z = (FULL && has_z)
+              ? buf_ld<Tio>(make_rsrc(static_cast<const Tio*>(a.z) + row0, avail), voff_in, 0)
+              : 0.0f;
+    r.bc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (pt < nt && pc < N) {
+      const int64_t bo = 2 * (b * L + ts) * N;
+      const int64_t bb = (int64_t)nt * N * 2 * ES;
+      const auto rB = make_rsrc(static_cast<const Tio*>(a.B) + bo, bb);
+      r.bc.x = buf_ld<Tio>(rB, voff_bc, 0);
+      r.bc.y = buf_ld<Tio>(rB, voff_bc + ES, 0);
+      if (FULL) {
+        const auto rC = make_rsrc(static_cast<const Tio*>(a.C) + bo, bb);
+        r.bc.z = buf_ld<Tio>(rC, voff_bc, 0);
+        r.bc.w = buf_ld<Tio>(rC, voff_bc + ES, 0);
+      }
+    }
+    return r;
+  };
+
+  Raw nx = load_raw(0);
+  for (int j = 0; j < ntile; ++j) {
+    const int64_t ts = t0 + (int64_t)kLCL * j;
+    const int nt = tile_rows(j);
+    const Raw cur = nx;
+    // prep of step pt of channel pc (tail channels and steps past the chunk
+    // take dt = 0: their states stay put)
+    const bool drive = pt < nt && p_active;
+    const float x = cur.x + pbv;
+    const float dt = sp ? softplus_cw(x) : x;
+    const float gate = (FULL && has_z) ? silu_gate(cur.z) : 1.0f;
+    xs[pc][pt] = make_float4(drive ? dt : 0.0f, drive ? dt * cur.u : 0.0f, cur.u, gate);
+    sBC[pt][pc] = cur.bc;
+    __syncthreads();                                  // (A) the tile's inputs are in LDS
+    if (j + 1 < ntile) nx = load_raw(j + 1);
+
+    RowScatter16 ro(n);
+#pragma unroll
+    for (int t = 0; t < kLCL; ++t) {
+      // (row pointers through an empty asm: a step's loads issue at most one
+      //  step early)
+      const float4* xrow = &xs[lc][0];
+      const float4* brow = &sBC[0][n];
+      __asm__ volatile("" : "+v"(xrow), "+v"(brow));
+      const float4 e = xrow[t];
+      const float4 bc = brow[16 * t];
+      float mr, mi;
+      cexpm1_dt(e.x, ar, ai, mr, mi);
+      if constexpr (FULL) {
+        cstep(mr, mi, e.y * bc.x, e.y * bc.y, hr, hi);
+        ro.up(t, __builtin_fmaf(bc.z, hr, -bc.w * hi));   // Re(C h)
+      } else {
+        const double dr = mr, di = mi;
+        cstep_d(dr, di, (double)e.y * bc.x, (double)e.y * bc.y, hr, hi);
+        cstep_d(dr, di, dr, di, Pr, Pi);               // (1 + P)(1 + m) - 1
+      }
+    }
+    if constexpr (FULL) {
+      const int tn = rev4(n);                          // the step whose sum this lane holds
+      const float4 e = xs[lc][tn];
+      ob[tn][lc] = __builtin_fmaf(lDv, e.z, ro.own) * e.w;   // (Re(C h) + D u) * gate
+    }
+    __syncthreads();                                  // (B) ob complete; xs, sBC free
+    if (FULL && drive) {
+      const int64_t row0 = (b * L + ts) * D + d0;
+      const int64_t bytes = ((int64_t)nt * D - d0) * ES;
+      buf_st<Tio>(ob[pt][pc], make_rsrc(static_cast<Tio*>(a.y) + row0, bytes), voff_in, 0);
+    }
+  }
+  if (!l_active || !sn) return;
+  if constexpr (!FULL) {
+    float* st = a.chunk_state + 4 * (((b * K + k) * N + n) * D + ld_);
+    *reinterpret_cast<float4*>(st) = make_float4((float)hr, (float)hi, (float)Pr, (float)Pi);
+  } else if (a.last_state && k == K - 1) {
+    st_param(a.last_state, 2 * ((b * D + ld_) * N + n), pd, hr);
+    st_param(a.last_state, 2 * ((b * D + ld_) * N + n) + 1, pd, hi);
+  }
+}
+
+template <typename T>
+hipError_t launch_cfwd_lanes(const FwdArgs& a, hipStream_t s) {
+  const int64_t nbd = (a.D + kLCPW - 1) / kLCPW;
+  hipError_t e;
+  if (a.K > 1) {
+    cfwd_lanes<T, false><<<dim3((unsigned)(a.Bn * (a.K - 1) * nbd)), dim3(256), 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.N > 0) {
+      const int64_t nc = (a.D + kCB - 1) / kCB;
+      cfwd_carry<<<dim3((unsigned)(a.Bn * a.N * nc)), dim3(kCB), 0, s>>>(a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  cfwd_lanes<T, true><<<dim3((unsigned)(a.Bn * a.K * nbd)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
 }
 
 // Fixed-order sum of `count` partials p[0], p[stride], ... (loads issued in

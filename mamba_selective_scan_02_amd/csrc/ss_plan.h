@@ -171,7 +171,8 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
 
 // Complex variant (A, B, C and the state complex, stored as (re, im) float
 // pairs).  Forward: G lanes per channel with NS complex states each
-// (NS * G >= N, NS <= 4 up to N = 64), 256 / G channels per workgroup, chunks chosen as
+// (NS * G >= N, NS <= 4 up to N = 64), 256 / G channels per workgroup; for
+// 8 < N <= 16 one lane per (channel, state) (G = 16, NS = 1); chunks chosen as
 // for the real scan.  Backward, N <= 16: one lane per (channel, state), 16
 // channels per workgroup, chunks of at most kCplxBwdLanesTile steps.  N > 16:
 // one lane per channel looping over the states, chunks of at most
@@ -193,9 +194,15 @@ inline Plan make_plan_complex(const ss_desc& d, bool backward) {
   if (N <= 4) {
     p.G = 1;
     p.NS = N <= 1 ? 1 : N <= 2 ? 2 : 4;
+  } else if (N <= 8) {
+    p.NS = 4;
+    p.G = 2;
+  } else if (N <= 16) {
+    p.NS = 1;           // one lane per (channel, state), 16 channels per workgroup
+    p.G = 16;
   } else if (N <= 64) {
     p.NS = 4;
-    p.G = N <= 8 ? 2 : N <= 16 ? 4 : N <= 32 ? 8 : 16;
+    p.G = N <= 32 ? 8 : 16;
   } else {
     p.G = 16;
     p.NS = N <= 128 ? 8 : 16;
