@@ -19,6 +19,7 @@
 #include "../../include/ss.h"
 #include "ss_device.h"
 #include "ss_plan.h"
+#include "ss_plan_complex.h"
 
 namespace ss {
 hipError_t launch_fwd(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_t s);

@@ -33,6 +33,7 @@
 
 #include "ss_device.h"
 #include "ss_plan.h"
+#include "ss_plan_complex.h"
 
 namespace ss {
 
