@@ -14,20 +14,24 @@
 //   du_t = dt sum_n Re(conj(B_t) lam_t) + D g_t,   dh0 = conj(a_0) lam_0
 // and gradients of complex inputs are returned as (dL/dRe, dL/dIm).
 //
-// Forward: G lanes per channel, each holding NS (at most 4 up to N = 64)
-// complex states in VGPRs; the per-step scalar work is repeated on the G
-// lanes; the readout is summed across them with lane shuffles.  Long sequences with few channels use the
-// same two-level chunked scan as the real path (summaries from zero, a carry
-// over chunks, then a final pass), except that a chunk's decay is the running
+// Forward: for 8 < N <= 16 one lane per (channel, state) (cfwd_lanes, the
+// layout of the N <= 16 backward below); otherwise G lanes per channel, each
+// holding NS (at most 4 up to N = 64) complex states in VGPRs, the per-step
+// scalar work repeated on the G lanes and the readout summed across them
+// with lane shuffles (cfwd).  Long sequences with few channels use the same
+// two-level chunked scan as the real path (summaries from zero, a carry over
+// chunks, then a final pass), except that a chunk's decay is the running
 // product of its steps' decays rather than exp(A * sum dt): for complex A the
 // closed form turns the rounding of sum dt into a phase error |Im A| times as
 // large, which over long chunks exceeds the sequential scan's own rounding.
 // The carry over chunks (forward and both backward chains) runs in double
 // and rounds each carried value to float once.
 // Backward: the same stages as the real general backward (summary, carry,
-// main, fixed-order finalizes) with one lane per channel, one state at a time,
-// 8-step chunks in registers, B / C of a chunk in LDS, and dB / dC summed over
-// the workgroup's 256 channels in LDS in a fixed order.  No atomics: every
+// main, fixed-order finalizes).  For N <= 16 one lane per (channel, state)
+// with 16-step chunks (cbwd_summary_lanes, cbwd_lanes); above, one lane per
+// channel looping over the states with 8-step chunks in registers, B / C of
+// a chunk in LDS and dB / dC summed over the workgroup's 256 channels in LDS
+// (cbwd_summary, cbwd_main).  Sums run in a fixed order, no atomics: every
 // output is bitwise reproducible.
 #include <type_traits>
 
