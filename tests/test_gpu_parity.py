@@ -855,6 +855,9 @@ COMPLEX_CASES = [  # (B, L, D, N, io): N covers every lanes-per-channel bucket
     (2, 90, 33, 17, "f32"), (1, 64, 20, 64, "f32"), (1, 40, 9, 130, "f32"),
     (1, 33, 7, 256, "f32"), (2, 120, 96, 16, "bf16"), (1, 77, 40, 8, "f16"),
     (1, 2048, 32, 16, "f32"),
+    # one lane per (channel, state) with idle lanes (N = 12), a tail channel
+    # block (D = 33) and partial 16-step tiles (L = 77)
+    (2, 77, 33, 12, "f16"), (1, 77, 33, 12, "f32"),
 ]
 
 
