@@ -5,7 +5,9 @@
 // N <= 32.  Mapping:
 //
 //   * 8 lanes own one channel d, all in one row of 16 lanes of the wave
-//     (tile_g / tile_channel), and lane g of the channel holds states
+//     (tile_g / tile_channel; fwd_wide's wide_g / wide_channel place them so
+//     that the readout's first two reduce stages are bank-masked DPP adds),
+//     and lane g of the channel holds states
 //     n = g*NS .. g*NS+NS-1 (NS = 1, 2 or 4).  A wave covers 8 channels, a
 //     256-lane workgroup 32.  This gives 8x the waves of one lane per
 //     channel, which the wave-per-SIMD issue rate needs (a lone wave issues
@@ -16,7 +18,8 @@
 //     the other 7 lanes of its channel through a per-wave LDS exchange.
 //   * The readout sum over a channel's states is a sum over its 8 lanes, done
 //     once per 8-step tile as a reduce-scatter through DPP moves within the
-//     row: lane g ends with the sum of step t0+g and applies the skip term
+//     row (the same pairs in both kernels, so their results agree bit for
+//     bit): lane g ends with the sum of step t0+g and applies the skip term
 //     and the gate to it.
 //   * The decays of each half tile issue as one run of exps (exp2_run).
 //   * B and C are staged per workgroup in LDS as f32, [n][t] per 64-step tile,
@@ -102,6 +105,52 @@ __device__ __forceinline__ float reduce_scatter8_dpp(const float (&o)[8], int g)
   }
   const float keep = b0 ? b[1] : b[0];
   const float send = b0 ? b[0] : b[1];
+  return keep + dpp<0xB1>(send);          // quad_perm [1,0,3,2]: lane l ^ 1
+}
+
+// Lane map of fwd_wide: wave lane l = 16 r + 8 q + 4 s + 2 c + p holds lane
+// g = 4 q + 2 s + p of channel c + 2 r.  The partners of the readout's first two
+// butterfly stages (g ^ 4 = l ^ 8, g ^ 2 = l ^ 4) then sit in other 4-lane
+// banks of the row, so each of those stages is two DPP adds per value that
+// write disjoint banks (bank_mask), with no selects; the last stage (g ^ 1 =
+// l ^ 1) is a quad permutation.
+__device__ __forceinline__ int wide_g(int tid) { return (tid & 1) | ((tid >> 1) & 6); }
+__device__ __forceinline__ int wide_channel(int tid) {
+  return ((tid >> 6) << 3) | ((tid >> 3) & 6) | ((tid >> 1) & 1);
+}
+
+// Reduce-scatter over a channel's 8 lanes (wide_g map): lane g holds o[0..7]
+// and ends with the channel's sum of o[g], summed in the same pairs as
+// reduce_scatter8_dpp.  Stage 1: lanes of banks 0-1 (g < 4) add the row_ror:8
+// partner's o[k] to theirs, banks 2-3 its o[4 + k]; stage 2: banks 0 and 2
+// take their partner 4 lanes up (row_ror:12: lane i reads lane i - 12 mod 16),
+// banks 1 and 3 the one 4 lanes down (row_ror:4).  The DPP adds are written
+// out (the compiler does not form bank-masked adds); s_nop 1 gives the two
+// wait states a DPP read of a VGPR written by the previous VALU op needs.
+// 12 DPP adds, 2 selects, 1 DPP add (21 VALU ops, 14 of them selects, before).
+__device__ __forceinline__ float reduce_scatter8_banked(const float (&o)[8], int g) {
+  float a0, a1, a2, a3, b0, b1;
+  __asm__ volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %6, %6 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %10, %10 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %7, %7 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %11, %11 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %2, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %2, %12, %12 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %3, %9, %9 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %3, %13, %13 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %4, %0, %0 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %4, %2, %2 row_ror:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %5, %1, %1 row_ror:12 row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %5, %3, %3 row_ror:4 row_mask:0xf bank_mask:0xa"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1)
+      : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "v"(o[5]), "v"(o[6]),
+        "v"(o[7]));
+  const bool b0sel = (g & 1) != 0;
+  const float keep = b0sel ? b1 : b0;
+  const float send = b0sel ? b0 : b1;
   return keep + dpp<0xB1>(send);          // quad_perm [1,0,3,2]: lane l ^ 1
 }
 
@@ -406,8 +455,8 @@ __global__ __launch_bounds__(kBlockT, (tile_waves_per_simd<NS, MODE>())) void fw
   __shared__ int vote[2][kBlockT / 64];                // FIXUP: per-wave "all states agree"
 
   const int tid = threadIdx.x;
-  const int g = tile_g(tid);
-  const int cl = tile_channel(tid);
+  const int g = wide_g(tid);
+  const int cl = wide_channel(tid);
   const int64_t nbd = (a.D + CPW - 1) / CPW;
   int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
   const int64_t db = blk % nbd;
@@ -611,7 +660,7 @@ __global__ __launch_bounds__(kBlockT, (tile_waves_per_simd<NS, MODE>())) void fw
         }
       }
       if constexpr (OUT) {
-        const float o_own = reduce_scatter8_dpp(ot, g);   // full readout of this lane's step
+        const float o_own = reduce_scatter8_banked(ot, g);   // full readout of this lane's step
         lds_put<T>(&sIn[1][(pt * GL + g) * RS + lds_own_col],
                    __builtin_fmaf(Dv, cur.uu, o_own) * cur.gate);
       }
@@ -652,9 +701,9 @@ __global__ __launch_bounds__(kBlockT, (tile_waves_per_simd<NS, MODE>())) void fw
   }
 
   if (SUMM) {                                       // the channel's sum over its 8 lanes
-    dsum += dpp<0x128>(dsum);
-    dsum += dpp<0x4E>(dsum);
-    dsum += dpp<0xB1>(dsum);
+    dsum += dpp<0x128>(dsum);   // row_ror:8: the pair g, g ^ 4
+    dsum += dpp<0x124>(dsum);   // row_ror:4: adds the other pair of the row half
+    dsum += dpp<0xB1>(dsum);    // quad_perm [1,0,3,2]: g ^ 1
   }
   if (!active) return;
   if (SUMM) {
