@@ -20,7 +20,7 @@ namespace ss {
 // the sum into a phase error of |Im A| times it.
 constexpr int kCplxBwdTile = 8;
 constexpr int kCplxBwdLanesTile = 16;
-constexpr int kCplxLanesCPW = 16;      // channels per workgroup of the N <= 16 backward
+constexpr int kCplxLanesCPW = 16;      // channels per workgroup of the lane-per-state kernels
 
 inline Plan make_plan_complex(const ss_desc& d, bool backward) {
   Plan p;
