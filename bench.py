@@ -400,6 +400,8 @@ def variant_legs(ss, w, dev, args_f, keys, steps, with_cpu=False):
 
 
 CONFIG_NAMES = ("tiny", "m130m", "m2p8b", "long", "bwd")
+# one GPU's share of an 8-way channel split of m2p8b and bwd (ss_inputs)
+SHARD_NAMES = ("m2p8b_d8", "bwd_d8")
 
 
 def rel_err(x, r) -> float:
@@ -540,9 +542,11 @@ def main():
                     help="skip the strided-B/C, packed-sequence and complex legs")
     ap.add_argument("--variants-only", action="store_true",
                     help="time only those legs (for a kernel trace of them alone)")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the per-GPU shard shapes (D / 8 of m2p8b and bwd)")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the per-workload warm / cold timings")
-    ap.add_argument("--configs-only", nargs="*", choices=CONFIG_NAMES, default=None,
+                    help="skip the per-workload warm / cold timings (and the shard shapes)")
+    ap.add_argument("--configs-only", nargs="*", choices=CONFIG_NAMES + SHARD_NAMES, default=None,
                     metavar="NAME",
                     help="only the per-workload timings (of the named workloads, default all)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -747,6 +751,16 @@ def main():
 
     if not args.no_configs:
         result["configs"] = configs_leg(ss, args.steps, with_oracle=not args.no_cpu_baseline)
+    if not args.no_configs and not args.no_shard:
+        # What one GPU of an 8-GPU node runs when the channels are split 8
+        # ways: the forward needs no communication there, so 8 x its rate is
+        # the node's forward rate on the full m2p8b problem; the backward adds
+        # one fixed-order sum of dB / dC over the GPUs (not measured here).
+        sh = configs_leg(ss, args.steps, SHARD_NAMES, with_oracle=not args.no_cpu_baseline)
+        for name, full in (("m2p8b_d8", "m2p8b"), ("bwd_d8", "bwd")):
+            sh[name]["share_of"] = f"{full} split 8 ways over D"
+            sh[name]["node_state_updates_per_s_8_gpus"] = 8 * sh[name]["state_updates_per_s_cold"]
+        result["shard"] = sh
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

@@ -16,6 +16,8 @@ m130m       4     1024  1536  16  f32     D skip, z, delta_bias, last_state
 m2p8b       8     2048  5120  16  bf16    D skip, z, delta_bias (A/D/bias f32)
 long        1   262144   512  16  f32     none
 bwd         2     2048  2048  16  f32     D skip, z, delta_bias, dy
+m2p8b_d8    8     2048   640  16  bf16    as m2p8b (one GPU's D / 8 share)
+bwd_d8      2     2048   256  16  f32     as bwd (one GPU's D / 8 share)
 =========  ==  =======  ====  ==  ======  ======================================
 
 Distributions (numpy ``Generator(PCG64(seed))``, f64 draws in C order, drawn in
@@ -79,6 +81,14 @@ WORKLOADS: Dict[str, Workload] = {
     "long": Workload("long", 1, 262144, 512, 16, seed=1004),
     "bwd": Workload("bwd", 2, 2048, 2048, 16, has_D=True, has_z=True,
                     has_bias=True, backward=True, seed=1005),
+    # one GPU's share of an 8-way split of the channels (D / 8): what a GPU of
+    # an 8-GPU node runs for m2p8b and bwd, where the forward needs no
+    # communication and the backward one sum of dB / dC
+    "m2p8b_d8": Workload("m2p8b_d8", 8, 2048, 640, 16, io_dtype="bf16",
+                         param_dtype="f32", has_D=True, has_z=True,
+                         has_bias=True, seed=1006),
+    "bwd_d8": Workload("bwd_d8", 2, 2048, 256, 16, has_D=True, has_z=True,
+                       has_bias=True, backward=True, seed=1007),
 }
 
 

@@ -247,6 +247,23 @@ def test_fwd_workloads_full(name):
     assert e_s <= max(tol, 1e-5), f"{name} last_state err {e_s:.3e}"
 
 
+def test_shard_shapes():
+    """One GPU's share of an 8-way channel split (D / 8) of the 2.8B forward
+    and of the backward workload, in the schedule the bench's shard leg times:
+    every output against the float64 oracle."""
+    w = WORKLOADS["m2p8b_d8"]
+    inp = make_inputs(w)
+    say("workload m2p8b_d8")
+    y, ls = _run_fwd(inp)
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True)
+    tol = TOL[inp["u"].dtype]
+    assert rel_err(to_np(y), yr) <= tol
+    assert rel_err(to_np(ls), lsr) <= max(tol, 1e-5)
+    say("workload bwd_d8")
+    errs = _check_bwd(make_inputs(WORKLOADS["bwd_d8"]), label="bwd_d8 workload")
+    say("bwd_d8 errors", errs)
+
+
 def test_fwd_deterministic():
     w = WORKLOADS["m2p8b"]
     inp = to_dev(make_inputs(w))
