@@ -952,6 +952,30 @@ def test_complex_random_shapes(seed):
         assert e <= tol, f"{k}: {e:.3e}"
 
 
+@pytest.mark.parametrize("chunk", [0, 1, 5, 16, 17])
+def test_complex_lanes_edges(chunk):
+    """The lane-per-state kernels (8 < N <= 16 forward, N <= 16 backward) on
+    a single partial channel block (D = 5), N = 9 (7 idle lanes per row),
+    sequences of 19 steps (a partial 16-step tile) and forced chunks of 1 to
+    17 steps, with h0: forward and backward against the oracle."""
+    Bn, L, D, N = 3, 19, 5, 9
+    inp, h0 = _complex_inputs(Bn, L, D, N, seed=7301 + chunk, backward=True)
+    d = to_dev(inp)
+    say("complex lanes edges, chunk", chunk)
+    y, ls = ss.fwd_complex(*[d[k] for k in KEYS], h0=h0.to(DEV), return_last_state=True,
+                           chunk_len=chunk)
+    g = ss.bwd_complex(*[d[k] for k in KEYS], dy=d["dy"], chunk_len=chunk, h0=h0.to(DEV))
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd_complex(**{k: inp[k] for k in KEYS}, h0=h0)
+    r = oracle.bwd_complex(**{k: inp[k] for k in KEYS}, dy=inp["dy"], h0=h0)
+    assert rel_err(to_np(y), yr) <= 1e-5
+    assert rel_err(to_np(ls), lsr) <= 1e-5
+    for k in GRADS + ("dh0",):
+        if r[k] is not None:
+            e = rel_err(to_np(g[k]), r[k])
+            assert e <= 1e-5, f"{k} chunk {chunk}: {e:.3e}"
+
+
 def test_complex_extreme_inputs():
     """The complex decay's edge branches: dt up to 30 with Im A up to ~1e4
     (angles dt Im A past 4096 take the double-precision reduction), Re A at
