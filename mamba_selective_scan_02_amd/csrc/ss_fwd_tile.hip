@@ -2,13 +2,12 @@
 //
 // Same recurrence as ss_fwd_scan.h (baracuda-kernels page
 // "src/attention/selective_scan.rs", module docs, "Algorithm summary"), for
-// N <= 32.  Mapping:
+// N <= 64.  Mapping:
 //
 //   * 8 lanes own one channel d, all in one row of 16 lanes of the wave
-//     (tile_g / tile_channel; fwd_wide's wide_g / wide_channel place them so
-//     that the readout's first two reduce stages are bank-masked DPP adds),
-//     and lane g of the channel holds states
-//     n = g*NS .. g*NS+NS-1 (NS = 1, 2 or 4).  A wave covers 8 channels, a
+//     (wide_g / wide_channel: placed so that the readout's first two reduce
+//     stages are bank-masked DPP adds), and lane g of the channel holds states
+//     n = g*NS .. g*NS+NS-1 (NS = 1, 2, 4 or 8).  A wave covers 8 channels, a
 //     256-lane workgroup 32.  This gives 8x the waves of one lane per
 //     channel, which the wave-per-SIMD issue rate needs (a lone wave issues
 //     far below the VALU rate; several resident waves per SIMD are needed).
@@ -18,7 +17,7 @@
 //     the other 7 lanes of its channel through a per-wave LDS exchange.
 //   * The readout sum over a channel's states is a sum over its 8 lanes, done
 //     once per 8-step tile as a reduce-scatter through DPP moves within the
-//     row (the same pairs in both kernels, so their results agree bit for
+//     row (the same code in both kernels, so their results agree bit for
 //     bit): lane g ends with the sum of step t0+g and applies the skip term
 //     and the gate to it.
 //   * The decays of each half tile issue as one run of exps (exp2_run).
@@ -73,43 +72,9 @@ constexpr int tile_waves_per_simd() {
   return NS <= 2 ? (MODE == TMODE_FIXUP ? 4 : 5) : NS <= 4 ? 3 : 2;
 }
 
-// Lane map of the forward tile kernels: a channel's 8 lanes lie in one row of 16 lanes, so
-// that every stage of the readout's reduce-scatter is a DPP move within the
-// row.  Wave lane l = 16 r + 8 q + 4 s + p holds lane g = 4 q + p of channel
-// c = 2 r + s (of the wave's 8).  Butterfly partners: g ^ 4 is lane l ^ 8
-// (row rotation by 8), g ^ 2 is l ^ 2 and g ^ 1 is l ^ 1 (quad permutations).
-__device__ __forceinline__ int tile_g(int tid) { return (tid & 3) | ((tid >> 1) & 4); }
-__device__ __forceinline__ int tile_channel(int tid) {
-  return ((tid >> 6) << 3) | ((tid >> 2) & 1) | ((tid >> 3) & 6);
-}
-
-// Reduce-scatter over a channel's 8 lanes (this lane map): lane g holds o[0..7]
-// and ends with the channel's sum of o[g].  Each stage keeps half of the
-// values (chosen by one bit of g) and adds the partner's matching half, sent
-// through DPP: 14 selects and 7 DPP adds, no lane swaps (a v_permlane*_swap
-// costs the SIMD about as much as two DPP adds: measured).
-__device__ __forceinline__ float reduce_scatter8_dpp(const float (&o)[8], int g) {
-  const bool hi = (g & 4) != 0, b1 = (g & 2) != 0, b0 = (g & 1) != 0;
-  float a[4], b[2];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float keep = hi ? o[4 + k] : o[k];
-    const float send = hi ? o[k] : o[4 + k];
-    a[k] = keep + dpp<0x128>(send);       // row_ror:8: lane l ^ 8
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float keep = b1 ? a[2 + k] : a[k];
-    const float send = b1 ? a[k] : a[2 + k];
-    b[k] = keep + dpp<0x4E>(send);        // quad_perm [2,3,0,1]: lane l ^ 2
-  }
-  const float keep = b0 ? b[1] : b[0];
-  const float send = b0 ? b[0] : b[1];
-  return keep + dpp<0xB1>(send);          // quad_perm [1,0,3,2]: lane l ^ 1
-}
-
-// Lane map of fwd_wide: wave lane l = 16 r + 8 q + 4 s + 2 c + p holds lane
-// g = 4 q + 2 s + p of channel c + 2 r.  The partners of the readout's first two
+// Lane map of the forward tile kernels: a channel's 8 lanes lie in one row of
+// 16 lanes, wave lane l = 16 r + 8 q + 4 s + 2 c + p holding lane
+// g = 4 q + 2 s + p of channel c + 2 r (of the wave's 8).  The partners of the readout's first two
 // butterfly stages (g ^ 4 = l ^ 8, g ^ 2 = l ^ 4) then sit in other 4-lane
 // banks of the row, so each of those stages is two DPP adds per value that
 // write disjoint banks (bank_mask), with no selects; the last stage (g ^ 1 =
@@ -120,14 +85,15 @@ __device__ __forceinline__ int wide_channel(int tid) {
 }
 
 // Reduce-scatter over a channel's 8 lanes (wide_g map): lane g holds o[0..7]
-// and ends with the channel's sum of o[g], summed in the same pairs as
-// reduce_scatter8_dpp.  Stage 1: lanes of banks 0-1 (g < 4) add the row_ror:8
+// and ends with the channel's sum of o[g]; stage s adds partners g ^ 4, g ^ 2,
+// g ^ 1 (a lane keeps the half of its values picked by that bit of g).  Stage 1: lanes of banks 0-1 (g < 4) add the row_ror:8
 // partner's o[k] to theirs, banks 2-3 its o[4 + k]; stage 2: banks 0 and 2
 // take their partner 4 lanes up (row_ror:12: lane i reads lane i - 12 mod 16),
 // banks 1 and 3 the one 4 lanes down (row_ror:4).  The DPP adds are written
 // out (the compiler does not form bank-masked adds); s_nop 1 gives the two
 // wait states a DPP read of a VGPR written by the previous VALU op needs.
-// 12 DPP adds, 2 selects, 1 DPP add (21 VALU ops, 14 of them selects, before).
+// 12 DPP adds, 2 selects, 1 DPP add (a select-based version: 14 selects and
+// 7 DPP adds).
 __device__ __forceinline__ float reduce_scatter8_banked(const float (&o)[8], int g) {
   float a0, a1, a2, a3, b0, b1;
   __asm__ volatile(
@@ -167,8 +133,8 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
   __shared__ __attribute__((aligned(16))) float2 xch[2][CPW][XS];
 
   const int tid = threadIdx.x;
-  const int g = tile_g(tid);
-  const int cl = tile_channel(tid);
+  const int g = wide_g(tid);
+  const int cl = wide_channel(tid);
   const int64_t nbd = (a.D + CPW - 1) / CPW;
   int64_t blk = xcd_pair_remap(blockIdx.x, gridDim.x);
   const int64_t db = blk % nbd;
@@ -355,7 +321,7 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
         }
       }
       if (MODE == TMODE_FULL) {
-        const float o_own = reduce_scatter8_dpp(ot, g);   // full readout of step t0 + p*8 + g
+        const float o_own = reduce_scatter8_banked(ot, g);   // full readout of step t0 + p*8 + g
         const float yv = __builtin_fmaf(Dv, cur.uu, o_own) * cur.gate;
         // tail lanes (d >= D) store channel D-1's value to channel D-1's
         // address; steps past the chunk fall outside the buffer and are dropped
@@ -368,9 +334,9 @@ __global__ __launch_bounds__(kBlockT, tile_waves_per_simd<NS>()) void fwd_tile(c
   }
 
   if (MODE == TMODE_SUMMARY) {                     // the channel's sum over its 8 lanes
-    dsum += dpp<0x128>(dsum);
-    dsum += dpp<0x4E>(dsum);
-    dsum += dpp<0xB1>(dsum);
+    dsum += dpp<0x128>(dsum);   // row_ror:8: the pair g, g ^ 4
+    dsum += dpp<0x124>(dsum);   // row_ror:4: adds the other pair of the row half
+    dsum += dpp<0xB1>(dsum);    // quad_perm [1,0,3,2]: g ^ 1
   }
   if (!active) return;
   if (MODE == TMODE_SUMMARY) {
