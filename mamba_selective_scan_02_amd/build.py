@@ -18,9 +18,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libss.so")
-SOURCES = ["ss_api.cpp", "ss_fwd.hip", "ss_fwd_scan_f32.hip", "ss_fwd_scan_f16.hip",
-           "ss_fwd_scan_bf16.hip", "ss_fwd_tile.hip", "ss_bwd.hip", "ss_bwd_tile.hip",
-           "ss_cplx.hip"]
+# (source, object name, extra flags): ss_fwd_scan.hip is compiled once per I/O
+# type so that its instantiations build in parallel.
+SOURCES = [("ss_api.cpp", "ss_api", []), ("ss_fwd.hip", "ss_fwd", []),
+           ("ss_fwd_scan.hip", "ss_fwd_scan_f32", ["-DSS_SCAN_IO=0"]),
+           ("ss_fwd_scan.hip", "ss_fwd_scan_f16", ["-DSS_SCAN_IO=1"]),
+           ("ss_fwd_scan.hip", "ss_fwd_scan_bf16", ["-DSS_SCAN_IO=2"]),
+           ("ss_fwd_tile.hip", "ss_fwd_tile", []), ("ss_bwd.hip", "ss_bwd", []),
+           ("ss_bwd_tile.hip", "ss_bwd_tile", []), ("ss_cplx.hip", "ss_cplx", [])]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed FP32 instructions are disabled: the compiler would otherwise form
@@ -31,10 +36,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-I" + os.path.join(ROOT, "include")]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(entry, verbose: bool) -> str:
+    src, name, flags = entry
+    obj = os.path.join(BUILD, name + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

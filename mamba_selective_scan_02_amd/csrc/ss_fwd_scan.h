@@ -1,20 +1,20 @@
-// The general forward scan kernel (N > 32), shared by the per-dtype sources
-// ss_fwd_scan_{f32,f16,bf16}.hip so that its many instantiations compile in
-// parallel.
+// The general forward scan kernel (N > 64; N <= 64 runs the 8-lane tile
+// kernels of ss_fwd_tile.hip).  ss_fwd_scan.hip instantiates it, one I/O type
+// per object.
 //
 // Recurrence: baracuda-kernels page "src/attention/selective_scan.rs", module
 // docs, "Algorithm summary".  Per channel (b, d) and state n:
 //   dt = softplus(delta + bias) (or delta + bias), a = exp(dt * A[d,n]),
 //   h = a * h + dt * B[b,t,n] * u[b,t,d], y = (sum_n C[b,t,n] h + D u) * silu(z).
 //
-// Mapping.  One lane owns one channel d of one batch row b (or, for N > 64,
-// G = 2 or 4 consecutive lanes share a channel, each holding 64 states).  A
-// workgroup is 256 lanes = 256 / G consecutive channels, so loads and stores of
-// u / delta / z / y are coalesced along D.  The lane keeps its states h[n] and
-// its row of A (pre-scaled by log2 e) in VGPRs.  B[b,t,:] and C[b,t,:] are
-// the same for every lane of the workgroup: with G = 1 their addresses are
-// wave-uniform, so they are fetched with scalar loads into SGPRs and used
-// directly as VALU operands.
+// Mapping.  G = 2 (N <= 128) or 4 consecutive lanes share a channel d of one
+// batch row b, lane g holding states 64 g .. 64 g + 63.  A workgroup is 256
+// lanes = 256 / G consecutive channels, so loads and stores of u / delta / z /
+// y are coalesced along D.  The lane keeps its states h[n] and its row of A
+// (pre-scaled by log2 e) in VGPRs.  B[b,t,:] and C[b,t,:] are the same for
+// every channel of the workgroup: a wave reads G distinct 64-state pieces of
+// each row per step (a single wave-uniform address, fetched into SGPRs, when
+// G = 1).
 //
 // Time is walked sequentially inside a chunk.  When B * D alone cannot fill the
 // GPU, L is cut into K chunks and the scan runs in two levels:
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void fwd_scan(const T* __restrict__ u_in,
   const T* Bp = B_in + sr.start * ldb + n0;
   const T* Cp = C_in + sr.start * ldc + n0;
 
-  // B / C rows, software-pipelined one step ahead (wave-uniform: SGPRs).
+  // B / C rows, software-pipelined one step ahead.
   // EXACT rows are prefetched as raw 32-bit words and converted at their use
   // one step later: a conversion right after the load would make the wave wait
   // for the load immediately (scalar-load waits cannot be partial).
@@ -238,33 +238,6 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   fwd_scan<T, NS, G, EXACT, MODE_FULL, HAS_Z><<<dim3((unsigned)grid), dim3(kBlock), 0, s>>>(
       U, DL, Bm, Cm, Z, Y, a);
   return hipGetLastError();
-}
-
-// EXACT (N fills the bucket) reads whole B / C rows; for 16-bit types that
-// needs 4-byte aligned rows: 4-byte aligned B and C and even row strides.
-template <typename T, int NS, int G>
-static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t s) {
-  const bool rows_ok = sizeof(T) == 4 || ((reinterpret_cast<uintptr_t>(a.B) % 4 == 0) &&
-                                          (reinterpret_cast<uintptr_t>(a.C) % 4 == 0) &&
-                                          a.ldb % 2 == 0 && a.ldc % 2 == 0);
-  const bool exact = a.N == (int64_t)NS * G && rows_ok;
-  if (a.z != nullptr)
-    return exact ? launch_fwd_t<T, NS, G, true, true>(a, s) : launch_fwd_t<T, NS, G, false, true>(a, s);
-  return exact ? launch_fwd_t<T, NS, G, true, false>(a, s) : launch_fwd_t<T, NS, G, false, false>(a, s);
-}
-
-// One lane per channel (G = 1) or G = 2, 4 lanes per channel, 64 states per
-// lane: the path for N > 32 (N <= 32 uses the 8-lane tile kernel).
-template <typename T>
-static hipError_t launch_fwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s) {
-  if (ns == 64 && gl == 1) {
-    return launch_fwd_e<T, 64, 1>(a, s);
-  } else if (ns == 64 && gl == 2) {
-    return launch_fwd_e<T, 64, 2>(a, s);
-  } else if (ns == 64 && gl == 4) {
-    return launch_fwd_e<T, 64, 4>(a, s);
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace ss
