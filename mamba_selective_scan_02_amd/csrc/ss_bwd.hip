@@ -132,14 +132,15 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_summary(const BwdArgs a
 
 // ------------------------------------------------------------------ carry
 
-// Thread per (chain, b, n, d), d fastest: the forward chain over k = 0 .. K-2
-// (fstate slot k becomes the state entering chunk k+1) and the reverse chain
-// over k = K-1 .. 1 (bstate slot k becomes the adjoint at the end of chunk
-// k-1) run in separate threads.  Each loads the summaries and dt sums of KB
-// chunks, computes their decays (independent of the chain), then runs the
-// chain through them.
+// One chain per (direction, b, n, d), G lanes each (carry_chain's in-wave
+// scan), 256 / G chains (consecutive d) per workgroup: the forward chain over
+// k = 0 .. K-2 (fstate slot k becomes the state entering chunk k+1) and the
+// reverse chain over k = K-1 .. 1 (bstate slot k becomes the adjoint at the
+// end of chunk k-1, c_{k-1} = P_k c_k + Sb_k).
+template <int G>
 __global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) {
-  const int64_t nbd = a.nwgd;
+  constexpr int CPB = kChannelsPerBlock / G;
+  const int64_t nbd = (a.D + CPB - 1) / CPB;
   int64_t blk = blockIdx.x;
   const int64_t db = blk % nbd;
   blk /= nbd;
@@ -147,37 +148,13 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_carry(const BwdArgs a) 
   blk /= a.N;
   const int64_t b = blk % a.Bn;
   const bool reverse = blk / a.Bn != 0;
-  const int64_t d = db * kChannelsPerBlock + threadIdx.x;
-  if (d >= a.D) return;
+  const int64_t d = db * CPB + threadIdx.x / G;
+  if (d >= a.D) return;                      // the chain's lanes leave together
   const int64_t D = a.D, N = a.N, K = a.K;
   const float Av = ld_param(a.A, d * N + n, a.param_dtype);
-  // the forward chain walks slots 0, 1, .. of fstate, the reverse chain slots
-  // K-1, K-2, .. of bstate: step j touches slot kj = j or K-1-j
   float* st = (reverse ? a.bstate : a.fstate) + (b * K * N + n) * D + d;   // + k * N * D
-  const float* ds = a.dsum + b * K * D + d;                                // + k * D
-  // the chain runs in double; each carried value is rounded to float once
-  double c = (!reverse && a.h0) ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0;
-  constexpr int KB = 16;
-  for (int64_t j0 = 0; j0 < K - 1; j0 += KB) {
-    float sv[KB], dv[KB];
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int64_t jj = (j0 + j < K - 1) ? j0 + j : K - 2;
-      const int64_t kj = reverse ? K - 1 - jj : jj;
-      sv[j] = st[kj * N * D];
-      dv[j] = ds[kj * D];
-    }
-    double pv[KB];
-#pragma unroll
-    for (int j = 0; j < KB; ++j) pv[j] = chunk_decay(Av, dv[j]);
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      if (j0 + j < K - 1) {
-        c = __builtin_fma(pv[j], c, static_cast<double>(sv[j]));
-        st[(reverse ? K - 1 - (j0 + j) : j0 + j) * N * D] = static_cast<float>(c);
-      }
-    }
-  }
+  const double c0 = (!reverse && a.h0) ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0;
+  carry_chain<G>(st, N * D, a.dsum + b * K * D + d, D, Av, c0, K - 1, K, reverse);
 }
 
 // ------------------------------------------------------------------- main
@@ -449,10 +426,14 @@ static hipError_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
 
 hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t s) {
   if (a.K <= 1 || a.N <= 0) return hipSuccess;
-  const int64_t nbd = (a.D + kChannelsPerBlock - 1) / kChannelsPerBlock;
-  BwdArgs c = a;
-  c.nwgd = nbd;  // the carry's own channel blocking (256 per workgroup)
-  bwd_carry<<<dim3((unsigned)(2 * a.Bn * a.N * nbd)), dim3(kChannelsPerBlock), 0, s>>>(c);
+  const int G = carry_lanes(a.K - 1);
+  const int64_t nbd = (a.D + kChannelsPerBlock / G - 1) / (kChannelsPerBlock / G);
+  const dim3 grid((unsigned)(2 * a.Bn * a.N * nbd)), block(kChannelsPerBlock);
+  switch (G) {
+    case 1: bwd_carry<1><<<grid, block, 0, s>>>(a); break;
+    case 4: bwd_carry<4><<<grid, block, 0, s>>>(a); break;
+    default: bwd_carry<8><<<grid, block, 0, s>>>(a); break;
+  }
   return hipGetLastError();
 }
 

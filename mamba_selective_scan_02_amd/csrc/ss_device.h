@@ -183,6 +183,125 @@ __device__ __forceinline__ double chunk_decay(float A, float dsum) {
   return exp_dbl(static_cast<double>(A) * static_cast<double>(dsum));
 }
 
+// ------------------------------------------------------------ chunk carries
+//
+// The carries across chunks fold, per chain, c_j = P_j c_{j-1} + S_j over the
+// chunk records j = 0 .. M-1 from c_{-1} = c0 (the recurrence of the
+// baracuda-kernels page "src/attention/selective_scan.rs", "Algorithm
+// summary", applied to whole chunks: a chunk maps the state entering it to
+// P h + S, P the product of its decays, S its end state from zero).  Maps of
+// this form compose associatively: (P1, S1) then (P2, S2) is
+// (P1 P2, P2 S1 + S2).  A chain takes G = 1, 2, 4 or 8 neighbouring lanes of
+// a wave; lane g owns a run of consecutive records and
+//   1. folds its run from zero into one pair (P_g, S_g),
+//   2. scans the G pairs in the wave (DPP row shifts by 1, 2 and 4 lanes; a
+//      lane combines only with lanes of its own chain), which gives every
+//      lane the composition of the runs before its own,
+//   3. applies that to c0 and walks its run again, writing every c_j.
+// Everything runs in double and each written value is rounded to float once.
+// The scan pays where it shortens the chain of dependent steps, from
+// M to about 2 M / G: chains of at most 2 RUN records keep one lane (G = 1:
+// step 3 alone, in rounds of RUN records whose loads are issued together),
+// longer ones take G = 4 up to 4 RUN records and 8 above; chains longer than
+// 8 RUN records take several rounds, each starting from the previous round's
+// last value.  A run's loads are unconditional (past the chain's end they
+// re-read its last record), so that they all stay in flight together.
+// Measured on the long sequence (K = 128 chunks of 2048 steps): 24 us with one
+// lane per chain, 9 us with 8; on the backward workload's 32 chunks two lanes
+// per chain were slower than one (18 against 14 us).
+constexpr int kCarryRun = 16;    // records per lane and round, at most
+
+// Lanes per chain for a chain of M records.
+inline int carry_lanes(int64_t M) {
+  return M <= 2 * kCarryRun ? 1 : M <= 4 * kCarryRun ? 4 : 8;
+}
+
+// v of the lane CTRL's row shift names (row_shr:k reads lane i - k of the same
+// row of 16); lanes whose source lies outside the row read 0.
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf,
+                                                            true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL,
+                                                            0xf, 0xf, true);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114;
+
+// Records per lane and round for a chain of M records over G lanes.
+template <int G, int RUN>
+__device__ __forceinline__ int carry_run(int64_t M) {
+  const int64_t q = (M + G - 1) / G;
+  return (int)(q < RUN ? q : RUN);
+}
+
+// One real chain over G lanes (all lanes of the chain call it together; lane
+// g = threadIdx.x % G).  Record j lives in slot kj = (rev ? K-1-j : j): its
+// end state from zero at st[kj * ss] (overwritten with c_j) and its dt sum at
+// ds[kj * dss]; P_j = exp(A * dt sum).
+template <int G>
+__device__ __forceinline__ void carry_chain(float* st, int64_t ss, const float* ds, int64_t dss,
+                                            float A, double c0, int64_t M, int64_t K, bool rev) {
+  constexpr int RUN = kCarryRun;
+  const int g = (int)(threadIdx.x & (G - 1));
+  const int run = carry_run<G, RUN>(M);       // uniform
+  for (int64_t r0 = 0; r0 < M; r0 += (int64_t)G * run) {
+    const int64_t j0 = r0 + (int64_t)g * run;
+    const int cnt = (int)(M - j0 <= 0 ? 0 : (M - j0 < run ? M - j0 : run));
+    float sv[RUN], dv[RUN];
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+      const int64_t j = j0 + i < M ? j0 + i : M - 1;
+      const int64_t kj = rev ? K - 1 - j : j;
+      sv[i] = st[kj * ss];
+      dv[i] = ds[kj * dss];
+    }
+    double pv[RUN];
+#pragma unroll
+    for (int i = 0; i < RUN; ++i)
+      if (i < run) pv[i] = chunk_decay(A, dv[i]);
+    double c = c0;
+    if constexpr (G > 1) {
+      double P = 1.0, S = 0.0;   // this lane's run from zero
+#pragma unroll
+      for (int i = 0; i < RUN; ++i) {
+        if (i < run) {
+          const bool in = i < cnt;
+          S = in ? __builtin_fma(pv[i], S, static_cast<double>(sv[i])) : S;
+          P = in ? P * pv[i] : P;
+        }
+      }
+      // inclusive scan over the chain's lanes: (P, S) of runs 0 .. g
+      {
+        const double Pp = dpp_d<kRowShr1>(P), Sp = dpp_d<kRowShr1>(S);
+        if (g >= 1) { S = __builtin_fma(P, Sp, S); P *= Pp; }
+      }
+      if constexpr (G > 2) {
+        const double Pp = dpp_d<kRowShr2>(P), Sp = dpp_d<kRowShr2>(S);
+        if (g >= 2) { S = __builtin_fma(P, Sp, S); P *= Pp; }
+      }
+      if constexpr (G > 4) {
+        const double Pp = dpp_d<kRowShr4>(P), Sp = dpp_d<kRowShr4>(S);
+        if (g >= 4) { S = __builtin_fma(P, Sp, S); P *= Pp; }
+      }
+      // runs 0 .. g-1 applied to c0, then this lane's run
+      const double Pe = dpp_d<kRowShr1>(P), Se = dpp_d<kRowShr1>(S);
+      if (g >= 1) c = __builtin_fma(Pe, c0, Se);
+    }
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+      if (i < cnt) {
+        c = __builtin_fma(pv[i], c, static_cast<double>(sv[i]));
+        st[(rev ? K - 1 - (j0 + i) : j0 + i) * ss] = static_cast<float>(c);
+      }
+    }
+    // the round's last value (the last lane ends there also when its run is empty)
+    if constexpr (G > 1) c0 = __shfl(c, G - 1, G);
+    else c0 = c;
+  }
+}
+
 // sigmoid(x) = 1 / (1 + e^{-x}); exp overflow gives rcp(inf) = 0.
 __device__ __forceinline__ float sigmoid(float x) {
   return fast_rcp(1.0f + fast_exp2(-x * kLog2e));

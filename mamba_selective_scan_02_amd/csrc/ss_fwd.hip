@@ -5,81 +5,60 @@
 //   dt = softplus(delta + bias) (or delta + bias), a = exp(dt * A[d,n]),
 //   h = a * h + dt * B[b,t,n] * u[b,t,d], y = (sum_n C[b,t,n] h + D u) * silu(z).
 //
-// Mapping.  One lane owns one channel d of one batch row b (or, for N > 64,
-// G = 2 or 4 consecutive lanes share a channel, each holding 64 states).  A
-// workgroup is 256 lanes = 256 / G consecutive channels, so loads and stores of
-// u / delta / z / y are coalesced along D.  The lane keeps its states h[n] and
-// its row of A (pre-scaled by log2 e) in VGPRs.  B[b,t,:] and C[b,t,:] are
-// the same for every lane of the workgroup: with G = 1 their addresses are
-// wave-uniform, so they are fetched with scalar loads into SGPRs and used
-// directly as VALU operands.
+// This file holds the carry across chunks (fwd_carry), the short-sequence
+// (decode-step) kernel fwd_short, and the dispatch over the forward kernels:
+// fwd_short for L <= 16, the tile kernels of ss_fwd_tile.hip for N <= 64, the
+// general scan of ss_fwd_scan.h for N > 64.
 //
-// Time is walked sequentially inside a chunk.  When B * D alone cannot fill the
-// GPU, L is cut into K chunks and the scan runs in two levels:
-//   1. fwd_scan<SUMMARY>: every chunk but the last runs from h = 0 and writes
-//      its end state S_k[n] and sum_k = sum of dt over the chunk;
-//   2. fwd_carry: per (b, d, n), h_in(k+1) = exp(A * sum_k) * h_in(k) + S_k,
-//      the decay and the chain in double precision (chunk_decay), each
-//      carried state rounded to float once,
-//      the composition (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) of the chunk
-//      summaries, folded over k (the product of a chunk's decays is
-//      exp(A * sum of its dt) in closed form);
-//   3. fwd_scan<FULL>: every chunk runs again from its carried-in state and
-//      writes y (and last_state for the final chunk).
-// With K = 1 only step 3 runs, from h = 0.
+// When B * D alone cannot fill the GPU, L is cut into K chunks and the scan
+// runs in two levels: a first pass writes every chunk's end state from zero
+// S_k and its sum of dt; fwd_carry turns them into the state entering each
+// chunk, h_in(k+1) = exp(A * sum_k) h_in(k) + S_k (the product of a chunk's
+// decays is exp(A * sum of its dt) in closed form); a second pass runs each
+// chunk from its carried-in state.  With K = 1 only the second pass runs.
 #include "ss_fwd_scan.h"
 
 namespace ss {
 
-// Carry across chunks.  Thread per (b, n, d), d fastest.  Slot k of
-// chunk_state holds S_k on entry and h_in(k+1) = state entering chunk k+1 on
-// exit (k = 0 .. K-2; the last chunk's summary is never produced or used).
-// The loads of a batch of KB chunks are issued before the dependent chain.
+// Carry across chunks, one chain per (b, n, d): slot k of chunk_state holds
+// S_k on entry and h_in(k+1) = state entering chunk k+1 on exit (k = 0 ..
+// K-2; the last chunk's summary is never produced or used).  G lanes per
+// chain (carry_chain's in-wave scan), 256 / G chains (consecutive d) per
+// workgroup.
+template <int G>
 __global__ __launch_bounds__(kBlock) void fwd_carry(const FwdArgs a) {
-  const int64_t nbd = (a.D + kBlock - 1) / kBlock;
+  constexpr int CPB = kBlock / G;
+  const int64_t nbd = (a.D + CPB - 1) / CPB;
   int64_t blk = blockIdx.x;
   const int64_t db = blk % nbd;
   blk /= nbd;
   const int64_t n = blk % a.N;
   const int64_t b = blk / a.N;
-  const int64_t d = db * kBlock + threadIdx.x;
-  if (d >= a.D) return;
+  const int64_t d = db * CPB + threadIdx.x / G;
+  if (d >= a.D) return;                      // the chain's lanes leave together
   const int64_t D = a.D, N = a.N, K = a.K;
   const float Av = ld_param(a.A, d * N + n, a.param_dtype);
-  float* __restrict__ st = a.chunk_state + (b * K * N + n) * D + d;  // + k * N * D
-  const float* __restrict__ ds = a.chunk_dsum + b * K * D + d;       // + k * D
-  // the chain runs in double; each carried state is rounded to float once
-  double hc = a.h0 ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0;  // h_in(0)
-  constexpr int KB = 16;
-  for (int64_t k0 = 0; k0 < K - 1; k0 += KB) {
-    float sv[KB], dv[KB];
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int64_t kk = (k0 + j < K - 1) ? k0 + j : K - 2;
-      sv[j] = st[kk * N * D];
-      dv[j] = ds[kk * D];
-    }
-    // the batch's decays first (independent of the chain), then the chain
-    double pv[KB];
-#pragma unroll
-    for (int j = 0; j < KB; ++j) pv[j] = chunk_decay(Av, dv[j]);
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      if (k0 + j < K - 1) {
-        hc = __builtin_fma(pv[j], hc, static_cast<double>(sv[j]));
-        st[(k0 + j) * N * D] = static_cast<float>(hc);
-      }
-    }
-  }
+  const double h0 = a.h0 ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype) : 0.0;
+  carry_chain<G>(a.chunk_state + (b * K * N + n) * D + d, N * D, a.chunk_dsum + b * K * D + d, D,
+                 Av, h0, K - 1, K, false);
 }
 
 // ------------------------------------------------------------------ launch
 
+template <int G>
+static hipError_t launch_fwd_carry_g(const FwdArgs& a, hipStream_t s) {
+  const int64_t nbd = (a.D + kBlock / G - 1) / (kBlock / G);
+  fwd_carry<G><<<dim3((unsigned)(a.Bn * a.N * nbd)), dim3(kBlock), 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_carry(const FwdArgs& a, hipStream_t s) {
   if (a.N <= 0 || a.K <= 1) return hipSuccess;
-  const int64_t nbd2 = (a.D + kBlock - 1) / kBlock;
-  fwd_carry<<<dim3((unsigned)(a.Bn * a.N * nbd2)), dim3(kBlock), 0, s>>>(a);
-  return hipGetLastError();
+  switch (carry_lanes(a.K - 1)) {
+    case 1: return launch_fwd_carry_g<1>(a, s);
+    case 4: return launch_fwd_carry_g<4>(a, s);
+    default: return launch_fwd_carry_g<8>(a, s);
+  }
 }
 
 hipError_t launch_fwd_tile(const FwdArgs& a, int io_dtype, int ns, hipStream_t s);

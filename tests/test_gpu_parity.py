@@ -812,6 +812,32 @@ def test_bwd_long_memory_short_chunks(chunk):
     assert not bad, bad
 
 
+@pytest.mark.parametrize("records", [16, 17, 32, 33, 64, 65, 128, 129, 300])
+def test_carry_chain_lengths(records):
+    """The chunk carries split a chain of M = K - 1 records over 1, 4 or 8
+    lanes (one lane up to 32 records, in rounds of 16; 4 lanes up to 64; 8
+    above, in rounds of 128 records past that): M at each boundary, forward
+    and backward, with h0 and a channel count that leaves part of the last
+    block of chains empty."""
+    chunk = 4
+    inp = random_inputs(2, chunk * (records + 1) - 1, 48, 16, seed=3100 + records,
+                        backward=True)
+    h0 = _state(inp, 3200 + records)
+    d = to_dev(inp)
+    say("carry chain", records, "records", tuple(inp["u"].shape))
+    y, ls = ss.fwd(*[d[k] for k in KEYS], return_last_state=True, chunk_len=chunk,
+                   h0=h0.to(DEV))
+    g = ss.bwd(*[d[k] for k in KEYS], dy=d["dy"], chunk_len=chunk, h0=h0.to(DEV))
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+    r = oracle.bwd(**{k: inp[k] for k in KEYS}, dy=inp["dy"], h0=h0)
+    errs = {"y": rel_err(to_np(y), yr), "last_state": rel_err(to_np(ls), lsr)}
+    errs.update({k: rel_err(to_np(g[k]), r[k]) for k in GRADS + ("dh0",) if r[k] is not None})
+    say("  ", {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if not v <= 1e-5}
+    assert not bad, bad
+
+
 def test_strided_bc_varlen_and_empty():
     lens = [37, 0, 130, 5, 64]
     D, N, R = 72, 16, 6
