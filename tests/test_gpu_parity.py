@@ -461,6 +461,37 @@ def test_decode_step_in_place(io, D):
     assert rel_err(to_np(state), lsr) <= max(tol, 1e-5)
 
 
+SHORT_CASES = [  # (io, param dtype, N, L, R): R = columns before B in an xdbl-like row, or None
+    ("bf16", "f32", 16, 7, 5),      # B / C rows not 4-byte aligned: element loads
+    ("bf16", "f32", 16, 16, 6),     # strided, 32-bit word loads
+    ("f16", "f32", 32, 3, None),    # 8 states per lane
+    ("f32", "f32", 8, 12, None),    # 2 states per lane: element loads
+    ("bf16", "bf16", 16, 5, None),  # 16-bit parameters
+    ("f32", "f32", 16, 1, 3),
+]
+
+
+@pytest.mark.parametrize("case", SHORT_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_short_sequence_loads(case):
+    """The short-sequence kernel (L <= 16) with its next-step prefetch and the
+    B / C word loads on and off, against the oracle, with h0."""
+    io, pa, N, L, R = case
+    inp = random_inputs(2, L, 72, N, seed=3300 + N + L, io_dtype=io, param_dtype=pa)
+    h0 = _state(inp, 3301 + L)
+    d = to_dev(inp)
+    args = {k: d[k] for k in KEYS}
+    if R is not None:
+        _, Bv, Cv = _xdbl(d["B"], d["C"], R, 3302 + R)
+        args.update(B=Bv, C=Cv)
+    say("short sequence", case)
+    y, ls = ss.fwd(**args, return_last_state=True, h0=h0.to(DEV))
+    torch.cuda.synchronize()
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+    tol = TOL[inp["u"].dtype]
+    assert rel_err(to_np(y), yr) <= tol
+    assert rel_err(to_np(ls), lsr) <= max(tol, 1e-5)
+
+
 BWD_H0_SHAPES = [((2, 150, 72, 16), "f32"), ((2, 300, 257, 16), "f32"), ((1, 47, 20, 17), "f32"),
                  ((1, 33, 10, 64), "f32"), ((2, 90, 70, 16), "bf16"), ((1, 1, 9, 16), "f32")]
 
