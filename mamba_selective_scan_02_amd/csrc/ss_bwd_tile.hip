@@ -5,8 +5,8 @@
 // recurrence of the baracuda-kernels page "src/attention/selective_scan.rs",
 // "Algorithm summary"; gradient set of its SelectiveScanBackwardArgs;
 // per-channel reverse sweep and fixed-order partial reductions as in stage B3
-// of the mamba-rs page "mamba_ssm/gpu/backward.rs").  Mapping as in the
-// forward tile kernel: 8 lanes own a channel (8 apart in the wave), lane g
+// of the mamba-rs page "mamba_ssm/gpu/backward.rs").  Mapping: 8 lanes own a
+// channel (8 apart in the wave: lane_g / lane_channel in ss_device.h), lane g
 // holds states n = g*NS .. g*NS+NS-1 (NS = 1, 2 or 4); a wave is 8 channels, a
 // 256-lane workgroup 32; per 8-step tile, lane g prepares the per-step
 // scalars of step t0 + 8j + g and hands them to the channel's lanes through

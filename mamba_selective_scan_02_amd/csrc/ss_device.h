@@ -486,9 +486,11 @@ struct BwdArgs {
 
 
 // ---------------------------------------------------------------------------
-// Lane maps and cross-lane sums of the 8-lanes-per-channel tile kernels
-// (forward and backward).  In a 256-lane workgroup, wave w's lane c + 8g is
-// lane g of channel 8w + c, so a channel's 8 lanes sit 8 apart.
+// Lane map and cross-lane sums of the 8-lanes-per-channel backward tile
+// kernels.  In a 256-lane workgroup, wave w's lane c + 8g is lane g of channel
+// 8w + c, so a channel's 8 lanes sit 8 apart.  (The forward tile kernels put a
+// channel's lanes in one row of 16 instead: wide_g / wide_channel in
+// ss_fwd_tile.hip.)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
