@@ -426,7 +426,7 @@ static hipError_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
 
 hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t s) {
   if (a.K <= 1 || a.N <= 0) return hipSuccess;
-  const int G = carry_lanes(a.K - 1);
+  const int G = carry_lanes(a.K - 1, 2 * a.Bn * a.N * a.D);
   const int64_t nbd = (a.D + kChannelsPerBlock / G - 1) / (kChannelsPerBlock / G);
   const dim3 grid((unsigned)(2 * a.Bn * a.N * nbd)), block(kChannelsPerBlock);
   switch (G) {

@@ -199,21 +199,29 @@ __device__ __forceinline__ double chunk_decay(float A, float dsum) {
 //      lane the composition of the runs before its own,
 //   3. applies that to c0 and walks its run again, writing every c_j.
 // Everything runs in double and each written value is rounded to float once.
-// The scan pays where it shortens the chain of dependent steps, from
-// M to about 2 M / G: chains of at most 2 RUN records keep one lane (G = 1:
-// step 3 alone, in rounds of RUN records whose loads are issued together),
-// longer ones take G = 4 up to 4 RUN records and 8 above; chains longer than
-// 8 RUN records take several rounds, each starting from the previous round's
-// last value.  A run's loads are unconditional (past the chain's end they
-// re-read its last record), so that they all stay in flight together.
-// Measured on the long sequence (K = 128 chunks of 2048 steps): 24 us with one
-// lane per chain, 9 us with 8; on the backward workload's 32 chunks two lanes
-// per chain were slower than one (18 against 14 us).
+// The scan pays where it shortens the chain of dependent steps, from M to
+// about 2 M / G, on a launch too small to hide that chain behind other
+// chains: chains of at most 2 RUN records, and launches whose chains fill
+// 2048 waves on one lane each, keep one lane (G = 1: step 3 alone, in rounds
+// of RUN records whose loads are issued together); otherwise G = 4 up to 4 RUN
+// records and 8 above, as far as the launch stays within 2048 waves; chains
+// longer than G RUN records take several rounds, each starting from the
+// previous round's last value.  A run's loads are unconditional (past the
+// chain's end they re-read its last record), so that they all stay in flight
+// together.  Measured: the long sequence (8192 chains of 127 records) 24 us
+// with one lane per chain, 9 us with 8; the backward workload's 32 chunks
+// with two lanes 18 against 14 us; 2x2048x2048 with N = 64 (2 x 262144 chains
+// of 255 records, a bandwidth-bound launch with one lane each) took 300 us
+// longer per backward call with 8 lanes.
 constexpr int kCarryRun = 16;    // records per lane and round, at most
 
-// Lanes per chain for a chain of M records.
-inline int carry_lanes(int64_t M) {
-  return M <= 2 * kCarryRun ? 1 : M <= 4 * kCarryRun ? 4 : 8;
+// Lanes per chain for `chains` chains of M records each.
+inline int carry_lanes(int64_t M, int64_t chains) {
+  constexpr int64_t kMaxLanes = int64_t(2048) * 64;
+  if (M <= 2 * kCarryRun) return 1;
+  const int g = M <= 4 * kCarryRun ? 4 : 8;
+  if (chains * g <= kMaxLanes) return g;
+  return chains * 4 <= kMaxLanes ? 4 : 1;
 }
 
 // v of the lane CTRL's row shift names (row_shr:k reads lane i - k of the same

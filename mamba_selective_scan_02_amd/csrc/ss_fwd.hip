@@ -54,7 +54,7 @@ static hipError_t launch_fwd_carry_g(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd_carry(const FwdArgs& a, hipStream_t s) {
   if (a.N <= 0 || a.K <= 1) return hipSuccess;
-  switch (carry_lanes(a.K - 1)) {
+  switch (carry_lanes(a.K - 1, a.Bn * a.N * a.D)) {
     case 1: return launch_fwd_carry_g<1>(a, s);
     case 4: return launch_fwd_carry_g<4>(a, s);
     default: return launch_fwd_carry_g<8>(a, s);

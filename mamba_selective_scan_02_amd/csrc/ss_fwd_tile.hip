@@ -566,13 +566,15 @@ __global__ __launch_bounds__(kBlockT, (tile_waves_per_simd<NS, MODE>())) void fw
   // pt runs (xch double buffered: one wave's LDS operations complete in
   // program order), so the exchange's LDS round trip overlaps the updates.
   // MASKED: the chunk ends inside this stage; otherwise no step is checked.
-  // With several waves per SIMD (busy), a wave raises its issue priority for
-  // the stage's last two tiles and the two barriers after them, and drops it
-  // after the stage, so that waves nearing a barrier, which hold up their
-  // workgroup, go first: 2.8B forward 322.2 -> 317.0 us and long sequence
-  // 556.5 -> 544.1 us in A/B runs; the 130M forward (under one wave per SIMD)
-  // ran 1 us slower with it, so small grids leave it off.
-  const bool busy = gridDim.x >= 1024;   // at least 4 waves per SIMD of 1024
+  // In a single pass over a grid of 5 waves per SIMD (busy: FULL, NS <= 2, a
+  // full grid), a wave raises its issue priority for the stage's last two
+  // tiles and the two barriers after them, and drops it after the stage, so
+  // that waves nearing a barrier, which hold up their workgroup, go first:
+  // 2.8B forward 325.9 -> 320.5 and 329.0 -> 323.0 us in A/B runs.  Left off
+  // elsewhere, where it measured neutral or worse: the chunked passes (long
+  // sequence -0.2 to -2.2%, 2x2048x2048 f32 +1.3%), the 130M forward (under
+  // one wave per SIMD, +1 us), N = 64 (NS = 8, 2 waves per SIMD: 379 -> 614 us).
+  const bool busy = MODE == TMODE_FULL && NS <= 2 && gridDim.x >= 1024;
   auto run_stage = [&](int st, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int left = (int)nsteps - st * TB;          // steps of the chunk from this stage on
