@@ -203,6 +203,40 @@ def time_calls(fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps, wall
 
 
+def state_sweep_leg(ss, steps: int) -> dict:
+    """Forward and backward over the state count N = 16 ... 256 on one shape
+    (B=2, L=2048, D=2048, f32, D skip / z / delta_bias, seeded inputs of the
+    usual distributions): per-update cost and its ratio to N = 16, back to
+    back after warm-up (each N picks its own kernels: the 8-lane tile kernels
+    up to N = 64 forward and 32 backward, the general ones above)."""
+    import torch
+    from ss_inputs import random_inputs
+    keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")
+    Bn, L, D = 2, 2048, 2048
+    out = {"workload": f"B={Bn}, L={L}, D={D}, f32 io and parameters, D skip, z, delta_bias, "
+                       "each N timed back to back after warm-up",
+           "per_n": {}}
+    base = None
+    for N in (16, 32, 64, 128, 256):
+        log(f"state sweep: N = {N}")
+        inp = random_inputs(Bn, L, D, N, seed=4000 + N, backward=True)
+        d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+        a = [d[k] for k in keys]
+        y = torch.empty_like(d["u"])
+        fwd_ms, _ = time_calls(lambda: ss.fwd(*a, y=y), steps, 3)
+        bwd_ms, _ = time_calls(lambda: ss.bwd(*a, dy=d["dy"]), steps, 3)
+        upd = Bn * L * D * N
+        row = {"fwd_us": fwd_ms * 1e3, "bwd_us": bwd_ms * 1e3,
+               "fwd_ps_per_update": fwd_ms * 1e9 / upd, "bwd_ps_per_update": bwd_ms * 1e9 / upd}
+        if base is None:
+            base = row
+        row["fwd_per_update_vs_n16"] = row["fwd_ps_per_update"] / base["fwd_ps_per_update"]
+        row["bwd_per_update_vs_n16"] = row["bwd_ps_per_update"] / base["bwd_ps_per_update"]
+        out["per_n"][str(N)] = row
+        del d, a, y, inp
+    return out
+
+
 def alu_roofline(updates_per_s: float, flops_per_update: int, mix=None) -> dict:
     """ALU roofline of a leg.  With mix = (transcendentals, FP32 operations)
     per update, the peak is that instruction mix's ALU peak (mix_peak_updates
@@ -544,6 +578,8 @@ def main():
                     help="time only those legs (for a kernel trace of them alone)")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the per-GPU shard shapes (D / 8 of m2p8b and bwd)")
+    ap.add_argument("--no-state-sweep", action="store_true",
+                    help="skip the forward / backward timings over N = 16 ... 256")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload warm / cold timings (and the shard shapes)")
     ap.add_argument("--configs-only", nargs="*", choices=CONFIG_NAMES + SHARD_NAMES, default=None,
@@ -761,6 +797,9 @@ def main():
             sh[name]["share_of"] = f"{full} split 8 ways over D"
             sh[name]["node_state_updates_per_s_8_gpus"] = 8 * sh[name]["state_updates_per_s_cold"]
         result["shard"] = sh
+
+    if not args.no_state_sweep:
+        result["state_sweep"] = state_sweep_leg(ss, max(5, args.steps // 2))
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

@@ -208,7 +208,7 @@ int fwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total
   if (in_place && p.K > 1)
     return fail(SS_ERR_UNSUPPORTED, "%s: an in-place state update (last_state == h0) needs a "
                 "single chunk, and this shape's rows exceed one chunk's 32-bit range", who);
-  st = check_ld(&ldb, &ldc, N, io, p.G == 8 ? p.chunk_len : 0, who);
+  st = check_ld(&ldb, &ldc, N, io, p.G == 8 && p.NS <= 8 ? p.chunk_len : 0, who);
   if (st != SS_OK) return st;
   st = check_workspace(p.ws_bytes, workspace, workspace_bytes, who);
   if (st != SS_OK) return st;
@@ -220,6 +220,8 @@ int fwd_impl(const char* who, const ss_desc* d, const int32_t* cu, int64_t total
   char* ws = static_cast<char*>(workspace);
   a.chunk_dsum = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_dsum) : nullptr;
   a.chunk_state = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_state) : nullptr;
+  a.b_pad = p.pad_rows ? ws + p.off_bpad : nullptr;
+  a.c_pad = p.pad_rows ? ws + p.off_cpad : nullptr;
   a.Bn = Bn; a.L = L; a.D = D; a.N = N;
   a.chunk_len = p.chunk_len; a.K = p.K;
   a.cu = cu; a.Lt = rows;

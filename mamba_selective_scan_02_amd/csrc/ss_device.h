@@ -443,6 +443,10 @@ struct FwdArgs {
   int64_t ldb, ldc;        // elements between consecutive rows of B / C (N when packed)
   int softplus;
   int param_dtype;
+  // General scan (N > 64) with N short of its lanes' NS * G states: B / C are
+  // first copied into rows of NS * G elements, zero past N (workspace).
+  void* b_pad;             // nullable
+  void* c_pad;             // nullable
 };
 
 // Backward launch parameters.  Workspace sub-buffers (f32):

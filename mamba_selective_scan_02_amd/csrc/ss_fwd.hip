@@ -229,6 +229,19 @@ static hipError_t launch_short(const FwdArgs& a, int ns, hipStream_t s) {
   return a.z ? launch_short_z<T, true, false>(a, ns, s) : launch_short_z<T, false, false>(a, ns, s);
 }
 
+// B and C rows (row stride ld, n elements) copied into rows of npad elements,
+// zero past n: the general scan then reads whole rows as vectors.
+template <typename W>
+__global__ void pad_bc_rows(const W* __restrict__ B, const W* __restrict__ C, W* __restrict__ Bp,
+                            W* __restrict__ Cp, int64_t rows, int64_t n, int64_t ldb, int64_t ldc,
+                            int64_t npad) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * npad) return;
+  const int64_t r = i / npad, c = i % npad;
+  Bp[i] = c < n ? B[r * ldb + c] : W(0);
+  Cp[i] = c < n ? C[r * ldc + c] : W(0);
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_t s) {
   if (gl == 4 && ns <= 8) {                     // short sequences (single chunk)
     switch (io_dtype) {
@@ -238,11 +251,31 @@ hipError_t launch_fwd(const FwdArgs& a, int io_dtype, int ns, int gl, hipStream_
     }
     return hipErrorInvalidValue;
   }
-  if (gl == 8) return launch_fwd_tile(a, io_dtype, ns, s);
+  if (gl == 8 && ns <= 8) return launch_fwd_tile(a, io_dtype, ns, s);
+  FwdArgs g = a;
+  if (a.b_pad != nullptr && a.N > 0 && a.Lt > 0) {   // N short of ns * gl: padded rows
+    const int64_t npad = (int64_t)ns * gl, total = a.Lt * npad;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (io_dtype == 0)
+      pad_bc_rows<uint32_t><<<grid, dim3(256), 0, s>>>(
+          static_cast<const uint32_t*>(a.B), static_cast<const uint32_t*>(a.C),
+          static_cast<uint32_t*>(a.b_pad), static_cast<uint32_t*>(a.c_pad), a.Lt, a.N, a.ldb,
+          a.ldc, npad);
+    else
+      pad_bc_rows<uint16_t><<<grid, dim3(256), 0, s>>>(
+          static_cast<const uint16_t*>(a.B), static_cast<const uint16_t*>(a.C),
+          static_cast<uint16_t*>(a.b_pad), static_cast<uint16_t*>(a.c_pad), a.Lt, a.N, a.ldb,
+          a.ldc, npad);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g.B = a.b_pad;
+    g.C = a.c_pad;
+    g.ldb = g.ldc = npad;
+  }
   switch (io_dtype) {
-    case 0: return launch_fwd_scan_f32(a, ns, gl, s);
-    case 1: return launch_fwd_scan_f16(a, ns, gl, s);
-    case 2: return launch_fwd_scan_bf16(a, ns, gl, s);
+    case 0: return launch_fwd_scan_f32(g, ns, gl, s);
+    case 1: return launch_fwd_scan_f16(g, ns, gl, s);
+    case 2: return launch_fwd_scan_bf16(g, ns, gl, s);
   }
   return hipErrorInvalidValue;
 }

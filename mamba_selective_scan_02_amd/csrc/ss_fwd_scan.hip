@@ -11,24 +11,26 @@
 
 namespace ss {
 
-// EXACT (N fills the bucket) reads whole B / C rows; for 16-bit types that
-// needs 4-byte aligned rows: 4-byte aligned B and C and even row strides.
+// EXACT (N fills the bucket, or B / C were copied into padded rows) reads
+// whole B / C rows; for 16-bit types that needs 4-byte aligned rows: 4-byte
+// aligned B and C and even row strides.
 template <typename T, int NS, int G>
 static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t s) {
   const bool rows_ok = sizeof(T) == 4 || ((reinterpret_cast<uintptr_t>(a.B) % 4 == 0) &&
                                           (reinterpret_cast<uintptr_t>(a.C) % 4 == 0) &&
                                           a.ldb % 2 == 0 && a.ldc % 2 == 0);
-  const bool exact = a.N == (int64_t)NS * G && rows_ok;
+  const bool padded = a.b_pad != nullptr && a.B == a.b_pad;
+  const bool exact = (a.N == (int64_t)NS * G || padded) && rows_ok;
   if (a.z != nullptr)
     return exact ? launch_fwd_t<T, NS, G, true, true>(a, s) : launch_fwd_t<T, NS, G, false, true>(a, s);
   return exact ? launch_fwd_t<T, NS, G, true, false>(a, s) : launch_fwd_t<T, NS, G, false, false>(a, s);
 }
 
-// G = 2 (N <= 128) or 4 lanes per channel, 64 states per lane.
+// G = 8 (N <= 128) or 16 lanes per channel, 16 states per lane.
 template <typename T>
 static hipError_t launch_fwd_ty(const FwdArgs& a, int ns, int gl, hipStream_t s) {
-  if (ns == 64 && gl == 2) return launch_fwd_e<T, 64, 2>(a, s);
-  if (ns == 64 && gl == 4) return launch_fwd_e<T, 64, 4>(a, s);
+  if (ns == 16 && gl == 8) return launch_fwd_e<T, 16, 8>(a, s);
+  if (ns == 16 && gl == 16) return launch_fwd_e<T, 16, 16>(a, s);
   return hipErrorInvalidValue;
 }
 

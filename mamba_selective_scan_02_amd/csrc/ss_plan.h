@@ -38,6 +38,8 @@ struct Plan {
   // workspace (bytes, 256-aligned offsets)
   size_t off_dsum = 0, off_state = 0, off_bstate = 0, off_part_bc = 0, off_part_dA = 0,
          off_part_dD = 0, off_part_db = 0;
+  size_t off_bpad = 0, off_cpad = 0;   // forward, N > 64 short of NS * G: padded B / C rows
+  bool pad_rows = false;
   size_t ws_bytes = 0;
   int64_t KG = 0, nwgd = 0;   // backward: chunk groups, channel blocks
   bool bwd_tile = false;      // backward: 8-lanes-per-channel tile kernels (N <= 32)
@@ -46,15 +48,16 @@ struct Plan {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Forward mapping by state count: N <= 64 uses 8 lanes per channel with NS
-// states each (the tile kernels; NS = 8 runs 2 waves per SIMD); larger N one
-// lane per channel with 64 states (G = 2 or 4 lanes above 64 states).
+// states each (the tile kernels; NS = 8 runs 2 waves per SIMD); larger N the
+// general scan with 16 states per lane, G = 8 (N <= 128) or 16 lanes per
+// channel.
 inline void pick_bucket(int64_t N, int* NS, int* G) {
   if (N <= 8) { *NS = 1; *G = 8; }
   else if (N <= 16) { *NS = 2; *G = 8; }
   else if (N <= 32) { *NS = 4; *G = 8; }
   else if (N <= 64) { *NS = 8; *G = 8; }
-  else if (N <= 128) { *NS = 64; *G = 2; }
-  else { *NS = 64; *G = 4; }
+  else if (N <= 128) { *NS = 16; *G = 8; }
+  else { *NS = 16; *G = 16; }
 }
 
 // Forward sequences of at most this many steps (decode steps) with N <= 32
@@ -122,8 +125,20 @@ inline Plan make_plan(const ss_desc& d, bool backward) {
       p.off_state = off;
       off = align256(off + sizeof(float) * (size_t)(Bn * p.K * N * D));
     }
+    // The general scan reads whole B / C rows of NS * G elements as vectors;
+    // a shorter N gets them copied into such rows first (zero past N): with
+    // element loads instead, N = 100 ran 2.6x slower per update than N = 128.
+    const int64_t npad = (int64_t)p.NS * p.G;
+    if (!short_seq && N > 64 && N != npad) {
+      const size_t es = d.io_dtype == 0 ? 4 : 2;
+      p.pad_rows = true;
+      p.off_bpad = off;
+      off = align256(off + es * (size_t)(Bn * L * npad));
+      p.off_cpad = off;
+      off = align256(off + es * (size_t)(Bn * L * npad));
+    }
     p.ws_bytes = off;
-    p.n_launches = p.K > 1 ? (N > 0 ? 3 : 2) : 1;
+    p.n_launches = (p.K > 1 ? (N > 0 ? 3 : 2) : 1) + (p.pad_rows ? 1 : 0);
     return p;
   }
   // backward.  N <= 32: tile kernels, chunks of up to 64 steps (32 above

@@ -281,10 +281,15 @@ def test_plan_is_a_function_of_shape():
     assert (p.chunk_len, p.n_chunks) == (7, 15)
     # N buckets
     for n, (ns, g) in {0: (1, 8), 1: (1, 8), 5: (1, 8), 9: (2, 8), 16: (2, 8), 17: (4, 8),
-                       32: (4, 8), 33: (8, 8), 64: (8, 8), 65: (64, 2), 200: (64, 4),
-                       256: (64, 4)}.items():
+                       32: (4, 8), 33: (8, 8), 64: (8, 8), 65: (16, 8), 128: (16, 8),
+                       200: (16, 16), 256: (16, 16)}.items():
         p = ss.plan(_desc(N=n))
         assert (p.states_per_lane, p.lanes_per_channel) == (ns, g), n
+    # N > 64 short of its lanes' states: B / C copied into padded rows first
+    # (one more launch, two [B * L, NS * G] buffers in the workspace)
+    d100, d128 = _desc(B=2, L=300, D=64, N=100), _desc(B=2, L=300, D=64, N=128)
+    assert ss.plan(d100).n_launches == ss.plan(d128).n_launches + 1
+    assert ss.ss_workspace_size(d100, 0) >= 2 * (2 * 300 * 128 * 4)
     # backward: N <= 16 uses the tile kernels with chunks of 64 steps, N <= 32
     # the tile kernels with 4 states per lane and chunks of 32 steps, larger N
     # the general kernels with chunks of 8 steps

@@ -461,6 +461,36 @@ def test_decode_step_in_place(io, D):
     assert rel_err(to_np(state), lsr) <= max(tol, 1e-5)
 
 
+PADDED_CASES = [  # (B, L, D, N, io, R, chunk): N > 64 short of its lanes' states
+    (2, 150, 40, 100, "f32", None, 0), (1, 90, 24, 200, "bf16", None, 16),
+    (2, 70, 33, 65, "f16", 5, 0), (1, 130, 20, 129, "f32", 3, 24),
+]
+
+
+@pytest.mark.parametrize("case", PADDED_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fwd_padded_rows(case):
+    """The general forward copies B / C into rows of NS * G elements (zero past
+    N) when N falls short of them: against the oracle with h0, strided B / C
+    and forced chunks, and equal to the packed call bit for bit."""
+    Bn, L, D, N, io, R, chunk = case
+    inp = random_inputs(Bn, L, D, N, seed=3400 + N + L, io_dtype=io)
+    h0 = _state(inp, 3401 + D)
+    d = to_dev(inp)
+    args = {k: d[k] for k in KEYS}
+    say("padded rows", case)
+    y0, l0 = ss.fwd(**args, return_last_state=True, chunk_len=chunk, h0=h0.to(DEV))
+    if R is not None:
+        _, Bv, Cv = _xdbl(d["B"], d["C"], R, 3402 + R)
+        args.update(B=Bv, C=Cv)
+    y1, l1 = ss.fwd(**args, return_last_state=True, chunk_len=chunk, h0=h0.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(l0, l1)
+    yr, lsr = oracle.fwd(**{k: inp[k] for k in KEYS}, return_last_state=True, h0=h0)
+    tol = TOL[inp["u"].dtype]
+    assert rel_err(to_np(y1), yr) <= tol
+    assert rel_err(to_np(l1), lsr) <= max(tol, 1e-5)
+
+
 SHORT_CASES = [  # (io, param dtype, N, L, R): R = columns before B in an xdbl-like row, or None
     ("bf16", "f32", 16, 7, 5),      # B / C rows not 4-byte aligned: element loads
     ("bf16", "f32", 16, 16, 6),     # strided, 32-bit word loads
