@@ -382,53 +382,13 @@ __device__ __forceinline__ void finalize_d(const BwdArgs& a, int64_t i) {
   }
 }
 
-// finalize_bc for 4 consecutive states per thread (N a multiple of 4: the
-// partial rows are 16-byte aligned), i = row * N / 4 + n / 4; the same sums in
-// the same order, read as float4.
-template <typename Tio>
-__device__ __forceinline__ void finalize_bc4(const BwdArgs& a, int64_t i) {
-  const int64_t N = a.N, N4 = N / 4;
-  if (i >= a.Lt * N4) return;
-  const int64_t bt = i / N4, n = (i % N4) * 4;
-  const float4* p = reinterpret_cast<const float4*>(a.part_bc + bt * a.nwgd * 2 * N + n);
-  const int64_t st = 2 * N4;                      // float4s between channel blocks
-  float4 sb = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sc = sb;
-  constexpr int U = 8;
-  int64_t w = 0;
-  for (; w + U <= a.nwgd; w += U) {
-    float4 vb[U], vc[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      vb[j] = p[(w + j) * st];
-      vc[j] = p[(w + j) * st + N4];
-    }
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      sb.x += vb[j].x; sb.y += vb[j].y; sb.z += vb[j].z; sb.w += vb[j].w;
-      sc.x += vc[j].x; sc.y += vc[j].y; sc.z += vc[j].z; sc.w += vc[j].w;
-    }
-  }
-  for (; w < a.nwgd; ++w) {
-    const float4 vb = p[w * st], vc = p[w * st + N4];
-    sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
-    sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
-  }
-  Tio* dB = static_cast<Tio*>(a.dB) + bt * a.ldb + n;
-  Tio* dC = static_cast<Tio*>(a.dC) + bt * a.ldc + n;
-  dB[0] = from_f32<Tio>(sb.x); dB[1] = from_f32<Tio>(sb.y);
-  dB[2] = from_f32<Tio>(sb.z); dB[3] = from_f32<Tio>(sb.w);
-  dC[0] = from_f32<Tio>(sc.x); dC[1] = from_f32<Tio>(sc.y);
-  dC[2] = from_f32<Tio>(sc.z); dC[3] = from_f32<Tio>(sc.w);
-}
-
 // Both finalizes in one launch: the first nbd blocks sum the per-channel
 // partials (few threads, each a chain of dependent-address loads, so they
-// start first), the rest the dB / dC partials (VEC4: 4 states per thread).
-template <typename Tio, bool VEC4>
+// start first), the rest the dB / dC partials.
+template <typename Tio>
 __global__ void bwd_finalize(const BwdArgs a, int64_t nbd) {
   const int64_t blk = blockIdx.x;
   if (blk < nbd) finalize_d(a, blk * blockDim.x + threadIdx.x);
-  else if (VEC4) finalize_bc4<Tio>(a, (blk - nbd) * blockDim.x + threadIdx.x);
   else finalize_bc<Tio>(a, (blk - nbd) * blockDim.x + threadIdx.x);
 }
 
@@ -477,26 +437,16 @@ hipError_t launch_bwd_carry(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool VEC4>
-static void launch_finalize_v(const BwdArgs& a, dim3 grid, int64_t nbd, hipStream_t s) {
-  switch (a.io_dtype) {
-    case 0: bwd_finalize<float, VEC4><<<grid, dim3(256), 0, s>>>(a, nbd); break;
-    case 1: bwd_finalize<f16_t, VEC4><<<grid, dim3(256), 0, s>>>(a, nbd); break;
-    default: bwd_finalize<bf16_t, VEC4><<<grid, dim3(256), 0, s>>>(a, nbd); break;
-  }
-}
-
 hipError_t launch_bwd_finalize(const BwdArgs& a, hipStream_t s) {
   const int64_t nd = (a.N > 0 ? a.N : 1) * a.D;
   const int64_t nbd = (nd + 255) / 256;
-  // the partial rows are 16-byte aligned when N is a multiple of 4 (the
-  // workspace offsets are 256-byte aligned)
-  const bool vec4 = a.N > 0 && a.N % 4 == 0 &&
-                    (reinterpret_cast<uintptr_t>(a.part_bc) & 15) == 0;
-  const int64_t nbc = (a.Lt * (vec4 ? a.N / 4 : a.N) + 255) / 256;
+  const int64_t nbc = (a.Lt * a.N + 255) / 256;
   const dim3 grid((unsigned)(nbd + nbc));
-  if (vec4) launch_finalize_v<true>(a, grid, nbd, s);
-  else launch_finalize_v<false>(a, grid, nbd, s);
+  switch (a.io_dtype) {
+    case 0: bwd_finalize<float><<<grid, dim3(256), 0, s>>>(a, nbd); break;
+    case 1: bwd_finalize<f16_t><<<grid, dim3(256), 0, s>>>(a, nbd); break;
+    default: bwd_finalize<bf16_t><<<grid, dim3(256), 0, s>>>(a, nbd); break;
+  }
   return hipGetLastError();
 }
 
