@@ -118,14 +118,14 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
 
   bstage<T, NP, BTC, BTS>(sB, sC, B_in, C_in, P.start + P.t0, nsteps, N, a.ldb, a.ldc);
 
-  // Sb is built two-level: per tile, sbl = sum_s (prod_{r<=s} a_r) g_s C_s over
-  // the tile's steps, run backwards from zero at the tile's end (sbl <-
-  // a_s (g_s C_s + sbl): two operations per update, the form the main
-  // kernel's tile-level reset uses), and then Sb += (decay of the chunk's
-  // earlier tiles) * sbl, the decay of a tile being exp2(A2 * sum of its dt);
-  // a product of per-step decays over 64 steps would drift by one rounding
-  // per step.  (A forward running product E_s and sbl += E_s g_s C_s took
-  // three operations per update: 225.5 -> 222.8 us per backward call.)
+  // Sb is built two-level: per tile from its own start (E, sbl) and then
+  // Sb += (decay of the chunk's earlier tiles) * sbl, the decay of a tile
+  // being exp2(A2 * sum of its dt); a product of per-step decays over 64 steps
+  // would drift by one rounding per step.  (Running sbl backwards from the
+  // tile's end, sbl <- a_s (g_s C_s + sbl), takes two operations per update
+  // instead of three, but holds the tile's decays and C in registers: 95
+  // instead of 73 VGPRs, 5 instead of 6 waves per SIMD, and no faster in a
+  // kernel-level A/B: 53.5 / 52.9 against 54.4 / 53.2 us.)
   float A2[NS], h[NS], Sb[NS], PP[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -176,43 +176,40 @@ __global__ __launch_bounds__(kBT) void bwd_tile_sum(const T* __restrict__ u_in,
     float4 ex[BGL];
 #pragma unroll
     for (int s = 0; s < BGL; ++s) ex[s] = xch[cl][s];
-    // forward over the tile (h), then its reverse summary from zero at the
-    // tile's end, step by step backwards: sbl = a_s (g_s C_s + sbl)
-    float ea[2][4 * NS];                   // the tile's decays, one run per half
-    float cv[BGL][NS];
+    float E[NS], sbl[NS];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int sh = 4 * hf;
+    for (int i = 0; i < NS; ++i) {
+      E[i] = 1.0f;
+      sbl[i] = 0.0f;
+    }
+#pragma unroll
+    for (int sh = 0; sh < BGL; sh += 4) {
       float4 bq[NS], cq[NS];
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         bq[i] = *reinterpret_cast<const float4*>(&sB[n0 + i][j * BGL + sh]);
         cq[i] = *reinterpret_cast<const float4*>(&sC[n0 + i][j * BGL + sh]);
-        cv[sh][i] = cq[i].x; cv[sh + 1][i] = cq[i].y; cv[sh + 2][i] = cq[i].z; cv[sh + 3][i] = cq[i].w;
       }
+      float ea[4 * NS];                    // the half tile's decays as one run
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss)
 #pragma unroll
-        for (int i = 0; i < NS; ++i) ea[hf][ss * NS + i] = ex[sh + ss].x * A2[i];
-      exp2_run(ea[hf]);
+        for (int i = 0; i < NS; ++i) ea[ss * NS + i] = ex[sh + ss].x * A2[i];
+      exp2_run(ea);
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss) {
         const float4 e = ex[sh + ss];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
           const float bvs = ss == 0 ? bq[i].x : ss == 1 ? bq[i].y : ss == 2 ? bq[i].z : bq[i].w;
-          h[i] = __builtin_fmaf(ea[hf][ss * NS + i], h[i], e.y * bvs);
+          const float cvs = ss == 0 ? cq[i].x : ss == 1 ? cq[i].y : ss == 2 ? cq[i].z : cq[i].w;
+          const float av = ea[ss * NS + i];
+          h[i] = __builtin_fmaf(av, h[i], e.y * bvs);
+          E[i] *= av;
+          sbl[i] = __builtin_fmaf(E[i], e.z * cvs, sbl[i]);
         }
       }
     }
-    float sbl[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) sbl[i] = 0.0f;
-#pragma unroll
-    for (int s = BGL - 1; s >= 0; --s)
-#pragma unroll
-      for (int i = 0; i < NS; ++i)
-        sbl[i] = ea[s / 4][(s % 4) * NS + i] * __builtin_fmaf(ex[s].z, cv[s][i], sbl[i]);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       Sb[i] = __builtin_fmaf(PP[i], sbl[i], Sb[i]);
