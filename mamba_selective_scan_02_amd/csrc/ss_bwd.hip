@@ -229,13 +229,25 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_main(const BwdArgs a) {
     }
     __syncthreads();  // tile visible
 
+    // each state's A, carried-in state and carried adjoint, loaded one state
+    // ahead (the loop's barriers would otherwise leave each state waiting for
+    // its own loads)
+    auto state_in = [&](int64_t n, float& An_, float& hin_, float& dh_) {
+      const int64_t nn = n < N ? n : N - 1;
+      An_ = ld_param(a.A, d * N + nn, a.param_dtype);
+      hin_ = (k > 0)  ? a.fstate[((b * K + (k - 1)) * N + nn) * D + d]
+             : a.h0   ? ld_param(a.h0, (b * D + d) * N + nn, a.param_dtype)
+                      : 0.0f;
+      dh_ = (k < K - 1) ? a.bstate[((b * K + (k + 1)) * N + nn) * D + d] : 0.0f;
+    };
+    float nA = 0.0f, nh = 0.0f, nd = 0.0f;
+    if (N > 0) state_in(0, nA, nh, nd);
     for (int64_t n = 0; n < N; ++n) {
-      const float An = ld_param(a.A, d * N + n, a.param_dtype);
+      const float An = nA;
       const float A2 = An * kLog2e;
-      const float hin = (k > 0)  ? a.fstate[((b * K + (k - 1)) * N + n) * D + d]
-                        : a.h0   ? ld_param(a.h0, (b * D + d) * N + n, a.param_dtype)
-                                 : 0.0f;
-      float dh = (k < K - 1) ? a.bstate[((b * K + (k + 1)) * N + n) * D + d] : 0.0f;
+      const float hin = nh;
+      float dh = nd;
+      state_in(n + 1, nA, nh, nd);
       const float* bn = sB + n * T;
       const float* cn = sC + n * T;
       float hs[T], ah[T];
