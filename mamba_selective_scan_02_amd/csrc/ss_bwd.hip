@@ -109,8 +109,12 @@ __global__ __launch_bounds__(kChannelsPerBlock) void bwd_summary(const BwdArgs a
   }
   __syncthreads();
 
+  // each state's A loaded one state ahead (a load at the top of the
+  // iteration would hold the state's whole update chain)
+  float nA = N > 0 ? ld_param(a.A, d * N, a.param_dtype) : 0.0f;
   for (int64_t n = 0; n < N; ++n) {
-    const float A2 = ld_param(a.A, d * N + n, a.param_dtype) * kLog2e;
+    const float A2 = nA * kLog2e;
+    nA = ld_param(a.A, d * N + (n + 1 < N ? n + 1 : n), a.param_dtype);
     const float* bn = sB + n * T;
     const float* cn = sC + n * T;
     float h = 0.0f, E = 1.0f, Sb = 0.0f;
